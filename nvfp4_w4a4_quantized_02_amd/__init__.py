@@ -1,0 +1,205 @@
+"""NVFP4 W4A4 linear layer for AMD Instinct MI355X (gfx950).
+
+Thin Python binding over the C ABI in ``include/nvfp4.h`` (library
+``libnvfp4.so`` built from ``csrc/``).  The binding only marshals arguments:
+PyTorch provides device memory and the current stream, and every step of the
+computation runs in the HIP kernels.  If the library is missing the import
+fails; there is no fallback.
+
+Entry points (same names as the C ABI):
+
+* ``nvfp4_quantize(x)`` -> ``(codes, scales, gs)``: on-the-fly NVFP4
+  quantization (paper "Why Gated DeltaNet Survives 4-Bit Quantization",
+  section 2 "NVFP4").
+* ``nvfp4_dequantize(codes, scales, gs, out_dtype)``: two-level dequant.
+* ``nvfp4_fuse_rescale(scales_list, gs_list)`` -> ``gs_shared``: the
+  fused-module repair (same paper, section 6), in place.
+* ``nvfp4_gemm(x, w_codes, w_scales, w_gs, out_dtype)``: the W4A4 linear
+  ``Y = X W^T`` with X quantized on the fly.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch  # loads the HIP runtime the library must share with PyTorch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libnvfp4.so")
+
+NVFP4_F32 = 0
+NVFP4_BF16 = 1
+MAX_FUSED = 16
+
+_STATUS = {
+    0: "NVFP4_OK", 1: "NVFP4_ERR_NULL", 2: "NVFP4_ERR_SHAPE", 3: "NVFP4_ERR_DTYPE",
+    4: "NVFP4_ERR_ALIGN", 5: "NVFP4_ERR_WORKSPACE", 6: "NVFP4_ERR_INVALID", 7: "NVFP4_ERR_DEVICE",
+}
+
+# Every symbol include/nvfp4.h declares.
+EXPORTS = (
+    "nvfp4_status_string", "nvfp4_version", "nvfp4_quantize_workspace_size", "nvfp4_quantize",
+    "nvfp4_dequantize", "nvfp4_fuse_rescale", "nvfp4_gemm_workspace_size", "nvfp4_gemm",
+)
+
+
+class Nvfp4Error(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__("%s: %s (%s)" % (where, _STATUS.get(status, "?"), status_string(status)))
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError("libnvfp4.so is not built; run `python -m nvfp4_w4a4_quantized_02_amd.build` "
+                          "(or __graft_entry__.build())")
+    L = ctypes.CDLL(LIB_PATH)
+    P, I64, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t
+    I = ctypes.c_int
+    L.nvfp4_status_string.argtypes = [I]
+    L.nvfp4_status_string.restype = ctypes.c_char_p
+    L.nvfp4_version.restype = I
+    L.nvfp4_quantize_workspace_size.argtypes = [I64, I64]
+    L.nvfp4_quantize_workspace_size.restype = SZ
+    L.nvfp4_quantize.argtypes = [P, I, I64, I64, I64, P, P, P, P, SZ, P]
+    L.nvfp4_quantize.restype = I
+    L.nvfp4_dequantize.argtypes = [P, P, P, I64, I64, P, I, I64, P]
+    L.nvfp4_dequantize.restype = I
+    L.nvfp4_fuse_rescale.argtypes = [I, ctypes.POINTER(P), ctypes.POINTER(I64), I64, ctypes.POINTER(P), P, P]
+    L.nvfp4_fuse_rescale.restype = I
+    L.nvfp4_gemm_workspace_size.argtypes = [I64, I64, I64]
+    L.nvfp4_gemm_workspace_size.restype = SZ
+    L.nvfp4_gemm.argtypes = [P, I, I64, I64, I64, P, P, P, I64, P, I, I64, P, SZ, P]
+    L.nvfp4_gemm.restype = I
+    _check_single_hip_runtime()
+    return L
+
+
+def _check_single_hip_runtime():
+    """The library must use the HIP runtime PyTorch loaded; two copies in one
+    process would not share streams or device pointers."""
+    try:
+        with open("/proc/self/maps") as f:
+            paths = {line.split()[-1] for line in f if "libamdhip64" in line}
+    except OSError:
+        return
+    real = {os.path.realpath(p) for p in paths}
+    if len(real) > 1:
+        raise ImportError("two HIP runtimes are loaded (%s); import torch before libnvfp4" % sorted(real))
+
+
+lib = _load()
+
+
+def status_string(status: int) -> str:
+    return lib.nvfp4_status_string(status).decode()
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise Nvfp4Error(status, where)
+
+
+def _dtype_code(dt: torch.dtype) -> int:
+    if dt == torch.float32:
+        return NVFP4_F32
+    if dt == torch.bfloat16:
+        return NVFP4_BF16
+    raise TypeError("supported dtypes are float32 and bfloat16, got %s" % dt)
+
+
+def _stream_ptr(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+_workspaces: dict = {}
+
+
+def workspace(nbytes: int, device) -> torch.Tensor:
+    """A per-device scratch buffer of at least nbytes (256-byte aligned).
+    Calls that use it are ordered on the current stream."""
+    dev = torch.device(device)
+    key = (dev.type, dev.index)
+    ws = _workspaces.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.empty(max(nbytes, 1 << 16), dtype=torch.uint8, device=dev)
+        assert ws.data_ptr() % 256 == 0
+        _workspaces[key] = ws
+    return ws
+
+
+def _rows_view(x: torch.Tensor) -> tuple:
+    if x.dim() != 2:
+        raise ValueError("expected a 2-D tensor, got shape %s" % (tuple(x.shape),))
+    if x.stride(1) != 1:
+        raise ValueError("the last dimension must be contiguous")
+    return x.shape[0], x.shape[1], x.stride(0) if x.shape[0] > 1 else max(x.shape[1], x.stride(0))
+
+
+def nvfp4_quantize(x: torch.Tensor):
+    """Quantize a [rows, K] float32/bfloat16 CUDA tensor.
+
+    Returns (codes uint8 [rows, K/2], scales uint8 [rows, K/16], gs float32 [1])."""
+    rows, K, ld = _rows_view(x)
+    codes = torch.empty((rows, K // 2), dtype=torch.uint8, device=x.device)
+    scales = torch.empty((rows, K // 16), dtype=torch.uint8, device=x.device)
+    gs = torch.empty(1, dtype=torch.float32, device=x.device)
+    nws = lib.nvfp4_quantize_workspace_size(rows, K)
+    ws = workspace(nws, x.device)
+    _check(lib.nvfp4_quantize(x.data_ptr(), _dtype_code(x.dtype), rows, K, ld, codes.data_ptr(),
+                              scales.data_ptr(), gs.data_ptr(), ws.data_ptr(), ws.numel(),
+                              _stream_ptr(x.device)), "nvfp4_quantize")
+    return codes, scales, gs
+
+
+def nvfp4_dequantize(codes: torch.Tensor, scales: torch.Tensor, gs: torch.Tensor,
+                     out_dtype: torch.dtype = torch.float32) -> torch.Tensor:
+    rows, half = codes.shape
+    K = 2 * half
+    out = torch.empty((rows, K), dtype=out_dtype, device=codes.device)
+    _check(lib.nvfp4_dequantize(codes.data_ptr(), scales.data_ptr(), gs.data_ptr(), rows, K, out.data_ptr(),
+                                _dtype_code(out_dtype), K, _stream_ptr(codes.device)), "nvfp4_dequantize")
+    return out
+
+
+def nvfp4_fuse_rescale(scales_list, gs_list) -> torch.Tensor:
+    """Repair a fused group in place; returns the shared tensor scale [1]."""
+    n = len(scales_list)
+    if not 1 <= n <= MAX_FUSED or len(gs_list) != n:
+        raise ValueError("need 1..%d members with one tensor scale each" % MAX_FUSED)
+    kb = scales_list[0].shape[1]
+    for s in scales_list:
+        if s.dim() != 2 or s.shape[1] != kb or not s.is_contiguous() or s.dtype != torch.uint8:
+            raise ValueError("member scales must be contiguous uint8 [rows, K/16] with one K")
+    dev = scales_list[0].device
+    shared = torch.empty(1, dtype=torch.float32, device=dev)
+    ptrs = (ctypes.c_void_p * n)(*[s.data_ptr() for s in scales_list])
+    rows = (ctypes.c_int64 * n)(*[s.shape[0] for s in scales_list])
+    gptrs = (ctypes.c_void_p * n)(*[g.data_ptr() for g in gs_list])
+    _check(lib.nvfp4_fuse_rescale(n, ptrs, rows, kb, gptrs, shared.data_ptr(), _stream_ptr(dev)),
+           "nvfp4_fuse_rescale")
+    return shared
+
+
+def nvfp4_gemm(x: torch.Tensor, w_codes: torch.Tensor, w_scales: torch.Tensor, w_gs: torch.Tensor,
+               out_dtype: torch.dtype = torch.bfloat16, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Y = X W^T with X [M, K] quantized on the fly and W given as NVFP4
+    (codes [N, K/2], scales [N, K/16], w_gs [1])."""
+    M, K, ld = _rows_view(x)
+    N = w_codes.shape[0]
+    if w_codes.shape[1] * 2 != K or w_scales.shape != (N, K // 16):
+        raise ValueError("weight shapes %s / %s do not match K=%d" % (tuple(w_codes.shape),
+                                                                       tuple(w_scales.shape), K))
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=x.device)
+    nws = lib.nvfp4_gemm_workspace_size(M, N, K)
+    ws = workspace(nws, x.device)
+    _check(lib.nvfp4_gemm(x.data_ptr(), _dtype_code(x.dtype), M, K, ld, w_codes.data_ptr(),
+                          w_scales.data_ptr(), w_gs.data_ptr(), N, out.data_ptr(), _dtype_code(out.dtype),
+                          out.stride(0) if M > 1 else max(N, out.stride(0)), ws.data_ptr(), ws.numel(),
+                          _stream_ptr(x.device)), "nvfp4_gemm")
+    return out
+
+
+__all__ = ["nvfp4_quantize", "nvfp4_dequantize", "nvfp4_fuse_rescale", "nvfp4_gemm", "Nvfp4Error",
+           "status_string", "lib", "EXPORTS", "LIB_PATH", "workspace"]

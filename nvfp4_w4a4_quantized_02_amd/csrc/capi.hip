@@ -1,0 +1,173 @@
+// C ABI of the library (declared in include/nvfp4.h): argument checks,
+// workspace carving and kernel launches.  Nothing here allocates memory or
+// synchronizes; every failure is reported before anything is launched.
+#include "../../include/nvfp4.h"
+
+#include <hip/hip_runtime.h>
+
+#include "launch.h"
+
+using namespace nvfp4;
+
+namespace {
+
+constexpr int64_t kMaxDim = (int64_t)1 << 31;  // per-dimension limit
+constexpr uint64_t kMaxBlocks = (uint64_t)1 << 31;
+
+inline bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+inline int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
+inline size_t esize(nvfp4_dtype_t t) { return t == NVFP4_BF16 ? 2u : 4u; }
+inline bool dtype_ok(nvfp4_dtype_t t) { return t == NVFP4_F32 || t == NVFP4_BF16; }
+
+nvfp4_status_t launched() {
+  hipError_t e = hipGetLastError();
+  return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_DEVICE;
+}
+
+// Shared checks for a [rows, K] activation/weight input with leading dim ld.
+nvfp4_status_t check_input(const void* x, nvfp4_dtype_t dt, int64_t rows, int64_t K, int64_t ld) {
+  if (!dtype_ok(dt)) return NVFP4_ERR_DTYPE;
+  if (rows < 0 || K < 0 || rows >= kMaxDim || K >= kMaxDim) return NVFP4_ERR_SHAPE;
+  if (K % 16 != 0) return NVFP4_ERR_SHAPE;
+  if (rows > 0 && K > 0) {
+    if (!x) return NVFP4_ERR_NULL;
+    if (ld < K) return NVFP4_ERR_SHAPE;
+    if (!aligned(x, 16) || ((uint64_t)ld * esize(dt)) % 16 != 0) return NVFP4_ERR_ALIGN;
+    // chunk indices (16 bytes) and block indices must fit 32 bits
+    if ((uint64_t)rows * (uint64_t)(K / 16) * 4u >= kMaxBlocks) return NVFP4_ERR_SHAPE;
+    if ((uint64_t)rows * (uint64_t)ld * esize(dt) / 16u >= ((uint64_t)1 << 32)) return NVFP4_ERR_SHAPE;
+  }
+  return NVFP4_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* nvfp4_status_string(nvfp4_status_t s) {
+  switch (s) {
+    case NVFP4_OK: return "ok";
+    case NVFP4_ERR_NULL: return "required pointer is NULL";
+    case NVFP4_ERR_SHAPE: return "invalid shape or leading dimension";
+    case NVFP4_ERR_DTYPE: return "unsupported dtype";
+    case NVFP4_ERR_ALIGN: return "pointer or leading dimension not 16-byte aligned";
+    case NVFP4_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+    case NVFP4_ERR_INVALID: return "invalid argument";
+    case NVFP4_ERR_DEVICE: return "HIP launch failed";
+  }
+  return "unknown status";
+}
+
+int nvfp4_version(void) { return 100; }
+
+size_t nvfp4_quantize_workspace_size(int64_t rows, int64_t K) {
+  (void)rows;
+  (void)K;
+  return kMaxPartials * sizeof(uint32_t);
+}
+
+nvfp4_status_t nvfp4_quantize(const void* x, nvfp4_dtype_t x_dtype, int64_t rows, int64_t K, int64_t ld_x,
+                              uint8_t* codes, uint8_t* scales, float* gs, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  nvfp4_status_t st = check_input(x, x_dtype, rows, K, ld_x);
+  if (st != NVFP4_OK) return st;
+  if (!gs) return NVFP4_ERR_NULL;
+  hipStream_t s = (hipStream_t)stream;
+  if (rows == 0 || K == 0) {
+    launch_fill_f32(gs, 0.0f, s);
+    return launched();
+  }
+  if (!codes || !scales) return NVFP4_ERR_NULL;
+  if (!aligned(codes, 8)) return NVFP4_ERR_ALIGN;
+  if (!workspace || !aligned(workspace, 256) ||
+      workspace_bytes < nvfp4_quantize_workspace_size(rows, K))
+    return NVFP4_ERR_WORKSPACE;
+  uint32_t* partials = (uint32_t*)((char*)workspace + kWsPartials);
+  int np = launch_amax(x, x_dtype == NVFP4_BF16, rows, K, ld_x, partials, s);
+  launch_quantize_packed(x, x_dtype == NVFP4_BF16, rows, K, ld_x, partials, np, codes, scales, gs, s);
+  return launched();
+}
+
+nvfp4_status_t nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales, const float* gs, int64_t rows,
+                                int64_t K, void* out, nvfp4_dtype_t out_dtype, int64_t ld_out, void* stream) {
+  if (!dtype_ok(out_dtype)) return NVFP4_ERR_DTYPE;
+  if (rows < 0 || K < 0 || rows >= kMaxDim || K >= kMaxDim || K % 16 != 0) return NVFP4_ERR_SHAPE;
+  if (rows == 0 || K == 0) return NVFP4_OK;
+  if (!codes || !scales || !gs || !out) return NVFP4_ERR_NULL;
+  if (ld_out < K) return NVFP4_ERR_SHAPE;
+  if ((uint64_t)rows * (uint64_t)(K / 8) >= kMaxBlocks) return NVFP4_ERR_SHAPE;
+  if (!aligned(codes, 4) || !aligned(out, 16) || ((uint64_t)ld_out * esize(out_dtype)) % 16 != 0)
+    return NVFP4_ERR_ALIGN;
+  launch_dequant(codes, scales, gs, rows, K, out, out_dtype == NVFP4_BF16, ld_out, (hipStream_t)stream);
+  return launched();
+}
+
+nvfp4_status_t nvfp4_fuse_rescale(int n, uint8_t* const* scales, const int64_t* rows, int64_t k_blocks,
+                                  const float* const* gs_in, float* gs_shared, void* stream) {
+  if (n < 1 || n > NVFP4_MAX_FUSED) return NVFP4_ERR_INVALID;
+  if (!scales || !rows || !gs_in || !gs_shared) return NVFP4_ERR_NULL;
+  if (k_blocks < 0 || k_blocks >= kMaxDim) return NVFP4_ERR_SHAPE;
+  RescaleArgs a = {};
+  a.n = n;
+  uint64_t off = 0;
+  for (int i = 0; i < n; ++i) {
+    if (rows[i] < 0 || rows[i] >= kMaxDim) return NVFP4_ERR_SHAPE;
+    if (!gs_in[i]) return NVFP4_ERR_NULL;
+    if (gs_in[i] == gs_shared) return NVFP4_ERR_INVALID;
+    uint64_t cnt = (uint64_t)rows[i] * (uint64_t)k_blocks;
+    if (cnt > 0 && !scales[i]) return NVFP4_ERR_NULL;
+    a.scales[i] = scales[i];
+    a.offset[i] = off;
+    a.gs[i] = gs_in[i];
+    off += cnt;
+  }
+  if (off >= ((uint64_t)1 << 40)) return NVFP4_ERR_SHAPE;
+  a.total = off;
+  a.gs_shared = gs_shared;
+  launch_fuse_rescale(a, (hipStream_t)stream);
+  return launched();
+}
+
+size_t nvfp4_gemm_workspace_size(int64_t M, int64_t N, int64_t K) {
+  (void)N;
+  if (M <= 0 || K <= 0) return kWsX16;
+  int64_t Mp = M <= kGemvMaxM ? M : round_up(M, kGemmBM);
+  int64_t Kp = round_up(K, kGemmBK);
+  return kWsX16 + (size_t)Mp * (size_t)Kp * 2u;
+}
+
+nvfp4_status_t nvfp4_gemm(const void* x, nvfp4_dtype_t x_dtype, int64_t M, int64_t K, int64_t ld_x,
+                          const uint8_t* w_codes, const uint8_t* w_scales, const float* w_gs, int64_t N, void* y,
+                          nvfp4_dtype_t y_dtype, int64_t ld_y, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  nvfp4_status_t st = check_input(x, x_dtype, M, K, ld_x);
+  if (st != NVFP4_OK) return st;
+  if (!dtype_ok(y_dtype)) return NVFP4_ERR_DTYPE;
+  if (N < 0 || N >= kMaxDim) return NVFP4_ERR_SHAPE;
+  if (K % 32 != 0) return NVFP4_ERR_SHAPE;
+  if (M == 0 || N == 0) return NVFP4_OK;
+  if (!y || !w_gs) return NVFP4_ERR_NULL;
+  if (ld_y < N) return NVFP4_ERR_SHAPE;
+  if (!aligned(y, 16) || ((uint64_t)ld_y * esize(y_dtype)) % 16 != 0) return NVFP4_ERR_ALIGN;
+  if (K > 0) {
+    if (!w_codes || !w_scales) return NVFP4_ERR_NULL;
+    if (!aligned(w_codes, 16) || !aligned(w_scales, 2)) return NVFP4_ERR_ALIGN;
+  }
+  if (!workspace || !aligned(workspace, 256) || workspace_bytes < nvfp4_gemm_workspace_size(M, N, K))
+    return NVFP4_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  const bool xb = x_dtype == NVFP4_BF16, yb = y_dtype == NVFP4_BF16;
+  uint32_t* partials = (uint32_t*)((char*)workspace + kWsPartials);
+  float* gsx = (float*)((char*)workspace + kWsGs);
+  void* x16 = (char*)workspace + kWsX16;
+  const int64_t Kp = round_up(K, kGemmBK);
+  int np = launch_amax(x, xb, M, K, ld_x, partials, s);
+  launch_quantize_f16(x, xb, M, K, ld_x, Kp, partials, np, x16, gsx, s);
+  if (M <= kGemvMaxM)
+    launch_gemv(x16, M, Kp, w_codes, w_scales, N, K, gsx, w_gs, y, yb, ld_y, s);
+  else
+    launch_gemm(x16, M, Kp, w_codes, w_scales, N, K, gsx, w_gs, y, yb, ld_y, s);
+  return launched();
+}
+
+}  // extern "C"

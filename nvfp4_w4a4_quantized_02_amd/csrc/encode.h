@@ -1,0 +1,141 @@
+// Block encoder shared by the quantize kernels: one lane owns one 16-element
+// block, computes its E4M3 scale and the 16 E2M1 codes.
+//
+// The code of an element is E2M1(RN(|x| / es)) with ties to the even code
+// (paper "Why Gated DeltaNet Survives 4-Bit Quantization", section 2
+// "NVFP4"; the exact rounding rule is this library's reading).  Instead of
+// one correctly rounded division per element, every decision point of that
+// rule is moved into |x|-space once per block: RN(q) > c holds exactly when
+// q lies above the midpoint between c and its fp32 successor (c even, so a
+// tie there rounds to c), and RN(q) >= c exactly when q reaches the midpoint
+// between c's predecessor and c.  With q = |x| / es and es > 0 this becomes
+// |x| > T * es or |x| >= T * es, where T (at most 25 significant bits) times
+// es (24 bits) is exact in fp64.  A directed rounding of that product to
+// fp32 turns both forms into one strict fp32 comparison |x| > B, so the
+// per-element work is a three-step binary search over seven block bounds.
+#pragma once
+
+#include "common.h"
+
+namespace nvfp4 {
+
+// Decision points of E2M1 round-to-nearest-even in quotient space:
+// code >= k  <=>  q (>|>=) kT[k-1].  Odd k: strict (the tie rounds down);
+// even k: inclusive (the tie rounds up).
+__device__ __forceinline__ double e2m1_decision(int k) {
+  switch (k) {
+    case 0: return 0.25 + 0x1p-26;   // RN(q) >  0.25
+    case 1: return 0.75 - 0x1p-25;   // RN(q) >= 0.75
+    case 2: return 1.25 + 0x1p-24;   // RN(q) >  1.25
+    case 3: return 1.75 - 0x1p-24;   // RN(q) >= 1.75
+    case 4: return 2.5 + 0x1p-23;    // RN(q) >  2.5
+    case 5: return 3.5 - 0x1p-23;    // RN(q) >= 3.5
+    default: return 5.0 + 0x1p-22;   // RN(q) >  5
+  }
+}
+
+struct Bounds {
+  float b[7];  // code >= k+1  <=>  |x| > b[k]
+};
+
+// Largest fp32 <= P (strict decision) or < P (inclusive decision).
+__device__ __forceinline__ float bound_from(double P, bool strict) {
+  float f = (float)P;  // round to nearest
+  double fd = (double)f;
+  bool step_down = strict ? (fd > P) : (fd >= P);
+  return step_down ? __uint_as_float(__float_as_uint(f) - 1u) : f;
+}
+
+__device__ __forceinline__ Bounds make_bounds(float es) {
+  Bounds B;
+  if (es == 0.0f) {
+#pragma unroll
+    for (int k = 0; k < 7; ++k) B.b[k] = __uint_as_float(0x7F800000u);  // nothing passes
+    return B;
+  }
+  double e = (double)es;
+#pragma unroll
+  for (int k = 0; k < 7; ++k) B.b[k] = bound_from(e2m1_decision(k) * e, (k & 1) == 0);
+  return B;
+}
+
+// Magnitude code of a = |x| (fp32 bits compared as integers: both are
+// non-negative, so integer and float order agree).
+__device__ __forceinline__ uint32_t mag_from_bounds(uint32_t a, const uint32_t (&b)[7]) {
+  uint32_t c4 = a > b[3];
+  uint32_t mid = c4 ? b[5] : b[1];
+  uint32_t c2 = a > mid;
+  uint32_t lo = c4 ? (c2 ? b[6] : b[4]) : (c2 ? b[2] : b[0]);
+  uint32_t c1 = a > lo;
+  return (c4 << 2) | (c2 << 1) | c1;
+}
+
+// Encode one block.  absbits[j] = fp32 bits of |x_j|, signs = bit j set when
+// x_j has its sign bit set.  Returns the scale byte; codes in two dwords
+// (element 2i -> low nibble of byte i).
+__device__ __forceinline__ uint32_t encode_block(const uint32_t (&absbits)[16], uint32_t signs, float gs,
+                                                 uint32_t& code_lo, uint32_t& code_hi) {
+  uint32_t bm = 0;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) bm = bm > absbits[j] ? bm : absbits[j];
+  BlockScale s = block_scale(__uint_as_float(bm), gs);
+  Bounds Bf = make_bounds(s.es);
+  uint32_t b[7];
+#pragma unroll
+  for (int k = 0; k < 7; ++k) b[k] = __float_as_uint(Bf.b[k]);
+  uint32_t lo = 0, hi = 0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    uint32_t c = mag_from_bounds(absbits[j], b) | (((signs >> j) & 1u) << 3);
+    lo |= c << (4 * j);
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    uint32_t c = mag_from_bounds(absbits[8 + j], b) | (((signs >> (8 + j)) & 1u) << 3);
+    hi |= c << (4 * j);
+  }
+  code_lo = lo;
+  code_hi = hi;
+  return s.sb;
+}
+
+// fp16 expansion of 8 packed codes sharing one scale byte: E2M1(code) *
+// E4M3value(sb), exact in fp16 (values from 2^-10 to 2688, at most 6
+// significant bits).  The scale splits into a power of two, applied by the
+// hardware FP4 conversion (which uses only the exponent of its scale
+// operand), and a small multiplier q applied by one packed fp16 multiply:
+// normal bytes: 2^(e-7) * (1 + m/8); subnormal bytes: 2^-9 * m.
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+
+struct ScaleSplit {
+  float p2;      // power of two (only its exponent matters)
+  half2_t q2;    // multiplier, both halves
+};
+
+__device__ __forceinline__ ScaleSplit split_scale(uint32_t sb) {
+  uint32_t e = (sb >> 3) & 15u, m = sb & 7u;
+  ScaleSplit s;
+  s.p2 = __uint_as_float((e ? (e + 120u) : 118u) << 23);
+  // fp16 bits of q: normal 1 + m/8 = 0x3C00 | m << 7; subnormal m (0..7)
+  uint32_t qn = 0x3C00u | (m << 7);
+  uint32_t qs = __builtin_bit_cast(uint16_t, (_Float16)(float)m);
+  uint32_t q = e ? qn : qs;
+  uint32_t q2 = q | (q << 16);
+  s.q2 = __builtin_bit_cast(half2_t, q2);
+  return s;
+}
+
+// out[i] = fp16 pair for codes byte i (element 2i low half).
+__device__ __forceinline__ void expand8(uint32_t codes8, ScaleSplit s, uint32_t (&out)[4]) {
+  half2_t v0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes8, s.p2, 0);
+  half2_t v1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes8, s.p2, 1);
+  half2_t v2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes8, s.p2, 2);
+  half2_t v3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes8, s.p2, 3);
+  out[0] = __builtin_bit_cast(uint32_t, v0 * s.q2);
+  out[1] = __builtin_bit_cast(uint32_t, v1 * s.q2);
+  out[2] = __builtin_bit_cast(uint32_t, v2 * s.q2);
+  out[3] = __builtin_bit_cast(uint32_t, v3 * s.q2);
+}
+
+}  // namespace nvfp4

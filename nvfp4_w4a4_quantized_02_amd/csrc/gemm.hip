@@ -1,0 +1,310 @@
+// Block-scaled W4A4 contraction (paper "Why Gated DeltaNet Survives 4-Bit
+// Quantization", section 2 "NVFP4": both operands NVFP4, FP32 accumulate).
+//
+// Both kernels compute C[n, m] = sum_k W[n, k] X[m, k] on the MFMA units in
+// fp16: every NVFP4 element E2M1(code) * E4M3(scale) is exact in fp16, so the
+// products are exact and only the FP32 accumulation rounds.  X arrives
+// already expanded to fp16 (the quantize kernel writes it); W is read as
+// packed codes and scale bytes and expanded in registers right before the
+// MFMA.  The epilogue applies RN(gs_x * gs_w) and stores Y[m, n].
+//
+// Inside one MFMA the order of K is free as long as both operands agree.
+// Each lane loads 16 bytes of W codes (32 consecutive k) and feeds dword j
+// of them to sub-step j; the X operand is read with the same k permutation.
+#include "encode.h"
+#include "launch.h"
+
+namespace nvfp4 {
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ f16x8 u4_as_f16x8(uint4 v) { return __builtin_bit_cast(f16x8, v); }
+
+__device__ __forceinline__ uint32_t dword_of(const uint4& v, int j) {
+  return j == 0 ? v.x : (j == 1 ? v.y : (j == 2 ? v.z : v.w));
+}
+
+// Store 4 consecutive outputs y[m, n .. n+3] (n + 3 may pass N on the last tile).
+template <bool kYBf16>
+__device__ __forceinline__ void store4(uint8_t* __restrict__ yrow, int n, int N, float v0, float v1, float v2,
+                                       float v3) {
+  if (kYBf16) {
+    uint32_t b0 = f32_to_bf16_rne(v0), b1 = f32_to_bf16_rne(v1), b2 = f32_to_bf16_rne(v2),
+             b3 = f32_to_bf16_rne(v3);
+    uint16_t* p = reinterpret_cast<uint16_t*>(yrow) + n;
+    if (n + 3 < N) {
+      *reinterpret_cast<uint2*>(p) = make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
+    } else {
+      if (n < N) p[0] = (uint16_t)b0;
+      if (n + 1 < N) p[1] = (uint16_t)b1;
+      if (n + 2 < N) p[2] = (uint16_t)b2;
+    }
+  } else {
+    float* p = reinterpret_cast<float*>(yrow) + n;
+    if (n + 3 < N) {
+      *reinterpret_cast<float4*>(p) = make_float4(v0, v1, v2, v3);
+    } else {
+      if (n < N) p[0] = v0;
+      if (n + 1 < N) p[1] = v1;
+      if (n + 2 < N) p[2] = v2;
+    }
+  }
+}
+
+// ====================================================================== GEMM
+// Workgroup tile 256 (W rows) x 256 (X rows), 4 waves in a 2 x 2 grid, each
+// wave 128 x 128 = 4 x 4 MFMA 32x32x16 tiles (256 fp32 accumulators per lane).
+// X tiles (256 rows x 64 k fp16 = 32 KB) go through LDS, double-buffered,
+// with the 16-byte chunk index XOR-swizzled by (row & 7) so the MFMA operand
+// reads are bank-conflict free.  W fragments go global -> registers and are
+// expanded per sub-step.
+template <bool kYBf16>
+__global__ __launch_bounds__(256, 1) void gemm_kernel(const uint4* __restrict__ x16, uint32_t kp_chunks,
+                                                       const uint8_t* __restrict__ wc,
+                                                       const uint8_t* __restrict__ ws, int N, int K, int M,
+                                                       const float* __restrict__ gsx_p,
+                                                       const float* __restrict__ gsw_p, uint8_t* __restrict__ y,
+                                                       size_t ld_y_bytes, int tiles_n, int nk) {
+  __shared__ uint4 lds[2][kGemmBM * 8];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wave_n = wave >> 1, wave_m = wave & 1;
+  const int tn = blockIdx.x % tiles_n, tm = blockIdx.x / tiles_n;
+  const int n0 = tn * kGemmBN, m0 = tm * kGemmBM;
+  const int l32 = lane & 31, h = lane >> 5;
+
+  const size_t kh = (size_t)K / 2, ks = (size_t)K / 16;
+  const uint8_t* wcp[4];
+  const uint8_t* wsp[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    int n = n0 + wave_n * 128 + t * 32 + l32;
+    n = n < N ? n : N - 1;
+    wcp[t] = wc + (size_t)n * kh + h * 16;
+    wsp[t] = ws + (size_t)n * ks + h * 2;
+  }
+
+  const int st_row0 = tid >> 3;
+  const int st_ch = (tid & 7) ^ (st_row0 & 7);
+  const uint4* xp = x16 + (size_t)(m0 + st_row0) * kp_chunks + (tid & 7);
+
+  floatx16 acc[4][4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[t][u][r] = 0.0f;
+
+  uint4 xr[8];
+  uint4 wcur[4], wnxt[4];
+  uint32_t scur[4], snxt[4];
+
+  if (nk > 0) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) xr[j] = xp[(size_t)(32 * j) * kp_chunks];
+    const bool ok = h * 32 < K;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      wcur[t] = ok ? *reinterpret_cast<const uint4*>(wcp[t]) : make_uint4(0, 0, 0, 0);
+      scur[t] = ok ? *reinterpret_cast<const uint16_t*>(wsp[t]) : 0u;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) lds[0][(st_row0 + 32 * j) * 8 + st_ch] = xr[j];
+  }
+  __syncthreads();
+
+  for (int kt = 0; kt < nk; ++kt) {
+    const int buf = kt & 1;
+    const bool more = kt + 1 < nk;
+    if (more) {
+      const int k1 = kt + 1;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) xr[j] = xp[(size_t)(32 * j) * kp_chunks + (size_t)k1 * 8];
+      const bool ok = k1 * 64 + h * 32 < K;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        wnxt[t] = ok ? *reinterpret_cast<const uint4*>(wcp[t] + (size_t)k1 * 32) : make_uint4(0, 0, 0, 0);
+        snxt[t] = ok ? *reinterpret_cast<const uint16_t*>(wsp[t] + (size_t)k1 * 4) : 0u;
+      }
+    }
+    ScaleSplit sp[4][2];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      sp[t][0] = split_scale(scur[t] & 0xFFu);
+      sp[t][1] = split_scale(scur[t] >> 8);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      f16x8 bx[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int row = wave_m * 128 + u * 32 + l32;
+        const int ch = (4 * h + j) ^ (row & 7);
+        bx[u] = u4_as_f16x8(lds[buf][row * 8 + ch]);
+      }
+      f16x8 aw[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        uint32_t e[4];
+        expand8(dword_of(wcur[t], j), sp[t][j >> 1], e);
+        aw[t] = u4_as_f16x8(make_uint4(e[0], e[1], e[2], e[3]));
+      }
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          acc[t][u] = __builtin_amdgcn_mfma_f32_32x32x16_f16(aw[t], bx[u], acc[t][u], 0, 0, 0);
+    }
+    if (more) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) lds[buf ^ 1][(st_row0 + 32 * j) * 8 + st_ch] = xr[j];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        wcur[t] = wnxt[t];
+        scur[t] = snxt[t];
+      }
+    }
+    __syncthreads();
+  }
+
+  const float scale = (*gsx_p) * (*gsw_p);
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int m = m0 + wave_m * 128 + u * 32 + l32;
+    if (m >= M) continue;
+    uint8_t* yrow = y + (size_t)m * ld_y_bytes;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int n = n0 + wave_n * 128 + t * 32 + 8 * q + 4 * h;
+        store4<kYBf16>(yrow, n, N, acc[t][u][4 * q] * scale, acc[t][u][4 * q + 1] * scale,
+                       acc[t][u][4 * q + 2] * scale, acc[t][u][4 * q + 3] * scale);
+      }
+    }
+  }
+}
+
+// ====================================================================== GEMV
+// M <= 16 (decode).  MFMA 16x16x32 with W as the 16-row A operand and the
+// (zero-padded) activations as the 16-column B operand.  A workgroup owns
+// NT*16 rows of W; its 4 waves split K round-robin in 128-k chunks and their
+// partial sums are added in a fixed order through LDS, so the result does
+// not depend on scheduling.
+template <int NT, bool kYBf16>
+__global__ __launch_bounds__(256) void gemv_kernel(const uint4* __restrict__ x16, uint32_t kp_chunks, int M,
+                                                    const uint8_t* __restrict__ wc, const uint8_t* __restrict__ ws,
+                                                    int N, int K, const float* __restrict__ gsx_p,
+                                                    const float* __restrict__ gsw_p, uint8_t* __restrict__ y,
+                                                    size_t ld_y_bytes) {
+  __shared__ floatx4 part[4][NT][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int l16 = lane & 15, g = lane >> 4;
+  const int n0 = blockIdx.x * (NT * 16);
+  const size_t kh = (size_t)K / 2, ks = (size_t)K / 16;
+
+  const uint8_t* wrow[NT];
+  const uint8_t* srow[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    int n = n0 + t * 16 + l16;
+    n = n < N ? n : N - 1;
+    wrow[t] = wc + (size_t)n * kh;
+    srow[t] = ws + (size_t)n * ks;
+  }
+  const bool mvalid = l16 < M;
+  const uint4* xrow = x16 + (size_t)(mvalid ? l16 : 0) * kp_chunks;
+
+  floatx4 acc[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) acc[t] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+
+  for (int kb = wave * 128; kb < K; kb += 512) {
+    const int kk = kb + 32 * g;
+    const bool kvalid = kk < K;
+    uint4 wv[NT];
+    uint32_t sv[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      wv[t] = kvalid ? *reinterpret_cast<const uint4*>(wrow[t] + kk / 2) : make_uint4(0, 0, 0, 0);
+      sv[t] = kvalid ? *reinterpret_cast<const uint16_t*>(srow[t] + kk / 16) : 0u;
+    }
+    uint4 xv[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) xv[j] = (mvalid && kvalid) ? xrow[kk / 8 + j] : make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      ScaleSplit s0 = split_scale(sv[t] & 0xFFu), s1 = split_scale(sv[t] >> 8);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        uint32_t e[4];
+        expand8(dword_of(wv[t], j), j < 2 ? s0 : s1, e);
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(u4_as_f16x8(make_uint4(e[0], e[1], e[2], e[3])),
+                                                        u4_as_f16x8(xv[j]), acc[t], 0, 0, 0);
+      }
+    }
+  }
+
+#pragma unroll
+  for (int t = 0; t < NT; ++t) part[wave][t][lane] = acc[t];
+  __syncthreads();
+  if (wave != 0) return;
+  const float scale = (*gsx_p) * (*gsw_p);
+  if (!mvalid) return;
+  uint8_t* yrow = y + (size_t)l16 * ld_y_bytes;
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    floatx4 s = part[0][t][lane];
+    floatx4 s1 = part[1][t][lane], s2 = part[2][t][lane], s3 = part[3][t][lane];
+    s = s + s1;
+    s = s + s2;
+    s = s + s3;
+    const int n = n0 + t * 16 + 4 * g;
+    store4<kYBf16>(yrow, n, N, s[0] * scale, s[1] * scale, s[2] * scale, s[3] * scale);
+  }
+}
+
+// ====================================================================== launch
+void launch_gemm(const void* x16, int64_t M, int64_t Kp, const uint8_t* wc, const uint8_t* ws, int64_t N, int64_t K,
+                 const float* gsx, const float* gsw, void* y, bool y_bf16, int64_t ld_y, hipStream_t s) {
+  const int tiles_n = (int)((N + kGemmBN - 1) / kGemmBN);
+  const int tiles_m = (int)((M + kGemmBM - 1) / kGemmBM);
+  const int nk = (int)(Kp / kGemmBK);
+  const size_t ldb = (size_t)ld_y * (y_bf16 ? 2u : 4u);
+  const uint32_t kpc = (uint32_t)(Kp / 8);
+  dim3 grid(tiles_n * tiles_m);
+  if (y_bf16)
+    gemm_kernel<true><<<grid, 256, 0, s>>>((const uint4*)x16, kpc, wc, ws, (int)N, (int)K, (int)M, gsx, gsw,
+                                           (uint8_t*)y, ldb, tiles_n, nk);
+  else
+    gemm_kernel<false><<<grid, 256, 0, s>>>((const uint4*)x16, kpc, wc, ws, (int)N, (int)K, (int)M, gsx, gsw,
+                                            (uint8_t*)y, ldb, tiles_n, nk);
+}
+
+template <int NT>
+static void gemv_nt(const void* x16, int64_t M, int64_t Kp, const uint8_t* wc, const uint8_t* ws, int64_t N,
+                    int64_t K, const float* gsx, const float* gsw, void* y, bool y_bf16, int64_t ld_y,
+                    hipStream_t s) {
+  const int grid = (int)((N + NT * 16 - 1) / (NT * 16));
+  const size_t ldb = (size_t)ld_y * (y_bf16 ? 2u : 4u);
+  const uint32_t kpc = (uint32_t)(Kp / 8);
+  if (y_bf16)
+    gemv_kernel<NT, true><<<grid, 256, 0, s>>>((const uint4*)x16, kpc, (int)M, wc, ws, (int)N, (int)K, gsx, gsw,
+                                               (uint8_t*)y, ldb);
+  else
+    gemv_kernel<NT, false><<<grid, 256, 0, s>>>((const uint4*)x16, kpc, (int)M, wc, ws, (int)N, (int)K, gsx, gsw,
+                                                (uint8_t*)y, ldb);
+}
+
+void launch_gemv(const void* x16, int64_t M, int64_t Kp, const uint8_t* wc, const uint8_t* ws, int64_t N, int64_t K,
+                 const float* gsx, const float* gsw, void* y, bool y_bf16, int64_t ld_y, hipStream_t s) {
+  // One 16-row tile per workgroup keeps the grid fine-grained when the
+  // activations are few; more rows per workgroup amortise the activation
+  // reads when M is larger.
+  if (M <= 4)
+    gemv_nt<1>(x16, M, Kp, wc, ws, N, K, gsx, gsw, y, y_bf16, ld_y, s);
+  else
+    gemv_nt<4>(x16, M, Kp, wc, ws, N, K, gsx, gsw, y, y_bf16, ld_y, s);
+}
+
+}  // namespace nvfp4

@@ -1,0 +1,52 @@
+// Internal launchers shared between the kernel sources and the C ABI layer.
+// Every launcher assumes its arguments were validated by the ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nvfp4 {
+
+constexpr int kMaxFused = 16;
+constexpr int kMaxPartials = 2048;  // absmax partials (one per workgroup)
+
+// Workspace layout shared by quantize and gemm (byte offsets, 256-aligned).
+constexpr size_t kWsPartials = 0;
+constexpr size_t kWsGs = kMaxPartials * sizeof(uint32_t);   // one float
+constexpr size_t kWsX16 = kWsGs + 256;                       // fp16 A operand
+
+// GEMM tiling (see gemm.hip).
+constexpr int kGemmBM = 256;   // X rows per workgroup tile
+constexpr int kGemmBN = 256;   // W rows per workgroup tile
+constexpr int kGemmBK = 64;    // K per main-loop step
+constexpr int kGemvMaxM = 16;  // M at or below this uses the GEMV kernel
+
+struct RescaleArgs {
+  int n;
+  uint64_t total;
+  uint8_t* scales[kMaxFused];
+  uint64_t offset[kMaxFused];
+  const float* gs[kMaxFused];
+  float* gs_shared;
+};
+
+// Returns the number of partials written.
+int launch_amax(const void* x, bool bf16, int64_t rows, int64_t K, int64_t ld, uint32_t* partials, hipStream_t s);
+void launch_quantize_packed(const void* x, bool bf16, int64_t rows, int64_t K, int64_t ld,
+                            const uint32_t* partials, int npartials, uint8_t* codes, uint8_t* scales, float* gs,
+                            hipStream_t s);
+void launch_quantize_f16(const void* x, bool bf16, int64_t rows, int64_t K, int64_t ld, int64_t Kp,
+                         const uint32_t* partials, int npartials, void* x16, float* gs, hipStream_t s);
+void launch_fill_f32(float* p, float v, hipStream_t s);
+void launch_dequant(const uint8_t* codes, const uint8_t* scales, const float* gs, int64_t rows, int64_t K,
+                    void* out, bool out_bf16, int64_t ld_out, hipStream_t s);
+void launch_fuse_rescale(const RescaleArgs& a, hipStream_t s);
+
+// C[m, n] = (sum_k X16[m, k] * W[n, k]) * gs_x * gs_w for the prefill tile
+// kernel (M > kGemvMaxM) and the small-M kernel.
+void launch_gemm(const void* x16, int64_t M, int64_t Kp, const uint8_t* wc, const uint8_t* ws, int64_t N, int64_t K,
+                 const float* gsx, const float* gsw, void* y, bool y_bf16, int64_t ld_y, hipStream_t s);
+void launch_gemv(const void* x16, int64_t M, int64_t Kp, const uint8_t* wc, const uint8_t* ws, int64_t N, int64_t K,
+                 const float* gsx, const float* gsw, void* y, bool y_bf16, int64_t ld_y, hipStream_t s);
+
+}  // namespace nvfp4

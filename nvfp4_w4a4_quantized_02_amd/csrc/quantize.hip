@@ -1,0 +1,324 @@
+// Quantize-side kernels: tensor absmax, NVFP4 encode (packed codes or fp16
+// expansion for the GEMM), dequant and the fused-group scale repair.
+//
+// Paper "Why Gated DeltaNet Survives 4-Bit Quantization", section 2 "NVFP4"
+// (E2M1 values, E4M3 scale per 16-element block, FP32 tensor scale) and
+// section 6 "Per-module calibration vs. fused-GEMM scaling" (the repair).
+#include "encode.h"
+#include "launch.h"
+
+namespace nvfp4 {
+
+// ------------------------------------------------------------------ amax
+// The tensor absmax is a max over fp32 bit patterns of |x| (integer order
+// equals float order for non-negative values), so it is exact and does not
+// depend on the reduction order.  Each workgroup writes one partial; the
+// consumers reduce the partials themselves, so no atomics, no memset.
+template <bool kBf16>
+__global__ __launch_bounds__(256) void amax_partials_kernel(const uint4* __restrict__ x, uint32_t chunks_per_row,
+                                                             uint32_t ld_chunks, uint32_t total_chunks, FastDiv fd,
+                                                             uint32_t* __restrict__ partials) {
+  __shared__ uint32_t red[4];
+  uint32_t m = 0;
+  const uint32_t stride = gridDim.x * 256u;
+  for (uint32_t c0 = blockIdx.x * 256u + threadIdx.x; c0 < total_chunks; c0 += 4u * stride) {
+    uint4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      uint32_t c = c0 + (uint32_t)u * stride;
+      v[u] = make_uint4(0, 0, 0, 0);
+      if (c < total_chunks) {
+        uint32_t r = fastdiv(c, fd);
+        v[u] = x[(size_t)r * ld_chunks + (c - r * chunks_per_row)];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (kBf16) {
+          uint32_t lo = (w[i] & 0x7FFFu) << 16, hi = w[i] & 0x7FFF0000u;
+          m = m > lo ? m : lo;
+          m = m > hi ? m : hi;
+        } else {
+          uint32_t a = w[i] & 0x7FFFFFFFu;
+          m = m > a ? m : a;
+        }
+      }
+    }
+  }
+  m = wave_max_u32(m);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t r = red[0];
+    for (int i = 1; i < 4; ++i) r = r > red[i] ? r : red[i];
+    partials[blockIdx.x] = r;
+  }
+}
+
+// All threads of the workgroup return the tensor scale RN(amax / 2688).
+__device__ __forceinline__ float reduce_partials_to_gs(const uint32_t* __restrict__ partials, int n,
+                                                       uint32_t* red4) {
+  uint32_t m = 0;
+  for (int i = threadIdx.x; i < n; i += blockDim.x) {
+    uint32_t p = partials[i];
+    m = m > p ? m : p;
+  }
+  m = wave_max_u32(m);
+  if ((threadIdx.x & 63) == 0) red4[threadIdx.x >> 6] = m;
+  __syncthreads();
+  uint32_t r = red4[0];
+  for (int i = 1; i < (int)(blockDim.x >> 6); ++i) r = r > red4[i] ? r : red4[i];
+  return tensor_scale(__uint_as_float(r));
+}
+
+// Load one 16-element block (bf16: two 16-byte chunks, fp32: four).
+template <bool kBf16>
+__device__ __forceinline__ void load_block(const uint8_t* __restrict__ p, uint32_t (&absbits)[16], uint32_t& signs) {
+  signs = 0;
+  if (kBf16) {
+    const uint4* q = reinterpret_cast<const uint4*>(p);
+    uint4 a = q[0], b = q[1];
+    uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      absbits[2 * i] = (w[i] & 0x7FFFu) << 16;
+      absbits[2 * i + 1] = w[i] & 0x7FFF0000u;
+      signs |= ((w[i] >> 15) & 1u) << (2 * i);
+      signs |= (w[i] >> 31) << (2 * i + 1);
+    }
+  } else {
+    const uint4* q = reinterpret_cast<const uint4*>(p);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      uint4 a = q[c];
+      uint32_t w[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        absbits[4 * c + i] = w[i] & 0x7FFFFFFFu;
+        signs |= (w[i] >> 31) << (4 * c + i);
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------ encode
+// One lane per 16-element block.  The loop walks the blocks from the end of
+// the tensor back to its start, the reverse of the absmax pass, so the part
+// of the tensor read last by that pass is read first here, while it may
+// still sit in the last-level cache.
+template <bool kBf16>
+__global__ __launch_bounds__(256) void quantize_packed_kernel(const uint8_t* __restrict__ x, size_t ld_bytes,
+                                                               uint32_t kblocks, uint32_t total_blocks, FastDiv fd,
+                                                               const uint32_t* __restrict__ partials, int npartials,
+                                                               uint8_t* __restrict__ codes,
+                                                               uint8_t* __restrict__ scales,
+                                                               float* __restrict__ gs_out) {
+  __shared__ uint32_t red[4];
+  const float gs = reduce_partials_to_gs(partials, npartials, red);
+  if (blockIdx.x == 0 && threadIdx.x == 0) *gs_out = gs;
+  const uint32_t stride = gridDim.x * 256u;
+  const uint32_t first = blockIdx.x * 256u + threadIdx.x;
+  if (first >= total_blocks) return;
+  const uint32_t iters = (total_blocks - 1u - first) / stride;  // last index = first + iters*stride
+  for (int32_t it = (int32_t)iters; it >= 0; --it) {
+    uint32_t b = first + (uint32_t)it * stride;
+    uint32_t r = fastdiv(b, fd);
+    uint32_t kb = b - r * kblocks;
+    uint32_t absbits[16], signs;
+    load_block<kBf16>(x + (size_t)r * ld_bytes + (size_t)kb * (kBf16 ? 32u : 64u), absbits, signs);
+    uint32_t lo, hi;
+    uint32_t sb = encode_block(absbits, signs, gs, lo, hi);
+    *reinterpret_cast<uint2*>(codes + (size_t)b * 8u) = make_uint2(lo, hi);
+    scales[b] = (uint8_t)sb;
+  }
+}
+
+// Same encoder, but the output is the fp16 value E2M1(code) * E4M3(scale)
+// of every element (the tensor scale stays separate), laid out
+// [rows, kp_blocks * 16] with zero blocks beyond K: the A-side operand of
+// the GEMM.  gs is written to *gs_out.
+template <bool kBf16>
+__global__ __launch_bounds__(256) void quantize_f16_kernel(const uint8_t* __restrict__ x, size_t ld_bytes,
+                                                            uint32_t kblocks, uint32_t kp_blocks,
+                                                            uint32_t total_blocks, FastDiv fd,
+                                                            const uint32_t* __restrict__ partials, int npartials,
+                                                            uint4* __restrict__ x16, float* __restrict__ gs_out) {
+  __shared__ uint32_t red[4];
+  const float gs = reduce_partials_to_gs(partials, npartials, red);
+  if (blockIdx.x == 0 && threadIdx.x == 0) *gs_out = gs;
+  const uint32_t stride = gridDim.x * 256u;
+  const uint32_t first = blockIdx.x * 256u + threadIdx.x;
+  if (first >= total_blocks) return;
+  const uint32_t iters = (total_blocks - 1u - first) / stride;
+  for (int32_t it = (int32_t)iters; it >= 0; --it) {
+    uint32_t b = first + (uint32_t)it * stride;
+    uint32_t r = fastdiv(b, fd);
+    uint32_t kb = b - r * kp_blocks;
+    uint4 o0 = make_uint4(0, 0, 0, 0), o1 = make_uint4(0, 0, 0, 0);
+    if (kb < kblocks) {
+      uint32_t absbits[16], signs;
+      load_block<kBf16>(x + (size_t)r * ld_bytes + (size_t)kb * (kBf16 ? 32u : 64u), absbits, signs);
+      uint32_t lo, hi;
+      uint32_t sb = encode_block(absbits, signs, gs, lo, hi);
+      ScaleSplit s = split_scale(sb);
+      uint32_t e0[4], e1[4];
+      expand8(lo, s, e0);
+      expand8(hi, s, e1);
+      o0 = make_uint4(e0[0], e0[1], e0[2], e0[3]);
+      o1 = make_uint4(e1[0], e1[1], e1[2], e1[3]);
+    }
+    x16[(size_t)b * 2u] = o0;
+    x16[(size_t)b * 2u + 1u] = o1;
+  }
+}
+
+__global__ void fill_f32_kernel(float* p, float v) { *p = v; }
+
+// ------------------------------------------------------------------ dequant
+// out = RN_fp32(E2M1(code) * E4M3(scale) * gs); the first product is exact.
+template <bool kOutBf16>
+__global__ __launch_bounds__(256) void dequant_kernel(const uint32_t* __restrict__ codes,
+                                                       const uint8_t* __restrict__ scales,
+                                                       const float* __restrict__ gs_p, uint32_t k8,
+                                                       uint32_t total, FastDiv fd, uint8_t* __restrict__ out,
+                                                       size_t ld_out_bytes) {
+  const float gs = *gs_p;
+  for (uint32_t c = blockIdx.x * 256u + threadIdx.x; c < total; c += gridDim.x * 256u) {
+    uint32_t r = fastdiv(c, fd);
+    uint32_t kc = c - r * k8;  // 8-element chunk within the row
+    uint32_t w = codes[c];
+    float sv = e4m3_value(scales[(size_t)r * (k8 >> 1) + (kc >> 1)]);
+    float v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      uint32_t code = (w >> (4 * j)) & 15u;
+      uint32_t mag = code & 7u, e = mag >> 1, m = mag & 1u;
+      float cv = e ? __uint_as_float(((e + 126u) << 23) | (m << 22)) : (m ? 0.5f : 0.0f);
+      float p = (cv * sv) * gs;
+      v[j] = (code & 8u) ? -p : p;
+    }
+    uint8_t* o = out + (size_t)r * ld_out_bytes + (size_t)kc * (kOutBf16 ? 16u : 32u);
+    if (kOutBf16) {
+      uint4 q;
+      q.x = f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16);
+      q.y = f32_to_bf16_rne(v[2]) | (f32_to_bf16_rne(v[3]) << 16);
+      q.z = f32_to_bf16_rne(v[4]) | (f32_to_bf16_rne(v[5]) << 16);
+      q.w = f32_to_bf16_rne(v[6]) | (f32_to_bf16_rne(v[7]) << 16);
+      *reinterpret_cast<uint4*>(o) = q;
+    } else {
+      reinterpret_cast<float4*>(o)[0] = make_float4(v[0], v[1], v[2], v[3]);
+      reinterpret_cast<float4*>(o)[1] = make_float4(v[4], v[5], v[6], v[7]);
+    }
+  }
+}
+
+// ------------------------------------------------------------------ repair
+__global__ __launch_bounds__(256) void fuse_rescale_kernel(RescaleArgs a) {
+  __shared__ float rho_s[kMaxFused];
+  __shared__ float S_s;
+  if (threadIdx.x == 0) {
+    float S = 0.0f;
+    for (int i = 0; i < a.n; ++i) {
+      float g = *a.gs[i];
+      S = g > S ? g : S;
+    }
+    S_s = S;
+  }
+  __syncthreads();
+  const float S = S_s;
+  if (threadIdx.x < (unsigned)a.n) {
+    float g = *a.gs[threadIdx.x];
+    rho_s[threadIdx.x] = (S == 0.0f) ? 1.0f : __fdiv_rn(g, S);
+  }
+  __syncthreads();
+  if (blockIdx.x == 0 && threadIdx.x == 0) *a.gs_shared = S;
+  for (uint64_t i = (uint64_t)blockIdx.x * 256u + threadIdx.x; i < a.total; i += (uint64_t)gridDim.x * 256u) {
+    int mbr = 0;
+    while (mbr + 1 < a.n && i >= a.offset[mbr + 1]) ++mbr;
+    uint8_t* p = a.scales[mbr] + (i - a.offset[mbr]);
+    uint32_t b = *p;
+    if ((b & 0x7Fu) == 0x7Fu) continue;  // NaN bytes are kept
+    float v = e4m3_value(b & 0x7Fu) * rho_s[mbr];
+    *p = (uint8_t)((b & 0x80u) | e4m3_encode_sat(v));
+  }
+}
+
+// ------------------------------------------------------------------ launchers
+static inline int grid_for(uint64_t work, uint64_t per_wg, int cap) {
+  uint64_t g = (work + per_wg - 1) / per_wg;
+  if (g < 1) g = 1;
+  if (g > (uint64_t)cap) g = cap;
+  return (int)g;
+}
+
+int launch_amax(const void* x, bool bf16, int64_t rows, int64_t K, int64_t ld, uint32_t* partials,
+                hipStream_t s) {
+  uint32_t esize = bf16 ? 2u : 4u;
+  uint32_t cpr = (uint32_t)(K * esize / 16);
+  uint32_t ldc = (uint32_t)(ld * esize / 16);
+  uint32_t total = (uint32_t)(rows * (int64_t)cpr);
+  int grid = grid_for(total, 1024, kMaxPartials);
+  FastDiv fd = make_fastdiv(cpr ? cpr : 1u);
+  if (bf16)
+    amax_partials_kernel<true><<<grid, 256, 0, s>>>((const uint4*)x, cpr, ldc, total, fd, partials);
+  else
+    amax_partials_kernel<false><<<grid, 256, 0, s>>>((const uint4*)x, cpr, ldc, total, fd, partials);
+  return grid;
+}
+
+void launch_quantize_packed(const void* x, bool bf16, int64_t rows, int64_t K, int64_t ld,
+                            const uint32_t* partials, int npartials, uint8_t* codes, uint8_t* scales, float* gs,
+                            hipStream_t s) {
+  uint32_t kb = (uint32_t)(K / 16);
+  uint32_t total = (uint32_t)(rows * (int64_t)kb);
+  size_t ld_bytes = (size_t)ld * (bf16 ? 2u : 4u);
+  int grid = grid_for(total, 256, 4096);
+  FastDiv fd = make_fastdiv(kb ? kb : 1u);
+  if (bf16)
+    quantize_packed_kernel<true><<<grid, 256, 0, s>>>((const uint8_t*)x, ld_bytes, kb, total, fd, partials,
+                                                      npartials, codes, scales, gs);
+  else
+    quantize_packed_kernel<false><<<grid, 256, 0, s>>>((const uint8_t*)x, ld_bytes, kb, total, fd, partials,
+                                                       npartials, codes, scales, gs);
+}
+
+void launch_quantize_f16(const void* x, bool bf16, int64_t rows, int64_t K, int64_t ld, int64_t Kp,
+                         const uint32_t* partials, int npartials, void* x16, float* gs, hipStream_t s) {
+  uint32_t kb = (uint32_t)(K / 16), kpb = (uint32_t)(Kp / 16);
+  uint32_t total = (uint32_t)(rows * (int64_t)kpb);
+  size_t ld_bytes = (size_t)ld * (bf16 ? 2u : 4u);
+  int grid = grid_for(total, 256, 4096);
+  FastDiv fd = make_fastdiv(kpb ? kpb : 1u);
+  if (bf16)
+    quantize_f16_kernel<true><<<grid, 256, 0, s>>>((const uint8_t*)x, ld_bytes, kb, kpb, total, fd, partials,
+                                                   npartials, (uint4*)x16, gs);
+  else
+    quantize_f16_kernel<false><<<grid, 256, 0, s>>>((const uint8_t*)x, ld_bytes, kb, kpb, total, fd, partials,
+                                                    npartials, (uint4*)x16, gs);
+}
+
+void launch_fill_f32(float* p, float v, hipStream_t s) { fill_f32_kernel<<<1, 1, 0, s>>>(p, v); }
+
+void launch_dequant(const uint8_t* codes, const uint8_t* scales, const float* gs, int64_t rows, int64_t K,
+                    void* out, bool out_bf16, int64_t ld_out, hipStream_t s) {
+  uint32_t k8 = (uint32_t)(K / 8);
+  uint32_t total = (uint32_t)(rows * (int64_t)k8);
+  int grid = grid_for(total, 256, 8192);
+  FastDiv fd = make_fastdiv(k8 ? k8 : 1u);
+  size_t ldb = (size_t)ld_out * (out_bf16 ? 2u : 4u);
+  if (out_bf16)
+    dequant_kernel<true><<<grid, 256, 0, s>>>((const uint32_t*)codes, scales, gs, k8, total, fd, (uint8_t*)out, ldb);
+  else
+    dequant_kernel<false><<<grid, 256, 0, s>>>((const uint32_t*)codes, scales, gs, k8, total, fd, (uint8_t*)out,
+                                               ldb);
+}
+
+void launch_fuse_rescale(const RescaleArgs& a, hipStream_t s) {
+  int grid = grid_for(a.total, 256, 4096);
+  fuse_rescale_kernel<<<grid, 256, 0, s>>>(a);
+}
+
+}  // namespace nvfp4

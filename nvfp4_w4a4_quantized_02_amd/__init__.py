@@ -191,7 +191,10 @@ def nvfp4_gemm(x: torch.Tensor, w_codes: torch.Tensor, w_scales: torch.Tensor, w
         raise ValueError("weight shapes %s / %s do not match K=%d" % (tuple(w_codes.shape),
                                                                        tuple(w_scales.shape), K))
     if out is None:
-        out = torch.empty((M, N), dtype=out_dtype, device=x.device)
+        # rows padded to a 16-byte multiple, as the kernels store 16-byte aligned
+        per16 = 16 // torch.empty((), dtype=out_dtype).element_size()
+        ld_pad = (N + per16 - 1) // per16 * per16
+        out = torch.empty((M, ld_pad), dtype=out_dtype, device=x.device)[:, :N]
     nws = lib.nvfp4_gemm_workspace_size(M, N, K)
     ws = workspace(nws, x.device)
     _check(lib.nvfp4_gemm(x.data_ptr(), _dtype_code(x.dtype), M, K, ld, w_codes.data_ptr(),

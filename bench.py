@@ -1,0 +1,376 @@
+#!/usr/bin/env python3
+"""Benchmark of the NVFP4 W4A4 linear layer on one MI355X.
+
+Headline (the `value`): NVFP4 W4A4 GEMM TFLOP/s on the prefill workload
+X[4096x5120] bf16 (quantized on the fly) x W[17408x5120] NVFP4 -> Y bf16.
+One step = one full serving-time pass: activation absmax, activation encode
+and the block-scaled GEMM with its epilogue (nvfp4_gemm_prepare followed by
+nvfp4_gemm_run, which together are nvfp4_gemm).  Weight quantization and
+the fused-group repair are checkpoint-side steps and are timed separately.
+
+The same JSON line carries, under "also", the decode GEMV (M = 1, 4, 16,
+fused gate/up W[34816x5120], GB/s with 4 rotated weight copies so that the
+last-level cache cannot hold them), the standalone activation quantize at
+long prefill (X[32768x5120], GB/s on the two-pass byte count), the fused
+q/k/v repair + GEMM and the offline weight quantize.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "NVFP4 W4A4 GEMM TFLOP/s at M=4096 and GB/s at M=1; quantize GB/s"
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, published
+PEAK_FP16_TFLOPS = 2500.0      # MI355X dense fp16/bf16 MFMA, published
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--headline-only", action="store_true",
+                    help="skip the secondary workloads (profiling runs)")
+    ap.add_argument("--copy-ref", action="store_true",
+                    help="first run one plain 1 GiB device copy, the reference kernel for HBM counters")
+    return ap.parse_args()
+
+
+def log(msg):
+    print("[bench] " + msg, file=sys.stderr, flush=True)
+
+
+def source_sha(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "nvfp4_w4a4_quantized_02_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(kernel_key, sha):
+    """HBM bytes per launch from committed rocprofv3 PMC summaries, if they
+    were taken on the current kernel source; otherwise None."""
+    path = os.path.join(PROFILE_DIR, "pmc_traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f).get(kernel_key)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_sha") != sha:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+class Timer:
+    """Per-step CUDA events on the current stream (the stream the library
+    launches on), split into named phases."""
+
+    def __init__(self, torch, steps, phases):
+        self.torch = torch
+        self.ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(phases) + 1)]
+                   for _ in range(steps)]
+        self.phases = phases
+
+    def mark(self, step, i):
+        self.ev[step][i].record()
+
+    def phase_ms(self, i):
+        return [e[i].elapsed_time(e[i + 1]) for e in self.ev]
+
+
+def time_steps(torch, steps, warmup, body, nphase):
+    """Run `body(step, mark)` warmup+steps times; returns (ms/step, per-phase
+    ms lists).  The timed region is bracketed by device synchronizations."""
+    for i in range(warmup):
+        body(i, lambda j: None)
+    torch.cuda.synchronize()
+    tm = Timer(torch, steps, list(range(nphase)))
+    t0 = time.perf_counter()
+    for i in range(steps):
+        body(i, lambda j, i=i: tm.mark(i, j))
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3 / steps
+    return wall, [tm.phase_ms(j) for j in range(nphase)]
+
+
+def mean(v):
+    return sum(v) / len(v)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import workloads
+    import nvfp4_w4a4_quantized_02_amd as nv
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    if args.copy_ref:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
+    def to_gpu(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(a).to(dev)
+
+    # ------------------------------------------------------------ headline
+    log("generating prefill workload X[4096x5120] bf16, W[17408x5120]")
+    p = workloads.prefill()
+    M, K, N = p.M, p.K, p.N
+    w32 = torch.from_numpy(p.w_parts[0]).to(dev)
+    wc, ws, wg = nv.nvfp4_quantize(w32)
+    del w32
+    x = to_gpu(p.x)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    ws_buf = torch.empty(nv.lib.nvfp4_gemm_workspace_size(M, N, K), dtype=torch.uint8, device=dev)
+
+    def step(i, mark):
+        mark(0)
+        prep = nv.nvfp4_gemm_prepare(x, ws=ws_buf)
+        mark(1)
+        nv.nvfp4_gemm_run(prep, wc, ws, wg, out=y)
+        mark(2)
+
+    log("timing prefill GEMM: %d warmup, %d steps" % (args.warmup, args.steps))
+    wall_ms, (prep_ms, run_ms) = time_steps(torch, args.steps, args.warmup, step, 2)
+    step_ms = wall_ms                      # timed region / steps, synchronized on both sides
+    flops = 2.0 * M * N * K
+    value = flops / (step_ms * 1e-3) / 1e12
+    gemm_tflops = flops / (mean(run_ms) * 1e-3) / 1e12
+    sha_gemm = source_sha("gemm.hip", "encode.h", "common.h")
+    traffic = traffic_for("gemm_prefill", sha_gemm)
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 4),
+        "device_ms_per_step": round(mean(prep_ms) + mean(run_ms), 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp16",
+        "arith": "NVFP4 (E2M1 x E4M3) operands expanded exactly to fp16; MFMA fp16 with fp32 accumulate",
+        "data": "synthetic (seeded; shapes and distributions of the prefill workload)",
+        "config": {"workload": "prefill W4A4 linear: X[4096x5120] bf16 Student-t(3) quantized on the fly "
+                               "x W[17408x5120] NVFP4 from N(0,0.02) -> Y bf16",
+                   "M": M, "N": N, "K": K, "x_dtype": "bf16", "y_dtype": "bf16"},
+        "phases_ms": {"activation_quantize": round(mean(prep_ms), 4), "gemm": round(mean(run_ms), 4)},
+        "roofline": {"bound": "mfma", "kernel": "gemm_kernel (fp16 MFMA 32x32x16)",
+                     "achieved": round(gemm_tflops, 2), "peak": PEAK_FP16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(gemm_tflops / PEAK_FP16_TFLOPS, 4), "traffic": traffic,
+                     "algorithmic": "2*M*N*K = %.4g flop per launch" % flops},
+    }
+    del y, x
+
+    also = []
+    if not args.headline_only:
+        also += secondary(torch, np, nv, workloads, to_gpu, dev, args)
+
+    # ------------------------------------------------------------ CPU oracle
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(np, p)
+    out["also"] = also
+    print(json.dumps(out), flush=True)
+
+
+def secondary(torch, np, nv, workloads, to_gpu, dev, args):
+    res = []
+    steps, warmup = args.steps, args.warmup
+
+    # ------------------------------------------------ decode GEMV, M = 1/4/16
+    log("generating decode workload (fused gate/up W[34816x5120])")
+    d = workloads.decode(M=1)
+    q = [nv.nvfp4_quantize(torch.from_numpy(w).to(dev)) for w in d.w_parts]
+    shared = nv.nvfp4_fuse_rescale([s for _, s, _ in q], [g for _, _, g in q])
+    wc0 = torch.cat([c for c, _, _ in q])
+    ws0 = torch.cat([s for _, s, _ in q])
+    del q
+    R = 4                                  # 4 x 100 MB > the 256 MB last-level cache
+    copies = [(wc0.clone(), ws0.clone()) for _ in range(R)]
+    del wc0, ws0
+    N, K = d.N, d.K
+    wbytes = copies[0][0].numel() + copies[0][1].numel()
+    for M in (1, 4, 16):
+        dm = workloads.decode(M=M, N_each=1)          # only X is used from it
+        x = to_gpu(dm.x)
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        wsb = torch.empty(nv.lib.nvfp4_gemm_workspace_size(M, N, K), dtype=torch.uint8, device=dev)
+
+        def step(i, mark, x=x, y=y, wsb=wsb):
+            c, s = copies[i % R]
+            mark(0)
+            prep = nv.nvfp4_gemm_prepare(x, ws=wsb)
+            mark(1)
+            nv.nvfp4_gemm_run(prep, c, s, shared, out=y)
+            mark(2)
+
+        wall, (prep_ms, run_ms) = time_steps(torch, max(steps, 40), warmup + 8, step, 2)
+        nbytes = wbytes + M * K * 2 + M * N * 2
+        step_ms = mean(prep_ms) + mean(run_ms)
+        gbs = nbytes / (step_ms * 1e-3) / 1e9
+        kgbs = nbytes / (mean(run_ms) * 1e-3) / 1e9
+        res.append({"metric": "decode GEMV GB/s at M=%d" % M, "value": round(gbs, 1), "unit": "GB/s",
+                    "ms_per_step": round(step_ms, 5), "wall_ms_per_step": round(wall, 5),
+                    "phases_ms": {"activation_quantize": round(mean(prep_ms), 5),
+                                  "gemv": round(mean(run_ms), 5)},
+                    "config": {"workload": "decode: X[%dx5120] bf16 x fused gate/up W[34816x5120] NVFP4 "
+                                           "(4 rotated copies) -> Y bf16" % M},
+                    "roofline": {"bound": "hbm", "kernel": "gemv_kernel", "achieved": round(kgbs, 1),
+                                 "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(kgbs / PEAK_HBM_GBS, 4),
+                                 "traffic": traffic_for("gemv_m%d" % M, source_sha("gemm.hip", "encode.h",
+                                                                                   "common.h")),
+                                 "algorithmic": "W codes+scales %d B + X + Y = %d B per launch" % (wbytes,
+                                                                                                  nbytes)}})
+        log("decode M=%d: %.1f GB/s step, %.1f GB/s kernel" % (M, gbs, kgbs))
+    del copies
+
+    # ------------------------------------------------ fused q/k/v repair + GEMM
+    log("fused q/k/v workload")
+    f = workloads.fused_qkv()
+    parts = [torch.from_numpy(w).to(dev) for w in f.w_parts]
+    qs = [nv.nvfp4_quantize(w) for w in parts]
+    scales = [s for _, s, _ in qs]
+    gss = [g for _, _, g in qs]
+    sc_backup = [s.clone() for s in scales]
+
+    def rstep(i, mark):
+        for s, b in zip(scales, sc_backup):
+            s.copy_(b)
+        mark(0)
+        nv.nvfp4_fuse_rescale(scales, gss)
+        mark(1)
+
+    _, (resc_ms,) = time_steps(torch, steps, warmup, rstep, 1)
+    shared = nv.nvfp4_fuse_rescale([s.copy_(b) for s, b in zip(scales, sc_backup)], gss)
+    fwc = torch.cat([c for c, _, _ in qs])
+    fws = torch.cat(scales)
+    x = to_gpu(f.x)
+    M, N, K = f.M, f.N, f.K
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    wsb = torch.empty(nv.lib.nvfp4_gemm_workspace_size(M, N, K), dtype=torch.uint8, device=dev)
+
+    def fstep(i, mark):
+        mark(0)
+        prep = nv.nvfp4_gemm_prepare(x, ws=wsb)
+        mark(1)
+        nv.nvfp4_gemm_run(prep, fwc, fws, shared, out=y)
+        mark(2)
+
+    _, (prep_ms, run_ms) = time_steps(torch, steps, warmup, fstep, 2)
+    flops = 2.0 * M * N * K
+    step_ms = mean(prep_ms) + mean(run_ms)
+    rbytes = 2 * sum(s.numel() for s in scales)
+    res.append({"metric": "fused q/k/v W4A4 GEMM TFLOP/s at M=2048", "value": round(flops / step_ms / 1e9, 2),
+                "unit": "TFLOP/s", "ms_per_step": round(step_ms, 4),
+                "phases_ms": {"activation_quantize": round(mean(prep_ms), 4), "gemm": round(mean(run_ms), 4),
+                              "fuse_rescale_offline": round(mean(resc_ms), 5)},
+                "config": {"workload": "fused q/k/v: X[2048x5120] bf16 x [q 6144; k 1024; v 1024]x5120 NVFP4, "
+                                       "block scales repaired onto the shared tensor scale"},
+                "roofline": {"bound": "mfma", "kernel": "gemm_kernel",
+                             "achieved": round(flops / mean(run_ms) / 1e9, 2), "peak": PEAK_FP16_TFLOPS,
+                             "unit": "TFLOP/s", "frac": round(flops / mean(run_ms) / 1e9 / PEAK_FP16_TFLOPS, 4)},
+                "fuse_rescale_GBs": round(rbytes / mean(resc_ms) / 1e6, 1)})
+    del parts, qs, x, y, wsb, fwc, fws
+
+    # ------------------------------------------------ standalone quantize, long prefill
+    log("generating long-prefill activations X[32768x5120] bf16")
+    xl = to_gpu(workloads.long_prefill_activations())
+    rows, K = xl.shape
+    codes = torch.empty((rows, K // 2), dtype=torch.uint8, device=dev)
+    scl = torch.empty((rows, K // 16), dtype=torch.uint8, device=dev)
+    gs = torch.empty(1, dtype=torch.float32, device=dev)
+    qws = nv.workspace(nv.lib.nvfp4_quantize_workspace_size(rows, K), dev)
+
+    def qstep(i, mark):
+        mark(0)
+        st = nv.lib.nvfp4_quantize(xl.data_ptr(), 1, rows, K, K, codes.data_ptr(), scl.data_ptr(), gs.data_ptr(),
+                                   qws.data_ptr(), qws.numel(), torch.cuda.current_stream().cuda_stream)
+        assert st == 0
+        mark(1)
+
+    _, (q_ms,) = time_steps(torch, steps, warmup, qstep, 1)
+    xbytes = rows * K * 2
+    two_pass = 2 * xbytes + rows * K // 2 + rows * K // 16
+    single = xbytes + rows * K // 2 + rows * K // 16
+    qgbs = two_pass / (mean(q_ms) * 1e-3) / 1e9
+    res.append({"metric": "activation quantize GB/s (two-pass bytes)", "value": round(qgbs, 1), "unit": "GB/s",
+                "ms_per_step": round(mean(q_ms), 4),
+                "single_read_GBs": round(single / (mean(q_ms) * 1e-3) / 1e9, 1),
+                "config": {"workload": "long-prefill quantize: X[32768x5120] bf16 Student-t(2.5), 16 hot "
+                                       "channels x200 -> packed E2M1 + E4M3 scales + FP32 scale"},
+                "roofline": {"bound": "hbm", "kernel": "amax_partials_kernel + quantize_packed_kernel",
+                             "achieved": round(qgbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                             "frac": round(qgbs / PEAK_HBM_GBS, 4),
+                             "algorithmic": "2 reads of X + codes + scales = %d B per call" % two_pass}})
+    log("quantize: %.1f GB/s (two-pass count)" % qgbs)
+    del xl, codes, scl
+
+    # ------------------------------------------------ offline weight quantize (fp32 in)
+    w = torch.from_numpy(workloads.gaussian(3, 1, 17408, 5120, 0.02)).to(dev)
+
+    def wstep(i, mark):
+        mark(0)
+        nv.nvfp4_quantize(w)
+        mark(1)
+
+    _, (w_ms,) = time_steps(torch, max(4, steps // 4), 2, wstep, 1)
+    wb = 2 * w.numel() * 4 + w.numel() // 2 + w.numel() // 16
+    res.append({"metric": "weight quantize GB/s (fp32 in, two-pass bytes)",
+                "value": round(wb / (mean(w_ms) * 1e-3) / 1e9, 1), "unit": "GB/s",
+                "ms_per_step": round(mean(w_ms), 4),
+                "config": {"workload": "offline weight quantize W[17408x5120] fp32 N(0,0.02)"}})
+    return res
+
+
+def cpu_baseline(np, p):
+    """The oracle, untuned, on a bounded sample of the headline workload: the
+    W4A4 linear for the first m rows of X against the whole weight (weights
+    quantized beforehand, untimed, as on the GPU)."""
+    import oracle
+    log("cpu baseline: oracle weight quantize (untimed)")
+    wc, ws, wg = oracle.quantize(p.w_parts[0])
+    N, K = p.N, p.K
+    t0 = time.perf_counter()
+    oracle.linear(np.ascontiguousarray(p.x[:1]), wc, ws, wg)
+    t1 = time.perf_counter() - t0
+    m = int(max(1, min(64, round(15.0 / max(t1, 1e-3)))))
+    log("cpu baseline: 1 row took %.2f s, timing %d rows" % (t1, m))
+    t0 = time.perf_counter()
+    oracle.linear(np.ascontiguousarray(p.x[:m]), wc, ws, wg)
+    dt = time.perf_counter() - t0
+    flops = 2.0 * m * N * K
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.num_threads(),
+            "kind": "oracle", "seconds": round(dt, 2),
+            "sample": "W4A4 linear of the first %d of 4096 activation rows (on-the-fly quantize of those rows "
+                      "+ exact int64 GEMM) against the full W[17408x5120]" % m}
+
+
+if __name__ == "__main__":
+    main()

@@ -179,6 +179,28 @@ nvfp4_status_t nvfp4_gemm(const void *x, nvfp4_dtype_t x_dtype, int64_t M, int64
                           const float *w_gs, int64_t N, void *y, nvfp4_dtype_t y_dtype,
                           int64_t ld_y, void *workspace, size_t workspace_bytes, void *stream);
 
+/* ------------------------------------------------------------------------
+ * nvfp4_gemm in two halves, for callers that multiply one activation by
+ * several weights (unfused q/k/v or gate/up: paper section 6 describes the
+ * fused alternative) or that time the contraction alone.
+ *
+ * nvfp4_gemm_prepare quantizes X exactly as nvfp4_gemm does and leaves the
+ * quantized operand and gs_x in the workspace (arguments as in nvfp4_gemm).
+ * nvfp4_gemm_run then computes Y = X W^T from that workspace; it may be
+ * called any number of times with different weights (same M and K) until
+ * the workspace is reused.  The workspace must hold
+ * nvfp4_gemm_workspace_size(M, N, K) bytes for both calls.  The pair is
+ * equivalent to one nvfp4_gemm call.
+ * ---------------------------------------------------------------------- */
+nvfp4_status_t nvfp4_gemm_prepare(const void *x, nvfp4_dtype_t x_dtype, int64_t M, int64_t K,
+                                  int64_t ld_x, void *workspace, size_t workspace_bytes,
+                                  void *stream);
+
+nvfp4_status_t nvfp4_gemm_run(int64_t M, int64_t K, const uint8_t *w_codes,
+                              const uint8_t *w_scales, const float *w_gs, int64_t N, void *y,
+                              nvfp4_dtype_t y_dtype, int64_t ld_y, const void *workspace,
+                              size_t workspace_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -40,6 +40,7 @@ _STATUS = {
 EXPORTS = (
     "nvfp4_status_string", "nvfp4_version", "nvfp4_quantize_workspace_size", "nvfp4_quantize",
     "nvfp4_dequantize", "nvfp4_fuse_rescale", "nvfp4_gemm_workspace_size", "nvfp4_gemm",
+    "nvfp4_gemm_prepare", "nvfp4_gemm_run",
 )
 
 
@@ -51,7 +52,7 @@ class Nvfp4Error(RuntimeError):
 
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
-        raise ImportError("libnvfp4.so is not built; run `python -m nvfp4_w4a4_quantized_02_amd.build` "
+        raise ImportError("libnvfp4.so is not built; run `python nvfp4_w4a4_quantized_02_amd/build.py` "
                           "(or __graft_entry__.build())")
     L = ctypes.CDLL(LIB_PATH)
     P, I64, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t
@@ -71,6 +72,10 @@ def _load() -> ctypes.CDLL:
     L.nvfp4_gemm_workspace_size.restype = SZ
     L.nvfp4_gemm.argtypes = [P, I, I64, I64, I64, P, P, P, I64, P, I, I64, P, SZ, P]
     L.nvfp4_gemm.restype = I
+    L.nvfp4_gemm_prepare.argtypes = [P, I, I64, I64, I64, P, SZ, P]
+    L.nvfp4_gemm_prepare.restype = I
+    L.nvfp4_gemm_run.argtypes = [I64, I64, P, P, P, I64, P, I, I64, P, SZ, P]
+    L.nvfp4_gemm_run.restype = I
     _check_single_hip_runtime()
     return L
 
@@ -181,28 +186,74 @@ def nvfp4_fuse_rescale(scales_list, gs_list) -> torch.Tensor:
     return shared
 
 
+def _out_tensor(M, N, out_dtype, device):
+    # rows padded to a 16-byte multiple, as the kernels store 16-byte aligned
+    per16 = 16 // torch.empty((), dtype=out_dtype).element_size()
+    ld_pad = (N + per16 - 1) // per16 * per16
+    return torch.empty((M, ld_pad), dtype=out_dtype, device=device)[:, :N]
+
+
+def _check_weight(w_codes, w_scales, K):
+    N = w_codes.shape[0]
+    if w_codes.shape[1] * 2 != K or tuple(w_scales.shape) != (N, K // 16):
+        raise ValueError("weight shapes %s / %s do not match K=%d" % (tuple(w_codes.shape),
+                                                                       tuple(w_scales.shape), K))
+    return N
+
+
+def _ld_out(out, M, N):
+    return out.stride(0) if M > 1 else max(N, out.stride(0))
+
+
 def nvfp4_gemm(x: torch.Tensor, w_codes: torch.Tensor, w_scales: torch.Tensor, w_gs: torch.Tensor,
                out_dtype: torch.dtype = torch.bfloat16, out: torch.Tensor | None = None) -> torch.Tensor:
     """Y = X W^T with X [M, K] quantized on the fly and W given as NVFP4
     (codes [N, K/2], scales [N, K/16], w_gs [1])."""
     M, K, ld = _rows_view(x)
-    N = w_codes.shape[0]
-    if w_codes.shape[1] * 2 != K or w_scales.shape != (N, K // 16):
-        raise ValueError("weight shapes %s / %s do not match K=%d" % (tuple(w_codes.shape),
-                                                                       tuple(w_scales.shape), K))
+    N = _check_weight(w_codes, w_scales, K)
     if out is None:
-        # rows padded to a 16-byte multiple, as the kernels store 16-byte aligned
-        per16 = 16 // torch.empty((), dtype=out_dtype).element_size()
-        ld_pad = (N + per16 - 1) // per16 * per16
-        out = torch.empty((M, ld_pad), dtype=out_dtype, device=x.device)[:, :N]
+        out = _out_tensor(M, N, out_dtype, x.device)
     nws = lib.nvfp4_gemm_workspace_size(M, N, K)
     ws = workspace(nws, x.device)
     _check(lib.nvfp4_gemm(x.data_ptr(), _dtype_code(x.dtype), M, K, ld, w_codes.data_ptr(),
                           w_scales.data_ptr(), w_gs.data_ptr(), N, out.data_ptr(), _dtype_code(out.dtype),
-                          out.stride(0) if M > 1 else max(N, out.stride(0)), ws.data_ptr(), ws.numel(),
-                          _stream_ptr(x.device)), "nvfp4_gemm")
+                          _ld_out(out, M, N), ws.data_ptr(), ws.numel(), _stream_ptr(x.device)), "nvfp4_gemm")
     return out
 
 
-__all__ = ["nvfp4_quantize", "nvfp4_dequantize", "nvfp4_fuse_rescale", "nvfp4_gemm", "Nvfp4Error",
+class PreparedActivations:
+    """Result of nvfp4_gemm_prepare: X quantized into its own workspace,
+    reusable by several nvfp4_gemm_run calls (same M and K)."""
+
+    def __init__(self, M, K, ws):
+        self.M, self.K, self.ws = M, K, ws
+
+
+def nvfp4_gemm_prepare(x: torch.Tensor, ws: torch.Tensor | None = None) -> PreparedActivations:
+    """Quantize X into a workspace of its own (or the given uint8 tensor)."""
+    M, K, ld = _rows_view(x)
+    nws = lib.nvfp4_gemm_workspace_size(M, 0, K)
+    if ws is None or ws.numel() < nws:
+        ws = torch.empty(max(nws, 256), dtype=torch.uint8, device=x.device)
+    assert ws.data_ptr() % 256 == 0
+    _check(lib.nvfp4_gemm_prepare(x.data_ptr(), _dtype_code(x.dtype), M, K, ld, ws.data_ptr(), ws.numel(),
+                                  _stream_ptr(x.device)), "nvfp4_gemm_prepare")
+    return PreparedActivations(M, K, ws)
+
+
+def nvfp4_gemm_run(prep: PreparedActivations, w_codes: torch.Tensor, w_scales: torch.Tensor,
+                   w_gs: torch.Tensor, out_dtype: torch.dtype = torch.bfloat16,
+                   out: torch.Tensor | None = None) -> torch.Tensor:
+    M, K = prep.M, prep.K
+    N = _check_weight(w_codes, w_scales, K)
+    if out is None:
+        out = _out_tensor(M, N, out_dtype, prep.ws.device)
+    _check(lib.nvfp4_gemm_run(M, K, w_codes.data_ptr(), w_scales.data_ptr(), w_gs.data_ptr(), N, out.data_ptr(),
+                              _dtype_code(out.dtype), _ld_out(out, M, N), prep.ws.data_ptr(), prep.ws.numel(),
+                              _stream_ptr(prep.ws.device)), "nvfp4_gemm_run")
+    return out
+
+
+__all__ = ["nvfp4_quantize", "nvfp4_dequantize", "nvfp4_fuse_rescale", "nvfp4_gemm", "nvfp4_gemm_prepare",
+           "nvfp4_gemm_run", "PreparedActivations", "Nvfp4Error",
            "status_string", "lib", "EXPORTS", "LIB_PATH", "workspace"]

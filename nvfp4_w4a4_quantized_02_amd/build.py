@@ -2,7 +2,8 @@
 
 Every ``csrc/*.hip`` file is compiled to an object under ``_build/`` and the
 objects are linked into ``nvfp4_w4a4_quantized_02_amd/libnvfp4.so``.  Run as
-``python -m nvfp4_w4a4_quantized_02_amd.build``.
+``python nvfp4_w4a4_quantized_02_amd/build.py`` (a script: importing the
+package itself needs the built library).
 """
 from __future__ import annotations
 

@@ -136,10 +136,57 @@ size_t nvfp4_gemm_workspace_size(int64_t M, int64_t N, int64_t K) {
   return kWsX16 + (size_t)Mp * (size_t)Kp * 2u;
 }
 
+nvfp4_status_t nvfp4_gemm_prepare(const void* x, nvfp4_dtype_t x_dtype, int64_t M, int64_t K, int64_t ld_x,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+  nvfp4_status_t st = check_input(x, x_dtype, M, K, ld_x);
+  if (st != NVFP4_OK) return st;
+  if (K % 32 != 0) return NVFP4_ERR_SHAPE;
+  if (M == 0) return NVFP4_OK;
+  if (!workspace || !aligned(workspace, 256) || workspace_bytes < nvfp4_gemm_workspace_size(M, 0, K))
+    return NVFP4_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  const bool xb = x_dtype == NVFP4_BF16;
+  uint32_t* partials = (uint32_t*)((char*)workspace + kWsPartials);
+  float* gsx = (float*)((char*)workspace + kWsGs);
+  void* x16 = (char*)workspace + kWsX16;
+  int np = launch_amax(x, xb, M, K, ld_x, partials, s);
+  launch_quantize_f16(x, xb, M, K, ld_x, round_up(K, kGemmBK), partials, np, x16, gsx, s);
+  return launched();
+}
+
+nvfp4_status_t nvfp4_gemm_run(int64_t M, int64_t K, const uint8_t* w_codes, const uint8_t* w_scales,
+                              const float* w_gs, int64_t N, void* y, nvfp4_dtype_t y_dtype, int64_t ld_y,
+                              const void* workspace, size_t workspace_bytes, void* stream) {
+  if (!dtype_ok(y_dtype)) return NVFP4_ERR_DTYPE;
+  if (M < 0 || K < 0 || N < 0 || M >= kMaxDim || K >= kMaxDim || N >= kMaxDim) return NVFP4_ERR_SHAPE;
+  if (K % 32 != 0) return NVFP4_ERR_SHAPE;
+  if (M == 0 || N == 0) return NVFP4_OK;
+  if (!y || !w_gs) return NVFP4_ERR_NULL;
+  if (ld_y < N) return NVFP4_ERR_SHAPE;
+  if (!aligned(y, 16) || ((uint64_t)ld_y * esize(y_dtype)) % 16 != 0) return NVFP4_ERR_ALIGN;
+  if (K > 0) {
+    if (!w_codes || !w_scales) return NVFP4_ERR_NULL;
+    if (!aligned(w_codes, 16) || !aligned(w_scales, 2)) return NVFP4_ERR_ALIGN;
+  }
+  if (!workspace || !aligned(workspace, 256) || workspace_bytes < nvfp4_gemm_workspace_size(M, N, K))
+    return NVFP4_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  const bool yb = y_dtype == NVFP4_BF16;
+  const float* gsx = (const float*)((const char*)workspace + kWsGs);
+  const void* x16 = (const char*)workspace + kWsX16;
+  const int64_t Kp = round_up(K, kGemmBK);
+  if (M <= kGemvMaxM)
+    launch_gemv(x16, M, Kp, w_codes, w_scales, N, K, gsx, w_gs, y, yb, ld_y, s);
+  else
+    launch_gemm(x16, M, Kp, w_codes, w_scales, N, K, gsx, w_gs, y, yb, ld_y, s);
+  return launched();
+}
+
 nvfp4_status_t nvfp4_gemm(const void* x, nvfp4_dtype_t x_dtype, int64_t M, int64_t K, int64_t ld_x,
                           const uint8_t* w_codes, const uint8_t* w_scales, const float* w_gs, int64_t N, void* y,
                           nvfp4_dtype_t y_dtype, int64_t ld_y, void* workspace, size_t workspace_bytes,
                           void* stream) {
+  // validate everything before the first launch
   nvfp4_status_t st = check_input(x, x_dtype, M, K, ld_x);
   if (st != NVFP4_OK) return st;
   if (!dtype_ok(y_dtype)) return NVFP4_ERR_DTYPE;
@@ -155,19 +202,9 @@ nvfp4_status_t nvfp4_gemm(const void* x, nvfp4_dtype_t x_dtype, int64_t M, int64
   }
   if (!workspace || !aligned(workspace, 256) || workspace_bytes < nvfp4_gemm_workspace_size(M, N, K))
     return NVFP4_ERR_WORKSPACE;
-  hipStream_t s = (hipStream_t)stream;
-  const bool xb = x_dtype == NVFP4_BF16, yb = y_dtype == NVFP4_BF16;
-  uint32_t* partials = (uint32_t*)((char*)workspace + kWsPartials);
-  float* gsx = (float*)((char*)workspace + kWsGs);
-  void* x16 = (char*)workspace + kWsX16;
-  const int64_t Kp = round_up(K, kGemmBK);
-  int np = launch_amax(x, xb, M, K, ld_x, partials, s);
-  launch_quantize_f16(x, xb, M, K, ld_x, Kp, partials, np, x16, gsx, s);
-  if (M <= kGemvMaxM)
-    launch_gemv(x16, M, Kp, w_codes, w_scales, N, K, gsx, w_gs, y, yb, ld_y, s);
-  else
-    launch_gemm(x16, M, Kp, w_codes, w_scales, N, K, gsx, w_gs, y, yb, ld_y, s);
-  return launched();
+  st = nvfp4_gemm_prepare(x, x_dtype, M, K, ld_x, workspace, workspace_bytes, stream);
+  if (st != NVFP4_OK) return st;
+  return nvfp4_gemm_run(M, K, w_codes, w_scales, w_gs, N, y, y_dtype, ld_y, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

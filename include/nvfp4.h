@@ -61,7 +61,7 @@ extern "C" {
 typedef enum nvfp4_status {
     NVFP4_OK = 0,
     NVFP4_ERR_NULL = 1,      /* a required pointer is NULL                    */
-    NVFP4_ERR_SHAPE = 2,     /* negative size, K not a multiple of 16 (32 for
+    NVFP4_ERR_SHAPE = 2,     /* negative size, K not a multiple of 16 (64 for
                                 the GEMM), leading dimension too small, or a
                                 size beyond 2^31 elements per dimension        */
     NVFP4_ERR_DTYPE = 3,     /* dtype argument not NVFP4_F32 / NVFP4_BF16      */
@@ -162,9 +162,10 @@ nvfp4_status_t nvfp4_fuse_rescale(int n, uint8_t *const *scales, const int64_t *
  *
  *   x        device [M, ld_x] row-major, F32 or BF16; 16-byte aligned,
  *            ld_x * element size a multiple of 16 bytes, ld_x >= K.
- *   M, K, N  >= 0; K % 32 == 0.
+ *   M, K, N  >= 0; K % 64 == 0 (the GEMM advances K 64 at a time, which
+ *            is 4 scale bytes, one aligned dword, per weight row).
  *   w_codes  device [N, K/2] uint8 dense, 16-byte aligned.
- *   w_scales device [N, K/16] uint8 dense.
+ *   w_scales device [N, K/16] uint8 dense, 4-byte aligned.
  *   w_gs     device, one float.  For a fused weight: the gs_shared of
  *            nvfp4_fuse_rescale.
  *   y        device out [M, ld_y] row-major, F32 or BF16; 16-byte aligned,

@@ -140,7 +140,7 @@ nvfp4_status_t nvfp4_gemm_prepare(const void* x, nvfp4_dtype_t x_dtype, int64_t 
                                   void* workspace, size_t workspace_bytes, void* stream) {
   nvfp4_status_t st = check_input(x, x_dtype, M, K, ld_x);
   if (st != NVFP4_OK) return st;
-  if (K % 32 != 0) return NVFP4_ERR_SHAPE;
+  if (K % 64 != 0) return NVFP4_ERR_SHAPE;
   if (M == 0) return NVFP4_OK;
   if (!workspace || !aligned(workspace, 256) || workspace_bytes < nvfp4_gemm_workspace_size(M, 0, K))
     return NVFP4_ERR_WORKSPACE;
@@ -159,14 +159,14 @@ nvfp4_status_t nvfp4_gemm_run(int64_t M, int64_t K, const uint8_t* w_codes, cons
                               const void* workspace, size_t workspace_bytes, void* stream) {
   if (!dtype_ok(y_dtype)) return NVFP4_ERR_DTYPE;
   if (M < 0 || K < 0 || N < 0 || M >= kMaxDim || K >= kMaxDim || N >= kMaxDim) return NVFP4_ERR_SHAPE;
-  if (K % 32 != 0) return NVFP4_ERR_SHAPE;
+  if (K % 64 != 0) return NVFP4_ERR_SHAPE;
   if (M == 0 || N == 0) return NVFP4_OK;
   if (!y || !w_gs) return NVFP4_ERR_NULL;
   if (ld_y < N) return NVFP4_ERR_SHAPE;
   if (!aligned(y, 16) || ((uint64_t)ld_y * esize(y_dtype)) % 16 != 0) return NVFP4_ERR_ALIGN;
   if (K > 0) {
     if (!w_codes || !w_scales) return NVFP4_ERR_NULL;
-    if (!aligned(w_codes, 16) || !aligned(w_scales, 2)) return NVFP4_ERR_ALIGN;
+    if (!aligned(w_codes, 16) || !aligned(w_scales, 4)) return NVFP4_ERR_ALIGN;
   }
   if (!workspace || !aligned(workspace, 256) || workspace_bytes < nvfp4_gemm_workspace_size(M, N, K))
     return NVFP4_ERR_WORKSPACE;
@@ -191,14 +191,14 @@ nvfp4_status_t nvfp4_gemm(const void* x, nvfp4_dtype_t x_dtype, int64_t M, int64
   if (st != NVFP4_OK) return st;
   if (!dtype_ok(y_dtype)) return NVFP4_ERR_DTYPE;
   if (N < 0 || N >= kMaxDim) return NVFP4_ERR_SHAPE;
-  if (K % 32 != 0) return NVFP4_ERR_SHAPE;
+  if (K % 64 != 0) return NVFP4_ERR_SHAPE;
   if (M == 0 || N == 0) return NVFP4_OK;
   if (!y || !w_gs) return NVFP4_ERR_NULL;
   if (ld_y < N) return NVFP4_ERR_SHAPE;
   if (!aligned(y, 16) || ((uint64_t)ld_y * esize(y_dtype)) % 16 != 0) return NVFP4_ERR_ALIGN;
   if (K > 0) {
     if (!w_codes || !w_scales) return NVFP4_ERR_NULL;
-    if (!aligned(w_codes, 16) || !aligned(w_scales, 2)) return NVFP4_ERR_ALIGN;
+    if (!aligned(w_codes, 16) || !aligned(w_scales, 4)) return NVFP4_ERR_ALIGN;
   }
   if (!workspace || !aligned(workspace, 256) || workspace_bytes < nvfp4_gemm_workspace_size(M, N, K))
     return NVFP4_ERR_WORKSPACE;

@@ -53,11 +53,49 @@ __device__ __forceinline__ void store4(uint8_t* __restrict__ yrow, int n, int N,
 
 // ====================================================================== GEMM
 // Workgroup tile 256 (W rows) x 256 (X rows), 4 waves in a 2 x 2 grid, each
-// wave 128 x 128 = 4 x 4 MFMA 32x32x16 tiles (256 fp32 accumulators per lane).
-// X tiles (256 rows x 64 k fp16 = 32 KB) go through LDS, double-buffered,
-// with the 16-byte chunk index XOR-swizzled by (row & 7) so the MFMA operand
-// reads are bank-conflict free.  W fragments go global -> registers and are
-// expanded per sub-step.
+// wave 128 x 128 = 4 x 4 MFMA 32x32x16 tiles (256 fp32 accumulators per lane,
+// held in the accumulation registers).  K advances 64 per step.
+//
+// Every operand byte reaches LDS by direct global->LDS transfers
+// (global_load_lds): the X tile (256 rows x 64 k fp16 = 32 KB), the W codes
+// (256 rows x 32 B) and the W scale bytes (256 rows x 4 B).  Three buffers
+// form a ring: step kt computes from buffer kt%3 while the transfers of step
+// kt+2 are in flight, so one barrier per step suffices and no staging
+// registers are needed.  Because all memory traffic is of this one kind and
+// completes in issue order, the wait before each barrier is exact.
+//
+// LDS layouts (16-byte slots): X chunk (row, c) sits in slot c ^ (row & 7) of
+// the row; W code half (row, h) in slot h ^ ((row >> 2) & 1).  Both keep the
+// operand reads free of bank conflicts.
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// Direct global->LDS transfers.  Lane i of the wave writes `size` bytes at
+// LDS byte address `lds` + i * size; `lds` is wave-uniform and goes through
+// M0 (one wait state after the SALU write of M0).  The transfers have no
+// destination registers, and the compiler is not told about them: every wait
+// on them is an explicit s_waitcnt below, which lets the main loop keep two
+// steps in flight where the compiler's own bookkeeping would drain them.
+// M0 is written only here; nothing else in these kernels uses it.
+__device__ __forceinline__ void lds_dma16(const void* g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void lds_dma4(const void* g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(lds)
+               : "memory", "m0");
+}
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return __builtin_amdgcn_readfirstlane((uint32_t)(size_t)(const lds_void_t*)p);
+}
+
+struct GemmBuf {
+  uint4 x[kGemmBM * 8];        // 32 KB
+  uint4 wc[kGemmBN * 2];       // 8 KB
+  uint32_t ws[kGemmBN];        // 1 KB
+};
+
+constexpr int kDmaPerStep = 11;  // per wave: 8 (X) + 2 (W codes) + 1 (W scales)
+
 template <bool kYBf16>
 __global__ __launch_bounds__(256, 1) void gemm_kernel(const uint4* __restrict__ x16, uint32_t kp_chunks,
                                                        const uint8_t* __restrict__ wc,
@@ -65,27 +103,44 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(const uint4* __restrict__ 
                                                        const float* __restrict__ gsx_p,
                                                        const float* __restrict__ gsw_p, uint8_t* __restrict__ y,
                                                        size_t ld_y_bytes, int tiles_n, int nk) {
-  __shared__ uint4 lds[2][kGemmBM * 8];
+  // Three distinct buffers (not one indexed array) so the compiler can see
+  // that a transfer into one buffer never feeds reads of another.
+  __shared__ GemmBuf b0, b1, b2;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wave_n = wave >> 1, wave_m = wave & 1;
   const int tn = blockIdx.x % tiles_n, tm = blockIdx.x / tiles_n;
   const int n0 = tn * kGemmBN, m0 = tm * kGemmBM;
   const int l32 = lane & 31, h = lane >> 5;
-
   const size_t kh = (size_t)K / 2, ks = (size_t)K / 16;
-  const uint8_t* wcp[4];
-  const uint8_t* wsp[4];
+
+  // ---- transfer sources (per lane), advanced by kt
+  // X: instruction j fills slots (wave*8+j)*64 + lane
+  const uint4* xsrc = x16 + (size_t)(m0 + wave * 64 + (lane >> 3)) * kp_chunks + ((lane & 7) ^ ((lane >> 3) & 7));
+  // W codes: instruction j fills slots (wave*2+j)*64 + lane = row*2 + physical half
+  const uint8_t* wcsrc[2];
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    int n = n0 + wave_n * 128 + t * 32 + l32;
+  for (int j = 0; j < 2; ++j) {
+    int row = (wave * 2 + j) * 32 + (lane >> 1);
+    int n = n0 + row < N ? n0 + row : N - 1;   // rows past N repeat the last one (not stored)
+    int half = (lane & 1) ^ ((lane >> 3) & 1);
+    wcsrc[j] = wc + (size_t)n * kh + half * 16;
+  }
+  // W scales: one dword (4 blocks) per row
+  const uint8_t* wssrc;
+  {
+    int n = n0 + wave * 64 + lane;
     n = n < N ? n : N - 1;
-    wcp[t] = wc + (size_t)n * kh + h * 16;
-    wsp[t] = ws + (size_t)n * ks + h * 2;
+    wssrc = ws + (size_t)n * ks;
   }
 
-  const int st_row0 = tid >> 3;
-  const int st_ch = (tid & 7) ^ (st_row0 & 7);
-  const uint4* xp = x16 + (size_t)(m0 + st_row0) * kp_chunks + (tid & 7);
+  auto issue = [&](int kt, GemmBuf& b) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      lds_dma16(xsrc + (size_t)(8 * j) * kp_chunks + (size_t)kt * 8, lds_addr(&b.x[(wave * 8 + j) * 64]));
+#pragma unroll
+    for (int j = 0; j < 2; ++j) lds_dma16(wcsrc[j] + (size_t)kt * 32, lds_addr(&b.wc[(wave * 2 + j) * 64]));
+    lds_dma4(wssrc + (size_t)kt * 4, lds_addr(&b.ws[wave * 64]));
+  };
 
   floatx16 acc[4][4];
 #pragma unroll
@@ -95,43 +150,22 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(const uint4* __restrict__ 
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[t][u][r] = 0.0f;
 
-  uint4 xr[8];
-  uint4 wcur[4], wnxt[4];
-  uint32_t scur[4], snxt[4];
-
-  if (nk > 0) {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) xr[j] = xp[(size_t)(32 * j) * kp_chunks];
-    const bool ok = h * 32 < K;
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      wcur[t] = ok ? *reinterpret_cast<const uint4*>(wcp[t]) : make_uint4(0, 0, 0, 0);
-      scur[t] = ok ? *reinterpret_cast<const uint16_t*>(wsp[t]) : 0u;
-    }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) lds[0][(st_row0 + 32 * j) * 8 + st_ch] = xr[j];
-  }
-  __syncthreads();
-
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    const bool more = kt + 1 < nk;
-    if (more) {
-      const int k1 = kt + 1;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) xr[j] = xp[(size_t)(32 * j) * kp_chunks + (size_t)k1 * 8];
-      const bool ok = k1 * 64 + h * 32 < K;
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        wnxt[t] = ok ? *reinterpret_cast<const uint4*>(wcp[t] + (size_t)k1 * 32) : make_uint4(0, 0, 0, 0);
-        snxt[t] = ok ? *reinterpret_cast<const uint16_t*>(wsp[t] + (size_t)k1 * 4) : 0u;
-      }
-    }
+  // One main-loop step: compute step kt from `cur` while the transfers of
+  // step kt+2 (into `nxt2`) are in flight.  Every step issues the same
+  // transfers (near the end they repeat the last step into a buffer that is
+  // no longer read), so the wait count is the same in every step.
+  auto step = [&](int kt, const GemmBuf& cur, GemmBuf& nxt2) {
+    const int last = nk - 1;
+    issue(kt + 2 < last ? kt + 2 : last, nxt2);
+    uint4 wv[4];
     ScaleSplit sp[4][2];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      sp[t][0] = split_scale(scur[t] & 0xFFu);
-      sp[t][1] = split_scale(scur[t] >> 8);
+      const int row = wave_n * 128 + t * 32 + l32;
+      wv[t] = cur.wc[row * 2 + (h ^ ((row >> 2) & 1))];
+      const uint32_t sb = cur.ws[row] >> (16 * h);
+      sp[t][0] = split_scale(sb & 0xFFu);
+      sp[t][1] = split_scale((sb >> 8) & 0xFFu);
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -139,14 +173,13 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(const uint4* __restrict__ 
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int row = wave_m * 128 + u * 32 + l32;
-        const int ch = (4 * h + j) ^ (row & 7);
-        bx[u] = u4_as_f16x8(lds[buf][row * 8 + ch]);
+        bx[u] = u4_as_f16x8(cur.x[row * 8 + ((4 * h + j) ^ (row & 7))]);
       }
       f16x8 aw[4];
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         uint32_t e[4];
-        expand8(dword_of(wcur[t], j), sp[t][j >> 1], e);
+        expand8(dword_of(wv[t], j), sp[t][j >> 1], e);
         aw[t] = u4_as_f16x8(make_uint4(e[0], e[1], e[2], e[3]));
       }
 #pragma unroll
@@ -155,16 +188,26 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(const uint4* __restrict__ 
         for (int u = 0; u < 4; ++u)
           acc[t][u] = __builtin_amdgcn_mfma_f32_32x32x16_f16(aw[t], bx[u], acc[t][u], 0, 0, 0);
     }
-    if (more) {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) lds[buf ^ 1][(st_row0 + 32 * j) * 8 + st_ch] = xr[j];
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        wcur[t] = wnxt[t];
-        scur[t] = snxt[t];
-      }
+    // The transfers of step kt+1 must have landed before the barrier; only
+    // this step's (kt+2) may still be in flight.  The barrier is a bare
+    // s_barrier: a workgroup fence would also wait for those.  The LDS reads
+    // of `cur` are complete here (their values fed the MFMAs above), so `cur`
+    // may be refilled after it.
+    asm volatile("s_waitcnt vmcnt(11)\n\ts_barrier" ::: "memory");
+  };
+  static_assert(kDmaPerStep == 11, "the wait count above must match the transfers per step");
+
+  if (nk > 0) {
+    issue(0, b0);
+    issue(nk > 1 ? 1 : 0, b1);
+    asm volatile("s_waitcnt vmcnt(11)\n\ts_barrier" ::: "memory");
+    for (int kt = 0; kt < nk; kt += 3) {
+      step(kt, b0, b2);
+      if (kt + 1 < nk) step(kt + 1, b1, b0);
+      if (kt + 2 < nk) step(kt + 2, b2, b1);
     }
-    __syncthreads();
+    // drain the repeated transfers before the workgroup can exit
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   }
 
   const float scale = (*gsx_p) * (*gsw_p);

@@ -56,7 +56,7 @@ def test_workspace_sizes(nv):
     assert small >= 16 * 5120 * 2
     assert big >= 4096 * 5120 * 2
     # ragged M pads to the 256-row tile, ragged K to 64
-    assert L.nvfp4_gemm_workspace_size(257, 1, 96) - L.nvfp4_gemm_workspace_size(0, 1, 0) == 512 * 128 * 2
+    assert L.nvfp4_gemm_workspace_size(257, 1, 128) - L.nvfp4_gemm_workspace_size(0, 1, 0) == 512 * 128 * 2
 
 
 def q(nv, x=A, dt=BF16, rows=4, K=32, ld=32, codes=A, scales=A, gs=A, ws=A, nws=BIG):
@@ -86,7 +86,8 @@ def g(nv, x=A, dt=BF16, M=32, K=64, ld=64, wc=A, wsc=A, wg=A, N=64, y=A, ydt=BF1
 def test_gemm_rejects(nv):
     assert g(nv, dt=2) == E_DTYPE
     assert g(nv, ydt=7) == E_DTYPE
-    assert g(nv, K=48, ld=48) == E_SHAPE              # K % 32
+    assert g(nv, K=48, ld=48) == E_SHAPE              # K % 64
+    assert g(nv, K=96, ld=96) == E_SHAPE
     assert g(nv, N=-3) == E_SHAPE
     assert g(nv, ldy=32) == E_SHAPE
     assert g(nv, y=None) == E_NULL

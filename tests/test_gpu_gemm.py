@@ -81,8 +81,8 @@ def test_decode_small_n(nv, orc, M, out):
     check_gemm(_run(nv, p, od), _full_ref(orc, p), out == "bf16", "decode M=%d" % M)
 
 
-@pytest.mark.parametrize("M,N,K", [(17, 300, 1056), (300, 260, 512), (256, 256, 256), (511, 129, 96),
-                                   (40, 1000, 5120)])
+@pytest.mark.parametrize("M,N,K", [(17, 300, 1088), (300, 260, 512), (256, 256, 256), (511, 129, 192),
+                                   (40, 1000, 5120), (300, 257, 64), (257, 300, 128), (600, 520, 320)])
 @pytest.mark.parametrize("out", ["bf16", "f32"])
 def test_gemm_ragged(nv, orc, M, N, K, out):
     p = workloads.prefill(M=M, K=K, N=N)

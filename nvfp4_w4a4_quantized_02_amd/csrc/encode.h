@@ -103,8 +103,10 @@ __device__ __forceinline__ uint32_t encode_block(const uint32_t (&absbits)[16], 
 // E4M3value(sb), exact in fp16 (values from 2^-10 to 2688, at most 6
 // significant bits).  The scale splits into a power of two, applied by the
 // hardware FP4 conversion (which uses only the exponent of its scale
-// operand), and a small multiplier q applied by one packed fp16 multiply:
-// normal bytes: 2^(e-7) * (1 + m/8); subnormal bytes: 2^-9 * m.
+// operand), and a small integer multiplier q applied by one packed fp16
+// multiply: E4M3value = 2^(max(e,1) - 10) * q with q = 8 + m for normal
+// bytes (e >= 1) and q = m for subnormal ones (e = 0).  Both factors and the
+// products stay exact in fp16.
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 
@@ -116,13 +118,9 @@ struct ScaleSplit {
 __device__ __forceinline__ ScaleSplit split_scale(uint32_t sb) {
   uint32_t e = (sb >> 3) & 15u, m = sb & 7u;
   ScaleSplit s;
-  s.p2 = __uint_as_float((e ? (e + 120u) : 118u) << 23);
-  // fp16 bits of q: normal 1 + m/8 = 0x3C00 | m << 7; subnormal m (0..7)
-  uint32_t qn = 0x3C00u | (m << 7);
-  uint32_t qs = __builtin_bit_cast(uint16_t, (_Float16)(float)m);
-  uint32_t q = e ? qn : qs;
-  uint32_t q2 = q | (q << 16);
-  s.q2 = __builtin_bit_cast(half2_t, q2);
+  s.p2 = __uint_as_float(((e > 1u ? e : 1u) + 117u) << 23);
+  uint32_t q = __builtin_bit_cast(uint16_t, (_Float16)(uint16_t)(m | ((e < 1u ? e : 1u) << 3)));
+  s.q2 = __builtin_bit_cast(half2_t, q | (q << 16));
   return s;
 }
 

@@ -64,24 +64,27 @@ __device__ __forceinline__ void store4(uint8_t* __restrict__ yrow, int n, int N,
 // registers are needed.  Because all memory traffic is of this one kind and
 // completes in issue order, the wait before each barrier is exact.
 //
-// LDS layouts (16-byte slots): X chunk (row, c) sits in slot c ^ (row & 7) of
-// the row; W code half (row, h) in slot h ^ ((row >> 2) & 1).  Both keep the
-// operand reads free of bank conflicts.
+// LDS layouts (16-byte slots): X chunk (row, c) sits in slot
+// c ^ (row & 7) ^ ((row >> 3) & 1) of its row; W code half (row, h) in slot
+// h ^ (((row >> 2) ^ (row >> 3)) & 1).  Any 8 or 16 consecutive rows then hit
+// distinct 16-byte bank groups, so the 128-bit operand reads are free of
+// bank conflicts whether the LDS serves 8 or 16 lanes per pass.
 typedef __attribute__((address_space(3))) void lds_void_t;
 
-// Direct global->LDS transfers.  Lane i of the wave writes `size` bytes at
-// LDS byte address `lds` + i * size; `lds` is wave-uniform and goes through
-// M0 (one wait state after the SALU write of M0).  The transfers have no
+// Direct global->LDS transfers from a wave-uniform base (scalar registers)
+// plus a 32-bit per-lane byte offset.  Lane i of the wave writes `size` bytes
+// at LDS byte address `lds` + i * size; `lds` is wave-uniform and goes
+// through M0 (one wait state after the SALU write of M0).  The transfers have no
 // destination registers, and the compiler is not told about them: every wait
 // on them is an explicit s_waitcnt below, which lets the main loop keep two
 // steps in flight where the compiler's own bookkeeping would drain them.
 // M0 is written only here; nothing else in these kernels uses it.
-__device__ __forceinline__ void lds_dma16(const void* g, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds)
+__device__ __forceinline__ void lds_dma16(const void* base, uint32_t off, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "s"(lds)
                : "memory", "m0");
 }
-__device__ __forceinline__ void lds_dma4(const void* g, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(lds)
+__device__ __forceinline__ void lds_dma4(const void* base, uint32_t off, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(off), "s"(base), "s"(lds)
                : "memory", "m0");
 }
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
@@ -113,33 +116,45 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(const uint4* __restrict__ 
   const int l32 = lane & 31, h = lane >> 5;
   const size_t kh = (size_t)K / 2, ks = (size_t)K / 16;
 
-  // ---- transfer sources (per lane), advanced by kt
-  // X: instruction j fills slots (wave*8+j)*64 + lane
-  const uint4* xsrc = x16 + (size_t)(m0 + wave * 64 + (lane >> 3)) * kp_chunks + ((lane & 7) ^ ((lane >> 3) & 7));
-  // W codes: instruction j fills slots (wave*2+j)*64 + lane = row*2 + physical half
-  const uint8_t* wcsrc[2];
+  // ---- transfer sources: a wave-uniform base per step plus per-lane byte
+  // offsets fixed for the whole loop.
+  const uint8_t* xbase = reinterpret_cast<const uint8_t*>(x16 + (size_t)m0 * kp_chunks);  // + 128 B per step
+  const uint8_t* wcbase = wc + (size_t)n0 * kh;                                          // + 32 B per step
+  const uint8_t* wsbase = ws + (size_t)n0 * ks;                                          // + 4 B per step
+  uint32_t xoff[8];  // X: instruction j fills slots (wave*8+j)*64 + lane (row wave*64+8j+lane/8)
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    xoff[j] = ((uint32_t)(wave * 64 + 8 * j + (lane >> 3)) * kp_chunks +
+               ((lane & 7) ^ ((lane >> 3) & 7) ^ (j & 1))) * 16u;
+  uint32_t wcoff[2];  // W codes: instruction j fills slots (wave*2+j)*64 + lane = row*2 + physical half
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     int row = (wave * 2 + j) * 32 + (lane >> 1);
-    int n = n0 + row < N ? n0 + row : N - 1;   // rows past N repeat the last one (not stored)
-    int half = (lane & 1) ^ ((lane >> 3) & 1);
-    wcsrc[j] = wc + (size_t)n * kh + half * 16;
+    row = n0 + row < N ? row : N - 1 - n0;   // rows past N repeat the last one (not stored)
+    wcoff[j] = (uint32_t)row * (uint32_t)kh + (uint32_t)(((lane & 1) ^ (((lane >> 3) ^ (lane >> 4)) & 1)) * 16);
   }
-  // W scales: one dword (4 blocks) per row
-  const uint8_t* wssrc;
+  uint32_t wsoff;  // W scales: one dword (4 blocks) per row
   {
-    int n = n0 + wave * 64 + lane;
-    n = n < N ? n : N - 1;
-    wssrc = ws + (size_t)n * ks;
+    int row = wave * 64 + lane;
+    row = n0 + row < N ? row : N - 1 - n0;
+    wsoff = (uint32_t)row * (uint32_t)ks;
   }
+  // LDS byte addresses of this wave's transfer slots in each buffer
+  const uint32_t lx0 = lds_addr(&b0.x[wave * 512]), lx1 = lds_addr(&b1.x[wave * 512]),
+                 lx2 = lds_addr(&b2.x[wave * 512]);
+  const uint32_t lc0 = lds_addr(&b0.wc[wave * 128]), lc1 = lds_addr(&b1.wc[wave * 128]),
+                 lc2 = lds_addr(&b2.wc[wave * 128]);
+  const uint32_t ls0 = lds_addr(&b0.ws[wave * 64]), ls1 = lds_addr(&b1.ws[wave * 64]),
+                 ls2 = lds_addr(&b2.ws[wave * 64]);
 
-  auto issue = [&](int kt, GemmBuf& b) {
+  auto issue = [&](int kt, uint32_t lx, uint32_t lc, uint32_t ls) {
+    const uint8_t* xb = xbase + (size_t)kt * 128;
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-      lds_dma16(xsrc + (size_t)(8 * j) * kp_chunks + (size_t)kt * 8, lds_addr(&b.x[(wave * 8 + j) * 64]));
+    for (int j = 0; j < 8; ++j) lds_dma16(xb, xoff[j], lx + j * 1024);
+    const uint8_t* cb = wcbase + (size_t)kt * 32;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) lds_dma16(wcsrc[j] + (size_t)kt * 32, lds_addr(&b.wc[(wave * 2 + j) * 64]));
-    lds_dma4(wssrc + (size_t)kt * 4, lds_addr(&b.ws[wave * 64]));
+    for (int j = 0; j < 2; ++j) lds_dma16(cb, wcoff[j], lc + j * 1024);
+    lds_dma4(wsbase + (size_t)kt * 4, wsoff, ls);
   };
 
   floatx16 acc[4][4];
@@ -150,43 +165,66 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(const uint4* __restrict__ 
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[t][u][r] = 0.0f;
 
+  // Operand fragments of sub-step j from buffer `cur`.
+  auto read_x = [&](const GemmBuf& cur, int j, f16x8 (&bx)[4]) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int row = wave_m * 128 + u * 32 + l32;
+      bx[u] = u4_as_f16x8(cur.x[row * 8 + ((4 * h + j) ^ (row & 7) ^ ((row >> 3) & 1))]);
+    }
+  };
+  auto expand_w = [&](const uint4 (&wv)[4], const ScaleSplit (&sp)[4][2], int j, f16x8 (&aw)[4]) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      uint32_t e[4];
+      expand8(dword_of(wv[t], j), sp[t][j >> 1], e);
+      aw[t] = u4_as_f16x8(make_uint4(e[0], e[1], e[2], e[3]));
+    }
+  };
+
   // One main-loop step: compute step kt from `cur` while the transfers of
-  // step kt+2 (into `nxt2`) are in flight.  Every step issues the same
-  // transfers (near the end they repeat the last step into a buffer that is
-  // no longer read), so the wait count is the same in every step.
-  auto step = [&](int kt, const GemmBuf& cur, GemmBuf& nxt2) {
+  // step kt+2 are in flight.  Every step issues the same transfers (near the
+  // end they repeat the last step into a buffer that is no longer read), so
+  // the wait count is the same in every step.  Within the step, the LDS
+  // reads and the W expansion of sub-step j+1 are issued ahead of the MFMAs
+  // of sub-step j.
+  auto step = [&](int kt, const GemmBuf& cur, uint32_t lx, uint32_t lc, uint32_t ls) {
     const int last = nk - 1;
-    issue(kt + 2 < last ? kt + 2 : last, nxt2);
     uint4 wv[4];
-    ScaleSplit sp[4][2];
+    uint32_t sw[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const int row = wave_n * 128 + t * 32 + l32;
-      wv[t] = cur.wc[row * 2 + (h ^ ((row >> 2) & 1))];
-      const uint32_t sb = cur.ws[row] >> (16 * h);
-      sp[t][0] = split_scale(sb & 0xFFu);
-      sp[t][1] = split_scale((sb >> 8) & 0xFFu);
+      wv[t] = cur.wc[row * 2 + (h ^ (((row >> 2) ^ (row >> 3)) & 1))];
+      sw[t] = cur.ws[row] >> (16 * h);
     }
+    f16x8 bx[4], aw[4];
+    read_x(cur, 0, bx);
+    issue(kt + 2 < last ? kt + 2 : last, lx, lc, ls);
+    ScaleSplit sp[4][2];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      sp[t][0] = split_scale(sw[t] & 0xFFu);
+      sp[t][1] = split_scale((sw[t] >> 8) & 0xFFu);
+    }
+    expand_w(wv, sp, 0, aw);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      f16x8 bx[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int row = wave_m * 128 + u * 32 + l32;
-        bx[u] = u4_as_f16x8(cur.x[row * 8 + ((4 * h + j) ^ (row & 7))]);
-      }
-      f16x8 aw[4];
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        uint32_t e[4];
-        expand8(dword_of(wv[t], j), sp[t][j >> 1], e);
-        aw[t] = u4_as_f16x8(make_uint4(e[0], e[1], e[2], e[3]));
-      }
+      f16x8 bxn[4], awn[4];
+      if (j < 3) read_x(cur, j + 1, bxn);
 #pragma unroll
       for (int t = 0; t < 4; ++t)
 #pragma unroll
         for (int u = 0; u < 4; ++u)
           acc[t][u] = __builtin_amdgcn_mfma_f32_32x32x16_f16(aw[t], bx[u], acc[t][u], 0, 0, 0);
+      if (j < 3) {
+        expand_w(wv, sp, j + 1, awn);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          bx[q] = bxn[q];
+          aw[q] = awn[q];
+        }
+      }
     }
     // The transfers of step kt+1 must have landed before the barrier; only
     // this step's (kt+2) may still be in flight.  The barrier is a bare
@@ -198,13 +236,13 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(const uint4* __restrict__ 
   static_assert(kDmaPerStep == 11, "the wait count above must match the transfers per step");
 
   if (nk > 0) {
-    issue(0, b0);
-    issue(nk > 1 ? 1 : 0, b1);
+    issue(0, lx0, lc0, ls0);
+    issue(nk > 1 ? 1 : 0, lx1, lc1, ls1);
     asm volatile("s_waitcnt vmcnt(11)\n\ts_barrier" ::: "memory");
     for (int kt = 0; kt < nk; kt += 3) {
-      step(kt, b0, b2);
-      if (kt + 1 < nk) step(kt + 1, b1, b0);
-      if (kt + 2 < nk) step(kt + 2, b2, b1);
+      step(kt, b0, lx2, lc2, ls2);
+      if (kt + 1 < nk) step(kt + 1, b1, lx0, lc0, ls0);
+      if (kt + 2 < nk) step(kt + 2, b2, lx1, lc1, ls1);
     }
     // drain the repeated transfers before the workgroup can exit
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");

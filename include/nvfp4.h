@@ -189,9 +189,11 @@ nvfp4_status_t nvfp4_gemm(const void *x, nvfp4_dtype_t x_dtype, int64_t M, int64
  * quantized operand and gs_x in the workspace (arguments as in nvfp4_gemm).
  * nvfp4_gemm_run then computes Y = X W^T from that workspace; it may be
  * called any number of times with different weights (same M and K) until
- * the workspace is reused.  The workspace must hold
- * nvfp4_gemm_workspace_size(M, N, K) bytes for both calls.  The pair is
- * equivalent to one nvfp4_gemm call.
+ * the workspace is reused.  nvfp4_gemm_prepare needs
+ * nvfp4_gemm_workspace_size(M, 0, K) bytes; nvfp4_gemm_run needs
+ * nvfp4_gemm_workspace_size(M, N, K), whose part past the prepared
+ * activations it uses as scratch (so runs sharing one workspace must be
+ * ordered).  The pair is equivalent to one nvfp4_gemm call.
  * ---------------------------------------------------------------------- */
 nvfp4_status_t nvfp4_gemm_prepare(const void *x, nvfp4_dtype_t x_dtype, int64_t M, int64_t K,
                                   int64_t ld_x, void *workspace, size_t workspace_bytes,
@@ -199,7 +201,7 @@ nvfp4_status_t nvfp4_gemm_prepare(const void *x, nvfp4_dtype_t x_dtype, int64_t 
 
 nvfp4_status_t nvfp4_gemm_run(int64_t M, int64_t K, const uint8_t *w_codes,
                               const uint8_t *w_scales, const float *w_gs, int64_t N, void *y,
-                              nvfp4_dtype_t y_dtype, int64_t ld_y, const void *workspace,
+                              nvfp4_dtype_t y_dtype, int64_t ld_y, void *workspace,
                               size_t workspace_bytes, void *stream);
 
 #ifdef __cplusplus

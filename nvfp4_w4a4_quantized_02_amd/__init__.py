@@ -229,10 +229,11 @@ class PreparedActivations:
         self.M, self.K, self.ws = M, K, ws
 
 
-def nvfp4_gemm_prepare(x: torch.Tensor, ws: torch.Tensor | None = None) -> PreparedActivations:
-    """Quantize X into a workspace of its own (or the given uint8 tensor)."""
+def nvfp4_gemm_prepare(x: torch.Tensor, ws: torch.Tensor | None = None, max_n: int = 0) -> PreparedActivations:
+    """Quantize X into a workspace of its own (or the given uint8 tensor),
+    sized for later runs against weights with up to max_n rows."""
     M, K, ld = _rows_view(x)
-    nws = lib.nvfp4_gemm_workspace_size(M, 0, K)
+    nws = lib.nvfp4_gemm_workspace_size(M, max_n, K)
     if ws is None or ws.numel() < nws:
         ws = torch.empty(max(nws, 256), dtype=torch.uint8, device=x.device)
     assert ws.data_ptr() % 256 == 0

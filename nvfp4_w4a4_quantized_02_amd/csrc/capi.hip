@@ -128,12 +128,21 @@ nvfp4_status_t nvfp4_fuse_rescale(int n, uint8_t* const* scales, const int64_t* 
   return launched();
 }
 
-size_t nvfp4_gemm_workspace_size(int64_t M, int64_t N, int64_t K) {
-  (void)N;
-  if (M <= 0 || K <= 0) return kWsX16;
+// Workspace: absmax partials | gs_x | fp16 activations [Mp, Kp] | fp32 K-part
+// sums of the split tiles (see plan_gemm).
+static size_t x16_bytes(int64_t M, int64_t K) {
+  if (M <= 0 || K <= 0) return 0;
   int64_t Mp = M <= kGemvMaxM ? M : round_up(M, kGemmBM);
-  int64_t Kp = round_up(K, kGemmBK);
-  return kWsX16 + (size_t)Mp * (size_t)Kp * 2u;
+  return (size_t)round_up((int64_t)Mp * round_up(K, kGemmBK) * 2, 256);
+}
+
+static size_t partial_bytes(int64_t M, int64_t N, int64_t K) {
+  if (M <= kGemvMaxM || N <= 0 || K <= 0) return 0;
+  return plan_gemm(M, N, K).partial_bytes;
+}
+
+size_t nvfp4_gemm_workspace_size(int64_t M, int64_t N, int64_t K) {
+  return kWsX16 + x16_bytes(M, K) + partial_bytes(M, N, K);
 }
 
 nvfp4_status_t nvfp4_gemm_prepare(const void* x, nvfp4_dtype_t x_dtype, int64_t M, int64_t K, int64_t ld_x,
@@ -142,7 +151,7 @@ nvfp4_status_t nvfp4_gemm_prepare(const void* x, nvfp4_dtype_t x_dtype, int64_t 
   if (st != NVFP4_OK) return st;
   if (K % 64 != 0) return NVFP4_ERR_SHAPE;
   if (M == 0) return NVFP4_OK;
-  if (!workspace || !aligned(workspace, 256) || workspace_bytes < nvfp4_gemm_workspace_size(M, 0, K))
+  if (!workspace || !aligned(workspace, 256) || workspace_bytes < kWsX16 + x16_bytes(M, K))
     return NVFP4_ERR_WORKSPACE;
   hipStream_t s = (hipStream_t)stream;
   const bool xb = x_dtype == NVFP4_BF16;
@@ -156,7 +165,7 @@ nvfp4_status_t nvfp4_gemm_prepare(const void* x, nvfp4_dtype_t x_dtype, int64_t 
 
 nvfp4_status_t nvfp4_gemm_run(int64_t M, int64_t K, const uint8_t* w_codes, const uint8_t* w_scales,
                               const float* w_gs, int64_t N, void* y, nvfp4_dtype_t y_dtype, int64_t ld_y,
-                              const void* workspace, size_t workspace_bytes, void* stream) {
+                              void* workspace, size_t workspace_bytes, void* stream) {
   if (!dtype_ok(y_dtype)) return NVFP4_ERR_DTYPE;
   if (M < 0 || K < 0 || N < 0 || M >= kMaxDim || K >= kMaxDim || N >= kMaxDim) return NVFP4_ERR_SHAPE;
   if (K % 64 != 0) return NVFP4_ERR_SHAPE;
@@ -174,11 +183,13 @@ nvfp4_status_t nvfp4_gemm_run(int64_t M, int64_t K, const uint8_t* w_codes, cons
   const bool yb = y_dtype == NVFP4_BF16;
   const float* gsx = (const float*)((const char*)workspace + kWsGs);
   const void* x16 = (const char*)workspace + kWsX16;
+  void* wsv = workspace;
   const int64_t Kp = round_up(K, kGemmBK);
   if (M <= kGemvMaxM)
     launch_gemv(x16, M, Kp, w_codes, w_scales, N, K, gsx, w_gs, y, yb, ld_y, s);
   else
-    launch_gemm(x16, M, Kp, w_codes, w_scales, N, K, gsx, w_gs, y, yb, ld_y, s);
+    launch_gemm(x16, M, Kp, w_codes, w_scales, N, K, gsx, w_gs, y, yb, ld_y,
+                (float*)((char*)wsv + kWsX16 + x16_bytes(M, K)), s);
   return launched();
 }
 

@@ -105,13 +105,25 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(const uint4* __restrict__ 
                                                        const uint8_t* __restrict__ ws, int N, int K, int M,
                                                        const float* __restrict__ gsx_p,
                                                        const float* __restrict__ gsw_p, uint8_t* __restrict__ y,
-                                                       size_t ld_y_bytes, int tiles_n, int nk) {
+                                                       size_t ld_y_bytes, int tiles_n, int nk, int full_tiles,
+                                                       int split, float* __restrict__ partials) {
   // Three distinct buffers (not one indexed array) so the compiler can see
   // that a transfer into one buffer never feeds reads of another.
   __shared__ GemmBuf b0, b1, b2;
+  __shared__ uint2 split_lut[256];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wave_n = wave >> 1, wave_m = wave & 1;
-  const int tn = blockIdx.x % tiles_n, tm = blockIdx.x / tiles_n;
+  // Whole tiles first; the workgroups past full_tiles each take one K part
+  // (steps [kb, ke)) of a remaining tile.
+  int tile = blockIdx.x, part = -1, kb = 0, ke = nk;
+  if (tile >= full_tiles) {
+    const int i = tile - full_tiles;
+    tile = full_tiles + i / split;
+    part = i % split;
+    kb = part * nk / split;
+    ke = (part + 1) * nk / split;
+  }
+  const int tn = tile % tiles_n, tm = tile / tiles_n;
   const int n0 = tn * kGemmBN, m0 = tm * kGemmBM;
   const int l32 = lane & 31, h = lane >> 5;
   const size_t kh = (size_t)K / 2, ks = (size_t)K / 16;
@@ -165,6 +177,14 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(const uint4* __restrict__ 
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[t][u][r] = 0.0f;
 
+  // Scale-byte table: entry b holds the power-of-two operand and the packed
+  // fp16 multiplier of split_scale(b), so a split costs one LDS read.
+#pragma unroll
+  for (int e = tid; e < 256; e += 256) {
+    ScaleSplit sp = split_scale((uint32_t)e);
+    split_lut[e] = make_uint2(__float_as_uint(sp.p2), __builtin_bit_cast(uint32_t, sp.q2));
+  }
+
   // Operand fragments of sub-step j from buffer `cur`.
   auto read_x = [&](const GemmBuf& cur, int j, f16x8 (&bx)[4]) {
 #pragma unroll
@@ -173,81 +193,133 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(const uint4* __restrict__ 
       bx[u] = u4_as_f16x8(cur.x[row * 8 + ((4 * h + j) ^ (row & 7) ^ ((row >> 3) & 1))]);
     }
   };
-  auto expand_w = [&](const uint4 (&wv)[4], const ScaleSplit (&sp)[4][2], int j, f16x8 (&aw)[4]) {
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      uint32_t e[4];
-      expand8(dword_of(wv[t], j), sp[t][j >> 1], e);
-      aw[t] = u4_as_f16x8(make_uint4(e[0], e[1], e[2], e[3]));
-    }
-  };
-
-  // One main-loop step: compute step kt from `cur` while the transfers of
-  // step kt+2 are in flight.  Every step issues the same transfers (near the
-  // end they repeat the last step into a buffer that is no longer read), so
-  // the wait count is the same in every step.  Within the step, the LDS
-  // reads and the W expansion of sub-step j+1 are issued ahead of the MFMAs
-  // of sub-step j.
-  auto step = [&](int kt, const GemmBuf& cur, uint32_t lx, uint32_t lc, uint32_t ls) {
-    const int last = nk - 1;
-    uint4 wv[4];
-    uint32_t sw[4];
+  // W codes (one dword per sub-step) and the two block scales of this lane.
+  auto read_w = [&](const GemmBuf& cur, uint4 (&wv)[4], uint32_t (&sw)[4]) {
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const int row = wave_n * 128 + t * 32 + l32;
       wv[t] = cur.wc[row * 2 + (h ^ (((row >> 2) ^ (row >> 3)) & 1))];
       sw[t] = cur.ws[row] >> (16 * h);
     }
-    f16x8 bx[4], aw[4];
-    read_x(cur, 0, bx);
-    issue(kt + 2 < last ? kt + 2 : last, lx, lc, ls);
-    ScaleSplit sp[4][2];
+  };
+  auto split_w = [&](const uint32_t (&sw)[4], uint2 (&sp)[4][2]) {
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      sp[t][0] = split_scale(sw[t] & 0xFFu);
-      sp[t][1] = split_scale((sw[t] >> 8) & 0xFFu);
+      sp[t][0] = split_lut[sw[t] & 0xFFu];
+      sp[t][1] = split_lut[(sw[t] >> 8) & 0xFFu];
     }
-    expand_w(wv, sp, 0, aw);
+  };
+  auto expand_w = [&](const uint4 (&wv)[4], const uint2 (&sp)[4][2], int j, f16x8 (&aw)[4]) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int t = 0; t < 4; ++t) {
+      const uint2 s2 = sp[t][j >> 1];
+      ScaleSplit ss;
+      ss.p2 = __uint_as_float(s2.x);
+      ss.q2 = __builtin_bit_cast(half2_t, s2.y);
+      uint32_t e[4];
+      expand8(dword_of(wv[t], j), ss, e);
+      aw[t] = u4_as_f16x8(make_uint4(e[0], e[1], e[2], e[3]));
+    }
+  };
+  auto mfma16 = [&](const f16x8 (&aw)[4], const f16x8 (&bx)[4]) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        acc[t][u] = __builtin_amdgcn_mfma_f32_32x32x16_f16(aw[t], bx[u], acc[t][u], 0, 0, 0);
+  };
+
+  // Register-resident operands carried across sub-steps and steps: the W
+  // codes and scale splits of the current step and the operands of its next
+  // sub-step.
+  uint4 wv[4];
+  uint2 sp[4][2];
+  f16x8 bx[4], aw[4];
+
+  // One main-loop step.  Sub-steps 0..2 of step kt run from `cur`, each
+  // overlapping the LDS reads and expansion of the following sub-step.  Then
+  // the wave waits for the transfers of step kt+1 and meets the barrier with
+  // the operands of sub-step 3 in registers; its 16 MFMAs run after the
+  // barrier and cover the LDS reads, scale lookups and first expansion of
+  // step kt+1 (from `nxt`).  The transfers of step kt+2 (into `nxt2`) are
+  // issued at the start; every step issues the same transfers (near the end
+  // they repeat the last step into a buffer that is no longer read), so the
+  // wait count is the same in every step.
+  auto step = [&](int kt, const GemmBuf& cur, const GemmBuf& nxt, uint32_t lx, uint32_t lc, uint32_t ls) {
+    const int last = ke - 1;
+    issue(kt + 2 < last ? kt + 2 : last, lx, lc, ls);
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
       f16x8 bxn[4], awn[4];
-      if (j < 3) read_x(cur, j + 1, bxn);
+      read_x(cur, j + 1, bxn);
+      mfma16(aw, bx);
+      expand_w(wv, sp, j + 1, awn);
 #pragma unroll
-      for (int t = 0; t < 4; ++t)
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-          acc[t][u] = __builtin_amdgcn_mfma_f32_32x32x16_f16(aw[t], bx[u], acc[t][u], 0, 0, 0);
-      if (j < 3) {
-        expand_w(wv, sp, j + 1, awn);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          bx[q] = bxn[q];
-          aw[q] = awn[q];
-        }
+      for (int q = 0; q < 4; ++q) {
+        bx[q] = bxn[q];
+        aw[q] = awn[q];
       }
     }
-    // The transfers of step kt+1 must have landed before the barrier; only
-    // this step's (kt+2) may still be in flight.  The barrier is a bare
-    // s_barrier: a workgroup fence would also wait for those.  The LDS reads
-    // of `cur` are complete here (their values fed the MFMAs above), so `cur`
-    // may be refilled after it.
-    asm volatile("s_waitcnt vmcnt(11)\n\ts_barrier" ::: "memory");
+    // All LDS reads of `cur` have completed and this wave's transfers of step
+    // kt+1 have landed (only step kt+2's 11 may be in flight); after the
+    // barrier every wave's have.  The barrier is a bare s_barrier: a
+    // workgroup fence would also wait for the transfers still in flight.
+    asm volatile("s_waitcnt vmcnt(11) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    f16x8 bx3[4], aw3[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      bx3[q] = bx[q];
+      aw3[q] = aw[q];
+    }
+    // Step kt+1's operands are prepared even after the last step (the
+    // buffer then holds a repeated, finite copy), which keeps this branch-free.
+    uint32_t sw[4];
+    read_w(nxt, wv, sw);
+    read_x(nxt, 0, bx);
+    mfma16(aw3, bx3);
+    split_w(sw, sp);
+    expand_w(wv, sp, 0, aw);
   };
   static_assert(kDmaPerStep == 11, "the wait count above must match the transfers per step");
 
-  if (nk > 0) {
-    issue(0, lx0, lc0, ls0);
-    issue(nk > 1 ? 1 : 0, lx1, lc1, ls1);
-    asm volatile("s_waitcnt vmcnt(11)\n\ts_barrier" ::: "memory");
-    for (int kt = 0; kt < nk; kt += 3) {
-      step(kt, b0, lx2, lc2, ls2);
-      if (kt + 1 < nk) step(kt + 1, b1, lx0, lc0, ls0);
-      if (kt + 2 < nk) step(kt + 2, b2, lx1, lc1, ls1);
+  if (ke > kb) {
+    issue(kb, lx0, lc0, ls0);
+    issue(kb + 1 < ke ? kb + 1 : kb, lx1, lc1, ls1);
+    // the scale table above is written with ordinary LDS stores
+    asm volatile("s_waitcnt vmcnt(11) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    {
+      uint32_t sw[4];
+      read_w(b0, wv, sw);
+      read_x(b0, 0, bx);
+      split_w(sw, sp);
+      expand_w(wv, sp, 0, aw);
+    }
+    for (int kt = kb; kt < ke; kt += 3) {
+      step(kt, b0, b1, lx2, lc2, ls2);
+      if (kt + 1 < ke) step(kt + 1, b1, b2, lx0, lc0, ls0);
+      if (kt + 2 < ke) step(kt + 2, b2, b0, lx1, lc1, ls1);
     }
     // drain the repeated transfers before the workgroup can exit
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   }
 
+  if (part >= 0) {
+    // raw fp32 partial sums, tile-local [256 x 256] row-major (m, n)
+    float* pp = partials + ((size_t)(tile - full_tiles) * split + part) * (kGemmBM * kGemmBN);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int ml = wave_m * 128 + u * 32 + l32;
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int nl = wave_n * 128 + t * 32 + 8 * q + 4 * h;
+          *reinterpret_cast<float4*>(pp + ml * kGemmBN + nl) =
+              make_float4(acc[t][u][4 * q], acc[t][u][4 * q + 1], acc[t][u][4 * q + 2], acc[t][u][4 * q + 3]);
+        }
+    }
+    return;
+  }
   const float scale = (*gsx_p) * (*gsw_p);
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
@@ -264,6 +336,34 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(const uint4* __restrict__ 
       }
     }
   }
+}
+
+// Adds the K parts of every split tile in part order, applies the scales
+// and stores Y.  One thread per 4 consecutive outputs of a tile row.
+template <bool kYBf16>
+__global__ __launch_bounds__(256) void gemm_split_reduce_kernel(const float* __restrict__ partials, int full_tiles,
+                                                                 int split, int tiles_n, int M, int N,
+                                                                 const float* __restrict__ gsx_p,
+                                                                 const float* __restrict__ gsw_p,
+                                                                 uint8_t* __restrict__ y, size_t ld_y_bytes) {
+  const int r = blockIdx.y;                        // remaining tile index
+  const int tile = full_tiles + r;
+  const int tn = tile % tiles_n, tm = tile / tiles_n;
+  const int e = (blockIdx.x * 256 + threadIdx.x) * 4;  // element in the tile
+  const int ml = e / kGemmBN, nl = e % kGemmBN;
+  const int m = tm * kGemmBM + ml, n = tn * kGemmBN + nl;
+  if (m >= M || n >= N) return;
+  const float* pp = partials + (size_t)r * split * (kGemmBM * kGemmBN) + e;
+  float4 a = *reinterpret_cast<const float4*>(pp);
+  for (int s = 1; s < split; ++s) {
+    const float4 b = *reinterpret_cast<const float4*>(pp + (size_t)s * (kGemmBM * kGemmBN));
+    a.x += b.x;
+    a.y += b.y;
+    a.z += b.z;
+    a.w += b.w;
+  }
+  const float scale = (*gsx_p) * (*gsw_p);
+  store4<kYBf16>(y + (size_t)m * ld_y_bytes, n, N, a.x * scale, a.y * scale, a.z * scale, a.w * scale);
 }
 
 // ====================================================================== GEMV
@@ -347,19 +447,28 @@ __global__ __launch_bounds__(256) void gemv_kernel(const uint4* __restrict__ x16
 
 // ====================================================================== launch
 void launch_gemm(const void* x16, int64_t M, int64_t Kp, const uint8_t* wc, const uint8_t* ws, int64_t N, int64_t K,
-                 const float* gsx, const float* gsw, void* y, bool y_bf16, int64_t ld_y, hipStream_t s) {
-  const int tiles_n = (int)((N + kGemmBN - 1) / kGemmBN);
-  const int tiles_m = (int)((M + kGemmBM - 1) / kGemmBM);
-  const int nk = (int)(Kp / kGemmBK);
+                 const float* gsx, const float* gsw, void* y, bool y_bf16, int64_t ld_y, float* partials,
+                 hipStream_t s) {
+  const GemmPlan p = plan_gemm(M, N, Kp);
+  const int rem = p.tiles_m * p.tiles_n - p.full_tiles;
   const size_t ldb = (size_t)ld_y * (y_bf16 ? 2u : 4u);
   const uint32_t kpc = (uint32_t)(Kp / 8);
-  dim3 grid(tiles_n * tiles_m);
+  dim3 grid(p.full_tiles + rem * p.split);
   if (y_bf16)
     gemm_kernel<true><<<grid, 256, 0, s>>>((const uint4*)x16, kpc, wc, ws, (int)N, (int)K, (int)M, gsx, gsw,
-                                           (uint8_t*)y, ldb, tiles_n, nk);
+                                           (uint8_t*)y, ldb, p.tiles_n, p.nk, p.full_tiles, p.split, partials);
   else
     gemm_kernel<false><<<grid, 256, 0, s>>>((const uint4*)x16, kpc, wc, ws, (int)N, (int)K, (int)M, gsx, gsw,
-                                            (uint8_t*)y, ldb, tiles_n, nk);
+                                            (uint8_t*)y, ldb, p.tiles_n, p.nk, p.full_tiles, p.split, partials);
+  if (p.split > 1) {
+    dim3 rgrid(kGemmBM * kGemmBN / 4 / 256, rem);
+    if (y_bf16)
+      gemm_split_reduce_kernel<true><<<rgrid, 256, 0, s>>>(partials, p.full_tiles, p.split, p.tiles_n, (int)M,
+                                                           (int)N, gsx, gsw, (uint8_t*)y, ldb);
+    else
+      gemm_split_reduce_kernel<false><<<rgrid, 256, 0, s>>>(partials, p.full_tiles, p.split, p.tiles_n, (int)M,
+                                                            (int)N, gsx, gsw, (uint8_t*)y, ldb);
+  }
 }
 
 template <int NT>

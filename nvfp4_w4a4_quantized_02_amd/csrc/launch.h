@@ -21,6 +21,40 @@ constexpr int kGemmBN = 256;   // W rows per workgroup tile
 constexpr int kGemmBK = 64;    // K per main-loop step
 constexpr int kGemvMaxM = 16;  // M at or below this uses the GEMV kernel
 
+// Tiling of one GEMM.  Whole 256 x 256 tiles fill complete rounds of the
+// machine; when the last round would leave most compute units idle, its
+// tiles are split along K into `split` parts that write fp32 partial sums,
+// which a second kernel adds in a fixed order.
+constexpr int kGemmCUs = 256;  // compute units of an MI355X
+
+struct GemmPlan {
+  int tiles_m, tiles_n, nk;
+  int full_tiles;     // tiles computed whole
+  int split;          // K parts of each remaining tile (1 = none)
+  size_t partial_bytes;
+};
+
+inline GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K) {
+  GemmPlan p;
+  p.tiles_m = (int)((M + kGemmBM - 1) / kGemmBM);
+  p.tiles_n = (int)((N + kGemmBN - 1) / kGemmBN);
+  p.nk = (int)((K + kGemmBK - 1) / kGemmBK);
+  const int tiles = p.tiles_m * p.tiles_n;
+  const int rem = tiles % kGemmCUs;
+  int split = rem ? kGemmCUs / rem : 1;
+  if (split > p.nk) split = p.nk;
+  if (split < 2 || M <= kGemvMaxM) {
+    p.full_tiles = tiles;
+    p.split = 1;
+    p.partial_bytes = 0;
+  } else {
+    p.full_tiles = tiles - rem;
+    p.split = split;
+    p.partial_bytes = (size_t)rem * split * kGemmBM * kGemmBN * sizeof(float);
+  }
+  return p;
+}
+
 struct RescaleArgs {
   int n;
   uint64_t total;
@@ -45,7 +79,8 @@ void launch_fuse_rescale(const RescaleArgs& a, hipStream_t s);
 // C[m, n] = (sum_k X16[m, k] * W[n, k]) * gs_x * gs_w for the prefill tile
 // kernel (M > kGemvMaxM) and the small-M kernel.
 void launch_gemm(const void* x16, int64_t M, int64_t Kp, const uint8_t* wc, const uint8_t* ws, int64_t N, int64_t K,
-                 const float* gsx, const float* gsw, void* y, bool y_bf16, int64_t ld_y, hipStream_t s);
+                 const float* gsx, const float* gsw, void* y, bool y_bf16, int64_t ld_y, float* partials,
+                 hipStream_t s);
 void launch_gemv(const void* x16, int64_t M, int64_t Kp, const uint8_t* wc, const uint8_t* ws, int64_t N, int64_t K,
                  const float* gsx, const float* gsw, void* y, bool y_bf16, int64_t ld_y, hipStream_t s);
 

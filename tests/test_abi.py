@@ -56,7 +56,13 @@ def test_workspace_sizes(nv):
     assert small >= 16 * 5120 * 2
     assert big >= 4096 * 5120 * 2
     # ragged M pads to the 256-row tile, ragged K to 64
-    assert L.nvfp4_gemm_workspace_size(257, 1, 128) - L.nvfp4_gemm_workspace_size(0, 1, 0) == 512 * 128 * 2
+    assert L.nvfp4_gemm_workspace_size(257, 0, 128) - L.nvfp4_gemm_workspace_size(0, 0, 0) == 512 * 128 * 2
+    # the last partial round of 256x256 tiles is split along K: fp32 parts
+    tiles = 16 * 68                                       # M=4096, N=17408
+    rem = tiles % 256
+    parts = 256 // rem
+    extra = L.nvfp4_gemm_workspace_size(4096, 17408, 5120) - L.nvfp4_gemm_workspace_size(4096, 0, 5120)
+    assert extra == rem * parts * 256 * 256 * 4
 
 
 def q(nv, x=A, dt=BF16, rows=4, K=32, ld=32, codes=A, scales=A, gs=A, ws=A, nws=BIG):

@@ -99,6 +99,56 @@ __device__ __forceinline__ uint32_t encode_block(const uint32_t (&absbits)[16], 
   return s.sb;
 }
 
+// Fast block encoder.  With y = RN(1/es), the products x*y_lo and x*y_hi,
+// where y_lo = RN(y (1 - 2^-20)) and y_hi = RN(y (1 + 2^-20)), bracket the
+// exact quotient q = x / es from below and above (each RN step moves a value
+// by at most 2^-24 relative, so the 2^-20 margins dominate), hence also
+// RN(q).  The hardware FP4 conversion (nearest, ties to even, saturating,
+// sign kept) is monotone, so when it gives the same code for both ends of
+// the bracket, that is the code of RN(q).  Otherwise RN(q) sits at or next
+// to a decision point and the block takes the exact path above.  Tiny
+// quotients stay below the first decision point at both ends and overflow
+// saturates at both ends, so neither needs special handling; es == 0, or a
+// reciprocal that overflows, sends the block to the exact path.
+__device__ __forceinline__ uint32_t cvt_fp4x8(const float (&x)[16], int base, float y) {
+  uint32_t r = 0;
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, x[base + 0] * y, x[base + 1] * y, 1.0f, 0);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, x[base + 2] * y, x[base + 3] * y, 1.0f, 1);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, x[base + 4] * y, x[base + 5] * y, 1.0f, 2);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, x[base + 6] * y, x[base + 7] * y, 1.0f, 3);
+  return r;
+}
+
+// x: the 16 values as fp32 (bf16 widened exactly).  Returns the scale byte.
+__device__ __forceinline__ uint32_t encode_block_fast(const float (&x)[16], float gs, uint32_t& code_lo,
+                                                      uint32_t& code_hi) {
+  uint32_t bm = 0;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    uint32_t a = __float_as_uint(x[j]) & 0x7FFFFFFFu;
+    bm = bm > a ? bm : a;
+  }
+  BlockScale s = block_scale(__uint_as_float(bm), gs);
+  const float y = __fdiv_rn(1.0f, s.es);
+  const float ylo = y * 0.99999904632568359375f;  // 1 - 2^-20
+  const float yhi = y * 1.00000095367431640625f;  // 1 + 2^-20
+  uint32_t lo_a = cvt_fp4x8(x, 0, ylo), lo_b = cvt_fp4x8(x, 0, yhi);
+  uint32_t hi_a = cvt_fp4x8(x, 8, ylo), hi_b = cvt_fp4x8(x, 8, yhi);
+  const bool fast = (s.es != 0.0f) && (y < __uint_as_float(0x7F800000u)) && lo_a == lo_b && hi_a == hi_b;
+  if (__builtin_expect(!fast, 0)) {
+    uint32_t absbits[16], signs = 0;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      absbits[j] = __float_as_uint(x[j]) & 0x7FFFFFFFu;
+      signs |= (__float_as_uint(x[j]) >> 31) << j;
+    }
+    return encode_block(absbits, signs, gs, code_lo, code_hi);
+  }
+  code_lo = lo_a;
+  code_hi = hi_a;
+  return s.sb;
+}
+
 // fp16 expansion of 8 packed codes sharing one scale byte: E2M1(code) *
 // E4M3value(sb), exact in fp16 (values from 2^-10 to 2688, at most 6
 // significant bits).  The scale splits into a power of two, applied by the

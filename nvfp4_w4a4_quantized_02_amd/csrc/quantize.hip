@@ -74,32 +74,27 @@ __device__ __forceinline__ float reduce_partials_to_gs(const uint32_t* __restric
   return tensor_scale(__uint_as_float(r));
 }
 
-// Load one 16-element block (bf16: two 16-byte chunks, fp32: four).
+// Load one 16-element block as fp32 (bf16: two 16-byte chunks widened
+// exactly; fp32: four chunks).
 template <bool kBf16>
-__device__ __forceinline__ void load_block(const uint8_t* __restrict__ p, uint32_t (&absbits)[16], uint32_t& signs) {
-  signs = 0;
+__device__ __forceinline__ void load_block(const uint8_t* __restrict__ p, float (&x)[16]) {
+  const uint4* q = reinterpret_cast<const uint4*>(p);
   if (kBf16) {
-    const uint4* q = reinterpret_cast<const uint4*>(p);
     uint4 a = q[0], b = q[1];
     uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      absbits[2 * i] = (w[i] & 0x7FFFu) << 16;
-      absbits[2 * i + 1] = w[i] & 0x7FFF0000u;
-      signs |= ((w[i] >> 15) & 1u) << (2 * i);
-      signs |= (w[i] >> 31) << (2 * i + 1);
+      x[2 * i] = __uint_as_float(w[i] << 16);
+      x[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
     }
   } else {
-    const uint4* q = reinterpret_cast<const uint4*>(p);
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       uint4 a = q[c];
-      uint32_t w[4] = {a.x, a.y, a.z, a.w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        absbits[4 * c + i] = w[i] & 0x7FFFFFFFu;
-        signs |= (w[i] >> 31) << (4 * c + i);
-      }
+      x[4 * c] = __uint_as_float(a.x);
+      x[4 * c + 1] = __uint_as_float(a.y);
+      x[4 * c + 2] = __uint_as_float(a.z);
+      x[4 * c + 3] = __uint_as_float(a.w);
     }
   }
 }
@@ -127,10 +122,10 @@ __global__ __launch_bounds__(256) void quantize_packed_kernel(const uint8_t* __r
     uint32_t b = first + (uint32_t)it * stride;
     uint32_t r = fastdiv(b, fd);
     uint32_t kb = b - r * kblocks;
-    uint32_t absbits[16], signs;
-    load_block<kBf16>(x + (size_t)r * ld_bytes + (size_t)kb * (kBf16 ? 32u : 64u), absbits, signs);
+    float xv[16];
+    load_block<kBf16>(x + (size_t)r * ld_bytes + (size_t)kb * (kBf16 ? 32u : 64u), xv);
     uint32_t lo, hi;
-    uint32_t sb = encode_block(absbits, signs, gs, lo, hi);
+    uint32_t sb = encode_block_fast(xv, gs, lo, hi);
     *reinterpret_cast<uint2*>(codes + (size_t)b * 8u) = make_uint2(lo, hi);
     scales[b] = (uint8_t)sb;
   }
@@ -159,10 +154,10 @@ __global__ __launch_bounds__(256) void quantize_f16_kernel(const uint8_t* __rest
     uint32_t kb = b - r * kp_blocks;
     uint4 o0 = make_uint4(0, 0, 0, 0), o1 = make_uint4(0, 0, 0, 0);
     if (kb < kblocks) {
-      uint32_t absbits[16], signs;
-      load_block<kBf16>(x + (size_t)r * ld_bytes + (size_t)kb * (kBf16 ? 32u : 64u), absbits, signs);
+      float xv[16];
+      load_block<kBf16>(x + (size_t)r * ld_bytes + (size_t)kb * (kBf16 ? 32u : 64u), xv);
       uint32_t lo, hi;
-      uint32_t sb = encode_block(absbits, signs, gs, lo, hi);
+      uint32_t sb = encode_block_fast(xv, gs, lo, hi);
       ScaleSplit s = split_scale(sb);
       uint32_t e0[4], e1[4];
       expand8(lo, s, e0);

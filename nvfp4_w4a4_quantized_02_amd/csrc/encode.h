@@ -99,17 +99,51 @@ __device__ __forceinline__ uint32_t encode_block(const uint32_t (&absbits)[16], 
   return s.sb;
 }
 
-// Fast block encoder.  With y = RN(1/es), the products x*y_lo and x*y_hi,
-// where y_lo = RN(y (1 - 2^-20)) and y_hi = RN(y (1 + 2^-20)), bracket the
-// exact quotient q = x / es from below and above (each RN step moves a value
-// by at most 2^-24 relative, so the 2^-20 margins dominate), hence also
-// RN(q).  The hardware FP4 conversion (nearest, ties to even, saturating,
-// sign kept) is monotone, so when it gives the same code for both ends of
-// the bracket, that is the code of RN(q).  Otherwise RN(q) sits at or next
-// to a decision point and the block takes the exact path above.  Tiny
-// quotients stay below the first decision point at both ends and overflow
-// saturates at both ends, so neither needs special handling; es == 0, or a
-// reciprocal that overflows, sends the block to the exact path.
+// Fast block encoder.  Every rounding decision is bracketed: a decision is
+// taken by the fast path only when both ends of a bracket around the exact
+// operand give the same result, and a block whose bracket straddles a
+// decision point is reported back (returns false) for the exact path.
+//
+// Scale: with r = RN(1 / RN(6 gs)), r_lo = RN(r (1 - 2^-20)) and r_hi =
+// RN(r (1 + 2^-20)), the products bmax * r_lo and bmax * r_hi lie strictly
+// below and above RN(bmax / RN(6 gs)) (each RN step moves a value by at most
+// 2^-24 relative, so the 2^-20 margins dominate); E4M3 rounding is
+// monotone, so equal bytes at both ends are the exact scale byte.
+//
+// Codes: likewise with y = 1 / es from the hardware reciprocal (relative
+// error below 2^-22) and y (1 -/+ 2^-20), the hardware FP4 conversion (round
+// to nearest, ties to even, saturating, sign kept) of x * y_lo and x * y_hi
+// brackets E2M1(RN(|x| / es)).  es == 0 uses y = 0, which yields the
+// sign-only codes the rule gives there.  Quotients below the first decision
+// point stay there at both ends, and saturation happens at both ends, so
+// neither needs special handling.  A subnormal es or a reciprocal that
+// overflows is reported to the exact path.
+struct FastScale {
+  float gs;
+  float rlo, rhi;  // bracket of 1 / RN(6 gs); both 0 when gs == 0
+  bool ok;         // false: every block takes the exact path
+};
+
+__device__ __forceinline__ FastScale fast_scale(float gs) {
+  FastScale f;
+  f.gs = gs;
+  const float t = 6.0f * gs;
+  const float r = (gs == 0.0f) ? 0.0f : __fdiv_rn(1.0f, t);
+  f.rlo = r * 0.99999904632568359375f;  // 1 - 2^-20
+  f.rhi = r * 1.00000095367431640625f;  // 1 + 2^-20
+  f.ok = (gs == 0.0f) || (t >= 0x1p-126f && r < 0x1p+126f);
+  return f;
+}
+
+// Branch-free form of e4m3_encode_sat for v >= 0.
+__device__ __forceinline__ uint32_t e4m3_encode_sat_sel(float v) {
+  const uint32_t u = __float_as_uint(v);
+  const uint32_t nrm = ((u + 0x7FFFFu + ((u >> 20) & 1u)) >> 20) - (120u << 3);
+  const uint32_t sub = (uint32_t)__builtin_rintf(v * 512.0f);
+  const uint32_t r = (v < 0.015625f) ? sub : nrm;
+  return (v < 448.0f) ? r : 0x7Eu;
+}
+
 __device__ __forceinline__ uint32_t cvt_fp4x8(const float (&x)[16], int base, float y) {
   uint32_t r = 0;
   r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, x[base + 0] * y, x[base + 1] * y, 1.0f, 0);
@@ -119,34 +153,35 @@ __device__ __forceinline__ uint32_t cvt_fp4x8(const float (&x)[16], int base, fl
   return r;
 }
 
-// x: the 16 values as fp32 (bf16 widened exactly).  Returns the scale byte.
-__device__ __forceinline__ uint32_t encode_block_fast(const float (&x)[16], float gs, uint32_t& code_lo,
-                                                      uint32_t& code_hi) {
-  uint32_t bm = 0;
-#pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    uint32_t a = __float_as_uint(x[j]) & 0x7FFFFFFFu;
-    bm = bm > a ? bm : a;
-  }
-  BlockScale s = block_scale(__uint_as_float(bm), gs);
-  const float y = __fdiv_rn(1.0f, s.es);
-  const float ylo = y * 0.99999904632568359375f;  // 1 - 2^-20
-  const float yhi = y * 1.00000095367431640625f;  // 1 + 2^-20
-  uint32_t lo_a = cvt_fp4x8(x, 0, ylo), lo_b = cvt_fp4x8(x, 0, yhi);
-  uint32_t hi_a = cvt_fp4x8(x, 8, ylo), hi_b = cvt_fp4x8(x, 8, yhi);
-  const bool fast = (s.es != 0.0f) && (y < __uint_as_float(0x7F800000u)) && lo_a == lo_b && hi_a == hi_b;
-  if (__builtin_expect(!fast, 0)) {
-    uint32_t absbits[16], signs = 0;
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      absbits[j] = __float_as_uint(x[j]) & 0x7FFFFFFFu;
-      signs |= (__float_as_uint(x[j]) >> 31) << j;
-    }
-    return encode_block(absbits, signs, gs, code_lo, code_hi);
-  }
+// x: the 16 values as fp32 (bf16 widened exactly); bm: fp32 bits of the
+// largest |x|.  On success writes the scale byte and the codes.
+__device__ __forceinline__ bool encode_block_fast(const float (&x)[16], uint32_t bm, const FastScale& f,
+                                                  uint32_t& sb, uint32_t& code_lo, uint32_t& code_hi) {
+  const float bmf = __uint_as_float(bm);
+  sb = e4m3_encode_sat_sel(bmf * f.rlo);
+  const uint32_t sb_hi = e4m3_encode_sat_sel(bmf * f.rhi);
+  const float es = e4m3_value(sb) * f.gs;
+  const float y = (es == 0.0f) ? 0.0f : __builtin_amdgcn_rcpf(es);
+  const float ylo = y * 0.99999904632568359375f;
+  const float yhi = y * 1.00000095367431640625f;
+  const uint32_t lo_a = cvt_fp4x8(x, 0, ylo), lo_b = cvt_fp4x8(x, 0, yhi);
+  const uint32_t hi_a = cvt_fp4x8(x, 8, ylo), hi_b = cvt_fp4x8(x, 8, yhi);
   code_lo = lo_a;
   code_hi = hi_a;
-  return s.sb;
+  const bool es_ok = (es == 0.0f) || (es >= 0x1p-126f && y < 0x1p+126f);
+  return f.ok && es_ok && sb == sb_hi && lo_a == lo_b && hi_a == hi_b;
+}
+
+// Exact encoder from the fp32 values (for blocks the fast path reports).
+__device__ __forceinline__ uint32_t encode_block_exact(const float (&x)[16], float gs, uint32_t& code_lo,
+                                                       uint32_t& code_hi) {
+  uint32_t absbits[16], signs = 0;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    absbits[j] = __float_as_uint(x[j]) & 0x7FFFFFFFu;
+    signs |= (__float_as_uint(x[j]) >> 31) << j;
+  }
+  return encode_block(absbits, signs, gs, code_lo, code_hi);
 }
 
 // fp16 expansion of 8 packed codes sharing one scale byte: E2M1(code) *

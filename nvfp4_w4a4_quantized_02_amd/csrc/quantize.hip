@@ -99,75 +99,123 @@ __device__ __forceinline__ void load_block(const uint8_t* __restrict__ p, float 
   }
 }
 
-// ------------------------------------------------------------------ encode
-// One lane per 16-element block.  The loop walks the blocks from the end of
-// the tensor back to its start, the reverse of the absmax pass, so the part
-// of the tensor read last by that pass is read first here, while it may
-// still sit in the last-level cache.
+// fp32 bits of the largest |x| of a block.  For bf16 input the max runs on
+// the packed 16-bit patterns (same order as the values for |x|).
 template <bool kBf16>
-__global__ __launch_bounds__(256) void quantize_packed_kernel(const uint8_t* __restrict__ x, size_t ld_bytes,
-                                                               uint32_t kblocks, uint32_t total_blocks, FastDiv fd,
-                                                               const uint32_t* __restrict__ partials, int npartials,
-                                                               uint8_t* __restrict__ codes,
-                                                               uint8_t* __restrict__ scales,
-                                                               float* __restrict__ gs_out) {
-  __shared__ uint32_t red[4];
-  const float gs = reduce_partials_to_gs(partials, npartials, red);
-  if (blockIdx.x == 0 && threadIdx.x == 0) *gs_out = gs;
-  const uint32_t stride = gridDim.x * 256u;
-  const uint32_t first = blockIdx.x * 256u + threadIdx.x;
-  if (first >= total_blocks) return;
-  const uint32_t iters = (total_blocks - 1u - first) / stride;  // last index = first + iters*stride
-  for (int32_t it = (int32_t)iters; it >= 0; --it) {
-    uint32_t b = first + (uint32_t)it * stride;
-    uint32_t r = fastdiv(b, fd);
-    uint32_t kb = b - r * kblocks;
-    float xv[16];
-    load_block<kBf16>(x + (size_t)r * ld_bytes + (size_t)kb * (kBf16 ? 32u : 64u), xv);
-    uint32_t lo, hi;
-    uint32_t sb = encode_block_fast(xv, gs, lo, hi);
-    *reinterpret_cast<uint2*>(codes + (size_t)b * 8u) = make_uint2(lo, hi);
-    scales[b] = (uint8_t)sb;
+__device__ __forceinline__ uint32_t block_absmax_bits(const float (&x)[16]) {
+  uint32_t bm = 0;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const uint32_t a = __float_as_uint(x[j]) & 0x7FFFFFFFu;
+    bm = bm > a ? bm : a;
   }
+  return bm;
 }
 
-// Same encoder, but the output is the fp16 value E2M1(code) * E4M3(scale)
-// of every element (the tensor scale stays separate), laid out
-// [rows, kp_blocks * 16] with zero blocks beyond K: the A-side operand of
-// the GEMM.  gs is written to *gs_out.
-template <bool kBf16>
-__global__ __launch_bounds__(256) void quantize_f16_kernel(const uint8_t* __restrict__ x, size_t ld_bytes,
-                                                            uint32_t kblocks, uint32_t kp_blocks,
-                                                            uint32_t total_blocks, FastDiv fd,
-                                                            const uint32_t* __restrict__ partials, int npartials,
-                                                            uint4* __restrict__ x16, float* __restrict__ gs_out) {
+// ------------------------------------------------------------------ encode
+// One lane per 16-element block, 64 consecutive blocks per wave and step.
+// The fast encoder settles almost every block; the few whose bracket
+// straddles a decision point (values on or next to a rounding tie, which
+// short bf16 and E4M3 significands make common enough to hit most waves)
+// are queued in the wave's slice of LDS and encoded exactly in batches of
+// up to 64, so the exact path runs with full waves instead of stalling the
+// fast path of every wave that holds one such block.
+//
+// The steps walk the tensor from its end back to its start, the reverse of
+// the absmax pass, so the part read last by that pass is read first here,
+// while it may still sit in the last-level cache.
+//
+// kF16 = false: packed codes [rows, K/2] and scale bytes [rows, K/16].
+// kF16 = true: the fp16 values E2M1(code) * E4M3(scale) (the tensor scale
+// stays separate) laid out [rows, out_kblocks * 16] with zero blocks beyond
+// K: the A-side operand of the GEMM.
+constexpr uint32_t kDeferCap = 128;  // queued blocks per wave
+
+template <bool kBf16, bool kF16>
+__global__ __launch_bounds__(256) void quantize_kernel(const uint8_t* __restrict__ x, size_t ld_bytes,
+                                                        uint32_t kblocks, uint32_t out_kblocks,
+                                                        uint32_t total_blocks, FastDiv fd,
+                                                        const uint32_t* __restrict__ partials, int npartials,
+                                                        uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
+                                                        uint4* __restrict__ x16, float* __restrict__ gs_out) {
   __shared__ uint32_t red[4];
+  __shared__ uint32_t deferred[4][kDeferCap];
   const float gs = reduce_partials_to_gs(partials, npartials, red);
   if (blockIdx.x == 0 && threadIdx.x == 0) *gs_out = gs;
-  const uint32_t stride = gridDim.x * 256u;
-  const uint32_t first = blockIdx.x * 256u + threadIdx.x;
-  if (first >= total_blocks) return;
-  const uint32_t iters = (total_blocks - 1u - first) / stride;
-  for (int32_t it = (int32_t)iters; it >= 0; --it) {
-    uint32_t b = first + (uint32_t)it * stride;
-    uint32_t r = fastdiv(b, fd);
-    uint32_t kb = b - r * kp_blocks;
-    uint4 o0 = make_uint4(0, 0, 0, 0), o1 = make_uint4(0, 0, 0, 0);
-    if (kb < kblocks) {
-      float xv[16];
-      load_block<kBf16>(x + (size_t)r * ld_bytes + (size_t)kb * (kBf16 ? 32u : 64u), xv);
-      uint32_t lo, hi;
-      uint32_t sb = encode_block_fast(xv, gs, lo, hi);
-      ScaleSplit s = split_scale(sb);
+  const FastScale fsc = fast_scale(gs);
+  const uint32_t lane = threadIdx.x & 63u;
+  uint32_t* queue = deferred[threadIdx.x >> 6];
+  const uint32_t waves = gridDim.x * 4u;
+  const uint32_t wave_id = blockIdx.x * 4u + (threadIdx.x >> 6);
+  const uint32_t chunks = (total_blocks + 63u) >> 6;
+  if (wave_id >= chunks) return;
+
+  auto load = [&](uint32_t b, uint32_t r, float (&xv)[16]) {
+    const uint32_t kb = b - r * out_kblocks;
+    load_block<kBf16>(x + (size_t)r * ld_bytes + (size_t)kb * (kBf16 ? 32u : 64u), xv);
+  };
+  auto store = [&](uint32_t b, uint32_t sb, uint32_t lo, uint32_t hi) {
+    if (kF16) {
+      const ScaleSplit sp = split_scale(sb);
       uint32_t e0[4], e1[4];
-      expand8(lo, s, e0);
-      expand8(hi, s, e1);
-      o0 = make_uint4(e0[0], e0[1], e0[2], e0[3]);
-      o1 = make_uint4(e1[0], e1[1], e1[2], e1[3]);
+      expand8(lo, sp, e0);
+      expand8(hi, sp, e1);
+      x16[(size_t)b * 2u] = make_uint4(e0[0], e0[1], e0[2], e0[3]);
+      x16[(size_t)b * 2u + 1u] = make_uint4(e1[0], e1[1], e1[2], e1[3]);
+    } else {
+      *reinterpret_cast<uint2*>(codes + (size_t)b * 8u) = make_uint2(lo, hi);
+      scales[b] = (uint8_t)sb;
     }
-    x16[(size_t)b * 2u] = o0;
-    x16[(size_t)b * 2u + 1u] = o1;
+  };
+  auto flush = [&](uint32_t n) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    for (uint32_t base = 0; base < n; base += 64u) {
+      if (base + lane < n) {
+        const uint32_t b = queue[base + lane];
+        float xv[16];
+        load(b, fastdiv(b, fd), xv);
+        uint32_t lo, hi;
+        const uint32_t sb = encode_block_exact(xv, gs, lo, hi);
+        store(b, sb, lo, hi);
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
+
+  uint32_t queued = 0;  // wave-uniform
+  for (int32_t it = (int32_t)((chunks - 1u - wave_id) / waves); it >= 0; --it) {
+    const uint32_t b = (wave_id + (uint32_t)it * waves) * 64u + lane;
+    bool settled = true;
+    if (b < total_blocks) {
+      const uint32_t r = fastdiv(b, fd);
+      if (kF16 && b - r * out_kblocks >= kblocks) {
+        x16[(size_t)b * 2u] = make_uint4(0, 0, 0, 0);
+        x16[(size_t)b * 2u + 1u] = make_uint4(0, 0, 0, 0);
+      } else {
+        float xv[16];
+        load(b, r, xv);
+        uint32_t sb, lo, hi;
+        settled = encode_block_fast(xv, block_absmax_bits<kBf16>(xv), fsc, sb, lo, hi);
+        if (settled) store(b, sb, lo, hi);
+      }
+    }
+    const uint64_t pending = __ballot(!settled);
+    if (pending) {
+      const uint32_t pos =
+          queued + __builtin_amdgcn_mbcnt_hi((uint32_t)(pending >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)pending, 0u));
+      if (!settled) queue[pos] = b;
+      queued += (uint32_t)__popcll(pending);
+      if (queued > kDeferCap - 64u) {
+        flush(queued);
+        queued = 0;
+      }
+    }
   }
+  if (queued) flush(queued);
 }
 
 __global__ void fill_f32_kernel(float* p, float v) { *p = v; }
@@ -273,11 +321,11 @@ void launch_quantize_packed(const void* x, bool bf16, int64_t rows, int64_t K, i
   int grid = grid_for(total, 256, 4096);
   FastDiv fd = make_fastdiv(kb ? kb : 1u);
   if (bf16)
-    quantize_packed_kernel<true><<<grid, 256, 0, s>>>((const uint8_t*)x, ld_bytes, kb, total, fd, partials,
-                                                      npartials, codes, scales, gs);
+    quantize_kernel<true, false><<<grid, 256, 0, s>>>((const uint8_t*)x, ld_bytes, kb, kb, total, fd, partials,
+                                                      npartials, codes, scales, nullptr, gs);
   else
-    quantize_packed_kernel<false><<<grid, 256, 0, s>>>((const uint8_t*)x, ld_bytes, kb, total, fd, partials,
-                                                       npartials, codes, scales, gs);
+    quantize_kernel<false, false><<<grid, 256, 0, s>>>((const uint8_t*)x, ld_bytes, kb, kb, total, fd, partials,
+                                                       npartials, codes, scales, nullptr, gs);
 }
 
 void launch_quantize_f16(const void* x, bool bf16, int64_t rows, int64_t K, int64_t ld, int64_t Kp,
@@ -288,11 +336,11 @@ void launch_quantize_f16(const void* x, bool bf16, int64_t rows, int64_t K, int6
   int grid = grid_for(total, 256, 4096);
   FastDiv fd = make_fastdiv(kpb ? kpb : 1u);
   if (bf16)
-    quantize_f16_kernel<true><<<grid, 256, 0, s>>>((const uint8_t*)x, ld_bytes, kb, kpb, total, fd, partials,
-                                                   npartials, (uint4*)x16, gs);
+    quantize_kernel<true, true><<<grid, 256, 0, s>>>((const uint8_t*)x, ld_bytes, kb, kpb, total, fd, partials,
+                                                     npartials, nullptr, nullptr, (uint4*)x16, gs);
   else
-    quantize_f16_kernel<false><<<grid, 256, 0, s>>>((const uint8_t*)x, ld_bytes, kb, kpb, total, fd, partials,
-                                                    npartials, (uint4*)x16, gs);
+    quantize_kernel<false, true><<<grid, 256, 0, s>>>((const uint8_t*)x, ld_bytes, kb, kpb, total, fd, partials,
+                                                      npartials, nullptr, nullptr, (uint4*)x16, gs);
 }
 
 void launch_fill_f32(float* p, float v, hipStream_t s) { fill_f32_kernel<<<1, 1, 0, s>>>(p, v); }

@@ -182,7 +182,7 @@ def main():
                                "x W[17408x5120] NVFP4 from N(0,0.02) -> Y bf16",
                    "M": M, "N": N, "K": K, "x_dtype": "bf16", "y_dtype": "bf16"},
         "phases_ms": {"activation_quantize": round(mean(prep_ms), 4), "gemm": round(mean(run_ms), 4)},
-        "roofline": {"bound": "mfma", "kernel": "gemm_kernel (fp16 MFMA 32x32x16)",
+        "roofline": {"bound": "mfma", "kernel": "nvfp4_gemm_run: gemm_kernel (fp16 MFMA 32x32x16) + split-K reduce",
                      "achieved": round(gemm_tflops, 2), "peak": PEAK_FP16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(gemm_tflops / PEAK_FP16_TFLOPS, 4), "traffic": traffic,
                      "algorithmic": "2*M*N*K = %.4g flop per launch" % flops},
@@ -325,9 +325,11 @@ def secondary(torch, np, nv, workloads, to_gpu, dev, args):
                 "single_read_GBs": round(single / (mean(q_ms) * 1e-3) / 1e9, 1),
                 "config": {"workload": "long-prefill quantize: X[32768x5120] bf16 Student-t(2.5), 16 hot "
                                        "channels x200 -> packed E2M1 + E4M3 scales + FP32 scale"},
-                "roofline": {"bound": "hbm", "kernel": "amax_partials_kernel + quantize_packed_kernel",
+                "roofline": {"bound": "hbm", "kernel": "nvfp4_quantize: amax_partials_kernel + quantize_kernel",
                              "achieved": round(qgbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                              "frac": round(qgbs / PEAK_HBM_GBS, 4),
+                             "traffic": traffic_for("quantize_long", source_sha("quantize.hip", "encode.h",
+                                                                                "common.h")),
                              "algorithmic": "2 reads of X + codes + scales = %d B per call" % two_pass}})
     log("quantize: %.1f GB/s (two-pass count)" % qgbs)
     del xl, codes, scl

@@ -13,43 +13,9 @@
 // of them to sub-step j; the X operand is read with the same k permutation.
 #include "encode.h"
 #include "launch.h"
+#include "mfma_util.h"
 
 namespace nvfp4 {
-
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-
-__device__ __forceinline__ f16x8 u4_as_f16x8(uint4 v) { return __builtin_bit_cast(f16x8, v); }
-
-__device__ __forceinline__ uint32_t dword_of(const uint4& v, int j) {
-  return j == 0 ? v.x : (j == 1 ? v.y : (j == 2 ? v.z : v.w));
-}
-
-// Store 4 consecutive outputs y[m, n .. n+3] (n + 3 may pass N on the last tile).
-template <bool kYBf16>
-__device__ __forceinline__ void store4(uint8_t* __restrict__ yrow, int n, int N, float v0, float v1, float v2,
-                                       float v3) {
-  if (kYBf16) {
-    uint32_t b0 = f32_to_bf16_rne(v0), b1 = f32_to_bf16_rne(v1), b2 = f32_to_bf16_rne(v2),
-             b3 = f32_to_bf16_rne(v3);
-    uint16_t* p = reinterpret_cast<uint16_t*>(yrow) + n;
-    if (n + 3 < N) {
-      *reinterpret_cast<uint2*>(p) = make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
-    } else {
-      if (n < N) p[0] = (uint16_t)b0;
-      if (n + 1 < N) p[1] = (uint16_t)b1;
-      if (n + 2 < N) p[2] = (uint16_t)b2;
-    }
-  } else {
-    float* p = reinterpret_cast<float*>(yrow) + n;
-    if (n + 3 < N) {
-      *reinterpret_cast<float4*>(p) = make_float4(v0, v1, v2, v3);
-    } else {
-      if (n < N) p[0] = v0;
-      if (n + 1 < N) p[1] = v1;
-      if (n + 2 < N) p[2] = v2;
-    }
-  }
-}
 
 // ====================================================================== GEMM
 // Workgroup tile 256 (W rows) x 256 (X rows), 4 waves in a 2 x 2 grid, each
@@ -69,27 +35,6 @@ __device__ __forceinline__ void store4(uint8_t* __restrict__ yrow, int n, int N,
 // h ^ (((row >> 2) ^ (row >> 3)) & 1).  Any 8 or 16 consecutive rows then hit
 // distinct 16-byte bank groups, so the 128-bit operand reads are free of
 // bank conflicts whether the LDS serves 8 or 16 lanes per pass.
-typedef __attribute__((address_space(3))) void lds_void_t;
-
-// Direct global->LDS transfers from a wave-uniform base (scalar registers)
-// plus a 32-bit per-lane byte offset.  Lane i of the wave writes `size` bytes
-// at LDS byte address `lds` + i * size; `lds` is wave-uniform and goes
-// through M0 (one wait state after the SALU write of M0).  The transfers have no
-// destination registers, and the compiler is not told about them: every wait
-// on them is an explicit s_waitcnt below, which lets the main loop keep two
-// steps in flight where the compiler's own bookkeeping would drain them.
-// M0 is written only here; nothing else in these kernels uses it.
-__device__ __forceinline__ void lds_dma16(const void* base, uint32_t off, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "s"(lds)
-               : "memory", "m0");
-}
-__device__ __forceinline__ void lds_dma4(const void* base, uint32_t off, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(off), "s"(base), "s"(lds)
-               : "memory", "m0");
-}
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return __builtin_amdgcn_readfirstlane((uint32_t)(size_t)(const lds_void_t*)p);
-}
 
 struct GemmBuf {
   uint4 x[kGemmBM * 8];        // 32 KB
@@ -366,85 +311,6 @@ __global__ __launch_bounds__(256) void gemm_split_reduce_kernel(const float* __r
   store4<kYBf16>(y + (size_t)m * ld_y_bytes, n, N, a.x * scale, a.y * scale, a.z * scale, a.w * scale);
 }
 
-// ====================================================================== GEMV
-// M <= 16 (decode).  MFMA 16x16x32 with W as the 16-row A operand and the
-// (zero-padded) activations as the 16-column B operand.  A workgroup owns
-// NT*16 rows of W; its 4 waves split K round-robin in 128-k chunks and their
-// partial sums are added in a fixed order through LDS, so the result does
-// not depend on scheduling.
-template <int NT, bool kYBf16>
-__global__ __launch_bounds__(256) void gemv_kernel(const uint4* __restrict__ x16, uint32_t kp_chunks, int M,
-                                                    const uint8_t* __restrict__ wc, const uint8_t* __restrict__ ws,
-                                                    int N, int K, const float* __restrict__ gsx_p,
-                                                    const float* __restrict__ gsw_p, uint8_t* __restrict__ y,
-                                                    size_t ld_y_bytes) {
-  __shared__ floatx4 part[4][NT][64];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int l16 = lane & 15, g = lane >> 4;
-  const int n0 = blockIdx.x * (NT * 16);
-  const size_t kh = (size_t)K / 2, ks = (size_t)K / 16;
-
-  const uint8_t* wrow[NT];
-  const uint8_t* srow[NT];
-#pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    int n = n0 + t * 16 + l16;
-    n = n < N ? n : N - 1;
-    wrow[t] = wc + (size_t)n * kh;
-    srow[t] = ws + (size_t)n * ks;
-  }
-  const bool mvalid = l16 < M;
-  const uint4* xrow = x16 + (size_t)(mvalid ? l16 : 0) * kp_chunks;
-
-  floatx4 acc[NT];
-#pragma unroll
-  for (int t = 0; t < NT; ++t) acc[t] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
-
-  for (int kb = wave * 128; kb < K; kb += 512) {
-    const int kk = kb + 32 * g;
-    const bool kvalid = kk < K;
-    uint4 wv[NT];
-    uint32_t sv[NT];
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      wv[t] = kvalid ? *reinterpret_cast<const uint4*>(wrow[t] + kk / 2) : make_uint4(0, 0, 0, 0);
-      sv[t] = kvalid ? *reinterpret_cast<const uint16_t*>(srow[t] + kk / 16) : 0u;
-    }
-    uint4 xv[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) xv[j] = (mvalid && kvalid) ? xrow[kk / 8 + j] : make_uint4(0, 0, 0, 0);
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      ScaleSplit s0 = split_scale(sv[t] & 0xFFu), s1 = split_scale(sv[t] >> 8);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        uint32_t e[4];
-        expand8(dword_of(wv[t], j), j < 2 ? s0 : s1, e);
-        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(u4_as_f16x8(make_uint4(e[0], e[1], e[2], e[3])),
-                                                        u4_as_f16x8(xv[j]), acc[t], 0, 0, 0);
-      }
-    }
-  }
-
-#pragma unroll
-  for (int t = 0; t < NT; ++t) part[wave][t][lane] = acc[t];
-  __syncthreads();
-  if (wave != 0) return;
-  const float scale = (*gsx_p) * (*gsw_p);
-  if (!mvalid) return;
-  uint8_t* yrow = y + (size_t)l16 * ld_y_bytes;
-#pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    floatx4 s = part[0][t][lane];
-    floatx4 s1 = part[1][t][lane], s2 = part[2][t][lane], s3 = part[3][t][lane];
-    s = s + s1;
-    s = s + s2;
-    s = s + s3;
-    const int n = n0 + t * 16 + 4 * g;
-    store4<kYBf16>(yrow, n, N, s[0] * scale, s[1] * scale, s[2] * scale, s[3] * scale);
-  }
-}
-
 // ====================================================================== launch
 void launch_gemm(const void* x16, int64_t M, int64_t Kp, const uint8_t* wc, const uint8_t* ws, int64_t N, int64_t K,
                  const float* gsx, const float* gsw, void* y, bool y_bf16, int64_t ld_y, float* partials,
@@ -469,32 +335,6 @@ void launch_gemm(const void* x16, int64_t M, int64_t Kp, const uint8_t* wc, cons
       gemm_split_reduce_kernel<false><<<rgrid, 256, 0, s>>>(partials, p.full_tiles, p.split, p.tiles_n, (int)M,
                                                             (int)N, gsx, gsw, (uint8_t*)y, ldb);
   }
-}
-
-template <int NT>
-static void gemv_nt(const void* x16, int64_t M, int64_t Kp, const uint8_t* wc, const uint8_t* ws, int64_t N,
-                    int64_t K, const float* gsx, const float* gsw, void* y, bool y_bf16, int64_t ld_y,
-                    hipStream_t s) {
-  const int grid = (int)((N + NT * 16 - 1) / (NT * 16));
-  const size_t ldb = (size_t)ld_y * (y_bf16 ? 2u : 4u);
-  const uint32_t kpc = (uint32_t)(Kp / 8);
-  if (y_bf16)
-    gemv_kernel<NT, true><<<grid, 256, 0, s>>>((const uint4*)x16, kpc, (int)M, wc, ws, (int)N, (int)K, gsx, gsw,
-                                               (uint8_t*)y, ldb);
-  else
-    gemv_kernel<NT, false><<<grid, 256, 0, s>>>((const uint4*)x16, kpc, (int)M, wc, ws, (int)N, (int)K, gsx, gsw,
-                                                (uint8_t*)y, ldb);
-}
-
-void launch_gemv(const void* x16, int64_t M, int64_t Kp, const uint8_t* wc, const uint8_t* ws, int64_t N, int64_t K,
-                 const float* gsx, const float* gsw, void* y, bool y_bf16, int64_t ld_y, hipStream_t s) {
-  // One 16-row tile per workgroup keeps the grid fine-grained when the
-  // activations are few; more rows per workgroup amortise the activation
-  // reads when M is larger.
-  if (M <= 4)
-    gemv_nt<1>(x16, M, Kp, wc, ws, N, K, gsx, gsw, y, y_bf16, ld_y, s);
-  else
-    gemv_nt<4>(x16, M, Kp, wc, ws, N, K, gsx, gsw, y, y_bf16, ld_y, s);
 }
 
 }  // namespace nvfp4

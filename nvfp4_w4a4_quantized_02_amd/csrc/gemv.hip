@@ -1,0 +1,312 @@
+// Small-M (decode) block-scaled W4A4 contraction: paper "Why Gated DeltaNet
+// Survives 4-Bit Quantization", section 2 "NVFP4" (both operands NVFP4, FP32
+// accumulate).  W arrives as packed codes and scale bytes and is expanded
+// exactly to fp16 in registers; X arrives already expanded to fp16 by the
+// quantize kernel.  The epilogue applies RN(gs_x * gs_w).
+#include "encode.h"
+#include "launch.h"
+#include "mfma_util.h"
+
+#include <type_traits>
+
+namespace nvfp4 {
+
+// ====================================================================== GEMV
+// M <= 16 (decode).  MFMA 16x16x32 with W as the 16-row A operand and the
+// (zero-padded) activations as the 16-column B operand.  A workgroup owns
+// NT*16 rows of W; its 4 waves split K round-robin in 128-k chunks and their
+// partial sums are added in a fixed order through LDS, so the result does
+// not depend on scheduling.
+template <int NT, bool kYBf16>
+__global__ __launch_bounds__(256) void gemv_kernel(const uint4* __restrict__ x16, uint32_t kp_chunks, int M,
+                                                    const uint8_t* __restrict__ wc, const uint8_t* __restrict__ ws,
+                                                    int N, int K, const float* __restrict__ gsx_p,
+                                                    const float* __restrict__ gsw_p, uint8_t* __restrict__ y,
+                                                    size_t ld_y_bytes) {
+  __shared__ floatx4 part[4][NT][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int l16 = lane & 15, g = lane >> 4;
+  const int n0 = blockIdx.x * (NT * 16);
+  const size_t kh = (size_t)K / 2, ks = (size_t)K / 16;
+
+  const uint8_t* wrow[NT];
+  const uint8_t* srow[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    int n = n0 + t * 16 + l16;
+    n = n < N ? n : N - 1;
+    wrow[t] = wc + (size_t)n * kh;
+    srow[t] = ws + (size_t)n * ks;
+  }
+  const bool mvalid = l16 < M;
+  const uint4* xrow = x16 + (size_t)(mvalid ? l16 : 0) * kp_chunks;
+
+  floatx4 acc[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) acc[t] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+
+  for (int kb = wave * 128; kb < K; kb += 512) {
+    const int kk = kb + 32 * g;
+    const bool kvalid = kk < K;
+    uint4 wv[NT];
+    uint32_t sv[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      wv[t] = kvalid ? *reinterpret_cast<const uint4*>(wrow[t] + kk / 2) : make_uint4(0, 0, 0, 0);
+      sv[t] = kvalid ? *reinterpret_cast<const uint16_t*>(srow[t] + kk / 16) : 0u;
+    }
+    uint4 xv[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) xv[j] = (mvalid && kvalid) ? xrow[kk / 8 + j] : make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      ScaleSplit s0 = split_scale(sv[t] & 0xFFu), s1 = split_scale(sv[t] >> 8);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        uint32_t e[4];
+        expand8(dword_of(wv[t], j), j < 2 ? s0 : s1, e);
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(u4_as_f16x8(make_uint4(e[0], e[1], e[2], e[3])),
+                                                        u4_as_f16x8(xv[j]), acc[t], 0, 0, 0);
+      }
+    }
+  }
+
+#pragma unroll
+  for (int t = 0; t < NT; ++t) part[wave][t][lane] = acc[t];
+  __syncthreads();
+  if (wave != 0) return;
+  const float scale = (*gsx_p) * (*gsw_p);
+  if (!mvalid) return;
+  uint8_t* yrow = y + (size_t)l16 * ld_y_bytes;
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    floatx4 s = part[0][t][lane];
+    floatx4 s1 = part[1][t][lane], s2 = part[2][t][lane], s3 = part[3][t][lane];
+    s = s + s1;
+    s = s + s2;
+    s = s + s3;
+    const int n = n0 + t * 16 + 4 * g;
+    store4<kYBf16>(yrow, n, N, s[0] * scale, s[1] * scale, s[2] * scale, s[3] * scale);
+  }
+}
+
+// ---------------------------------------------------------------- M <= 4
+// Decode: the GEMV reads 100 MB of weights once, so it is bound by how many
+// bytes are in flight and by how cheaply each instruction moves them.  A
+// workgroup is one wave; it owns a 16-row tile of W over the whole of K.
+//
+// Everything reaches LDS by direct global->LDS transfers that the compiler
+// does not see, so every wait is an explicit, exact s_waitcnt:
+//   * first the tile's scale bytes (16 rows x K/16, contiguous in memory),
+//     in 1 KB pieces;
+//   * then a ring of D chunks of 256 k: the codes (16 rows x 128 B, two
+//     transfers that each fill 8 whole 128-byte lines) and the activations
+//     (M rows x 512 B of fp16, 32 lanes per row).
+// Code piece p of row r lands in 16-byte slot p ^ (r & 7) of its 128-byte
+// LDS row, so the 16 lanes of one read pass hit distinct bank groups.
+//
+// Inside a chunk, lane (r = lane % 16, g = lane / 16) takes k 64g .. 64g+63
+// of row r: 32 code bytes, read as two 16-byte pieces, whose dword t feeds
+// MFMA step t (16x16x32, k = 64g + 8t .. +7 on both operands); the lane's
+// four scale bytes for those k are one dword of the staged scales.  Lanes of
+// activation rows m >= M read a zero block.  Partial sums stay in the wave,
+// so the result does not depend on scheduling.
+constexpr uint32_t kGvChunkCodes = 2048;  // 16 rows x 128 B
+constexpr uint32_t kGvZero = 512;         // zero block for unused activation rows
+
+template <int D, int XI, bool kYBf16>
+__global__ __launch_bounds__(64) void gemv_stream_kernel(const uint8_t* __restrict__ x16, uint32_t ld_x16_bytes,
+                                                          int M, const uint8_t* __restrict__ wc,
+                                                          const uint8_t* __restrict__ ws, int N, int K,
+                                                          uint32_t scale_bytes_lds, const float* __restrict__ gsx_p,
+                                                          const float* __restrict__ gsw_p,
+                                                          uint8_t* __restrict__ y, size_t ld_y_bytes) {
+  extern __shared__ uint4 smem[];
+  constexpr uint32_t kSlot = kGvChunkCodes + XI * 1024u;
+  uint8_t* lds = reinterpret_cast<uint8_t*>(smem);
+  uint8_t* sc_lds = lds + D * kSlot;                    // staged scales [16][K/16]
+  uint8_t* zero_lds = sc_lds + scale_bytes_lds;         // kGvZero bytes of zeros
+
+  const int lane = threadIdx.x, l16 = lane & 15, g = lane >> 4;
+  const int tile = blockIdx.x;
+  const uint32_t kh = (uint32_t)K / 2, ks = (uint32_t)K / 16;
+  const int nck = K >> 8;  // a multiple of D
+
+  // ---- transfers
+  const uint32_t ring0 = lds_addr(lds), sc0 = lds_addr(sc_lds);
+  // codes: transfer h, lane i -> row 8h + i/8, slot i%8 holding piece (i%8) ^ (row & 7)
+  int crow[2];
+  uint32_t coff[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int r = 8 * h + (lane >> 3);
+    int n = tile * 16 + r;
+    n = n < N ? n : N - 1;
+    crow[h] = r;
+    coff[h] = (uint32_t)n * kh + 16u * (uint32_t)((lane & 7) ^ (r & 7));
+  }
+  // activations: transfer v, lane i -> row 2v + i/32 (clamped to M-1), 16 B piece i%32
+  uint32_t xoff[XI];
+#pragma unroll
+  for (int v = 0; v < XI; ++v) {
+    int m = 2 * v + (lane >> 5);
+    m = m < M ? m : M - 1;
+    xoff[v] = (uint32_t)m * ld_x16_bytes + 16u * (uint32_t)(lane & 31);
+  }
+  int next = 0;  // next chunk to transfer
+  auto issue = [&](int d) {
+    const int c = next < nck ? next : nck - 1;
+    const uint32_t slot = ring0 + (uint32_t)d * kSlot;
+    lds_dma16(wc, coff[0] + (uint32_t)c * 128u, slot);
+    lds_dma16(wc, coff[1] + (uint32_t)c * 128u, slot + 1024u);
+#pragma unroll
+    for (int v = 0; v < XI; ++v) lds_dma16(x16, xoff[v] + (uint32_t)c * 512u, slot + kGvChunkCodes + 1024u * v);
+    ++next;
+  };
+
+  // Scales first: 16 rows x ks bytes are contiguous; pieces past the end
+  // re-read the last piece (their LDS bytes are never read).
+  {
+    int n0 = tile * 16;
+    const uint32_t rows_here = (uint32_t)((N - n0) < 16 ? (N - n0) : 16);
+    const uint32_t bytes = rows_here * ks;  // a multiple of 4 (K % 64 == 0)
+    const uint32_t base = (uint32_t)n0 * ks;
+    const uint32_t npieces = (16u * ks + 1023u) / 1024u;
+    for (uint32_t q = 0; q < npieces; ++q) {
+      uint32_t off = q * 1024u + 16u * (uint32_t)lane;
+      off = off + 16u <= bytes ? off : (bytes >= 16u ? bytes - 16u : 0u);
+      lds_dma16(ws, base + off, sc0 + q * 1024u);
+    }
+  }
+  reinterpret_cast<uint2*>(zero_lds)[lane] = make_uint2(0, 0);
+#pragma unroll
+  for (int d = 0; d < D; ++d) issue(d);
+
+  const bool mvalid = l16 < M;
+  const float scale = (*gsx_p) * (*gsw_p);
+  // this lane's reads
+  const uint32_t sw = (uint32_t)(l16 & 7);
+  const uint32_t cpos0 = (uint32_t)l16 * 128u + 16u * ((2u * g) ^ sw);
+  const uint32_t cpos1 = (uint32_t)l16 * 128u + 16u * ((2u * g + 1u) ^ sw);
+  const uint8_t* sc_row = sc_lds + (uint32_t)l16 * ks + 4u * g;
+
+  floatx4 acc = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int c0 = 0; c0 < nck; c0 += D) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      wait_vmcnt<(D - 1) * (2 + XI)>();
+      const uint8_t* slot = lds + d * kSlot;
+      const uint4 w0 = *reinterpret_cast<const uint4*>(slot + cpos0);
+      const uint4 w1 = *reinterpret_cast<const uint4*>(slot + cpos1);
+      const uint32_t sd = *reinterpret_cast<const uint32_t*>(sc_row + (uint32_t)(c0 + d) * 16u);
+      const uint8_t* xb = mvalid ? slot + kGvChunkCodes + 512u * l16 + 128u * g : zero_lds + 128u * g;
+      const ScaleSplit s0 = split_scale(sd & 0xFFu), s1 = split_scale((sd >> 8) & 0xFFu),
+                       s2 = split_scale((sd >> 16) & 0xFFu), s3 = split_scale(sd >> 24);
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const uint4 xv = *reinterpret_cast<const uint4*>(xb + 16 * t);
+        const ScaleSplit& sp = t < 2 ? s0 : (t < 4 ? s1 : (t < 6 ? s2 : s3));
+        uint32_t e[4];
+        expand8(dword_of(t < 4 ? w0 : w1, t & 3), sp, e);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(u4_as_f16x8(make_uint4(e[0], e[1], e[2], e[3])),
+                                                     u4_as_f16x8(xv), acc, 0, 0, 0);
+      }
+      issue(d);
+    }
+  }
+  wait_vmcnt<0>();
+  if (mvalid)
+    store4<kYBf16>(y + (size_t)l16 * ld_y_bytes, tile * 16 + 4 * g, N, acc[0] * scale, acc[1] * scale,
+                   acc[2] * scale, acc[3] * scale);
+}
+
+// LDS of one streaming workgroup, and the depth that keeps every tile in one
+// round of the machine; 0 when the streaming kernel does not apply.
+struct GvPlan {
+  int depth, xi;
+  size_t lds;
+};
+
+static GvPlan plan_gemv_stream(int64_t M, int64_t N, int64_t K) {
+  GvPlan p{0, 0, 0};
+  if (M < 1 || M > 4 || K < 256 || K % 256 != 0 || (uint64_t)N * (uint64_t)K / 2 >= (1ull << 32)) return p;
+  static int cus = 0, lds_cu = 0;
+  if (!cus) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipDeviceGetAttribute(&lds_cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) != hipSuccess) {
+      cus = 0;
+      return p;
+    }
+  }
+  const int xi = M <= 2 ? 1 : 2;
+  const int64_t tiles = (N + 15) / 16;
+  const size_t sc = (size_t)((16 * (K / 16) + 1023) / 1024) * 1024;
+  const int nck = (int)(K / 256);
+  for (int d : {4, 2, 1}) {
+    if (nck % d) continue;
+    const size_t lds = (size_t)d * (kGvChunkCodes + 1024u * xi) + sc + kGvZero;
+    if (lds > 65536) continue;
+    const int64_t per_cu = lds_cu / (int64_t)lds;
+    if (d > 1 && per_cu * cus < tiles) continue;
+    p.depth = d;
+    p.xi = xi;
+    p.lds = lds;
+    return p;
+  }
+  return p;
+}
+
+template <int NT>
+static void gemv_nt(const void* x16, int64_t M, int64_t Kp, const uint8_t* wc, const uint8_t* ws, int64_t N,
+                    int64_t K, const float* gsx, const float* gsw, void* y, bool y_bf16, int64_t ld_y,
+                    hipStream_t s) {
+  const int grid = (int)((N + NT * 16 - 1) / (NT * 16));
+  const size_t ldb = (size_t)ld_y * (y_bf16 ? 2u : 4u);
+  const uint32_t kpc = (uint32_t)(Kp / 8);
+  if (y_bf16)
+    gemv_kernel<NT, true><<<grid, 256, 0, s>>>((const uint4*)x16, kpc, (int)M, wc, ws, (int)N, (int)K, gsx, gsw,
+                                               (uint8_t*)y, ldb);
+  else
+    gemv_kernel<NT, false><<<grid, 256, 0, s>>>((const uint4*)x16, kpc, (int)M, wc, ws, (int)N, (int)K, gsx, gsw,
+                                                (uint8_t*)y, ldb);
+}
+
+void launch_gemv(const void* x16, int64_t M, int64_t Kp, const uint8_t* wc, const uint8_t* ws, int64_t N, int64_t K,
+                 const float* gsx, const float* gsw, void* y, bool y_bf16, int64_t ld_y, hipStream_t s) {
+  const GvPlan gp = plan_gemv_stream(M, N, K);
+  if (gp.depth) {
+    const int tiles = (int)((N + 15) / 16);
+    const size_t ldb = (size_t)ld_y * (y_bf16 ? 2u : 4u);
+    const uint32_t ldx = (uint32_t)(Kp * 2);
+    const uint32_t sc = (uint32_t)((16 * (K / 16) + 1023) / 1024) * 1024u;
+    auto go = [&](auto dc, auto xc) {
+      constexpr int D = decltype(dc)::value, XI = decltype(xc)::value;
+      if (y_bf16)
+        gemv_stream_kernel<D, XI, true><<<tiles, 64, gp.lds, s>>>((const uint8_t*)x16, ldx, (int)M, wc, ws, (int)N,
+                                                                  (int)K, sc, gsx, gsw, (uint8_t*)y, ldb);
+      else
+        gemv_stream_kernel<D, XI, false><<<tiles, 64, gp.lds, s>>>((const uint8_t*)x16, ldx, (int)M, wc, ws,
+                                                                   (int)N, (int)K, sc, gsx, gsw, (uint8_t*)y, ldb);
+    };
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    using I4 = std::integral_constant<int, 4>;
+    if (gp.xi == 1) {
+      if (gp.depth == 4) go(I4(), I1()); else if (gp.depth == 2) go(I2(), I1()); else go(I1(), I1());
+    } else {
+      if (gp.depth == 4) go(I4(), I2()); else if (gp.depth == 2) go(I2(), I2()); else go(I1(), I2());
+    }
+    return;
+  }
+  // One 16-row tile per workgroup keeps the grid fine-grained when the
+  // activations are few; more rows per workgroup amortise the activation
+  // reads when M is larger.
+  if (M <= 4)
+    gemv_nt<1>(x16, M, Kp, wc, ws, N, K, gsx, gsw, y, y_bf16, ld_y, s);
+  else
+    gemv_nt<4>(x16, M, Kp, wc, ws, N, K, gsx, gsw, y, y_bf16, ld_y, s);
+}
+
+}  // namespace nvfp4

@@ -186,39 +186,31 @@ __device__ __forceinline__ uint32_t encode_block_exact(const float (&x)[16], flo
 
 // fp16 expansion of 8 packed codes sharing one scale byte: E2M1(code) *
 // E4M3value(sb), exact in fp16 (values from 2^-10 to 2688, at most 6
-// significant bits).  The scale splits into a power of two, applied by the
-// hardware FP4 conversion (which uses only the exponent of its scale
-// operand), and a small integer multiplier q applied by one packed fp16
-// multiply: E4M3value = 2^(max(e,1) - 10) * q with q = 8 + m for normal
-// bytes (e >= 1) and q = m for subnormal ones (e = 0).  Both factors and the
-// products stay exact in fp16.
+// significant bits).  E4M3 and fp16 share their layout below the exponent
+// field's top bit: the byte's seven magnitude bits shifted left by 7 are the
+// fp16 whose value is E4M3value(sb) * 2^-8, for normal and subnormal bytes
+// alike (the fp16 exponent bias, 15, is the E4M3 bias, 7, plus 8).  The
+// hardware FP4 conversion multiplies by 2^8 (it uses only the exponent of its
+// scale operand), giving E2M1 * 2^8 in [128, 1536], and one packed fp16
+// multiply by that fp16 applies the scale.  Every step is exact.
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 
-struct ScaleSplit {
-  float p2;      // power of two (only its exponent matters)
-  half2_t q2;    // multiplier, both halves
-};
-
-__device__ __forceinline__ ScaleSplit split_scale(uint32_t sb) {
-  uint32_t e = (sb >> 3) & 15u, m = sb & 7u;
-  ScaleSplit s;
-  s.p2 = __uint_as_float(((e > 1u ? e : 1u) + 117u) << 23);
-  uint32_t q = __builtin_bit_cast(uint16_t, (_Float16)(uint16_t)(m | ((e < 1u ? e : 1u) << 3)));
-  s.q2 = __builtin_bit_cast(half2_t, q | (q << 16));
-  return s;
+// Both halves = E4M3value(sb & 0x7F) * 2^-8.
+__device__ __forceinline__ half2_t scale_f16x2(uint32_t sb) {
+  return __builtin_bit_cast(half2_t, (sb & 0x7Fu) * 0x00800080u);
 }
 
 // out[i] = fp16 pair for codes byte i (element 2i low half).
-__device__ __forceinline__ void expand8(uint32_t codes8, ScaleSplit s, uint32_t (&out)[4]) {
-  half2_t v0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes8, s.p2, 0);
-  half2_t v1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes8, s.p2, 1);
-  half2_t v2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes8, s.p2, 2);
-  half2_t v3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes8, s.p2, 3);
-  out[0] = __builtin_bit_cast(uint32_t, v0 * s.q2);
-  out[1] = __builtin_bit_cast(uint32_t, v1 * s.q2);
-  out[2] = __builtin_bit_cast(uint32_t, v2 * s.q2);
-  out[3] = __builtin_bit_cast(uint32_t, v3 * s.q2);
+__device__ __forceinline__ void expand8(uint32_t codes8, half2_t q2, uint32_t (&out)[4]) {
+  const half2_t v0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes8, 256.0f, 0);
+  const half2_t v1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes8, 256.0f, 1);
+  const half2_t v2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes8, 256.0f, 2);
+  const half2_t v3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes8, 256.0f, 3);
+  out[0] = __builtin_bit_cast(uint32_t, v0 * q2);
+  out[1] = __builtin_bit_cast(uint32_t, v1 * q2);
+  out[2] = __builtin_bit_cast(uint32_t, v2 * q2);
+  out[3] = __builtin_bit_cast(uint32_t, v3 * q2);
 }
 
 }  // namespace nvfp4

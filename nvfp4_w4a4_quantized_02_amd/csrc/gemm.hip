@@ -55,7 +55,7 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(const uint4* __restrict__ 
   // Three distinct buffers (not one indexed array) so the compiler can see
   // that a transfer into one buffer never feeds reads of another.
   __shared__ GemmBuf b0, b1, b2;
-  __shared__ uint2 split_lut[256];
+  __shared__ uint32_t scale_lut[128];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wave_n = wave >> 1, wave_m = wave & 1;
   // Whole tiles first; the workgroups past full_tiles each take one K part
@@ -122,13 +122,9 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(const uint4* __restrict__ 
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[t][u][r] = 0.0f;
 
-  // Scale-byte table: entry b holds the power-of-two operand and the packed
-  // fp16 multiplier of split_scale(b), so a split costs one LDS read.
-#pragma unroll
-  for (int e = tid; e < 256; e += 256) {
-    ScaleSplit sp = split_scale((uint32_t)e);
-    split_lut[e] = make_uint2(__float_as_uint(sp.p2), __builtin_bit_cast(uint32_t, sp.q2));
-  }
+  // Scale-byte table: entry b holds scale_f16x2(b), so a scale costs one
+  // LDS read (the sign bit of a scale byte is ignored, as by scale_f16x2).
+  if (tid < 128) scale_lut[tid] = __builtin_bit_cast(uint32_t, scale_f16x2((uint32_t)tid));
 
   // Operand fragments of sub-step j from buffer `cur`.
   auto read_x = [&](const GemmBuf& cur, int j, f16x8 (&bx)[4]) {
@@ -147,22 +143,18 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(const uint4* __restrict__ 
       sw[t] = cur.ws[row] >> (16 * h);
     }
   };
-  auto split_w = [&](const uint32_t (&sw)[4], uint2 (&sp)[4][2]) {
+  auto split_w = [&](const uint32_t (&sw)[4], uint32_t (&sp)[4][2]) {
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      sp[t][0] = split_lut[sw[t] & 0xFFu];
-      sp[t][1] = split_lut[(sw[t] >> 8) & 0xFFu];
+      sp[t][0] = scale_lut[sw[t] & 0x7Fu];
+      sp[t][1] = scale_lut[(sw[t] >> 8) & 0x7Fu];
     }
   };
-  auto expand_w = [&](const uint4 (&wv)[4], const uint2 (&sp)[4][2], int j, f16x8 (&aw)[4]) {
+  auto expand_w = [&](const uint4 (&wv)[4], const uint32_t (&sp)[4][2], int j, f16x8 (&aw)[4]) {
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      const uint2 s2 = sp[t][j >> 1];
-      ScaleSplit ss;
-      ss.p2 = __uint_as_float(s2.x);
-      ss.q2 = __builtin_bit_cast(half2_t, s2.y);
       uint32_t e[4];
-      expand8(dword_of(wv[t], j), ss, e);
+      expand8(dword_of(wv[t], j), __builtin_bit_cast(half2_t, sp[t][j >> 1]), e);
       aw[t] = u4_as_f16x8(make_uint4(e[0], e[1], e[2], e[3]));
     }
   };
@@ -178,7 +170,7 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(const uint4* __restrict__ 
   // codes and scale splits of the current step and the operands of its next
   // sub-step.
   uint4 wv[4];
-  uint2 sp[4][2];
+  uint32_t sp[4][2];
   f16x8 bx[4], aw[4];
 
   // One main-loop step.  Sub-steps 0..2 of step kt run from `cur`, each

@@ -60,7 +60,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(const uint4* __restrict__ x16
     for (int j = 0; j < 4; ++j) xv[j] = (mvalid && kvalid) ? xrow[kk / 8 + j] : make_uint4(0, 0, 0, 0);
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-      ScaleSplit s0 = split_scale(sv[t] & 0xFFu), s1 = split_scale(sv[t] >> 8);
+      const half2_t s0 = scale_f16x2(sv[t]), s1 = scale_f16x2(sv[t] >> 8);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         uint32_t e[4];
@@ -103,29 +103,28 @@ __global__ __launch_bounds__(256) void gemv_kernel(const uint4* __restrict__ x16
 //     transfers that each fill 8 whole 128-byte lines) and the activations
 //     (M rows x 512 B of fp16, 32 lanes per row).
 // Code piece p of row r lands in 16-byte slot p ^ (r & 7) of its 128-byte
-// LDS row, so the 16 lanes of one read pass hit distinct bank groups.
+// LDS row, and activation piece 8a + b in slot 8a + (b ^ a) of its row, so
+// the lanes of one read pass hit distinct bank groups.
 //
 // Inside a chunk, lane (r = lane % 16, g = lane / 16) takes k 64g .. 64g+63
 // of row r: 32 code bytes, read as two 16-byte pieces, whose dword t feeds
 // MFMA step t (16x16x32, k = 64g + 8t .. +7 on both operands); the lane's
 // four scale bytes for those k are one dword of the staged scales.  Lanes of
-// activation rows m >= M read a zero block.  Partial sums stay in the wave,
+// activation rows m >= M keep zero operands.  Partial sums stay in the wave,
 // so the result does not depend on scheduling.
 constexpr uint32_t kGvChunkCodes = 2048;  // 16 rows x 128 B
-constexpr uint32_t kGvZero = 512;         // zero block for unused activation rows
 
 template <int D, int XI, bool kYBf16>
 __global__ __launch_bounds__(64) void gemv_stream_kernel(const uint8_t* __restrict__ x16, uint32_t ld_x16_bytes,
                                                           int M, const uint8_t* __restrict__ wc,
                                                           const uint8_t* __restrict__ ws, int N, int K,
-                                                          uint32_t scale_bytes_lds, const float* __restrict__ gsx_p,
+                                                          const float* __restrict__ gsx_p,
                                                           const float* __restrict__ gsw_p,
                                                           uint8_t* __restrict__ y, size_t ld_y_bytes) {
   extern __shared__ uint4 smem[];
   constexpr uint32_t kSlot = kGvChunkCodes + XI * 1024u;
   uint8_t* lds = reinterpret_cast<uint8_t*>(smem);
   uint8_t* sc_lds = lds + D * kSlot;                    // staged scales [16][K/16]
-  uint8_t* zero_lds = sc_lds + scale_bytes_lds;         // kGvZero bytes of zeros
 
   const int lane = threadIdx.x, l16 = lane & 15, g = lane >> 4;
   const int tile = blockIdx.x;
@@ -145,13 +144,15 @@ __global__ __launch_bounds__(64) void gemv_stream_kernel(const uint8_t* __restri
     crow[h] = r;
     coff[h] = (uint32_t)n * kh + 16u * (uint32_t)((lane & 7) ^ (r & 7));
   }
-  // activations: transfer v, lane i -> row 2v + i/32 (clamped to M-1), 16 B piece i%32
+  // activations: transfer v, lane i -> row 2v + i/32 (clamped to M-1), LDS
+  // slot p = i % 32 of that row holding piece 8 (p / 8) + ((p % 8) ^ (p / 8))
   uint32_t xoff[XI];
 #pragma unroll
   for (int v = 0; v < XI; ++v) {
     int m = 2 * v + (lane >> 5);
     m = m < M ? m : M - 1;
-    xoff[v] = (uint32_t)m * ld_x16_bytes + 16u * (uint32_t)(lane & 31);
+    const uint32_t p = (uint32_t)(lane & 31), piece = (p & ~7u) | ((p & 7u) ^ (p >> 3));
+    xoff[v] = (uint32_t)m * ld_x16_bytes + 16u * piece;
   }
   int next = 0;  // next chunk to transfer
   auto issue = [&](int d) {
@@ -178,7 +179,6 @@ __global__ __launch_bounds__(64) void gemv_stream_kernel(const uint8_t* __restri
       lds_dma16(ws, base + off, sc0 + q * 1024u);
     }
   }
-  reinterpret_cast<uint2*>(zero_lds)[lane] = make_uint2(0, 0);
 #pragma unroll
   for (int d = 0; d < D; ++d) issue(d);
 
@@ -190,6 +190,10 @@ __global__ __launch_bounds__(64) void gemv_stream_kernel(const uint8_t* __restri
   const uint32_t cpos1 = (uint32_t)l16 * 128u + 16u * ((2u * g + 1u) ^ sw);
   const uint8_t* sc_row = sc_lds + (uint32_t)l16 * ks + 4u * g;
 
+  const uint32_t xg = (uint32_t)g;
+  uint4 xv[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) xv[t] = make_uint4(0, 0, 0, 0);
   floatx4 acc = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
   for (int c0 = 0; c0 < nck; c0 += D) {
 #pragma unroll
@@ -199,17 +203,22 @@ __global__ __launch_bounds__(64) void gemv_stream_kernel(const uint8_t* __restri
       const uint4 w0 = *reinterpret_cast<const uint4*>(slot + cpos0);
       const uint4 w1 = *reinterpret_cast<const uint4*>(slot + cpos1);
       const uint32_t sd = *reinterpret_cast<const uint32_t*>(sc_row + (uint32_t)(c0 + d) * 16u);
-      const uint8_t* xb = mvalid ? slot + kGvChunkCodes + 512u * l16 + 128u * g : zero_lds + 128u * g;
-      const ScaleSplit s0 = split_scale(sd & 0xFFu), s1 = split_scale((sd >> 8) & 0xFFu),
-                       s2 = split_scale((sd >> 16) & 0xFFu), s3 = split_scale(sd >> 24);
+      // Only the lanes of real activation rows read them; the others keep
+      // the zeros their operand registers started with.
+      if (mvalid) {
+        const uint8_t* xb = slot + kGvChunkCodes + 512u * l16 + 128u * g;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) xv[t] = *reinterpret_cast<const uint4*>(xb + 16u * ((uint32_t)t ^ xg));
+      }
+      const half2_t s0 = scale_f16x2(sd), s1 = scale_f16x2(sd >> 8), s2 = scale_f16x2(sd >> 16),
+                    s3 = scale_f16x2(sd >> 24);
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
-        const uint4 xv = *reinterpret_cast<const uint4*>(xb + 16 * t);
-        const ScaleSplit& sp = t < 2 ? s0 : (t < 4 ? s1 : (t < 6 ? s2 : s3));
+        const half2_t sp = t < 2 ? s0 : (t < 4 ? s1 : (t < 6 ? s2 : s3));
         uint32_t e[4];
         expand8(dword_of(t < 4 ? w0 : w1, t & 3), sp, e);
         acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(u4_as_f16x8(make_uint4(e[0], e[1], e[2], e[3])),
-                                                     u4_as_f16x8(xv), acc, 0, 0, 0);
+                                                     u4_as_f16x8(xv[t]), acc, 0, 0, 0);
       }
       issue(d);
     }
@@ -246,7 +255,7 @@ static GvPlan plan_gemv_stream(int64_t M, int64_t N, int64_t K) {
   const int nck = (int)(K / 256);
   for (int d : {4, 2, 1}) {
     if (nck % d) continue;
-    const size_t lds = (size_t)d * (kGvChunkCodes + 1024u * xi) + sc + kGvZero;
+    const size_t lds = (size_t)d * (kGvChunkCodes + 1024u * xi) + sc;
     if (lds > 65536) continue;
     const int64_t per_cu = lds_cu / (int64_t)lds;
     if (d > 1 && per_cu * cus < tiles) continue;
@@ -280,15 +289,14 @@ void launch_gemv(const void* x16, int64_t M, int64_t Kp, const uint8_t* wc, cons
     const int tiles = (int)((N + 15) / 16);
     const size_t ldb = (size_t)ld_y * (y_bf16 ? 2u : 4u);
     const uint32_t ldx = (uint32_t)(Kp * 2);
-    const uint32_t sc = (uint32_t)((16 * (K / 16) + 1023) / 1024) * 1024u;
     auto go = [&](auto dc, auto xc) {
       constexpr int D = decltype(dc)::value, XI = decltype(xc)::value;
       if (y_bf16)
         gemv_stream_kernel<D, XI, true><<<tiles, 64, gp.lds, s>>>((const uint8_t*)x16, ldx, (int)M, wc, ws, (int)N,
-                                                                  (int)K, sc, gsx, gsw, (uint8_t*)y, ldb);
+                                                                  (int)K, gsx, gsw, (uint8_t*)y, ldb);
       else
         gemv_stream_kernel<D, XI, false><<<tiles, 64, gp.lds, s>>>((const uint8_t*)x16, ldx, (int)M, wc, ws,
-                                                                   (int)N, (int)K, sc, gsx, gsw, (uint8_t*)y, ldb);
+                                                                   (int)N, (int)K, gsx, gsw, (uint8_t*)y, ldb);
     };
     using I1 = std::integral_constant<int, 1>;
     using I2 = std::integral_constant<int, 2>;

@@ -7,6 +7,8 @@
 #include "encode.h"
 #include "launch.h"
 
+#include <type_traits>
+
 namespace nvfp4 {
 
 // ------------------------------------------------------------------ amax
@@ -138,15 +140,16 @@ __global__ __launch_bounds__(256) void quantize_kernel(const uint8_t* __restrict
                                                         const uint32_t* __restrict__ partials, int npartials,
                                                         uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
                                                         uint4* __restrict__ x16, float* __restrict__ gs_out) {
-  __shared__ uint32_t red[4];
-  __shared__ uint32_t deferred[4][kDeferCap];
+  constexpr int kWaves = 4;
+  __shared__ uint32_t red[kWaves];
+  __shared__ uint32_t deferred[kWaves][kDeferCap];
   const float gs = reduce_partials_to_gs(partials, npartials, red);
   if (blockIdx.x == 0 && threadIdx.x == 0) *gs_out = gs;
   const FastScale fsc = fast_scale(gs);
   const uint32_t lane = threadIdx.x & 63u;
   uint32_t* queue = deferred[threadIdx.x >> 6];
-  const uint32_t waves = gridDim.x * 4u;
-  const uint32_t wave_id = blockIdx.x * 4u + (threadIdx.x >> 6);
+  const uint32_t waves = gridDim.x * (uint32_t)kWaves;
+  const uint32_t wave_id = blockIdx.x * (uint32_t)kWaves + (threadIdx.x >> 6);
   const uint32_t chunks = (total_blocks + 63u) >> 6;
   if (wave_id >= chunks) return;
 
@@ -156,10 +159,10 @@ __global__ __launch_bounds__(256) void quantize_kernel(const uint8_t* __restrict
   };
   auto store = [&](uint32_t b, uint32_t sb, uint32_t lo, uint32_t hi) {
     if (kF16) {
-      const ScaleSplit sp = split_scale(sb);
+      const half2_t q2 = scale_f16x2(sb);
       uint32_t e0[4], e1[4];
-      expand8(lo, sp, e0);
-      expand8(hi, sp, e1);
+      expand8(lo, q2, e0);
+      expand8(hi, q2, e1);
       x16[(size_t)b * 2u] = make_uint4(e0[0], e0[1], e0[2], e0[3]);
       x16[(size_t)b * 2u + 1u] = make_uint4(e1[0], e1[1], e1[2], e1[3]);
     } else {
@@ -216,6 +219,89 @@ __global__ __launch_bounds__(256) void quantize_kernel(const uint8_t* __restrict
     }
   }
   if (queued) flush(queued);
+}
+
+// Small tensors (decode-sized activations): one launch instead of the
+// absmax + encode pair, which is what decides the time at this size.  Each
+// workgroup of 1024 threads takes the absmax of the whole tensor itself (it
+// is at most 256 KB and sits in cache after the first workgroup reads it;
+// surplus lanes re-read the last block, which cannot change a max, so every
+// load is unconditional), then encodes its own 1024 blocks, one per thread,
+// the rare bracket misses inline.
+constexpr int kSmallThreads = 1024;
+
+// Tensors of at most this many blocks take the one-launch kernel.
+static inline uint32_t small_block_limit(bool) { return 8u * kSmallThreads; }
+
+template <bool kBf16, bool kF16>
+__global__ __launch_bounds__(1024) void quantize_small_kernel(const uint8_t* __restrict__ x, size_t ld_bytes,
+                                                               uint32_t kblocks, uint32_t out_kblocks,
+                                                               uint32_t total_blocks, FastDiv fd,
+                                                               uint8_t* __restrict__ codes,
+                                                               uint8_t* __restrict__ scales,
+                                                               uint4* __restrict__ x16, float* __restrict__ gs_out) {
+  __shared__ uint32_t red[kSmallThreads / 64];
+  if (total_blocks == 0) {  // (the launcher never sends one) no element to clamp onto
+    if (blockIdx.x == 0 && threadIdx.x == 0) *gs_out = 0.0f;
+    return;
+  }
+  auto block_ptr = [&](uint32_t b, uint32_t& kb) {
+    const uint32_t r = fastdiv(b, fd);
+    kb = b - r * out_kblocks;
+    const uint32_t kc = kb < kblocks ? kb : kblocks - 1u;
+    return x + (size_t)r * ld_bytes + (size_t)kc * (kBf16 ? 32u : 64u);
+  };
+
+  uint32_t m = 0;
+  for (uint32_t b0 = threadIdx.x; b0 < total_blocks; b0 += 4u * kSmallThreads) {
+    float xv[4][16];
+    uint32_t kb[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      uint32_t b = b0 + (uint32_t)u * kSmallThreads;
+      b = b < total_blocks ? b : total_blocks - 1u;
+      load_block<kBf16>(block_ptr(b, kb[u]), xv[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const uint32_t a = kb[u] < kblocks ? block_absmax_bits<kBf16>(xv[u]) : 0u;  // padding blocks are zeros
+      m = m > a ? m : a;
+    }
+  }
+  m = wave_max_u32(m);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  uint32_t amax = red[0];
+#pragma unroll
+  for (int i = 1; i < kSmallThreads / 64; ++i) amax = amax > red[i] ? amax : red[i];
+  const float gs = tensor_scale(__uint_as_float(amax));
+  if (blockIdx.x == 0 && threadIdx.x == 0) *gs_out = gs;
+
+  const uint32_t b = blockIdx.x * kSmallThreads + threadIdx.x;
+  if (b >= total_blocks) return;
+  uint32_t kb;
+  const uint8_t* p = block_ptr(b, kb);
+  if (kF16 && kb >= kblocks) {
+    x16[(size_t)b * 2u] = make_uint4(0, 0, 0, 0);
+    x16[(size_t)b * 2u + 1u] = make_uint4(0, 0, 0, 0);
+    return;
+  }
+  float xv[16];
+  load_block<kBf16>(p, xv);
+  uint32_t sb, lo, hi;
+  if (!encode_block_fast(xv, block_absmax_bits<kBf16>(xv), fast_scale(gs), sb, lo, hi))
+    sb = encode_block_exact(xv, gs, lo, hi);
+  if (kF16) {
+    const half2_t q2 = scale_f16x2(sb);
+    uint32_t e0[4], e1[4];
+    expand8(lo, q2, e0);
+    expand8(hi, q2, e1);
+    x16[(size_t)b * 2u] = make_uint4(e0[0], e0[1], e0[2], e0[3]);
+    x16[(size_t)b * 2u + 1u] = make_uint4(e1[0], e1[1], e1[2], e1[3]);
+  } else {
+    *reinterpret_cast<uint2*>(codes + (size_t)b * 8u) = make_uint2(lo, hi);
+    scales[b] = (uint8_t)sb;
+  }
 }
 
 __global__ void fill_f32_kernel(float* p, float v) { *p = v; }
@@ -299,6 +385,7 @@ static inline int grid_for(uint64_t work, uint64_t per_wg, int cap) {
 
 int launch_amax(const void* x, bool bf16, int64_t rows, int64_t K, int64_t ld, uint32_t* partials,
                 hipStream_t s) {
+  if (rows * (K / 16) <= (int64_t)small_block_limit(bf16)) return 0;  // one-workgroup quantize instead
   uint32_t esize = bf16 ? 2u : 4u;
   uint32_t cpr = (uint32_t)(K * esize / 16);
   uint32_t ldc = (uint32_t)(ld * esize / 16);
@@ -312,35 +399,49 @@ int launch_amax(const void* x, bool bf16, int64_t rows, int64_t K, int64_t ld, u
   return grid;
 }
 
+// npartials == 0 (launch_amax launched nothing): one workgroup does it all.
+template <bool kF16>
+static void launch_quantize(const void* x, bool bf16, int64_t rows, int64_t K, int64_t ld, int64_t Kp,
+                            const uint32_t* partials, int npartials, uint8_t* codes, uint8_t* scales, void* x16,
+                            float* gs, hipStream_t s) {
+  const uint32_t kb = (uint32_t)(K / 16), okb = (uint32_t)(Kp / 16);
+  const uint32_t total = (uint32_t)(rows * (int64_t)okb);
+  const size_t ld_bytes = (size_t)ld * (bf16 ? 2u : 4u);
+  const FastDiv fd = make_fastdiv(okb ? okb : 1u);
+  const uint8_t* xb = (const uint8_t*)x;
+  uint4* xo = (uint4*)x16;
+  if (total == 0) {  // nothing to encode; the absmax of no elements is 0
+    launch_fill_f32(gs, 0.0f, s);
+    return;
+  }
+  if (npartials == 0) {
+    const int grid = (int)((total + kSmallThreads - 1) / kSmallThreads);
+    if (bf16)
+      quantize_small_kernel<true, kF16><<<grid, kSmallThreads, 0, s>>>(xb, ld_bytes, kb, okb, total, fd, codes,
+                                                                       scales, xo, gs);
+    else
+      quantize_small_kernel<false, kF16><<<grid, kSmallThreads, 0, s>>>(xb, ld_bytes, kb, okb, total, fd, codes,
+                                                                        scales, xo, gs);
+    return;
+  }
+  const int grid = grid_for(total, 256, 4096);
+  if (bf16)
+    quantize_kernel<true, kF16><<<grid, 256, 0, s>>>(xb, ld_bytes, kb, okb, total, fd, partials, npartials, codes,
+                                                     scales, xo, gs);
+  else
+    quantize_kernel<false, kF16><<<grid, 256, 0, s>>>(xb, ld_bytes, kb, okb, total, fd, partials, npartials,
+                                                      codes, scales, xo, gs);
+}
+
 void launch_quantize_packed(const void* x, bool bf16, int64_t rows, int64_t K, int64_t ld,
                             const uint32_t* partials, int npartials, uint8_t* codes, uint8_t* scales, float* gs,
                             hipStream_t s) {
-  uint32_t kb = (uint32_t)(K / 16);
-  uint32_t total = (uint32_t)(rows * (int64_t)kb);
-  size_t ld_bytes = (size_t)ld * (bf16 ? 2u : 4u);
-  int grid = grid_for(total, 256, 4096);
-  FastDiv fd = make_fastdiv(kb ? kb : 1u);
-  if (bf16)
-    quantize_kernel<true, false><<<grid, 256, 0, s>>>((const uint8_t*)x, ld_bytes, kb, kb, total, fd, partials,
-                                                      npartials, codes, scales, nullptr, gs);
-  else
-    quantize_kernel<false, false><<<grid, 256, 0, s>>>((const uint8_t*)x, ld_bytes, kb, kb, total, fd, partials,
-                                                       npartials, codes, scales, nullptr, gs);
+  launch_quantize<false>(x, bf16, rows, K, ld, K, partials, npartials, codes, scales, nullptr, gs, s);
 }
 
 void launch_quantize_f16(const void* x, bool bf16, int64_t rows, int64_t K, int64_t ld, int64_t Kp,
                          const uint32_t* partials, int npartials, void* x16, float* gs, hipStream_t s) {
-  uint32_t kb = (uint32_t)(K / 16), kpb = (uint32_t)(Kp / 16);
-  uint32_t total = (uint32_t)(rows * (int64_t)kpb);
-  size_t ld_bytes = (size_t)ld * (bf16 ? 2u : 4u);
-  int grid = grid_for(total, 256, 4096);
-  FastDiv fd = make_fastdiv(kpb ? kpb : 1u);
-  if (bf16)
-    quantize_kernel<true, true><<<grid, 256, 0, s>>>((const uint8_t*)x, ld_bytes, kb, kpb, total, fd, partials,
-                                                     npartials, nullptr, nullptr, (uint4*)x16, gs);
-  else
-    quantize_kernel<false, true><<<grid, 256, 0, s>>>((const uint8_t*)x, ld_bytes, kb, kpb, total, fd, partials,
-                                                      npartials, nullptr, nullptr, (uint4*)x16, gs);
+  launch_quantize<true>(x, bf16, rows, K, ld, Kp, partials, npartials, nullptr, nullptr, x16, gs, s);
 }
 
 void launch_fill_f32(float* p, float v, hipStream_t s) { fill_f32_kernel<<<1, 1, 0, s>>>(p, v); }

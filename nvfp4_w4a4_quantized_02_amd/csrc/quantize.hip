@@ -23,19 +23,19 @@ __global__ __launch_bounds__(256) void amax_partials_kernel(const uint4* __restr
   __shared__ uint32_t red[4];
   uint32_t m = 0;
   const uint32_t stride = gridDim.x * 256u;
-  for (uint32_t c0 = blockIdx.x * 256u + threadIdx.x; c0 < total_chunks; c0 += 4u * stride) {
-    uint4 v[4];
+  // Eight 16-byte loads in flight per lane; lanes past the end re-read the
+  // last chunk, which cannot change a max, so every load is unconditional.
+  for (uint32_t c0 = blockIdx.x * 256u + threadIdx.x; c0 < total_chunks; c0 += 8u * stride) {
+    uint4 v[8];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < 8; ++u) {
       uint32_t c = c0 + (uint32_t)u * stride;
-      v[u] = make_uint4(0, 0, 0, 0);
-      if (c < total_chunks) {
-        uint32_t r = fastdiv(c, fd);
-        v[u] = x[(size_t)r * ld_chunks + (c - r * chunks_per_row)];
-      }
+      c = c < total_chunks ? c : total_chunks - 1u;
+      const uint32_t r = fastdiv(c, fd);
+      v[u] = x[(size_t)r * ld_chunks + (c - r * chunks_per_row)];
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < 8; ++u) {
       uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -189,9 +189,32 @@ __global__ __launch_bounds__(256) void quantize_kernel(const uint8_t* __restrict
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   };
 
+  // Raw input words of one block.  The next block's words are fetched
+  // before the current block is encoded, so every wave keeps two blocks in
+  // flight; blocks past the end or in padding fetch a valid block (the last
+  // one, or the row's last real one) that is never encoded, so every fetch is
+  // unconditional.
+  constexpr int kWords = kBf16 ? 8 : 16;
+  auto fetch = [&](uint32_t b, uint32_t (&w)[kWords]) {
+    const uint32_t bb = b < total_blocks ? b : total_blocks - 1u;
+    const uint32_t r = fastdiv(bb, fd);
+    uint32_t kb = bb - r * out_kblocks;
+    kb = kb < kblocks ? kb : kblocks - 1u;
+    const uint4* q = reinterpret_cast<const uint4*>(x + (size_t)r * ld_bytes + (size_t)kb * (kBf16 ? 32u : 64u));
+#pragma unroll
+    for (int c = 0; c < kWords / 4; ++c) {
+      const uint4 v = q[c];
+      w[4 * c] = v.x;
+      w[4 * c + 1] = v.y;
+      w[4 * c + 2] = v.z;
+      w[4 * c + 3] = v.w;
+    }
+  };
+  const int32_t last = (int32_t)((chunks - 1u - wave_id) / waves);
+  auto block_of = [&](int32_t it) { return (wave_id + (uint32_t)it * waves) * 64u + lane; };
+
   uint32_t queued = 0;  // wave-uniform
-  for (int32_t it = (int32_t)((chunks - 1u - wave_id) / waves); it >= 0; --it) {
-    const uint32_t b = (wave_id + (uint32_t)it * waves) * 64u + lane;
+  auto encode = [&](uint32_t b, const uint32_t (&w)[kWords]) {
     bool settled = true;
     if (b < total_blocks) {
       const uint32_t r = fastdiv(b, fd);
@@ -200,7 +223,15 @@ __global__ __launch_bounds__(256) void quantize_kernel(const uint8_t* __restrict
         x16[(size_t)b * 2u + 1u] = make_uint4(0, 0, 0, 0);
       } else {
         float xv[16];
-        load(b, r, xv);
+#pragma unroll
+        for (int i = 0; i < kWords; ++i) {
+          if (kBf16) {
+            xv[2 * i] = __uint_as_float(w[i] << 16);
+            xv[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+          } else {
+            xv[i] = __uint_as_float(w[i]);
+          }
+        }
         uint32_t sb, lo, hi;
         settled = encode_block_fast(xv, block_absmax_bits<kBf16>(xv), fsc, sb, lo, hi);
         if (settled) store(b, sb, lo, hi);
@@ -217,6 +248,18 @@ __global__ __launch_bounds__(256) void quantize_kernel(const uint8_t* __restrict
         queued = 0;
       }
     }
+  };
+
+  // Two register sets alternate (no copies, which would wait for the fetch).
+  uint32_t wa[kWords], wb[kWords];
+  fetch(block_of(last), wa);
+  for (int32_t it = last;; it -= 2) {
+    fetch(block_of(it >= 1 ? it - 1 : 0), wb);
+    encode(block_of(it), wa);
+    if (it < 1) break;
+    fetch(block_of(it >= 2 ? it - 2 : 0), wa);
+    encode(block_of(it - 1), wb);
+    if (it < 2) break;
   }
   if (queued) flush(queued);
 }
@@ -390,7 +433,9 @@ int launch_amax(const void* x, bool bf16, int64_t rows, int64_t K, int64_t ld, u
   uint32_t cpr = (uint32_t)(K * esize / 16);
   uint32_t ldc = (uint32_t)(ld * esize / 16);
   uint32_t total = (uint32_t)(rows * (int64_t)cpr);
-  int grid = grid_for(total, 1024, kMaxPartials);
+  // 512 workgroups keep 16 MB in flight, enough for full bandwidth, and
+  // give the encode kernel few partials to reduce.
+  int grid = grid_for(total, 256 * 8, 512);
   FastDiv fd = make_fastdiv(cpr ? cpr : 1u);
   if (bf16)
     amax_partials_kernel<true><<<grid, 256, 0, s>>>((const uint4*)x, cpr, ldc, total, fd, partials);
@@ -424,7 +469,10 @@ static void launch_quantize(const void* x, bool bf16, int64_t rows, int64_t K, i
                                                                         scales, xo, gs);
     return;
   }
-  const int grid = grid_for(total, 256, 4096);
+  // Four workgroups per compute unit, all resident at once:
+  // each wave then walks several chunks and every workgroup reduces the
+  // partials once.
+  const int grid = grid_for(total, 256, 1024);
   if (bf16)
     quantize_kernel<true, kF16><<<grid, 256, 0, s>>>(xb, ld_bytes, kb, okb, total, fd, partials, npartials, codes,
                                                      scales, xo, gs);

@@ -18,9 +18,10 @@
 namespace nvfp4 {
 
 // ====================================================================== GEMM
-// Workgroup tile 256 (W rows) x 256 (X rows), 4 waves in a 2 x 2 grid, each
-// wave 128 x 128 = 4 x 4 MFMA 32x32x16 tiles (256 fp32 accumulators per lane,
-// held in the accumulation registers).  K advances 64 per step.
+// Workgroup tile 256 (W rows) x 256 (X rows), 8 waves in a 4 x 2 grid (two
+// per SIMD, so one can issue while the other waits), each wave 64 x 128 =
+// 2 x 4 MFMA 32x32x16 tiles (128 fp32 accumulators per lane, held in the
+// accumulation registers).  K advances 64 per step.
 //
 // Every operand byte reaches LDS by direct global->LDS transfers
 // (global_load_lds): the X tile (256 rows x 64 k fp16 = 32 KB), the W codes
@@ -39,13 +40,14 @@ namespace nvfp4 {
 struct GemmBuf {
   uint4 x[kGemmBM * 8];        // 32 KB
   uint4 wc[kGemmBN * 2];       // 8 KB
-  uint32_t ws[kGemmBN];        // 1 KB
+  uint32_t ws[8 * 64];         // 2 KB: wave w's 32 rows at [64w, 64w+32), repeated in [64w+32, 64w+64)
 };
 
-constexpr int kDmaPerStep = 11;  // per wave: 8 (X) + 2 (W codes) + 1 (W scales)
+constexpr int kGemmWaves = 8;
+constexpr int kDmaPerStep = 6;  // per wave: 4 (X) + 1 (W codes) + 1 (W scales)
 
 template <bool kYBf16>
-__global__ __launch_bounds__(256, 1) void gemm_kernel(const uint4* __restrict__ x16, uint32_t kp_chunks,
+__global__ __launch_bounds__(512, 1) void gemm_kernel(const uint4* __restrict__ x16, uint32_t kp_chunks,
                                                        const uint8_t* __restrict__ wc,
                                                        const uint8_t* __restrict__ ws, int N, int K, int M,
                                                        const float* __restrict__ gsx_p,
@@ -57,7 +59,7 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(const uint4* __restrict__ 
   __shared__ GemmBuf b0, b1, b2;
   __shared__ uint32_t scale_lut[128];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wave_n = wave >> 1, wave_m = wave & 1;
+  const int wave_n = wave >> 1, wave_m = wave & 1;  // W rows 64 wave_n.., X rows 128 wave_m..
   // Whole tiles first; the workgroups past full_tiles each take one K part
   // (steps [kb, ke)) of a remaining tile.
   int tile = blockIdx.x, part = -1, kb = 0, ke = nk;
@@ -78,45 +80,42 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(const uint4* __restrict__ 
   const uint8_t* xbase = reinterpret_cast<const uint8_t*>(x16 + (size_t)m0 * kp_chunks);  // + 128 B per step
   const uint8_t* wcbase = wc + (size_t)n0 * kh;                                          // + 32 B per step
   const uint8_t* wsbase = ws + (size_t)n0 * ks;                                          // + 4 B per step
-  uint32_t xoff[8];  // X: instruction j fills slots (wave*8+j)*64 + lane (row wave*64+8j+lane/8)
+  uint32_t xoff[4];  // X: instruction j fills slots (wave*4+j)*64 + lane (row (wave*4+j)*8 + lane/8)
 #pragma unroll
-  for (int j = 0; j < 8; ++j)
-    xoff[j] = ((uint32_t)(wave * 64 + 8 * j + (lane >> 3)) * kp_chunks +
+  for (int j = 0; j < 4; ++j)
+    xoff[j] = ((uint32_t)((wave * 4 + j) * 8 + (lane >> 3)) * kp_chunks +
                ((lane & 7) ^ ((lane >> 3) & 7) ^ (j & 1))) * 16u;
-  uint32_t wcoff[2];  // W codes: instruction j fills slots (wave*2+j)*64 + lane = row*2 + physical half
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    int row = (wave * 2 + j) * 32 + (lane >> 1);
-    row = n0 + row < N ? row : N - 1 - n0;   // rows past N repeat the last one (not stored)
-    wcoff[j] = (uint32_t)row * (uint32_t)kh + (uint32_t)(((lane & 1) ^ (((lane >> 3) ^ (lane >> 4)) & 1)) * 16);
-  }
-  uint32_t wsoff;  // W scales: one dword (4 blocks) per row
+  uint32_t wcoff;  // W codes: the instruction fills slots wave*64 + lane = row*2 + physical half
   {
-    int row = wave * 64 + lane;
+    int row = wave * 32 + (lane >> 1);
+    row = n0 + row < N ? row : N - 1 - n0;   // rows past N repeat the last one (not stored)
+    wcoff = (uint32_t)row * (uint32_t)kh + (uint32_t)(((lane & 1) ^ (((lane >> 3) ^ (lane >> 4)) & 1)) * 16);
+  }
+  uint32_t wsoff;  // W scales: one dword (4 blocks) per row; lanes 32..63 repeat lanes 0..31
+  {
+    int row = wave * 32 + (lane & 31);
     row = n0 + row < N ? row : N - 1 - n0;
     wsoff = (uint32_t)row * (uint32_t)ks;
   }
   // LDS byte addresses of this wave's transfer slots in each buffer
-  const uint32_t lx0 = lds_addr(&b0.x[wave * 512]), lx1 = lds_addr(&b1.x[wave * 512]),
-                 lx2 = lds_addr(&b2.x[wave * 512]);
-  const uint32_t lc0 = lds_addr(&b0.wc[wave * 128]), lc1 = lds_addr(&b1.wc[wave * 128]),
-                 lc2 = lds_addr(&b2.wc[wave * 128]);
+  const uint32_t lx0 = lds_addr(&b0.x[wave * 256]), lx1 = lds_addr(&b1.x[wave * 256]),
+                 lx2 = lds_addr(&b2.x[wave * 256]);
+  const uint32_t lc0 = lds_addr(&b0.wc[wave * 64]), lc1 = lds_addr(&b1.wc[wave * 64]),
+                 lc2 = lds_addr(&b2.wc[wave * 64]);
   const uint32_t ls0 = lds_addr(&b0.ws[wave * 64]), ls1 = lds_addr(&b1.ws[wave * 64]),
                  ls2 = lds_addr(&b2.ws[wave * 64]);
 
   auto issue = [&](int kt, uint32_t lx, uint32_t lc, uint32_t ls) {
     const uint8_t* xb = xbase + (size_t)kt * 128;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) lds_dma16(xb, xoff[j], lx + j * 1024);
-    const uint8_t* cb = wcbase + (size_t)kt * 32;
-#pragma unroll
-    for (int j = 0; j < 2; ++j) lds_dma16(cb, wcoff[j], lc + j * 1024);
+    for (int j = 0; j < 4; ++j) lds_dma16(xb, xoff[j], lx + j * 1024);
+    lds_dma16(wcbase + (size_t)kt * 32, wcoff, lc);
     lds_dma4(wsbase + (size_t)kt * 4, wsoff, ls);
   };
 
-  floatx16 acc[4][4];
+  floatx16 acc[2][4];
 #pragma unroll
-  for (int t = 0; t < 4; ++t)
+  for (int t = 0; t < 2; ++t)
 #pragma unroll
     for (int u = 0; u < 4; ++u)
 #pragma unroll
@@ -135,32 +134,32 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(const uint4* __restrict__ 
     }
   };
   // W codes (one dword per sub-step) and the two block scales of this lane.
-  auto read_w = [&](const GemmBuf& cur, uint4 (&wv)[4], uint32_t (&sw)[4]) {
+  auto read_w = [&](const GemmBuf& cur, uint4 (&wv)[2], uint32_t (&sw)[2]) {
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int row = wave_n * 128 + t * 32 + l32;
+    for (int t = 0; t < 2; ++t) {
+      const int row = wave_n * 64 + t * 32 + l32;
       wv[t] = cur.wc[row * 2 + (h ^ (((row >> 2) ^ (row >> 3)) & 1))];
-      sw[t] = cur.ws[row] >> (16 * h);
+      sw[t] = cur.ws[(wave_n * 2 + t) * 64 + l32] >> (16 * h);
     }
   };
-  auto split_w = [&](const uint32_t (&sw)[4], uint32_t (&sp)[4][2]) {
+  auto split_w = [&](const uint32_t (&sw)[2], uint32_t (&sp)[2][2]) {
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
+    for (int t = 0; t < 2; ++t) {
       sp[t][0] = scale_lut[sw[t] & 0x7Fu];
       sp[t][1] = scale_lut[(sw[t] >> 8) & 0x7Fu];
     }
   };
-  auto expand_w = [&](const uint4 (&wv)[4], const uint32_t (&sp)[4][2], int j, f16x8 (&aw)[4]) {
+  auto expand_w = [&](const uint4 (&wv)[2], const uint32_t (&sp)[2][2], int j, f16x8 (&aw)[2]) {
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
+    for (int t = 0; t < 2; ++t) {
       uint32_t e[4];
       expand8(dword_of(wv[t], j), __builtin_bit_cast(half2_t, sp[t][j >> 1]), e);
       aw[t] = u4_as_f16x8(make_uint4(e[0], e[1], e[2], e[3]));
     }
   };
-  auto mfma16 = [&](const f16x8 (&aw)[4], const f16x8 (&bx)[4]) {
+  auto mfma8 = [&](const f16x8 (&aw)[2], const f16x8 (&bx)[4]) {
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int u = 0; u < 4; ++u)
         acc[t][u] = __builtin_amdgcn_mfma_f32_32x32x16_f16(aw[t], bx[u], acc[t][u], 0, 0, 0);
@@ -169,9 +168,9 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(const uint4* __restrict__ 
   // Register-resident operands carried across sub-steps and steps: the W
   // codes and scale splits of the current step and the operands of its next
   // sub-step.
-  uint4 wv[4];
-  uint32_t sp[4][2];
-  f16x8 bx[4], aw[4];
+  uint4 wv[2];
+  uint32_t sp[2][2];
+  f16x8 bx[4], aw[2];
 
   // One main-loop step.  Sub-steps 0..2 of step kt run from `cur`, each
   // overlapping the LDS reads and expansion of the following sub-step.  Then
@@ -187,45 +186,43 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(const uint4* __restrict__ 
     issue(kt + 2 < last ? kt + 2 : last, lx, lc, ls);
 #pragma unroll
     for (int j = 0; j < 3; ++j) {
-      f16x8 bxn[4], awn[4];
+      f16x8 bxn[4], awn[2];
       read_x(cur, j + 1, bxn);
-      mfma16(aw, bx);
+      mfma8(aw, bx);
       expand_w(wv, sp, j + 1, awn);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        bx[q] = bxn[q];
-        aw[q] = awn[q];
-      }
+      for (int q = 0; q < 4; ++q) bx[q] = bxn[q];
+#pragma unroll
+      for (int q = 0; q < 2; ++q) aw[q] = awn[q];
     }
     // All LDS reads of `cur` have completed and this wave's transfers of step
-    // kt+1 have landed (only step kt+2's 11 may be in flight); after the
+    // kt+1 have landed (only step kt+2's 6 may be in flight); after the
     // barrier every wave's have.  The barrier is a bare s_barrier: a
     // workgroup fence would also wait for the transfers still in flight.
-    asm volatile("s_waitcnt vmcnt(11) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    f16x8 bx3[4], aw3[4];
+    asm volatile("s_waitcnt vmcnt(6) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    f16x8 bx3[4], aw3[2];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      bx3[q] = bx[q];
-      aw3[q] = aw[q];
-    }
+    for (int q = 0; q < 4; ++q) bx3[q] = bx[q];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) aw3[q] = aw[q];
     // Step kt+1's operands are prepared even after the last step (the
     // buffer then holds a repeated, finite copy), which keeps this branch-free.
-    uint32_t sw[4];
+    uint32_t sw[2];
     read_w(nxt, wv, sw);
     read_x(nxt, 0, bx);
-    mfma16(aw3, bx3);
+    mfma8(aw3, bx3);
     split_w(sw, sp);
     expand_w(wv, sp, 0, aw);
   };
-  static_assert(kDmaPerStep == 11, "the wait count above must match the transfers per step");
+  static_assert(kDmaPerStep == 6, "the wait count above must match the transfers per step");
 
   if (ke > kb) {
     issue(kb, lx0, lc0, ls0);
     issue(kb + 1 < ke ? kb + 1 : kb, lx1, lc1, ls1);
     // the scale table above is written with ordinary LDS stores
-    asm volatile("s_waitcnt vmcnt(11) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    asm volatile("s_waitcnt vmcnt(6) lgkmcnt(0)\n\ts_barrier" ::: "memory");
     {
-      uint32_t sw[4];
+      uint32_t sw[2];
       read_w(b0, wv, sw);
       read_x(b0, 0, bx);
       split_w(sw, sp);
@@ -247,10 +244,10 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(const uint4* __restrict__ 
     for (int u = 0; u < 4; ++u) {
       const int ml = wave_m * 128 + u * 32 + l32;
 #pragma unroll
-      for (int t = 0; t < 4; ++t)
+      for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const int nl = wave_n * 128 + t * 32 + 8 * q + 4 * h;
+          const int nl = wave_n * 64 + t * 32 + 8 * q + 4 * h;
           *reinterpret_cast<float4*>(pp + ml * kGemmBN + nl) =
               make_float4(acc[t][u][4 * q], acc[t][u][4 * q + 1], acc[t][u][4 * q + 2], acc[t][u][4 * q + 3]);
         }
@@ -264,10 +261,10 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(const uint4* __restrict__ 
     if (m >= M) continue;
     uint8_t* yrow = y + (size_t)m * ld_y_bytes;
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
+    for (int t = 0; t < 2; ++t) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int n = n0 + wave_n * 128 + t * 32 + 8 * q + 4 * h;
+        const int n = n0 + wave_n * 64 + t * 32 + 8 * q + 4 * h;
         store4<kYBf16>(yrow, n, N, acc[t][u][4 * q] * scale, acc[t][u][4 * q + 1] * scale,
                        acc[t][u][4 * q + 2] * scale, acc[t][u][4 * q + 3] * scale);
       }
@@ -313,10 +310,10 @@ void launch_gemm(const void* x16, int64_t M, int64_t Kp, const uint8_t* wc, cons
   const uint32_t kpc = (uint32_t)(Kp / 8);
   dim3 grid(p.full_tiles + rem * p.split);
   if (y_bf16)
-    gemm_kernel<true><<<grid, 256, 0, s>>>((const uint4*)x16, kpc, wc, ws, (int)N, (int)K, (int)M, gsx, gsw,
+    gemm_kernel<true><<<grid, kGemmWaves * 64, 0, s>>>((const uint4*)x16, kpc, wc, ws, (int)N, (int)K, (int)M, gsx, gsw,
                                            (uint8_t*)y, ldb, p.tiles_n, p.nk, p.full_tiles, p.split, partials);
   else
-    gemm_kernel<false><<<grid, 256, 0, s>>>((const uint4*)x16, kpc, wc, ws, (int)N, (int)K, (int)M, gsx, gsw,
+    gemm_kernel<false><<<grid, kGemmWaves * 64, 0, s>>>((const uint4*)x16, kpc, wc, ws, (int)N, (int)K, (int)M, gsx, gsw,
                                             (uint8_t*)y, ldb, p.tiles_n, p.nk, p.full_tiles, p.split, partials);
   if (p.split > 1) {
     dim3 rgrid(kGemmBM * kGemmBN / 4 / 256, rem);

@@ -161,7 +161,7 @@ def main():
     flops = 2.0 * M * N * K
     value = flops / (step_ms * 1e-3) / 1e12
     gemm_tflops = flops / (mean(run_ms) * 1e-3) / 1e12
-    sha_gemm = source_sha("gemm.hip", "encode.h", "common.h")
+    sha_gemm = source_sha("gemm.hip", "encode.h", "common.h", "mfma_util.h")
     traffic = traffic_for("gemm_prefill", sha_gemm)
     out = {
         "metric": METRIC,
@@ -242,10 +242,10 @@ def secondary(torch, np, nv, workloads, to_gpu, dev, args):
                                   "gemv": round(mean(run_ms), 5)},
                     "config": {"workload": "decode: X[%dx5120] bf16 x fused gate/up W[34816x5120] NVFP4 "
                                            "(4 rotated copies) -> Y bf16" % M},
-                    "roofline": {"bound": "hbm", "kernel": "gemv_kernel", "achieved": round(kgbs, 1),
+                    "roofline": {"bound": "hbm", "kernel": "nvfp4_gemm_run: gemv kernel", "achieved": round(kgbs, 1),
                                  "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(kgbs / PEAK_HBM_GBS, 4),
-                                 "traffic": traffic_for("gemv_m%d" % M, source_sha("gemm.hip", "encode.h",
-                                                                                   "common.h")),
+                                 "traffic": traffic_for("gemv_m%d" % M, source_sha("gemv.hip", "encode.h",
+                                                                                   "common.h", "mfma_util.h")),
                                  "algorithmic": "W codes+scales %d B + X + Y = %d B per launch" % (wbytes,
                                                                                                   nbytes)}})
         log("decode M=%d: %.1f GB/s step, %.1f GB/s kernel" % (M, gbs, kgbs))

@@ -42,6 +42,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--headline-only", action="store_true",
                     help="skip the secondary workloads (profiling runs)")
+    ap.add_argument("--no-box-peaks", action="store_true",
+                    help="skip the box-measured reference rates (device copy, torch fp16 GEMM)")
     ap.add_argument("--copy-ref", action="store_true",
                     help="first run one plain 1 GiB device copy, the reference kernel for HBM counters")
     return ap.parse_args()
@@ -192,6 +194,10 @@ def main():
     also = []
     if not args.headline_only:
         also += secondary(torch, np, nv, workloads, to_gpu, dev, args)
+
+    # ------------------------------------------------------------ box-measured peaks
+    if not args.headline_only and not args.no_box_peaks:
+        out["box_peaks"] = box_peaks(torch, dev, M, N, K)
 
     # ------------------------------------------------------------ CPU oracle
     if not args.no_cpu_baseline:
@@ -349,6 +355,44 @@ def secondary(torch, np, nv, workloads, to_gpu, dev, args):
                 "ms_per_step": round(mean(w_ms), 4),
                 "config": {"workload": "offline weight quantize W[17408x5120] fp32 N(0,0.02)"}})
     return res
+
+
+def box_peaks(torch, dev, M, N, K):
+    """What this machine sustains on plain work, measured beside the
+    nominal peaks: a 1 GiB device-to-device copy (HBM read + write) and
+    torch's own fp16 GEMM (hipBLASLt) at the prefill shape with fp32
+    accumulation, the same MFMA arithmetic the W4A4 GEMM runs after its exact
+    expansion.  Context for the roofline fractions, not part of any step."""
+    log("box peaks: 1 GiB copy, fp16 GEMM %dx%dx%d" % (M, N, K))
+    a = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
+    b = torch.empty_like(a)
+    ms = []
+    for i in range(8):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        b.copy_(a)
+        e1.record()
+        torch.cuda.synchronize()
+        if i >= 3:
+            ms.append(e0.elapsed_time(e1))
+    copy_gbs = 2 * (1 << 30) / (min(ms) * 1e-3) / 1e9
+    del a, b
+    x = torch.randn(M, K, device=dev, dtype=torch.float16)
+    w = torch.randn(N, K, device=dev, dtype=torch.float16)
+    ms = []
+    for i in range(8):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        torch.mm(x, w.t())
+        e1.record()
+        torch.cuda.synchronize()
+        if i >= 3:
+            ms.append(e0.elapsed_time(e1))
+    gemm_tf = 2.0 * M * N * K / (min(ms) * 1e-3) / 1e12
+    del x, w
+    return {"hbm_copy_GBs": round(copy_gbs, 1),
+            "fp16_gemm_TFLOPs": round(gemm_tf, 1),
+            "note": "best of 5 timed runs; copy counts read + write bytes; torch fp16 GEMM at the prefill shape"}
 
 
 def cpu_baseline(np, p):

@@ -229,6 +229,124 @@ __global__ __launch_bounds__(64) void gemv_stream_kernel(const uint8_t* __restri
                    acc[2] * scale, acc[3] * scale);
 }
 
+// ------------------------------------------------------------ 4 < M <= 16
+// With more activation rows the activation operand outweighs the weights
+// (16 rows of fp16 against 16 rows of 4-bit codes), so the activations are
+// shared: a workgroup of 8 waves owns 128 rows of W (16 per wave) and all
+// waves read one copy of each activation chunk from LDS.  K advances 256 per
+// step through a ring of three stages, one barrier per step, transfers of
+// step kt+2 in flight while step kt is computed.  Every wave issues the same
+// four transfers per step: its 16 rows of codes (two transfers of 8 rows x
+// 128 B), its 16 rows of scale bytes (16 lanes x 16 B) and two activation
+// rows (rows past M repeat row M-1; their lanes never read them).  The
+// per-lane computation is the one of the kernel above.
+constexpr int kGwWaves = 8;
+struct GwStage {
+  uint4 codes[128 * 8];  // 16 KB: [row][8 slots]
+  uint4 scales[128];     //  2 KB: [row] 16 scale bytes
+  uint4 x[16 * 32];      //  8 KB: [m][32 slots]
+};
+
+template <bool kYBf16>
+__global__ __launch_bounds__(512) void gemv_shared_kernel(const uint8_t* __restrict__ x16, uint32_t ld_x16_bytes,
+                                                          int M, const uint8_t* __restrict__ wc,
+                                                          const uint8_t* __restrict__ ws, int N, int K,
+                                                          const float* __restrict__ gsx_p,
+                                                          const float* __restrict__ gsw_p,
+                                                          uint8_t* __restrict__ y, size_t ld_y_bytes) {
+  __shared__ GwStage st0, st1, st2;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, l16 = lane & 15, g = lane >> 4;
+  const int tile = blockIdx.x * kGwWaves + wave;  // 16-row tile of this wave
+  const uint32_t kh = (uint32_t)K / 2, ks = (uint32_t)K / 16;
+  const int nk = K >> 8;
+
+  // transfer offsets (fixed; + 128 B codes, 16 B scales, 512 B activations per step)
+  uint32_t coff[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int r = 8 * h + (lane >> 3);
+    int n = tile * 16 + r;
+    n = n < N ? n : N - 1;
+    coff[h] = (uint32_t)n * kh + 16u * (uint32_t)((lane & 7) ^ (r & 7));
+  }
+  uint32_t soff;
+  {
+    int n = tile * 16 + l16;
+    n = n < N ? n : N - 1;
+    soff = (uint32_t)n * ks;
+  }
+  uint32_t xoff;
+  {
+    int m = 2 * wave + (lane >> 5);
+    m = m < M ? m : M - 1;
+    const uint32_t p = (uint32_t)(lane & 31), piece = (p & ~7u) | ((p & 7u) ^ (p >> 3));
+    xoff = (uint32_t)m * ld_x16_bytes + 16u * piece;
+  }
+  const uint32_t lc[3] = {lds_addr(&st0.codes[wave * 128]), lds_addr(&st1.codes[wave * 128]),
+                          lds_addr(&st2.codes[wave * 128])};
+  const uint32_t lsc[3] = {lds_addr(&st0.scales[wave * 16]), lds_addr(&st1.scales[wave * 16]),
+                           lds_addr(&st2.scales[wave * 16])};
+  const uint32_t lxx[3] = {lds_addr(&st0.x[wave * 64]), lds_addr(&st1.x[wave * 64]),
+                           lds_addr(&st2.x[wave * 64])};
+  auto issue = [&](int kt, int b) {
+    kt = kt < nk ? kt : nk - 1;  // past the end: repeat the last step into a stage no longer read
+    lds_dma16(wc, coff[0] + (uint32_t)kt * 128u, lc[b]);
+    lds_dma16(wc, coff[1] + (uint32_t)kt * 128u, lc[b] + 1024u);
+    if (lane < 16) lds_dma16(ws, soff + (uint32_t)kt * 16u, lsc[b]);
+    lds_dma16(x16, xoff + (uint32_t)kt * 512u, lxx[b]);
+  };
+
+  const bool mvalid = l16 < M;
+  const uint32_t sw = (uint32_t)(l16 & 7), xg = (uint32_t)g;
+  const int crow = wave * 16 + l16;
+  const uint32_t cpos0 = (uint32_t)crow * 8u + ((2u * g) ^ sw), cpos1 = (uint32_t)crow * 8u + ((2u * g + 1u) ^ sw);
+  uint4 xv[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) xv[t] = make_uint4(0, 0, 0, 0);
+  floatx4 acc = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+
+  auto compute = [&](const GwStage& S) {
+    const uint4 w0 = S.codes[cpos0], w1 = S.codes[cpos1];
+    const uint32_t sd = reinterpret_cast<const uint32_t*>(&S.scales[crow])[g];
+    if (mvalid) {
+      const uint4* xr = &S.x[l16 * 32 + 8 * g];
+#pragma unroll
+      for (int t = 0; t < 8; ++t) xv[t] = xr[(uint32_t)t ^ xg];
+    }
+    const half2_t s0 = scale_f16x2(sd), s1 = scale_f16x2(sd >> 8), s2 = scale_f16x2(sd >> 16),
+                  s3 = scale_f16x2(sd >> 24);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const half2_t sp = t < 2 ? s0 : (t < 4 ? s1 : (t < 6 ? s2 : s3));
+      uint32_t e[4];
+      expand8(dword_of(t < 4 ? w0 : w1, t & 3), sp, e);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(u4_as_f16x8(make_uint4(e[0], e[1], e[2], e[3])),
+                                                   u4_as_f16x8(xv[t]), acc, 0, 0, 0);
+    }
+  };
+  // Step kt: wait for this wave's transfers of step kt (those of kt+1 may
+  // still fly), barrier (everyone's have landed, and everyone is done with
+  // the stage of step kt-1), issue step kt+2 into that stage, compute.
+  auto step = [&](int kt, const GwStage& S, int nb) {
+    asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    issue(kt + 2, nb);
+    compute(S);
+  };
+
+  issue(0, 0);
+  issue(1, 1);
+  for (int kt = 0; kt < nk; kt += 3) {
+    step(kt, st0, 2);
+    if (kt + 1 < nk) step(kt + 1, st1, 0);
+    if (kt + 2 < nk) step(kt + 2, st2, 1);
+  }
+  wait_vmcnt<0>();
+  const float scale = (*gsx_p) * (*gsw_p);
+  if (mvalid)
+    store4<kYBf16>(y + (size_t)l16 * ld_y_bytes, tile * 16 + 4 * g, N, acc[0] * scale, acc[1] * scale,
+                   acc[2] * scale, acc[3] * scale);
+}
+
 // LDS of one streaming workgroup, and the depth that keeps every tile in one
 // round of the machine; 0 when the streaming kernel does not apply.
 struct GvPlan {
@@ -306,6 +424,18 @@ void launch_gemv(const void* x16, int64_t M, int64_t Kp, const uint8_t* wc, cons
     } else {
       if (gp.depth == 4) go(I4(), I2()); else if (gp.depth == 2) go(I2(), I2()); else go(I1(), I2());
     }
+    return;
+  }
+  if (M > 4 && M <= 16 && K >= 256 && K % 256 == 0 && (uint64_t)N * (uint64_t)K / 2 < (1ull << 32)) {
+    const int grid = (int)((N + 16 * kGwWaves - 1) / (16 * kGwWaves));
+    const size_t ldb = (size_t)ld_y * (y_bf16 ? 2u : 4u);
+    const uint32_t ldx = (uint32_t)(Kp * 2);
+    if (y_bf16)
+      gemv_shared_kernel<true><<<grid, kGwWaves * 64, 0, s>>>((const uint8_t*)x16, ldx, (int)M, wc, ws, (int)N,
+                                                               (int)K, gsx, gsw, (uint8_t*)y, ldb);
+    else
+      gemv_shared_kernel<false><<<grid, kGwWaves * 64, 0, s>>>((const uint8_t*)x16, ldx, (int)M, wc, ws, (int)N,
+                                                                (int)K, gsx, gsw, (uint8_t*)y, ldb);
     return;
   }
   // One 16-row tile per workgroup keeps the grid fine-grained when the

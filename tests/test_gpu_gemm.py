@@ -91,6 +91,21 @@ def test_gemm_ragged(nv, orc, M, N, K, out):
     check_gemm(_run(nv, p, od), _full_ref(orc, p), out == "bf16", "gemm %dx%dx%d" % (M, N, K))
 
 
+# Small M (decode) shapes for every GEMV form: one-wave streaming tiles
+# (M <= 4, K % 256 == 0, with 1, 2 and 4 activation rows per transfer), the
+# workgroup-shared kernel (4 < M <= 16, K % 256 == 0, ragged last workgroup),
+# and the general kernel for K that is not a multiple of 256.
+@pytest.mark.parametrize("M,N,K", [(2, 520, 5120), (3, 520, 5120), (4, 40, 256), (5, 520, 5120),
+                                   (8, 40, 256), (13, 300, 1024), (16, 520, 512), (3, 200, 320),
+                                   (9, 100, 1088), (1, 7, 64), (16, 129, 768)])
+@pytest.mark.parametrize("out", ["bf16", "f32"])
+def test_gemv_shapes(nv, orc, M, N, K, out):
+    p = workloads.prefill(M=M, K=K, N=N)
+    print("case: gemv M=%d N=%d K=%d %s" % (M, N, K, out), flush=True)
+    od = torch.bfloat16 if out == "bf16" else torch.float32
+    check_gemm(_run(nv, p, od), _full_ref(orc, p), out == "bf16", "gemv %dx%dx%d" % (M, N, K))
+
+
 def test_gemm_fp32_activations(nv, orc):
     p = workloads.tiny(M=100, K=256, N=200)
     check_gemm(_run(nv, p, torch.float32), _full_ref(orc, p), False, "fp32 X, M=100")

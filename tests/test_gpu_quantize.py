@@ -89,6 +89,10 @@ def _cases():
     z = np.zeros((8, 64), np.float32)
     z[2, 3] = -0.0
     yield "zeros_with_negative_zero", z
+    # around the size where one launch (absmax inside) gives way to two
+    yield "one_launch_8192_blocks_bf16", workloads.to_bf16_bits(workloads.student_t(7, 6, 512, 256, 3.0))
+    yield "two_launches_8193_blocks_bf16", workloads.to_bf16_bits(workloads.student_t(7, 7, 8193, 16, 3.0))
+    yield "one_launch_8_workgroups_f32", workloads.gaussian(7, 8, 16, 8192, 1.0)
 
 
 @pytest.mark.parametrize("name,x", list(_cases()), ids=[n for n, _ in _cases()])

@@ -153,8 +153,43 @@ __device__ __forceinline__ uint32_t cvt_fp4x8(const float (&x)[16], int base, fl
   return r;
 }
 
+// Exact code of one element whose bracket straddles a decision point.  The
+// bracket ends differ by one step (decision points are at least 0.5 apart in
+// quotient space, the bracket is 2^-19 wide), so the magnitude is k or k + 1
+// with k the lower end's, and the one bound between them decides it exactly
+// (the same bound make_bounds gives).  ca: the lower end's code (sign kept).
+__device__ __forceinline__ uint32_t resolve_code(float x, float es, uint32_t ca) {
+  const uint32_t k = ca & 7u;
+  const double T = k == 0 ? e2m1_decision(0)
+                 : k == 1 ? e2m1_decision(1)
+                 : k == 2 ? e2m1_decision(2)
+                 : k == 3 ? e2m1_decision(3)
+                 : k == 4 ? e2m1_decision(4)
+                 : k == 5 ? e2m1_decision(5) : e2m1_decision(6);
+  const float b = bound_from(T * (double)es, (k & 1u) == 0u);
+  const uint32_t a = __float_as_uint(x) & 0x7FFFFFFFu;  // |x| and b are non-negative: integer order is float order
+  return (ca & 8u) | (k + (a > __float_as_uint(b) ? 1u : 0u));
+}
+
+// Replace every code nibble of `a` that differs from `b` by its exact value.
+__device__ __forceinline__ uint32_t resolve_codes8(const float (&x)[16], int base, float es, uint32_t a,
+                                                   uint32_t b) {
+  const uint32_t d = a ^ b;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    if ((d >> (4 * j)) & 15u) {
+      const uint32_t c = resolve_code(x[base + j], es, (a >> (4 * j)) & 15u);
+      a = (a & ~(15u << (4 * j))) | (c << (4 * j));
+    }
+  }
+  return a;
+}
+
 // x: the 16 values as fp32 (bf16 widened exactly); bm: fp32 bits of the
-// largest |x|.  On success writes the scale byte and the codes.
+// largest |x|.  On success writes the scale byte and the codes; elements on
+// or next to a decision point are settled one by one.  Returns false only
+// when the scale itself is not settled (see above); the block then takes the
+// exact path.
 __device__ __forceinline__ bool encode_block_fast(const float (&x)[16], uint32_t bm, const FastScale& f,
                                                   uint32_t& sb, uint32_t& code_lo, uint32_t& code_hi) {
   const float bmf = __uint_as_float(bm);
@@ -164,12 +199,19 @@ __device__ __forceinline__ bool encode_block_fast(const float (&x)[16], uint32_t
   const float y = (es == 0.0f) ? 0.0f : __builtin_amdgcn_rcpf(es);
   const float ylo = y * 0.99999904632568359375f;
   const float yhi = y * 1.00000095367431640625f;
-  const uint32_t lo_a = cvt_fp4x8(x, 0, ylo), lo_b = cvt_fp4x8(x, 0, yhi);
-  const uint32_t hi_a = cvt_fp4x8(x, 8, ylo), hi_b = cvt_fp4x8(x, 8, yhi);
+  uint32_t lo_a = cvt_fp4x8(x, 0, ylo);
+  const uint32_t lo_b = cvt_fp4x8(x, 0, yhi);
+  uint32_t hi_a = cvt_fp4x8(x, 8, ylo);
+  const uint32_t hi_b = cvt_fp4x8(x, 8, yhi);
+  const bool es_ok = (es == 0.0f) || (es >= 0x1p-126f && y < 0x1p+126f);
+  if (!(f.ok && es_ok && sb == sb_hi)) return false;
+  if (__builtin_expect(((lo_a ^ lo_b) | (hi_a ^ hi_b)) != 0u, 0)) {
+    lo_a = resolve_codes8(x, 0, es, lo_a, lo_b);
+    hi_a = resolve_codes8(x, 8, es, hi_a, hi_b);
+  }
   code_lo = lo_a;
   code_hi = hi_a;
-  const bool es_ok = (es == 0.0f) || (es >= 0x1p-126f && y < 0x1p+126f);
-  return f.ok && es_ok && sb == sb_hi && lo_a == lo_b && hi_a == hi_b;
+  return true;
 }
 
 // Exact encoder from the fp32 values (for blocks the fast path reports).

@@ -347,6 +347,153 @@ __global__ __launch_bounds__(512) void gemv_shared_kernel(const uint8_t* __restr
                    acc[2] * scale, acc[3] * scale);
 }
 
+// ---------------------------------------------------------- K split (M <= 16)
+// A workgroup of K/512 waves covers all of K for a run of 16-row tiles: wave
+// w owns k [512w, 512w + 512) and keeps the activations of that slice in
+// registers for the whole kernel (16 rows x 512 k of fp16: 64 registers a
+// lane), so the activations are read once per workgroup.  The weights of
+// the wave's slice stream through a ring of three LDS slots by direct
+// global->LDS transfers with explicit waits (as in the streaming kernel):
+// per tile, the codes (16 rows x 256 B, four transfers of 4 rows x 256 B,
+// code piece p of row r in slot p ^ (r & 7) of its row) and the scales (16
+// rows x 32 B, one 32-lane gather).  Lane (r, g) takes k 128g .. 128g+127 of
+// the slice: 64 code bytes and 8 scale bytes; MFMA step s (16x16x32) uses
+// dword s of the codes, and the activation operand holds the same k.  Per
+// tile the slices' partial sums meet in LDS; wave (tile index mod waves)
+// adds them in wave order and keeps the result in registers until the end,
+// so nothing but the transfers touches memory inside the loop and the result
+// does not depend on scheduling.
+constexpr int kKsMaxWaves = 10;     // K <= 5120
+constexpr int kKsMaxResults = 4;    // tiles a wave reduces (bounded by the grid)
+constexpr uint32_t kKsSlot = 4096 + 512;  // codes + scales of one wave and tile
+
+template <bool kYBf16>
+__global__ __launch_bounds__(640) void gemv_ksplit_kernel(const uint8_t* __restrict__ x16, uint32_t ld_x16_bytes,
+                                                          int M, const uint8_t* __restrict__ wc,
+                                                          const uint8_t* __restrict__ ws, int N, int K,
+                                                          int tiles, const float* __restrict__ gsx_p,
+                                                          const float* __restrict__ gsw_p,
+                                                          uint8_t* __restrict__ y, size_t ld_y_bytes) {
+  __shared__ __attribute__((aligned(16))) uint8_t ring[3][kKsMaxWaves][kKsSlot];
+  __shared__ floatx4 part[2][kKsMaxWaves][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, l16 = lane & 15, g = lane >> 4;
+  const int waves = blockDim.x >> 6;
+  const uint32_t ks0 = (uint32_t)wave * 512u;                 // slice start
+  const uint32_t k0 = ks0 + 128u * (uint32_t)g;               // this lane's first k
+  const uint32_t kh = (uint32_t)K / 2, ks = (uint32_t)K / 16;
+  const bool mvalid = l16 < M;
+
+  // activations of the slice, loaded unconditionally (rows m >= M read row 0
+  // and are zeroed), all before the first transfer
+  uint4 xv[16];
+  {
+    const uint4* xr = reinterpret_cast<const uint4*>(x16 + (size_t)(mvalid ? l16 : 0) * ld_x16_bytes + k0 * 2u);
+#pragma unroll
+    for (int q = 0; q < 16; ++q) xv[q] = xr[q];
+#pragma unroll
+    for (int q = 0; q < 16; ++q) xv[q] = mvalid ? xv[q] : make_uint4(0, 0, 0, 0);
+  }
+
+  // transfer offsets within a tile (+ 16 rows of W per tile)
+  uint32_t coff[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint32_t r = 4u * q + (uint32_t)(lane >> 4), p = (uint32_t)(lane & 15);
+    coff[q] = r * kh + (ks0 >> 1) + 16u * (p ^ (r & 7u));
+  }
+  const uint32_t soff = (uint32_t)(lane >> 1) * ks + (ks0 >> 4) + 16u * (uint32_t)(lane & 1);
+  const uint32_t lr0 = lds_addr(&ring[0][wave][0]);
+  constexpr uint32_t kSlotStride = kKsMaxWaves * kKsSlot;  // between ring slots
+  const int first = blockIdx.x, step = gridDim.x;
+  auto issue = [&](int t, int b) {
+    t = t < tiles ? t : tiles - 1;  // past the end: repeat the last tile into a slot not read again
+    const uint32_t rows = (uint32_t)t * 16u;
+    const uint32_t dst = lr0 + (uint32_t)b * kSlotStride;
+    const int last = N - 1;
+    // rows past N repeat row N-1 (their sums are never stored)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t r = 4u * q + (uint32_t)(lane >> 4);
+      const uint32_t n = rows + r < (uint32_t)N ? rows + r : (uint32_t)last;
+      lds_dma16(wc, coff[q] + (n - r) * kh, dst + 1024u * q);
+    }
+    if (lane < 32) {
+      const uint32_t r = (uint32_t)(lane >> 1);
+      const uint32_t n = rows + r < (uint32_t)N ? rows + r : (uint32_t)last;
+      lds_dma16(ws, soff + (n - r) * ks, dst + 4096u);
+    }
+  };
+
+  const float scale = (*gsx_p) * (*gsw_p);
+  const uint32_t sw = (uint32_t)(l16 & 7);
+  floatx4 res[kKsMaxResults];
+  int res_tile[kKsMaxResults];
+#pragma unroll
+  for (int r = 0; r < kKsMaxResults; ++r) res_tile[r] = -1;
+  int nres = 0;
+
+  auto compute = [&](int t, int b, int pb, int local) {
+    const uint8_t* slot = &ring[b][wave][0];
+    uint4 w[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      w[q] = *reinterpret_cast<const uint4*>(slot + l16 * 256 + 16 * (((uint32_t)(4 * g + q)) ^ sw));
+    const uint2 sc = *reinterpret_cast<const uint2*>(slot + 4096 + l16 * 32 + 8 * g);
+    floatx4 acc = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int s = 0; s < 16; ++s) {
+      const uint32_t sb = (s < 8 ? sc.x : sc.y) >> (8 * ((s >> 1) & 3));
+      uint32_t e[4];
+      expand8(dword_of(w[s >> 2], s & 3), scale_f16x2(sb), e);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(u4_as_f16x8(make_uint4(e[0], e[1], e[2], e[3])),
+                                                   u4_as_f16x8(xv[s]), acc, 0, 0, 0);
+    }
+    part[pb][wave][lane] = acc;
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if (wave == local % waves) {
+      floatx4 sum = part[pb][0][lane];
+      for (int v = 1; v < waves; ++v) sum = sum + part[pb][v][lane];
+#pragma unroll
+      for (int r = 0; r < kKsMaxResults; ++r)
+        if (r == nres) {
+          res[r] = sum;
+          res_tile[r] = t;
+        }
+      ++nres;
+    }
+  };
+
+  // ring: slot b of tile i is i % 3; tile i+2 goes out once every wave is
+  // past tile i-1 (the barrier in tile i's step)
+  issue(first, 0);
+  issue(first + step, 1);
+  int local = 0;
+  for (int t = first; t < tiles; t += 3 * step) {
+    wait_vmcnt<5>();
+    issue(t + 2 * step, 2);
+    compute(t, 0, local & 1, local);
+    ++local;
+    if (t + step >= tiles) break;
+    wait_vmcnt<5>();
+    issue(t + 3 * step, 0);
+    compute(t + step, 1, local & 1, local);
+    ++local;
+    if (t + 2 * step >= tiles) break;
+    wait_vmcnt<5>();
+    issue(t + 4 * step, 1);
+    compute(t + 2 * step, 2, local & 1, local);
+    ++local;
+  }
+  wait_vmcnt<0>();
+  if (mvalid) {
+#pragma unroll
+    for (int r = 0; r < kKsMaxResults; ++r)
+      if (res_tile[r] >= 0)
+        store4<kYBf16>(y + (size_t)l16 * ld_y_bytes, res_tile[r] * 16 + 4 * g, N, res[r][0] * scale,
+                       res[r][1] * scale, res[r][2] * scale, res[r][3] * scale);
+  }
+}
+
 // LDS of one streaming workgroup, and the depth that keeps every tile in one
 // round of the machine; 0 when the streaming kernel does not apply.
 struct GvPlan {
@@ -402,6 +549,35 @@ static void gemv_nt(const void* x16, int64_t M, int64_t Kp, const uint8_t* wc, c
 
 void launch_gemv(const void* x16, int64_t M, int64_t Kp, const uint8_t* wc, const uint8_t* ws, int64_t N, int64_t K,
                  const float* gsx, const float* gsw, void* y, bool y_bf16, int64_t ld_y, hipStream_t s) {
+  if (M > 4 && M <= 16 && K >= 512 && K <= 512 * kKsMaxWaves && K % 512 == 0 &&
+      (uint64_t)N * (uint64_t)K / 2 < (1ull << 32)) {
+    static int cus = 0;
+    if (!cus) {
+      int dev = 0;
+      if (hipGetDevice(&dev) != hipSuccess ||
+          hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        cus = 0;
+    }
+    if (cus) {
+      const int tiles = (int)((N + 15) / 16);
+      const int waves = (int)(K / 512);
+      // one workgroup per compute unit, but enough of them that no wave
+      // reduces more than kKsMaxResults tiles
+      int grid = tiles < cus ? tiles : cus;
+      const int need = (tiles + waves * kKsMaxResults - 1) / (waves * kKsMaxResults);
+      grid = grid > need ? grid : need;
+      const int threads = waves * 64;
+      const size_t ldb = (size_t)ld_y * (y_bf16 ? 2u : 4u);
+      const uint32_t ldx = (uint32_t)(Kp * 2);
+      if (y_bf16)
+        gemv_ksplit_kernel<true><<<grid, threads, 0, s>>>((const uint8_t*)x16, ldx, (int)M, wc, ws, (int)N, (int)K,
+                                                         tiles, gsx, gsw, (uint8_t*)y, ldb);
+      else
+        gemv_ksplit_kernel<false><<<grid, threads, 0, s>>>((const uint8_t*)x16, ldx, (int)M, wc, ws, (int)N,
+                                                          (int)K, tiles, gsx, gsw, (uint8_t*)y, ldb);
+      return;
+    }
+  }
   const GvPlan gp = plan_gemv_stream(M, N, K);
   if (gp.depth) {
     const int tiles = (int)((N + 15) / 16);

@@ -204,6 +204,39 @@ nvfp4_status_t nvfp4_gemm_run(int64_t M, int64_t K, const uint8_t *w_codes,
                               nvfp4_dtype_t y_dtype, int64_t ld_y, void *workspace,
                               size_t workspace_bytes, void *stream);
 
+/* ------------------------------------------------------------------------
+ * Static (calibrated) activation scale.  The checkpoints of the paper are
+ * produced by a calibration tool that fixes one FP32 global scale per
+ * module (paper section 3 "Checkpoints", section 6 "Per-module calibration
+ * vs. fused-GEMM scaling"); served that way, the activation quantize needs
+ * no absmax pass: one read of X instead of two, one launch at decode.
+ *
+ * nvfp4_quantize_static quantizes X with the given tensor scale *gs (a
+ * device float, finite and >= 0): block scales and codes follow the same
+ * rules as nvfp4_quantize with gs in place of RN(amax / 2688), saturating at
+ * 448 and 6 where |x| exceeds what gs allows.  No workspace is needed and gs
+ * is not written.  rows == 0 or K == 0 does nothing.
+ *
+ * nvfp4_gemm_prepare_static is nvfp4_gemm_prepare with the activation
+ * tensor scale given by *gs_x (copied into the workspace, so nvfp4_gemm_run
+ * is used unchanged); nvfp4_gemm_static is the pair in one call (arguments
+ * as in nvfp4_gemm).  A negative or non-finite scale gives unspecified
+ * codes.
+ * ---------------------------------------------------------------------- */
+nvfp4_status_t nvfp4_quantize_static(const void *x, nvfp4_dtype_t x_dtype, int64_t rows, int64_t K,
+                                     int64_t ld_x, const float *gs, uint8_t *codes, uint8_t *scales,
+                                     void *stream);
+
+nvfp4_status_t nvfp4_gemm_prepare_static(const void *x, nvfp4_dtype_t x_dtype, int64_t M, int64_t K,
+                                         int64_t ld_x, const float *gs_x, void *workspace,
+                                         size_t workspace_bytes, void *stream);
+
+nvfp4_status_t nvfp4_gemm_static(const void *x, nvfp4_dtype_t x_dtype, int64_t M, int64_t K,
+                                 int64_t ld_x, const float *gs_x, const uint8_t *w_codes,
+                                 const uint8_t *w_scales, const float *w_gs, int64_t N, void *y,
+                                 nvfp4_dtype_t y_dtype, int64_t ld_y, void *workspace,
+                                 size_t workspace_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

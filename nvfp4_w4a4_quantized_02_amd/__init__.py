@@ -40,7 +40,8 @@ _STATUS = {
 EXPORTS = (
     "nvfp4_status_string", "nvfp4_version", "nvfp4_quantize_workspace_size", "nvfp4_quantize",
     "nvfp4_dequantize", "nvfp4_fuse_rescale", "nvfp4_gemm_workspace_size", "nvfp4_gemm",
-    "nvfp4_gemm_prepare", "nvfp4_gemm_run",
+    "nvfp4_gemm_prepare", "nvfp4_gemm_run", "nvfp4_quantize_static", "nvfp4_gemm_prepare_static",
+    "nvfp4_gemm_static",
 )
 
 
@@ -76,6 +77,12 @@ def _load() -> ctypes.CDLL:
     L.nvfp4_gemm_prepare.restype = I
     L.nvfp4_gemm_run.argtypes = [I64, I64, P, P, P, I64, P, I, I64, P, SZ, P]
     L.nvfp4_gemm_run.restype = I
+    L.nvfp4_quantize_static.argtypes = [P, I, I64, I64, I64, P, P, P, P]
+    L.nvfp4_quantize_static.restype = I
+    L.nvfp4_gemm_prepare_static.argtypes = [P, I, I64, I64, I64, P, P, SZ, P]
+    L.nvfp4_gemm_prepare_static.restype = I
+    L.nvfp4_gemm_static.argtypes = [P, I, I64, I64, I64, P, P, P, P, I64, P, I, I64, P, SZ, P]
+    L.nvfp4_gemm_static.restype = I
     _check_single_hip_runtime()
     return L
 
@@ -157,6 +164,18 @@ def nvfp4_quantize(x: torch.Tensor):
     return codes, scales, gs
 
 
+def nvfp4_quantize_static(x: torch.Tensor, gs: torch.Tensor):
+    """Quantize with a given (calibrated) tensor scale gs (float32 [1] on the
+    device).  Returns (codes uint8 [rows, K/2], scales uint8 [rows, K/16])."""
+    rows, K, ld = _rows_view(x)
+    codes = torch.empty((rows, K // 2), dtype=torch.uint8, device=x.device)
+    scales = torch.empty((rows, K // 16), dtype=torch.uint8, device=x.device)
+    _check(lib.nvfp4_quantize_static(x.data_ptr(), _dtype_code(x.dtype), rows, K, ld, gs.data_ptr(),
+                                     codes.data_ptr(), scales.data_ptr(), _stream_ptr(x.device)),
+           "nvfp4_quantize_static")
+    return codes, scales
+
+
 def nvfp4_dequantize(codes: torch.Tensor, scales: torch.Tensor, gs: torch.Tensor,
                      out_dtype: torch.dtype = torch.float32) -> torch.Tensor:
     rows, half = codes.shape
@@ -206,18 +225,27 @@ def _ld_out(out, M, N):
 
 
 def nvfp4_gemm(x: torch.Tensor, w_codes: torch.Tensor, w_scales: torch.Tensor, w_gs: torch.Tensor,
-               out_dtype: torch.dtype = torch.bfloat16, out: torch.Tensor | None = None) -> torch.Tensor:
+               out_dtype: torch.dtype = torch.bfloat16, out: torch.Tensor | None = None,
+               x_gs: torch.Tensor | None = None) -> torch.Tensor:
     """Y = X W^T with X [M, K] quantized on the fly and W given as NVFP4
-    (codes [N, K/2], scales [N, K/16], w_gs [1])."""
+    (codes [N, K/2], scales [N, K/16], w_gs [1]).  x_gs: a calibrated
+    activation tensor scale (float32 [1] on the device) instead of the
+    absmax one."""
     M, K, ld = _rows_view(x)
     N = _check_weight(w_codes, w_scales, K)
     if out is None:
         out = _out_tensor(M, N, out_dtype, x.device)
     nws = lib.nvfp4_gemm_workspace_size(M, N, K)
     ws = workspace(nws, x.device)
-    _check(lib.nvfp4_gemm(x.data_ptr(), _dtype_code(x.dtype), M, K, ld, w_codes.data_ptr(),
-                          w_scales.data_ptr(), w_gs.data_ptr(), N, out.data_ptr(), _dtype_code(out.dtype),
-                          _ld_out(out, M, N), ws.data_ptr(), ws.numel(), _stream_ptr(x.device)), "nvfp4_gemm")
+    if x_gs is None:
+        _check(lib.nvfp4_gemm(x.data_ptr(), _dtype_code(x.dtype), M, K, ld, w_codes.data_ptr(),
+                              w_scales.data_ptr(), w_gs.data_ptr(), N, out.data_ptr(), _dtype_code(out.dtype),
+                              _ld_out(out, M, N), ws.data_ptr(), ws.numel(), _stream_ptr(x.device)), "nvfp4_gemm")
+    else:
+        _check(lib.nvfp4_gemm_static(x.data_ptr(), _dtype_code(x.dtype), M, K, ld, x_gs.data_ptr(),
+                                     w_codes.data_ptr(), w_scales.data_ptr(), w_gs.data_ptr(), N, out.data_ptr(),
+                                     _dtype_code(out.dtype), _ld_out(out, M, N), ws.data_ptr(), ws.numel(),
+                                     _stream_ptr(x.device)), "nvfp4_gemm_static")
     return out
 
 
@@ -229,16 +257,23 @@ class PreparedActivations:
         self.M, self.K, self.ws = M, K, ws
 
 
-def nvfp4_gemm_prepare(x: torch.Tensor, ws: torch.Tensor | None = None, max_n: int = 0) -> PreparedActivations:
+def nvfp4_gemm_prepare(x: torch.Tensor, ws: torch.Tensor | None = None, max_n: int = 0,
+                       x_gs: torch.Tensor | None = None) -> PreparedActivations:
     """Quantize X into a workspace of its own (or the given uint8 tensor),
-    sized for later runs against weights with up to max_n rows."""
+    sized for later runs against weights with up to max_n rows.  x_gs: a
+    calibrated activation tensor scale instead of the absmax one."""
     M, K, ld = _rows_view(x)
     nws = lib.nvfp4_gemm_workspace_size(M, max_n, K)
     if ws is None or ws.numel() < nws:
         ws = torch.empty(max(nws, 256), dtype=torch.uint8, device=x.device)
     assert ws.data_ptr() % 256 == 0
-    _check(lib.nvfp4_gemm_prepare(x.data_ptr(), _dtype_code(x.dtype), M, K, ld, ws.data_ptr(), ws.numel(),
-                                  _stream_ptr(x.device)), "nvfp4_gemm_prepare")
+    if x_gs is None:
+        _check(lib.nvfp4_gemm_prepare(x.data_ptr(), _dtype_code(x.dtype), M, K, ld, ws.data_ptr(), ws.numel(),
+                                      _stream_ptr(x.device)), "nvfp4_gemm_prepare")
+    else:
+        _check(lib.nvfp4_gemm_prepare_static(x.data_ptr(), _dtype_code(x.dtype), M, K, ld, x_gs.data_ptr(),
+                                             ws.data_ptr(), ws.numel(), _stream_ptr(x.device)),
+               "nvfp4_gemm_prepare_static")
     return PreparedActivations(M, K, ws)
 
 
@@ -255,6 +290,6 @@ def nvfp4_gemm_run(prep: PreparedActivations, w_codes: torch.Tensor, w_scales: t
     return out
 
 
-__all__ = ["nvfp4_quantize", "nvfp4_dequantize", "nvfp4_fuse_rescale", "nvfp4_gemm", "nvfp4_gemm_prepare",
-           "nvfp4_gemm_run", "PreparedActivations", "Nvfp4Error",
+__all__ = ["nvfp4_quantize", "nvfp4_quantize_static", "nvfp4_dequantize", "nvfp4_fuse_rescale", "nvfp4_gemm",
+           "nvfp4_gemm_prepare", "nvfp4_gemm_run", "PreparedActivations", "Nvfp4Error",
            "status_string", "lib", "EXPORTS", "LIB_PATH", "workspace"]

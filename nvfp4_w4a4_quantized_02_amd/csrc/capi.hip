@@ -84,7 +84,20 @@ nvfp4_status_t nvfp4_quantize(const void* x, nvfp4_dtype_t x_dtype, int64_t rows
     return NVFP4_ERR_WORKSPACE;
   uint32_t* partials = (uint32_t*)((char*)workspace + kWsPartials);
   int np = launch_amax(x, x_dtype == NVFP4_BF16, rows, K, ld_x, partials, s);
-  launch_quantize_packed(x, x_dtype == NVFP4_BF16, rows, K, ld_x, partials, np, codes, scales, gs, s);
+  launch_quantize_packed(x, x_dtype == NVFP4_BF16, rows, K, ld_x, partials, np, nullptr, codes, scales, gs, s);
+  return launched();
+}
+
+nvfp4_status_t nvfp4_quantize_static(const void* x, nvfp4_dtype_t x_dtype, int64_t rows, int64_t K, int64_t ld_x,
+                                     const float* gs, uint8_t* codes, uint8_t* scales, void* stream) {
+  nvfp4_status_t st = check_input(x, x_dtype, rows, K, ld_x);
+  if (st != NVFP4_OK) return st;
+  if (!gs) return NVFP4_ERR_NULL;
+  if (rows == 0 || K == 0) return NVFP4_OK;
+  if (!codes || !scales) return NVFP4_ERR_NULL;
+  if (!aligned(codes, 8)) return NVFP4_ERR_ALIGN;
+  launch_quantize_packed(x, x_dtype == NVFP4_BF16, rows, K, ld_x, nullptr, 0, gs, codes, scales, nullptr,
+                         (hipStream_t)stream);
   return launched();
 }
 
@@ -159,7 +172,24 @@ nvfp4_status_t nvfp4_gemm_prepare(const void* x, nvfp4_dtype_t x_dtype, int64_t 
   float* gsx = (float*)((char*)workspace + kWsGs);
   void* x16 = (char*)workspace + kWsX16;
   int np = launch_amax(x, xb, M, K, ld_x, partials, s);
-  launch_quantize_f16(x, xb, M, K, ld_x, round_up(K, kGemmBK), partials, np, x16, gsx, s);
+  launch_quantize_f16(x, xb, M, K, ld_x, round_up(K, kGemmBK), partials, np, nullptr, x16, gsx, s);
+  return launched();
+}
+
+nvfp4_status_t nvfp4_gemm_prepare_static(const void* x, nvfp4_dtype_t x_dtype, int64_t M, int64_t K, int64_t ld_x,
+                                         const float* gs_x, void* workspace, size_t workspace_bytes,
+                                         void* stream) {
+  nvfp4_status_t st = check_input(x, x_dtype, M, K, ld_x);
+  if (st != NVFP4_OK) return st;
+  if (K % 64 != 0) return NVFP4_ERR_SHAPE;
+  if (!gs_x) return NVFP4_ERR_NULL;
+  if (M == 0) return NVFP4_OK;
+  if (!workspace || !aligned(workspace, 256) || workspace_bytes < kWsX16 + x16_bytes(M, K))
+    return NVFP4_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  float* gsx = (float*)((char*)workspace + kWsGs);
+  void* x16 = (char*)workspace + kWsX16;
+  launch_quantize_f16(x, x_dtype == NVFP4_BF16, M, K, ld_x, round_up(K, kGemmBK), nullptr, 0, gs_x, x16, gsx, s);
   return launched();
 }
 
@@ -193,13 +223,10 @@ nvfp4_status_t nvfp4_gemm_run(int64_t M, int64_t K, const uint8_t* w_codes, cons
   return launched();
 }
 
-nvfp4_status_t nvfp4_gemm(const void* x, nvfp4_dtype_t x_dtype, int64_t M, int64_t K, int64_t ld_x,
-                          const uint8_t* w_codes, const uint8_t* w_scales, const float* w_gs, int64_t N, void* y,
-                          nvfp4_dtype_t y_dtype, int64_t ld_y, void* workspace, size_t workspace_bytes,
-                          void* stream) {
-  // validate everything before the first launch
-  nvfp4_status_t st = check_input(x, x_dtype, M, K, ld_x);
-  if (st != NVFP4_OK) return st;
+// The checks nvfp4_gemm makes besides those of the activations.
+static nvfp4_status_t run_args_ok(int64_t M, int64_t K, const uint8_t* w_codes, const uint8_t* w_scales,
+                                  const float* w_gs, int64_t N, const void* y, nvfp4_dtype_t y_dtype,
+                                  int64_t ld_y, const void* workspace, size_t workspace_bytes) {
   if (!dtype_ok(y_dtype)) return NVFP4_ERR_DTYPE;
   if (N < 0 || N >= kMaxDim) return NVFP4_ERR_SHAPE;
   if (K % 64 != 0) return NVFP4_ERR_SHAPE;
@@ -213,7 +240,34 @@ nvfp4_status_t nvfp4_gemm(const void* x, nvfp4_dtype_t x_dtype, int64_t M, int64
   }
   if (!workspace || !aligned(workspace, 256) || workspace_bytes < nvfp4_gemm_workspace_size(M, N, K))
     return NVFP4_ERR_WORKSPACE;
+  return NVFP4_OK;
+}
+
+nvfp4_status_t nvfp4_gemm(const void* x, nvfp4_dtype_t x_dtype, int64_t M, int64_t K, int64_t ld_x,
+                          const uint8_t* w_codes, const uint8_t* w_scales, const float* w_gs, int64_t N, void* y,
+                          nvfp4_dtype_t y_dtype, int64_t ld_y, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  // validate everything before the first launch
+  nvfp4_status_t st = check_input(x, x_dtype, M, K, ld_x);
+  if (st != NVFP4_OK) return st;
+  st = run_args_ok(M, K, w_codes, w_scales, w_gs, N, y, y_dtype, ld_y, workspace, workspace_bytes);
+  if (st != NVFP4_OK || M == 0 || N == 0) return st;
   st = nvfp4_gemm_prepare(x, x_dtype, M, K, ld_x, workspace, workspace_bytes, stream);
+  if (st != NVFP4_OK) return st;
+  return nvfp4_gemm_run(M, K, w_codes, w_scales, w_gs, N, y, y_dtype, ld_y, workspace, workspace_bytes, stream);
+}
+
+nvfp4_status_t nvfp4_gemm_static(const void* x, nvfp4_dtype_t x_dtype, int64_t M, int64_t K, int64_t ld_x,
+                                 const float* gs_x, const uint8_t* w_codes, const uint8_t* w_scales,
+                                 const float* w_gs, int64_t N, void* y, nvfp4_dtype_t y_dtype, int64_t ld_y,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+  // validate everything before launching anything
+  nvfp4_status_t st = check_input(x, x_dtype, M, K, ld_x);
+  if (st != NVFP4_OK) return st;
+  if (!gs_x) return NVFP4_ERR_NULL;
+  st = run_args_ok(M, K, w_codes, w_scales, w_gs, N, y, y_dtype, ld_y, workspace, workspace_bytes);
+  if (st != NVFP4_OK || M == 0 || N == 0) return st;
+  st = nvfp4_gemm_prepare_static(x, x_dtype, M, K, ld_x, gs_x, workspace, workspace_bytes, stream);
   if (st != NVFP4_OK) return st;
   return nvfp4_gemm_run(M, K, w_codes, w_scales, w_gs, N, y, y_dtype, ld_y, workspace, workspace_bytes, stream);
 }

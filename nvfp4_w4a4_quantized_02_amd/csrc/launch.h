@@ -66,12 +66,17 @@ struct RescaleArgs {
 
 // Returns the number of partials written.
 int launch_amax(const void* x, bool bf16, int64_t rows, int64_t K, int64_t ld, uint32_t* partials, hipStream_t s);
+// gs_in != nullptr: quantize with that (calibrated) tensor scale instead of
+// the absmax one; partials/npartials are then ignored and gs may be nullptr
+// (otherwise *gs receives the scale used).
 void launch_quantize_packed(const void* x, bool bf16, int64_t rows, int64_t K, int64_t ld,
-                            const uint32_t* partials, int npartials, uint8_t* codes, uint8_t* scales, float* gs,
-                            hipStream_t s);
+                            const uint32_t* partials, int npartials, const float* gs_in, uint8_t* codes,
+                            uint8_t* scales, float* gs, hipStream_t s);
 void launch_quantize_f16(const void* x, bool bf16, int64_t rows, int64_t K, int64_t ld, int64_t Kp,
-                         const uint32_t* partials, int npartials, void* x16, float* gs, hipStream_t s);
+                         const uint32_t* partials, int npartials, const float* gs_in, void* x16, float* gs,
+                         hipStream_t s);
 void launch_fill_f32(float* p, float v, hipStream_t s);
+void launch_copy_f32(float* p, const float* v, hipStream_t s);
 void launch_dequant(const uint8_t* codes, const uint8_t* scales, const float* gs, int64_t rows, int64_t K,
                     void* out, bool out_bf16, int64_t ld_out, hipStream_t s);
 void launch_fuse_rescale(const RescaleArgs& a, hipStream_t s);

@@ -133,18 +133,21 @@ __device__ __forceinline__ uint32_t block_absmax_bits(const float (&x)[16]) {
 // K: the A-side operand of the GEMM.
 constexpr uint32_t kDeferCap = 128;  // queued blocks per wave
 
+// gs_in != nullptr: the tensor scale is given (a calibrated, static scale)
+// and the partials are not read.  gs_out may be nullptr.
 template <bool kBf16, bool kF16>
 __global__ __launch_bounds__(256) void quantize_kernel(const uint8_t* __restrict__ x, size_t ld_bytes,
                                                         uint32_t kblocks, uint32_t out_kblocks,
                                                         uint32_t total_blocks, FastDiv fd,
                                                         const uint32_t* __restrict__ partials, int npartials,
+                                                        const float* __restrict__ gs_in,
                                                         uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
                                                         uint4* __restrict__ x16, float* __restrict__ gs_out) {
   constexpr int kWaves = 4;
   __shared__ uint32_t red[kWaves];
   __shared__ uint32_t deferred[kWaves][kDeferCap];
-  const float gs = reduce_partials_to_gs(partials, npartials, red);
-  if (blockIdx.x == 0 && threadIdx.x == 0) *gs_out = gs;
+  const float gs = gs_in ? *gs_in : reduce_partials_to_gs(partials, npartials, red);
+  if (gs_out && blockIdx.x == 0 && threadIdx.x == 0) *gs_out = gs;
   const FastScale fsc = fast_scale(gs);
   const uint32_t lane = threadIdx.x & 63u;
   uint32_t* queue = deferred[threadIdx.x >> 6];
@@ -276,16 +279,19 @@ constexpr int kSmallThreads = 1024;
 // Tensors of at most this many blocks take the one-launch kernel.
 static inline uint32_t small_block_limit(bool) { return 8u * kSmallThreads; }
 
+// gs_in != nullptr: the tensor scale is given and no absmax is taken.
+// gs_out may be nullptr.
 template <bool kBf16, bool kF16>
 __global__ __launch_bounds__(1024) void quantize_small_kernel(const uint8_t* __restrict__ x, size_t ld_bytes,
                                                                uint32_t kblocks, uint32_t out_kblocks,
                                                                uint32_t total_blocks, FastDiv fd,
+                                                               const float* __restrict__ gs_in,
                                                                uint8_t* __restrict__ codes,
                                                                uint8_t* __restrict__ scales,
                                                                uint4* __restrict__ x16, float* __restrict__ gs_out) {
   __shared__ uint32_t red[kSmallThreads / 64];
   if (total_blocks == 0) {  // (the launcher never sends one) no element to clamp onto
-    if (blockIdx.x == 0 && threadIdx.x == 0) *gs_out = 0.0f;
+    if (gs_out && blockIdx.x == 0 && threadIdx.x == 0) *gs_out = gs_in ? *gs_in : 0.0f;
     return;
   }
   auto block_ptr = [&](uint32_t b, uint32_t& kb) {
@@ -295,30 +301,35 @@ __global__ __launch_bounds__(1024) void quantize_small_kernel(const uint8_t* __r
     return x + (size_t)r * ld_bytes + (size_t)kc * (kBf16 ? 32u : 64u);
   };
 
-  uint32_t m = 0;
-  for (uint32_t b0 = threadIdx.x; b0 < total_blocks; b0 += 4u * kSmallThreads) {
-    float xv[4][16];
-    uint32_t kb[4];
+  float gs;
+  if (gs_in) {
+    gs = *gs_in;
+  } else {
+    uint32_t m = 0;
+    for (uint32_t b0 = threadIdx.x; b0 < total_blocks; b0 += 4u * kSmallThreads) {
+      float xv[4][16];
+      uint32_t kb[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      uint32_t b = b0 + (uint32_t)u * kSmallThreads;
-      b = b < total_blocks ? b : total_blocks - 1u;
-      load_block<kBf16>(block_ptr(b, kb[u]), xv[u]);
-    }
+      for (int u = 0; u < 4; ++u) {
+        uint32_t b = b0 + (uint32_t)u * kSmallThreads;
+        b = b < total_blocks ? b : total_blocks - 1u;
+        load_block<kBf16>(block_ptr(b, kb[u]), xv[u]);
+      }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const uint32_t a = kb[u] < kblocks ? block_absmax_bits<kBf16>(xv[u]) : 0u;  // padding blocks are zeros
-      m = m > a ? m : a;
+      for (int u = 0; u < 4; ++u) {
+        const uint32_t a = kb[u] < kblocks ? block_absmax_bits<kBf16>(xv[u]) : 0u;  // padding blocks are zeros
+        m = m > a ? m : a;
+      }
     }
+    m = wave_max_u32(m);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+    __syncthreads();
+    uint32_t amax = red[0];
+#pragma unroll
+    for (int i = 1; i < kSmallThreads / 64; ++i) amax = amax > red[i] ? amax : red[i];
+    gs = tensor_scale(__uint_as_float(amax));
   }
-  m = wave_max_u32(m);
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
-  __syncthreads();
-  uint32_t amax = red[0];
-#pragma unroll
-  for (int i = 1; i < kSmallThreads / 64; ++i) amax = amax > red[i] ? amax : red[i];
-  const float gs = tensor_scale(__uint_as_float(amax));
-  if (blockIdx.x == 0 && threadIdx.x == 0) *gs_out = gs;
+  if (gs_out && blockIdx.x == 0 && threadIdx.x == 0) *gs_out = gs;
 
   const uint32_t b = blockIdx.x * kSmallThreads + threadIdx.x;
   if (b >= total_blocks) return;
@@ -348,6 +359,7 @@ __global__ __launch_bounds__(1024) void quantize_small_kernel(const uint8_t* __r
 }
 
 __global__ void fill_f32_kernel(float* p, float v) { *p = v; }
+__global__ void copy_f32_kernel(float* p, const float* v) { *p = *v; }
 
 // ------------------------------------------------------------------ dequant
 // out = RN_fp32(E2M1(code) * E4M3(scale) * gs); the first product is exact.
@@ -445,10 +457,13 @@ int launch_amax(const void* x, bool bf16, int64_t rows, int64_t K, int64_t ld, u
 }
 
 // npartials == 0 (launch_amax launched nothing): one workgroup does it all.
+// gs_in != nullptr: the tensor scale is given; no absmax is taken (and
+// partials/npartials are ignored): small tensors take the one-launch kernel,
+// large ones the encode kernel alone.
 template <bool kF16>
 static void launch_quantize(const void* x, bool bf16, int64_t rows, int64_t K, int64_t ld, int64_t Kp,
-                            const uint32_t* partials, int npartials, uint8_t* codes, uint8_t* scales, void* x16,
-                            float* gs, hipStream_t s) {
+                            const uint32_t* partials, int npartials, const float* gs_in, uint8_t* codes,
+                            uint8_t* scales, void* x16, float* gs, hipStream_t s) {
   const uint32_t kb = (uint32_t)(K / 16), okb = (uint32_t)(Kp / 16);
   const uint32_t total = (uint32_t)(rows * (int64_t)okb);
   const size_t ld_bytes = (size_t)ld * (bf16 ? 2u : 4u);
@@ -456,17 +471,19 @@ static void launch_quantize(const void* x, bool bf16, int64_t rows, int64_t K, i
   const uint8_t* xb = (const uint8_t*)x;
   uint4* xo = (uint4*)x16;
   if (total == 0) {  // nothing to encode; the absmax of no elements is 0
-    launch_fill_f32(gs, 0.0f, s);
+    if (gs && !gs_in) launch_fill_f32(gs, 0.0f, s);
+    if (gs && gs_in) launch_copy_f32(gs, gs_in, s);
     return;
   }
-  if (npartials == 0) {
+  const bool small = gs_in ? total <= small_block_limit(bf16) : npartials == 0;
+  if (small) {
     const int grid = (int)((total + kSmallThreads - 1) / kSmallThreads);
     if (bf16)
-      quantize_small_kernel<true, kF16><<<grid, kSmallThreads, 0, s>>>(xb, ld_bytes, kb, okb, total, fd, codes,
-                                                                       scales, xo, gs);
+      quantize_small_kernel<true, kF16><<<grid, kSmallThreads, 0, s>>>(xb, ld_bytes, kb, okb, total, fd, gs_in,
+                                                                       codes, scales, xo, gs);
     else
-      quantize_small_kernel<false, kF16><<<grid, kSmallThreads, 0, s>>>(xb, ld_bytes, kb, okb, total, fd, codes,
-                                                                        scales, xo, gs);
+      quantize_small_kernel<false, kF16><<<grid, kSmallThreads, 0, s>>>(xb, ld_bytes, kb, okb, total, fd, gs_in,
+                                                                        codes, scales, xo, gs);
     return;
   }
   // Four workgroups per compute unit, all resident at once:
@@ -474,25 +491,27 @@ static void launch_quantize(const void* x, bool bf16, int64_t rows, int64_t K, i
   // partials once.
   const int grid = grid_for(total, 256, 1024);
   if (bf16)
-    quantize_kernel<true, kF16><<<grid, 256, 0, s>>>(xb, ld_bytes, kb, okb, total, fd, partials, npartials, codes,
-                                                     scales, xo, gs);
+    quantize_kernel<true, kF16><<<grid, 256, 0, s>>>(xb, ld_bytes, kb, okb, total, fd, partials, npartials, gs_in,
+                                                     codes, scales, xo, gs);
   else
     quantize_kernel<false, kF16><<<grid, 256, 0, s>>>(xb, ld_bytes, kb, okb, total, fd, partials, npartials,
-                                                      codes, scales, xo, gs);
+                                                      gs_in, codes, scales, xo, gs);
 }
 
 void launch_quantize_packed(const void* x, bool bf16, int64_t rows, int64_t K, int64_t ld,
-                            const uint32_t* partials, int npartials, uint8_t* codes, uint8_t* scales, float* gs,
-                            hipStream_t s) {
-  launch_quantize<false>(x, bf16, rows, K, ld, K, partials, npartials, codes, scales, nullptr, gs, s);
+                            const uint32_t* partials, int npartials, const float* gs_in, uint8_t* codes,
+                            uint8_t* scales, float* gs, hipStream_t s) {
+  launch_quantize<false>(x, bf16, rows, K, ld, K, partials, npartials, gs_in, codes, scales, nullptr, gs, s);
 }
 
 void launch_quantize_f16(const void* x, bool bf16, int64_t rows, int64_t K, int64_t ld, int64_t Kp,
-                         const uint32_t* partials, int npartials, void* x16, float* gs, hipStream_t s) {
-  launch_quantize<true>(x, bf16, rows, K, ld, Kp, partials, npartials, nullptr, nullptr, x16, gs, s);
+                         const uint32_t* partials, int npartials, const float* gs_in, void* x16, float* gs,
+                         hipStream_t s) {
+  launch_quantize<true>(x, bf16, rows, K, ld, Kp, partials, npartials, gs_in, nullptr, nullptr, x16, gs, s);
 }
 
 void launch_fill_f32(float* p, float v, hipStream_t s) { fill_f32_kernel<<<1, 1, 0, s>>>(p, v); }
+void launch_copy_f32(float* p, const float* v, hipStream_t s) { copy_f32_kernel<<<1, 1, 0, s>>>(p, v); }
 
 void launch_dequant(const uint8_t* codes, const uint8_t* scales, const float* gs, int64_t rows, int64_t K,
                     void* out, bool out_bf16, int64_t ld_out, hipStream_t s) {

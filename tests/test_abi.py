@@ -136,3 +136,45 @@ def test_fuse_rescale_rejects(nv):
     assert call(1, [A], [1], 4, [None], A + 256) == E_NULL
     assert call(1, [A], [-1], 4, [A + 4096], A + 256) == E_SHAPE
     assert L.nvfp4_fuse_rescale(1, None, None, 4, None, A, None) == E_NULL
+
+
+def qs(nv, x=A, dt=BF16, rows=4, K=32, ld=32, gs=A, codes=A, scales=A):
+    return nv.lib.nvfp4_quantize_static(x, dt, rows, K, ld, gs, codes, scales, None)
+
+
+def test_quantize_static_rejects(nv):
+    assert qs(nv, dt=5) == E_DTYPE
+    assert qs(nv, K=24, ld=24) == E_SHAPE
+    assert qs(nv, ld=16) == E_SHAPE
+    assert qs(nv, x=None) == E_NULL
+    assert qs(nv, gs=None) == E_NULL
+    assert qs(nv, scales=None) == E_NULL
+    assert qs(nv, x=A + 8) == E_ALIGN
+    assert qs(nv, codes=A + 4) == E_ALIGN
+    # nothing to write: valid, and nothing is launched (no tensor scale is produced)
+    assert qs(nv, rows=0) == OK
+    assert qs(nv, K=0, ld=0) == OK
+
+
+def gst(nv, x=A, dt=BF16, M=32, K=64, ld=64, gx=A, wc=A, wsc=A, wg=A, N=64, y=A, ydt=BF16, ldy=64, ws=A,
+        nws=BIG):
+    return nv.lib.nvfp4_gemm_static(x, dt, M, K, ld, gx, wc, wsc, wg, N, y, ydt, ldy, ws, nws, None)
+
+
+def test_gemm_static_rejects(nv):
+    L = nv.lib
+    assert gst(nv, dt=2) == E_DTYPE
+    assert gst(nv, ydt=7) == E_DTYPE
+    assert gst(nv, K=48, ld=48) == E_SHAPE
+    assert gst(nv, gx=None) == E_NULL
+    assert gst(nv, wg=None) == E_NULL
+    assert gst(nv, y=A + 8) == E_ALIGN
+    assert gst(nv, nws=10) == E_WS
+    assert gst(nv, M=0) == OK
+    assert gst(nv, N=0) == OK
+    # prepare with a given scale: same checks as the absmax prepare plus the scale pointer
+    assert L.nvfp4_gemm_prepare_static(A, BF16, 32, 48, 48, A, A, BIG, None) == E_SHAPE
+    assert L.nvfp4_gemm_prepare_static(A, BF16, 32, 64, 64, None, A, BIG, None) == E_NULL
+    assert L.nvfp4_gemm_prepare_static(A, BF16, 32, 64, 64, A, A + 16, BIG, None) == E_WS
+    assert L.nvfp4_gemm_prepare_static(A, BF16, 32, 64, 64, A, A, 100, None) == E_WS
+    assert L.nvfp4_gemm_prepare_static(A, BF16, 0, 64, 64, A, A, BIG, None) == OK

@@ -12,7 +12,9 @@ The same JSON line carries, under "also", the decode GEMV (M = 1, 4, 16,
 fused gate/up W[34816x5120], GB/s with 4 rotated weight copies so that the
 last-level cache cannot hold them), the standalone activation quantize at
 long prefill (X[32768x5120], GB/s on the two-pass byte count), the fused
-q/k/v repair + GEMM and the offline weight quantize.
+q/k/v repair + GEMM and the offline weight quantize.  The decode and quantize
+lines also time the calibrated-scale form (the activation tensor scale given,
+no absmax pass) under "calibrated_scale".
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 """
@@ -238,6 +240,18 @@ def secondary(torch, np, nv, workloads, to_gpu, dev, args):
             mark(2)
 
         wall, (prep_ms, run_ms) = time_steps(torch, max(steps, 40), warmup + 8, step, 2)
+        # the same step with a calibrated activation scale (no absmax pass)
+        xgs = nv.nvfp4_quantize(x)[2]
+
+        def sstep(i, mark, x=x, y=y, wsb=wsb, xgs=xgs):
+            c, s = copies[i % R]
+            mark(0)
+            prep = nv.nvfp4_gemm_prepare(x, ws=wsb, x_gs=xgs)
+            mark(1)
+            nv.nvfp4_gemm_run(prep, c, s, shared, out=y)
+            mark(2)
+
+        _, (sprep_ms, srun_ms) = time_steps(torch, max(steps, 40), warmup + 8, sstep, 2)
         nbytes = wbytes + M * K * 2 + M * N * 2
         step_ms = mean(prep_ms) + mean(run_ms)
         gbs = nbytes / (step_ms * 1e-3) / 1e9
@@ -246,6 +260,10 @@ def secondary(torch, np, nv, workloads, to_gpu, dev, args):
                     "ms_per_step": round(step_ms, 5), "wall_ms_per_step": round(wall, 5),
                     "phases_ms": {"activation_quantize": round(mean(prep_ms), 5),
                                   "gemv": round(mean(run_ms), 5)},
+                    "calibrated_scale": {"ms_per_step": round(mean(sprep_ms) + mean(srun_ms), 5),
+                                         "activation_quantize_ms": round(mean(sprep_ms), 5),
+                                         "GBs": round(nbytes / ((mean(sprep_ms) + mean(srun_ms)) * 1e-3) / 1e9,
+                                                      1)},
                     "config": {"workload": "decode: X[%dx5120] bf16 x fused gate/up W[34816x5120] NVFP4 "
                                            "(4 rotated copies) -> Y bf16" % M},
                     "roofline": {"bound": "hbm", "kernel": "nvfp4_gemm_run: gemv kernel", "achieved": round(kgbs, 1),
@@ -322,6 +340,16 @@ def secondary(torch, np, nv, workloads, to_gpu, dev, args):
         mark(1)
 
     _, (q_ms,) = time_steps(torch, steps, warmup, qstep, 1)
+    gcal = gs.clone()
+
+    def sqstep(i, mark):
+        mark(0)
+        st = nv.lib.nvfp4_quantize_static(xl.data_ptr(), 1, rows, K, K, gcal.data_ptr(), codes.data_ptr(),
+                                          scl.data_ptr(), torch.cuda.current_stream().cuda_stream)
+        assert st == 0
+        mark(1)
+
+    _, (sq_ms,) = time_steps(torch, steps, warmup, sqstep, 1)
     xbytes = rows * K * 2
     two_pass = 2 * xbytes + rows * K // 2 + rows * K // 16
     single = xbytes + rows * K // 2 + rows * K // 16
@@ -329,6 +357,12 @@ def secondary(torch, np, nv, workloads, to_gpu, dev, args):
     res.append({"metric": "activation quantize GB/s (two-pass bytes)", "value": round(qgbs, 1), "unit": "GB/s",
                 "ms_per_step": round(mean(q_ms), 4),
                 "single_read_GBs": round(single / (mean(q_ms) * 1e-3) / 1e9, 1),
+                "calibrated_scale": {"ms_per_step": round(mean(sq_ms), 4),
+                                     "GBs": round(single / (mean(sq_ms) * 1e-3) / 1e9, 1),
+                                     "frac": round(single / (mean(sq_ms) * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                                     "algorithmic": "1 read of X + codes + scales = %d B per call" % single,
+                                     "traffic": traffic_for("quantize_long_static",
+                                                            source_sha("quantize.hip", "encode.h", "common.h"))},
                 "config": {"workload": "long-prefill quantize: X[32768x5120] bf16 Student-t(2.5), 16 hot "
                                        "channels x200 -> packed E2M1 + E4M3 scales + FP32 scale"},
                 "roofline": {"bound": "hbm", "kernel": "nvfp4_quantize: amax_partials_kernel + quantize_kernel",
@@ -337,7 +371,8 @@ def secondary(torch, np, nv, workloads, to_gpu, dev, args):
                              "traffic": traffic_for("quantize_long", source_sha("quantize.hip", "encode.h",
                                                                                 "common.h")),
                              "algorithmic": "2 reads of X + codes + scales = %d B per call" % two_pass}})
-    log("quantize: %.1f GB/s (two-pass count)" % qgbs)
+    log("quantize: %.1f GB/s (two-pass count); calibrated scale %.1f GB/s (one read)"
+        % (qgbs, single / (mean(sq_ms) * 1e-3) / 1e9))
     del xl, codes, scl
 
     # ------------------------------------------------ offline weight quantize (fp32 in)

@@ -133,9 +133,9 @@ __device__ __forceinline__ uint32_t block_absmax_bits(const float (&x)[16]) {
 // K: the A-side operand of the GEMM.
 constexpr uint32_t kDeferCap = 128;  // queued blocks per wave
 
-// gs_in != nullptr: the tensor scale is given (a calibrated, static scale)
-// and the partials are not read.  gs_out may be nullptr.
-template <bool kBf16, bool kF16>
+// kGiven: the tensor scale is *gs_in (a calibrated, static scale) and the
+// partials are not read.  gs_out may be nullptr.
+template <bool kBf16, bool kF16, bool kGiven>
 __global__ __launch_bounds__(256) void quantize_kernel(const uint8_t* __restrict__ x, size_t ld_bytes,
                                                         uint32_t kblocks, uint32_t out_kblocks,
                                                         uint32_t total_blocks, FastDiv fd,
@@ -146,7 +146,7 @@ __global__ __launch_bounds__(256) void quantize_kernel(const uint8_t* __restrict
   constexpr int kWaves = 4;
   __shared__ uint32_t red[kWaves];
   __shared__ uint32_t deferred[kWaves][kDeferCap];
-  const float gs = gs_in ? *gs_in : reduce_partials_to_gs(partials, npartials, red);
+  const float gs = kGiven ? *gs_in : reduce_partials_to_gs(partials, npartials, red);
   if (gs_out && blockIdx.x == 0 && threadIdx.x == 0) *gs_out = gs;
   const FastScale fsc = fast_scale(gs);
   const uint32_t lane = threadIdx.x & 63u;
@@ -279,9 +279,9 @@ constexpr int kSmallThreads = 1024;
 // Tensors of at most this many blocks take the one-launch kernel.
 static inline uint32_t small_block_limit(bool) { return 8u * kSmallThreads; }
 
-// gs_in != nullptr: the tensor scale is given and no absmax is taken.
-// gs_out may be nullptr.
-template <bool kBf16, bool kF16>
+// kGiven: the tensor scale is *gs_in and no absmax is taken.  gs_out may be
+// nullptr.
+template <bool kBf16, bool kF16, bool kGiven>
 __global__ __launch_bounds__(1024) void quantize_small_kernel(const uint8_t* __restrict__ x, size_t ld_bytes,
                                                                uint32_t kblocks, uint32_t out_kblocks,
                                                                uint32_t total_blocks, FastDiv fd,
@@ -291,7 +291,7 @@ __global__ __launch_bounds__(1024) void quantize_small_kernel(const uint8_t* __r
                                                                uint4* __restrict__ x16, float* __restrict__ gs_out) {
   __shared__ uint32_t red[kSmallThreads / 64];
   if (total_blocks == 0) {  // (the launcher never sends one) no element to clamp onto
-    if (gs_out && blockIdx.x == 0 && threadIdx.x == 0) *gs_out = gs_in ? *gs_in : 0.0f;
+    if (gs_out && blockIdx.x == 0 && threadIdx.x == 0) *gs_out = kGiven ? *gs_in : 0.0f;
     return;
   }
   auto block_ptr = [&](uint32_t b, uint32_t& kb) {
@@ -302,7 +302,7 @@ __global__ __launch_bounds__(1024) void quantize_small_kernel(const uint8_t* __r
   };
 
   float gs;
-  if (gs_in) {
+  if constexpr (kGiven) {
     gs = *gs_in;
   } else {
     uint32_t m = 0;
@@ -456,6 +456,24 @@ int launch_amax(const void* x, bool bf16, int64_t rows, int64_t K, int64_t ld, u
   return grid;
 }
 
+template <bool kBf16, bool kF16, bool kGiven>
+static void launch_encode(bool small, const uint8_t* xb, size_t ld_bytes, uint32_t kb, uint32_t okb, uint32_t total,
+                          FastDiv fd, const uint32_t* partials, int npartials, const float* gs_in, uint8_t* codes,
+                          uint8_t* scales, uint4* xo, float* gs, hipStream_t s) {
+  if (small) {
+    const int grid = (int)((total + kSmallThreads - 1) / kSmallThreads);
+    quantize_small_kernel<kBf16, kF16, kGiven><<<grid, kSmallThreads, 0, s>>>(xb, ld_bytes, kb, okb, total, fd,
+                                                                              gs_in, codes, scales, xo, gs);
+    return;
+  }
+  // Four workgroups per compute unit, all resident at once:
+  // each wave then walks several chunks and every workgroup reduces the
+  // partials once.
+  const int grid = grid_for(total, 256, 1024);
+  quantize_kernel<kBf16, kF16, kGiven><<<grid, 256, 0, s>>>(xb, ld_bytes, kb, okb, total, fd, partials, npartials,
+                                                            gs_in, codes, scales, xo, gs);
+}
+
 // npartials == 0 (launch_amax launched nothing): one workgroup does it all.
 // gs_in != nullptr: the tensor scale is given; no absmax is taken (and
 // partials/npartials are ignored): small tensors take the one-launch kernel,
@@ -476,26 +494,18 @@ static void launch_quantize(const void* x, bool bf16, int64_t rows, int64_t K, i
     return;
   }
   const bool small = gs_in ? total <= small_block_limit(bf16) : npartials == 0;
-  if (small) {
-    const int grid = (int)((total + kSmallThreads - 1) / kSmallThreads);
-    if (bf16)
-      quantize_small_kernel<true, kF16><<<grid, kSmallThreads, 0, s>>>(xb, ld_bytes, kb, okb, total, fd, gs_in,
-                                                                       codes, scales, xo, gs);
-    else
-      quantize_small_kernel<false, kF16><<<grid, kSmallThreads, 0, s>>>(xb, ld_bytes, kb, okb, total, fd, gs_in,
-                                                                        codes, scales, xo, gs);
-    return;
-  }
-  // Four workgroups per compute unit, all resident at once:
-  // each wave then walks several chunks and every workgroup reduces the
-  // partials once.
-  const int grid = grid_for(total, 256, 1024);
-  if (bf16)
-    quantize_kernel<true, kF16><<<grid, 256, 0, s>>>(xb, ld_bytes, kb, okb, total, fd, partials, npartials, gs_in,
-                                                     codes, scales, xo, gs);
+  if (bf16 && gs_in)
+    launch_encode<true, kF16, true>(small, xb, ld_bytes, kb, okb, total, fd, partials, npartials, gs_in, codes,
+                                    scales, xo, gs, s);
+  else if (bf16)
+    launch_encode<true, kF16, false>(small, xb, ld_bytes, kb, okb, total, fd, partials, npartials, gs_in, codes,
+                                     scales, xo, gs, s);
+  else if (gs_in)
+    launch_encode<false, kF16, true>(small, xb, ld_bytes, kb, okb, total, fd, partials, npartials, gs_in, codes,
+                                     scales, xo, gs, s);
   else
-    quantize_kernel<false, kF16><<<grid, 256, 0, s>>>(xb, ld_bytes, kb, okb, total, fd, partials, npartials,
-                                                      gs_in, codes, scales, xo, gs);
+    launch_encode<false, kF16, false>(small, xb, ld_bytes, kb, okb, total, fd, partials, npartials, gs_in, codes,
+                                      scales, xo, gs, s);
 }
 
 void launch_quantize_packed(const void* x, bool bf16, int64_t rows, int64_t K, int64_t ld,

@@ -1,7 +1,8 @@
 """NVFP4 oracle: TEST INFRASTRUCTURE ONLY.
 
 A plain CPU statement of the NVFP4 W4A4 linear layer (quantize, dequantize,
-fused-module repair, exact block-scaled GEMM), written in C
+fused-module repair, exact block-scaled GEMM) and of the W4A16 form of the
+same weights against 16-bit activations, written in C
 (``nvfp4_oracle.c``) and wrapped here with ctypes over numpy arrays.  Only the
 tests, ``__graft_entry__.smoke()`` and the CPU-baseline leg of ``bench.py`` may
 import it.  It shares nothing with the HIP library in
@@ -12,7 +13,8 @@ Every function follows the paper "Why Gated DeltaNet Survives 4-Bit
 Quantization: NVFP4 W4A4 for the Recurrent Half of a Hybrid 27B LLM",
 section 2 ("NVFP4") and section 6 ("Per-module calibration vs. fused-GEMM
 scaling"), and the model card "Gemma-4-31B-IT-NVFP4-FP8attn-text",
-section "Verification"; the readings where those pages are silent are listed
+sections "Verification" and "Limitations" (W4A16); the readings where those
+pages are silent are listed
 at the top of ``nvfp4_oracle.c``.
 """
 from __future__ import annotations
@@ -75,6 +77,8 @@ def lib() -> ctypes.CDLL:
         L.orc_gemm_exact_sampled.argtypes = [P, P, ctypes.c_float, P, P, ctypes.c_float, I64, I64,
                                              P, P, P]
         L.orc_num_threads.restype = ctypes.c_int
+        L.orc_gemm_w4a16.argtypes = [P, ctypes.c_int, I64, I64, I64, P, P, ctypes.c_float, I64, P]
+        L.orc_gemm_w4a16_sampled.argtypes = [P, ctypes.c_int, I64, I64, P, P, ctypes.c_float, I64, P, P, P]
         _lib = L
     return _lib
 
@@ -223,6 +227,32 @@ def linear(x, wc, ws, gsw):
     Returns (y fp64 [M, N], (xc, xs, gsx))."""
     xc, xs, gsx = quantize(x)
     return gemm_exact(xc, xs, gsx, wc, ws, gsw), (xc, xs, gsx)
+
+
+def gemm_w4a16(x, wc, ws, gsw) -> np.ndarray:
+    """W4A16: y = x . deq(W)^T as fp64 [M, N], x a [M, K] float32 or
+    bf16-bits tensor used as given (no activation quantization)."""
+    xa, is_bf16 = _as_input(x)
+    wc, ws = np.ascontiguousarray(wc), np.ascontiguousarray(ws)
+    M, K = xa.shape
+    N = wc.shape[0]
+    assert wc.shape[1] * 2 == K and ws.shape[1] * 16 == K
+    y = np.empty((M, N), dtype=np.float64)
+    lib().orc_gemm_w4a16(_ptr(xa), is_bf16, M, K, K, _ptr(wc), _ptr(ws), float(np.float32(gsw)), N, _ptr(y))
+    return y
+
+
+def gemm_w4a16_sampled(x, wc, ws, gsw, m_idx, n_idx) -> np.ndarray:
+    xa, is_bf16 = _as_input(x)
+    wc, ws = np.ascontiguousarray(wc), np.ascontiguousarray(ws)
+    K = xa.shape[1]
+    m_idx = np.ascontiguousarray(m_idx, dtype=np.int64)
+    n_idx = np.ascontiguousarray(n_idx, dtype=np.int64)
+    assert m_idx.shape == n_idx.shape
+    y = np.empty(m_idx.shape, dtype=np.float64)
+    lib().orc_gemm_w4a16_sampled(_ptr(xa), is_bf16, K, K, _ptr(wc), _ptr(ws), float(np.float32(gsw)),
+                                 m_idx.size, _ptr(m_idx), _ptr(n_idx), _ptr(y))
+    return y
 
 
 def num_threads() -> int:

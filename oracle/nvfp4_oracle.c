@@ -383,6 +383,54 @@ void orc_gemm_exact_sampled(const uint8_t *xc, const uint8_t *xs, float gsx, con
     }
 }
 
+/* ---------------------------------------------------------------------- */
+/* W4A16: NVFP4 weights against 16-bit activations (model card             */
+/* "Gemma-4-31B-IT-NVFP4-FP8attn-text", section "Limitations": without     */
+/* native FP4 tensor cores the weights are served as W4A16)                */
+/* ---------------------------------------------------------------------- */
+
+/* y[m, n] = gs_w * sum_k x[m, k] * E2M1(code[n, k]) * E4M3(scale[n, k/16]).
+ * x is widened exactly to fp32 (bf16 or fp32 input).  Each product
+ * x * (E2M1 * E4M3) has at most 24 + 6 significant bits, so it is exact in
+ * fp64; the K terms are summed in fp64 in k order, which is within
+ * K * 2^-53 * sum|terms| of the exact sum, and the sum is multiplied by
+ * gs_w in fp64. */
+static double dot_w4a16(const void *x, int is_bf16, int64_t ld, int64_t m, const uint8_t *wc,
+                        const uint8_t *ws, int64_t K, float gsw)
+{
+    int64_t k;
+    double acc = 0.0;
+    for (k = 0; k < K; ++k) {
+        double w = ldexp((double)elem_units(wc, ws, k), -10);
+        acc += (double)load_elem(x, is_bf16, ld, m, k) * w;
+    }
+    return acc * (double)gsw;
+}
+
+void orc_gemm_w4a16(const void *x, int is_bf16, int64_t M, int64_t K, int64_t ld, const uint8_t *wc,
+                    const uint8_t *ws, float gsw, int64_t N, double *y)
+{
+    int64_t m;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (m = 0; m < M; ++m) {
+        int64_t n;
+        for (n = 0; n < N; ++n)
+            y[m * N + n] = dot_w4a16(x, is_bf16, ld, m, wc + n * (K / 2), ws + n * (K / 16), K, gsw);
+    }
+}
+
+/* Only the listed output elements (m_idx[i], n_idx[i]). */
+void orc_gemm_w4a16_sampled(const void *x, int is_bf16, int64_t K, int64_t ld, const uint8_t *wc,
+                            const uint8_t *ws, float gsw, int64_t count, const int64_t *m_idx,
+                            const int64_t *n_idx, double *y)
+{
+    int64_t i;
+#pragma omp parallel for schedule(static)
+    for (i = 0; i < count; ++i)
+        y[i] = dot_w4a16(x, is_bf16, ld, m_idx[i], wc + n_idx[i] * (K / 2), ws + n_idx[i] * (K / 16),
+                         K, gsw);
+}
+
 int orc_num_threads(void)
 {
 #ifdef _OPENMP

@@ -237,6 +237,32 @@ nvfp4_status_t nvfp4_gemm_static(const void *x, nvfp4_dtype_t x_dtype, int64_t M
                                  nvfp4_dtype_t y_dtype, int64_t ld_y, void *workspace,
                                  size_t workspace_bytes, void *stream);
 
+/* ----------------------------------------------------------------------
+ * W4A16: NVFP4 weights against 16-bit activations.  The model card
+ * "Gemma-4-31B-IT-NVFP4-FP8attn-text", section "Limitations", notes that
+ * without native FP4 tensor cores the NVFP4 weights are served as W4A16
+ * (the activations stay in 16 bits and are never quantized); the weight
+ * format is the paper's (section 2 "NVFP4").
+ *
+ * nvfp4_gemm_w4a16 computes Y[m, n] = gs_w * sum_k X[m, k] * E2M1(code[n, k])
+ * * E4M3(scale[n, k / 16]) with FP32 accumulation, X taken as given.
+ *   x        [M, ld_x] bf16 (x_dtype must be NVFP4_BF16), 16-byte aligned
+ *            rows; no activation quantization, so no tensor scale for X.
+ *   K        a multiple of 64.
+ *   w_codes, w_scales, w_gs, N, y, y_dtype, ld_y: as in nvfp4_gemm.
+ *   workspace: nvfp4_gemm_w4a16_workspace_size(M, N, K) bytes, 256-byte
+ *            aligned; it may be NULL when that size is 0 (always for
+ *            M <= 16).
+ * Errors as in nvfp4_gemm; fp32 activations give NVFP4_ERR_DTYPE.  M == 0
+ * or N == 0 does nothing; K == 0 stores zeros.
+ * ---------------------------------------------------------------------- */
+size_t nvfp4_gemm_w4a16_workspace_size(int64_t M, int64_t N, int64_t K);
+
+nvfp4_status_t nvfp4_gemm_w4a16(const void *x, nvfp4_dtype_t x_dtype, int64_t M, int64_t K, int64_t ld_x,
+                                const uint8_t *w_codes, const uint8_t *w_scales, const float *w_gs,
+                                int64_t N, void *y, nvfp4_dtype_t y_dtype, int64_t ld_y, void *workspace,
+                                size_t workspace_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -41,7 +41,7 @@ EXPORTS = (
     "nvfp4_status_string", "nvfp4_version", "nvfp4_quantize_workspace_size", "nvfp4_quantize",
     "nvfp4_dequantize", "nvfp4_fuse_rescale", "nvfp4_gemm_workspace_size", "nvfp4_gemm",
     "nvfp4_gemm_prepare", "nvfp4_gemm_run", "nvfp4_quantize_static", "nvfp4_gemm_prepare_static",
-    "nvfp4_gemm_static",
+    "nvfp4_gemm_static", "nvfp4_gemm_w4a16_workspace_size", "nvfp4_gemm_w4a16",
 )
 
 
@@ -83,6 +83,10 @@ def _load() -> ctypes.CDLL:
     L.nvfp4_gemm_prepare_static.restype = I
     L.nvfp4_gemm_static.argtypes = [P, I, I64, I64, I64, P, P, P, P, I64, P, I, I64, P, SZ, P]
     L.nvfp4_gemm_static.restype = I
+    L.nvfp4_gemm_w4a16_workspace_size.argtypes = [I64, I64, I64]
+    L.nvfp4_gemm_w4a16_workspace_size.restype = SZ
+    L.nvfp4_gemm_w4a16.argtypes = [P, I, I64, I64, I64, P, P, P, I64, P, I, I64, P, SZ, P]
+    L.nvfp4_gemm_w4a16.restype = I
     _check_single_hip_runtime()
     return L
 
@@ -290,6 +294,25 @@ def nvfp4_gemm_run(prep: PreparedActivations, w_codes: torch.Tensor, w_scales: t
     return out
 
 
+def nvfp4_gemm_w4a16(x: torch.Tensor, w_codes: torch.Tensor, w_scales: torch.Tensor, w_gs: torch.Tensor,
+                     out_dtype: torch.dtype = torch.bfloat16, out: torch.Tensor | None = None) -> torch.Tensor:
+    """W4A16: Y = X W^T with X [M, K] bf16 used as given (no activation
+    quantization) and W given as NVFP4 (codes [N, K/2], scales [N, K/16],
+    w_gs [1])."""
+    M, K, ld = _rows_view(x)
+    N = _check_weight(w_codes, w_scales, K)
+    if out is None:
+        out = _out_tensor(M, N, out_dtype, x.device)
+    nws = lib.nvfp4_gemm_w4a16_workspace_size(M, N, K)
+    ws = workspace(nws, x.device) if nws else None
+    _check(lib.nvfp4_gemm_w4a16(x.data_ptr(), _dtype_code(x.dtype), M, K, ld, w_codes.data_ptr(),
+                                w_scales.data_ptr(), w_gs.data_ptr(), N, out.data_ptr(), _dtype_code(out.dtype),
+                                _ld_out(out, M, N), ws.data_ptr() if ws is not None else None,
+                                ws.numel() if ws is not None else 0, _stream_ptr(x.device)), "nvfp4_gemm_w4a16")
+    return out
+
+
 __all__ = ["nvfp4_quantize", "nvfp4_quantize_static", "nvfp4_dequantize", "nvfp4_fuse_rescale", "nvfp4_gemm",
+           "nvfp4_gemm_w4a16",
            "nvfp4_gemm_prepare", "nvfp4_gemm_run", "PreparedActivations", "Nvfp4Error",
            "status_string", "lib", "EXPORTS", "LIB_PATH", "workspace"]

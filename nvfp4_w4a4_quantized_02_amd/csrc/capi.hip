@@ -158,6 +158,12 @@ size_t nvfp4_gemm_workspace_size(int64_t M, int64_t N, int64_t K) {
   return kWsX16 + x16_bytes(M, K) + partial_bytes(M, N, K);
 }
 
+// W4A16 needs only the fp32 K-part sums of the split tiles.
+size_t nvfp4_gemm_w4a16_workspace_size(int64_t M, int64_t N, int64_t K) {
+  if (M < 0 || N < 0 || K < 0 || M >= kMaxDim || N >= kMaxDim || K >= kMaxDim) return 0;
+  return partial_bytes(M, N, round_up(K, kGemmBK));
+}
+
 nvfp4_status_t nvfp4_gemm_prepare(const void* x, nvfp4_dtype_t x_dtype, int64_t M, int64_t K, int64_t ld_x,
                                   void* workspace, size_t workspace_bytes, void* stream) {
   nvfp4_status_t st = check_input(x, x_dtype, M, K, ld_x);
@@ -216,9 +222,9 @@ nvfp4_status_t nvfp4_gemm_run(int64_t M, int64_t K, const uint8_t* w_codes, cons
   void* wsv = workspace;
   const int64_t Kp = round_up(K, kGemmBK);
   if (M <= kGemvMaxM)
-    launch_gemv(x16, M, Kp, w_codes, w_scales, N, K, gsx, w_gs, y, yb, ld_y, s);
+    launch_gemv(false, x16, (size_t)Kp * 2, M, K, w_codes, w_scales, N, gsx, w_gs, y, yb, ld_y, s);
   else
-    launch_gemm(x16, M, Kp, w_codes, w_scales, N, K, gsx, w_gs, y, yb, ld_y,
+    launch_gemm(false, x16, (size_t)Kp * 2, M, K, w_codes, w_scales, N, gsx, w_gs, y, yb, ld_y,
                 (float*)((char*)wsv + kWsX16 + x16_bytes(M, K)), s);
   return launched();
 }
@@ -270,6 +276,36 @@ nvfp4_status_t nvfp4_gemm_static(const void* x, nvfp4_dtype_t x_dtype, int64_t M
   st = nvfp4_gemm_prepare_static(x, x_dtype, M, K, ld_x, gs_x, workspace, workspace_bytes, stream);
   if (st != NVFP4_OK) return st;
   return nvfp4_gemm_run(M, K, w_codes, w_scales, w_gs, N, y, y_dtype, ld_y, workspace, workspace_bytes, stream);
+}
+
+nvfp4_status_t nvfp4_gemm_w4a16(const void* x, nvfp4_dtype_t x_dtype, int64_t M, int64_t K, int64_t ld_x,
+                                const uint8_t* w_codes, const uint8_t* w_scales, const float* w_gs, int64_t N,
+                                void* y, nvfp4_dtype_t y_dtype, int64_t ld_y, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  nvfp4_status_t st = check_input(x, x_dtype, M, K, ld_x);
+  if (st != NVFP4_OK) return st;
+  if (x_dtype != NVFP4_BF16) return NVFP4_ERR_DTYPE;
+  if (!dtype_ok(y_dtype)) return NVFP4_ERR_DTYPE;
+  if (N < 0 || N >= kMaxDim || K % 64 != 0) return NVFP4_ERR_SHAPE;
+  if (M == 0 || N == 0) return NVFP4_OK;
+  if (!y || !w_gs) return NVFP4_ERR_NULL;
+  if (ld_y < N) return NVFP4_ERR_SHAPE;
+  if (!aligned(y, 16) || ((uint64_t)ld_y * esize(y_dtype)) % 16 != 0) return NVFP4_ERR_ALIGN;
+  if (K > 0) {
+    if (!w_codes || !w_scales) return NVFP4_ERR_NULL;
+    if (!aligned(w_codes, 16) || !aligned(w_scales, 4)) return NVFP4_ERR_ALIGN;
+  }
+  const size_t need = nvfp4_gemm_w4a16_workspace_size(M, N, K);
+  if (need && (!workspace || !aligned(workspace, 256) || workspace_bytes < need)) return NVFP4_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  const bool yb = y_dtype == NVFP4_BF16;
+  // K == 0 runs no K step (nothing of X or W is read) and stores zeros.
+  const size_t ldb = (size_t)ld_x * 2;
+  if (M <= kGemvMaxM)
+    launch_gemv(true, x, ldb, M, K, w_codes, w_scales, N, nullptr, w_gs, y, yb, ld_y, s);
+  else
+    launch_gemm(true, x, ldb, M, K, w_codes, w_scales, N, nullptr, w_gs, y, yb, ld_y, (float*)workspace, s);
+  return launched();
 }
 
 }  // extern "C"

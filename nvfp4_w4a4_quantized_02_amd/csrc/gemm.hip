@@ -8,6 +8,11 @@
 // packed codes and scale bytes and expanded in registers right before the
 // MFMA.  The epilogue applies RN(gs_x * gs_w) and stores Y[m, n].
 //
+// The same kernels serve W4A16 (model card "Gemma-4-31B-IT-NVFP4-FP8attn-
+// text", section "Limitations": NVFP4 weights against 16-bit activations):
+// with kA16 the operands are bf16, X is the caller's bf16 tensor read as
+// given, W expands exactly to bf16, and the epilogue applies gs_w alone.
+//
 // Inside one MFMA the order of K is free as long as both operands agree.
 // Each lane loads 16 bytes of W codes (32 consecutive k) and feeds dword j
 // of them to sub-step j; the X operand is read with the same k permutation.
@@ -46,7 +51,7 @@ struct GemmBuf {
 constexpr int kGemmWaves = 8;
 constexpr int kDmaPerStep = 6;  // per wave: 4 (X) + 1 (W codes) + 1 (W scales)
 
-template <bool kYBf16>
+template <bool kA16, bool kYBf16>
 __global__ __launch_bounds__(512, 1) void gemm_kernel(const uint4* __restrict__ x16, uint32_t kp_chunks,
                                                        const uint8_t* __restrict__ wc,
                                                        const uint8_t* __restrict__ ws, int N, int K, int M,
@@ -56,6 +61,8 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const uint4* __restrict__ 
                                                        int split, float* __restrict__ partials) {
   // Three distinct buffers (not one indexed array) so the compiler can see
   // that a transfer into one buffer never feeds reads of another.
+  using O = Op<kA16>;
+  using V = typename O::vec8;
   __shared__ GemmBuf b0, b1, b2;
   __shared__ uint32_t scale_lut[128];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -82,9 +89,11 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const uint4* __restrict__ 
   const uint8_t* wsbase = ws + (size_t)n0 * ks;                                          // + 4 B per step
   uint32_t xoff[4];  // X: instruction j fills slots (wave*4+j)*64 + lane (row (wave*4+j)*8 + lane/8)
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
-    xoff[j] = ((uint32_t)((wave * 4 + j) * 8 + (lane >> 3)) * kp_chunks +
-               ((lane & 7) ^ ((lane >> 3) & 7) ^ (j & 1))) * 16u;
+  for (int j = 0; j < 4; ++j) {
+    int row = (wave * 4 + j) * 8 + (lane >> 3);
+    row = m0 + row < M ? row : M - 1 - m0;   // rows past M repeat the last one (not stored)
+    xoff[j] = ((uint32_t)row * kp_chunks + ((lane & 7) ^ ((lane >> 3) & 7) ^ (j & 1))) * 16u;
+  }
   uint32_t wcoff;  // W codes: the instruction fills slots wave*64 + lane = row*2 + physical half
   {
     int row = wave * 32 + (lane >> 1);
@@ -121,16 +130,17 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const uint4* __restrict__ 
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[t][u][r] = 0.0f;
 
-  // Scale-byte table: entry b holds scale_f16x2(b), so a scale costs one
-  // LDS read (the sign bit of a scale byte is ignored, as by scale_f16x2).
-  if (tid < 128) scale_lut[tid] = __builtin_bit_cast(uint32_t, scale_f16x2((uint32_t)tid));
+  // Scale-byte table: entry b holds what scale byte b becomes for the W
+  // expansion, so a scale costs one LDS read (the sign bit of a scale byte
+  // is ignored).
+  if (tid < 128) scale_lut[tid] = O::scale_bits((uint32_t)tid);
 
   // Operand fragments of sub-step j from buffer `cur`.
-  auto read_x = [&](const GemmBuf& cur, int j, f16x8 (&bx)[4]) {
+  auto read_x = [&](const GemmBuf& cur, int j, V (&bx)[4]) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int row = wave_m * 128 + u * 32 + l32;
-      bx[u] = u4_as_f16x8(cur.x[row * 8 + ((4 * h + j) ^ (row & 7) ^ ((row >> 3) & 1))]);
+      bx[u] = O::vec(cur.x[row * 8 + ((4 * h + j) ^ (row & 7) ^ ((row >> 3) & 1))]);
     }
   };
   // W codes (one dword per sub-step) and the two block scales of this lane.
@@ -149,20 +159,19 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const uint4* __restrict__ 
       sp[t][1] = scale_lut[(sw[t] >> 8) & 0x7Fu];
     }
   };
-  auto expand_w = [&](const uint4 (&wv)[2], const uint32_t (&sp)[2][2], int j, f16x8 (&aw)[2]) {
+  auto expand_w = [&](const uint4 (&wv)[2], const uint32_t (&sp)[2][2], int j, V (&aw)[2]) {
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       uint32_t e[4];
-      expand8(dword_of(wv[t], j), __builtin_bit_cast(half2_t, sp[t][j >> 1]), e);
-      aw[t] = u4_as_f16x8(make_uint4(e[0], e[1], e[2], e[3]));
+      O::expand(dword_of(wv[t], j), sp[t][j >> 1], e);
+      aw[t] = O::vec(make_uint4(e[0], e[1], e[2], e[3]));
     }
   };
-  auto mfma8 = [&](const f16x8 (&aw)[2], const f16x8 (&bx)[4]) {
+  auto mfma8 = [&](const V (&aw)[2], const V (&bx)[4]) {
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
-        acc[t][u] = __builtin_amdgcn_mfma_f32_32x32x16_f16(aw[t], bx[u], acc[t][u], 0, 0, 0);
+      for (int u = 0; u < 4; ++u) acc[t][u] = O::mfma32(aw[t], bx[u], acc[t][u]);
   };
 
   // Register-resident operands carried across sub-steps and steps: the W
@@ -170,7 +179,7 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const uint4* __restrict__ 
   // sub-step.
   uint4 wv[2];
   uint32_t sp[2][2];
-  f16x8 bx[4], aw[2];
+  V bx[4], aw[2];
 
   // One main-loop step.  Sub-steps 0..2 of step kt run from `cur`, each
   // overlapping the LDS reads and expansion of the following sub-step.  Then
@@ -186,7 +195,7 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const uint4* __restrict__ 
     issue(kt + 2 < last ? kt + 2 : last, lx, lc, ls);
 #pragma unroll
     for (int j = 0; j < 3; ++j) {
-      f16x8 bxn[4], awn[2];
+      V bxn[4], awn[2];
       read_x(cur, j + 1, bxn);
       mfma8(aw, bx);
       expand_w(wv, sp, j + 1, awn);
@@ -200,7 +209,7 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const uint4* __restrict__ 
     // barrier every wave's have.  The barrier is a bare s_barrier: a
     // workgroup fence would also wait for the transfers still in flight.
     asm volatile("s_waitcnt vmcnt(6) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    f16x8 bx3[4], aw3[2];
+    V bx3[4], aw3[2];
 #pragma unroll
     for (int q = 0; q < 4; ++q) bx3[q] = bx[q];
 #pragma unroll
@@ -254,7 +263,7 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const uint4* __restrict__ 
     }
     return;
   }
-  const float scale = (*gsx_p) * (*gsw_p);
+  const float scale = kA16 ? *gsw_p : (*gsx_p) * (*gsw_p);
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     const int m = m0 + wave_m * 128 + u * 32 + l32;
@@ -274,7 +283,7 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const uint4* __restrict__ 
 
 // Adds the K parts of every split tile in part order, applies the scales
 // and stores Y.  One thread per 4 consecutive outputs of a tile row.
-template <bool kYBf16>
+template <bool kA16, bool kYBf16>
 __global__ __launch_bounds__(256) void gemm_split_reduce_kernel(const float* __restrict__ partials, int full_tiles,
                                                                  int split, int tiles_n, int M, int N,
                                                                  const float* __restrict__ gsx_p,
@@ -296,34 +305,46 @@ __global__ __launch_bounds__(256) void gemm_split_reduce_kernel(const float* __r
     a.z += b.z;
     a.w += b.w;
   }
-  const float scale = (*gsx_p) * (*gsw_p);
+  const float scale = kA16 ? *gsw_p : (*gsx_p) * (*gsw_p);
   store4<kYBf16>(y + (size_t)m * ld_y_bytes, n, N, a.x * scale, a.y * scale, a.z * scale, a.w * scale);
 }
 
 // ====================================================================== launch
-void launch_gemm(const void* x16, int64_t M, int64_t Kp, const uint8_t* wc, const uint8_t* ws, int64_t N, int64_t K,
-                 const float* gsx, const float* gsw, void* y, bool y_bf16, int64_t ld_y, float* partials,
-                 hipStream_t s) {
-  const GemmPlan p = plan_gemm(M, N, Kp);
+template <bool kA16>
+static void gemm_go(const void* x, uint32_t ld_x_chunks, int64_t M, int64_t K, const uint8_t* wc, const uint8_t* ws,
+                    int64_t N, const float* gsx, const float* gsw, void* y, bool y_bf16, int64_t ld_y,
+                    float* partials, hipStream_t s) {
+  const GemmPlan p = plan_gemm(M, N, K);
   const int rem = p.tiles_m * p.tiles_n - p.full_tiles;
   const size_t ldb = (size_t)ld_y * (y_bf16 ? 2u : 4u);
-  const uint32_t kpc = (uint32_t)(Kp / 8);
   dim3 grid(p.full_tiles + rem * p.split);
   if (y_bf16)
-    gemm_kernel<true><<<grid, kGemmWaves * 64, 0, s>>>((const uint4*)x16, kpc, wc, ws, (int)N, (int)K, (int)M, gsx, gsw,
-                                           (uint8_t*)y, ldb, p.tiles_n, p.nk, p.full_tiles, p.split, partials);
+    gemm_kernel<kA16, true><<<grid, kGemmWaves * 64, 0, s>>>((const uint4*)x, ld_x_chunks, wc, ws, (int)N, (int)K,
+                                                            (int)M, gsx, gsw, (uint8_t*)y, ldb, p.tiles_n, p.nk,
+                                                            p.full_tiles, p.split, partials);
   else
-    gemm_kernel<false><<<grid, kGemmWaves * 64, 0, s>>>((const uint4*)x16, kpc, wc, ws, (int)N, (int)K, (int)M, gsx, gsw,
-                                            (uint8_t*)y, ldb, p.tiles_n, p.nk, p.full_tiles, p.split, partials);
+    gemm_kernel<kA16, false><<<grid, kGemmWaves * 64, 0, s>>>((const uint4*)x, ld_x_chunks, wc, ws, (int)N, (int)K,
+                                                             (int)M, gsx, gsw, (uint8_t*)y, ldb, p.tiles_n, p.nk,
+                                                             p.full_tiles, p.split, partials);
   if (p.split > 1) {
     dim3 rgrid(kGemmBM * kGemmBN / 4 / 256, rem);
     if (y_bf16)
-      gemm_split_reduce_kernel<true><<<rgrid, 256, 0, s>>>(partials, p.full_tiles, p.split, p.tiles_n, (int)M,
-                                                           (int)N, gsx, gsw, (uint8_t*)y, ldb);
+      gemm_split_reduce_kernel<kA16, true><<<rgrid, 256, 0, s>>>(partials, p.full_tiles, p.split, p.tiles_n, (int)M,
+                                                                 (int)N, gsx, gsw, (uint8_t*)y, ldb);
     else
-      gemm_split_reduce_kernel<false><<<rgrid, 256, 0, s>>>(partials, p.full_tiles, p.split, p.tiles_n, (int)M,
-                                                            (int)N, gsx, gsw, (uint8_t*)y, ldb);
+      gemm_split_reduce_kernel<kA16, false><<<rgrid, 256, 0, s>>>(partials, p.full_tiles, p.split, p.tiles_n,
+                                                                  (int)M, (int)N, gsx, gsw, (uint8_t*)y, ldb);
   }
+}
+
+void launch_gemm(bool a16, const void* x, size_t ld_x_bytes, int64_t M, int64_t K, const uint8_t* wc,
+                 const uint8_t* ws, int64_t N, const float* gsx, const float* gsw, void* y, bool y_bf16,
+                 int64_t ld_y, float* partials, hipStream_t s) {
+  const uint32_t ldc = (uint32_t)(ld_x_bytes / 16);
+  if (a16)
+    gemm_go<true>(x, ldc, M, K, wc, ws, N, gsx, gsw, y, y_bf16, ld_y, partials, s);
+  else
+    gemm_go<false>(x, ldc, M, K, wc, ws, N, gsx, gsw, y, y_bf16, ld_y, partials, s);
 }
 
 }  // namespace nvfp4

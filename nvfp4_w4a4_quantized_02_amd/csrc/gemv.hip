@@ -3,6 +3,11 @@
 // accumulate).  W arrives as packed codes and scale bytes and is expanded
 // exactly to fp16 in registers; X arrives already expanded to fp16 by the
 // quantize kernel.  The epilogue applies RN(gs_x * gs_w).
+//
+// With kA16 the same kernels compute W4A16 (model card "Gemma-4-31B-IT-
+// NVFP4-FP8attn-text", section "Limitations"): bf16 operands, X the caller's
+// bf16 activations as given, W expanded exactly to bf16, and gs_w alone in
+// the epilogue.
 #include "encode.h"
 #include "launch.h"
 #include "mfma_util.h"
@@ -17,12 +22,13 @@ namespace nvfp4 {
 // NT*16 rows of W; its 4 waves split K round-robin in 128-k chunks and their
 // partial sums are added in a fixed order through LDS, so the result does
 // not depend on scheduling.
-template <int NT, bool kYBf16>
+template <int NT, bool kA16, bool kYBf16>
 __global__ __launch_bounds__(256) void gemv_kernel(const uint4* __restrict__ x16, uint32_t kp_chunks, int M,
                                                     const uint8_t* __restrict__ wc, const uint8_t* __restrict__ ws,
                                                     int N, int K, const float* __restrict__ gsx_p,
                                                     const float* __restrict__ gsw_p, uint8_t* __restrict__ y,
                                                     size_t ld_y_bytes) {
+  using O = Op<kA16>;
   __shared__ floatx4 part[4][NT][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int l16 = lane & 15, g = lane >> 4;
@@ -60,13 +66,12 @@ __global__ __launch_bounds__(256) void gemv_kernel(const uint4* __restrict__ x16
     for (int j = 0; j < 4; ++j) xv[j] = (mvalid && kvalid) ? xrow[kk / 8 + j] : make_uint4(0, 0, 0, 0);
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-      const half2_t s0 = scale_f16x2(sv[t]), s1 = scale_f16x2(sv[t] >> 8);
+      const uint32_t s0 = O::scale_bits(sv[t]), s1 = O::scale_bits(sv[t] >> 8);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         uint32_t e[4];
-        expand8(dword_of(wv[t], j), j < 2 ? s0 : s1, e);
-        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(u4_as_f16x8(make_uint4(e[0], e[1], e[2], e[3])),
-                                                        u4_as_f16x8(xv[j]), acc[t], 0, 0, 0);
+        O::expand(dword_of(wv[t], j), j < 2 ? s0 : s1, e);
+        acc[t] = O::mfma16(O::vec(make_uint4(e[0], e[1], e[2], e[3])), O::vec(xv[j]), acc[t]);
       }
     }
   }
@@ -75,7 +80,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(const uint4* __restrict__ x16
   for (int t = 0; t < NT; ++t) part[wave][t][lane] = acc[t];
   __syncthreads();
   if (wave != 0) return;
-  const float scale = (*gsx_p) * (*gsw_p);
+  const float scale = kA16 ? *gsw_p : (*gsx_p) * (*gsw_p);
   if (!mvalid) return;
   uint8_t* yrow = y + (size_t)l16 * ld_y_bytes;
 #pragma unroll
@@ -114,13 +119,14 @@ __global__ __launch_bounds__(256) void gemv_kernel(const uint4* __restrict__ x16
 // so the result does not depend on scheduling.
 constexpr uint32_t kGvChunkCodes = 2048;  // 16 rows x 128 B
 
-template <int D, int XI, bool kYBf16>
+template <int D, int XI, bool kA16, bool kYBf16>
 __global__ __launch_bounds__(64) void gemv_stream_kernel(const uint8_t* __restrict__ x16, uint32_t ld_x16_bytes,
                                                           int M, const uint8_t* __restrict__ wc,
                                                           const uint8_t* __restrict__ ws, int N, int K,
                                                           const float* __restrict__ gsx_p,
                                                           const float* __restrict__ gsw_p,
                                                           uint8_t* __restrict__ y, size_t ld_y_bytes) {
+  using O = Op<kA16>;
   extern __shared__ uint4 smem[];
   constexpr uint32_t kSlot = kGvChunkCodes + XI * 1024u;
   uint8_t* lds = reinterpret_cast<uint8_t*>(smem);
@@ -183,7 +189,7 @@ __global__ __launch_bounds__(64) void gemv_stream_kernel(const uint8_t* __restri
   for (int d = 0; d < D; ++d) issue(d);
 
   const bool mvalid = l16 < M;
-  const float scale = (*gsx_p) * (*gsw_p);
+  const float scale = kA16 ? *gsw_p : (*gsx_p) * (*gsw_p);
   // this lane's reads
   const uint32_t sw = (uint32_t)(l16 & 7);
   const uint32_t cpos0 = (uint32_t)l16 * 128u + 16u * ((2u * g) ^ sw);
@@ -210,15 +216,14 @@ __global__ __launch_bounds__(64) void gemv_stream_kernel(const uint8_t* __restri
 #pragma unroll
         for (int t = 0; t < 8; ++t) xv[t] = *reinterpret_cast<const uint4*>(xb + 16u * ((uint32_t)t ^ xg));
       }
-      const half2_t s0 = scale_f16x2(sd), s1 = scale_f16x2(sd >> 8), s2 = scale_f16x2(sd >> 16),
-                    s3 = scale_f16x2(sd >> 24);
+      const uint32_t s0 = O::scale_bits(sd), s1 = O::scale_bits(sd >> 8), s2 = O::scale_bits(sd >> 16),
+                     s3 = O::scale_bits(sd >> 24);
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
-        const half2_t sp = t < 2 ? s0 : (t < 4 ? s1 : (t < 6 ? s2 : s3));
+        const uint32_t sp = t < 2 ? s0 : (t < 4 ? s1 : (t < 6 ? s2 : s3));
         uint32_t e[4];
-        expand8(dword_of(t < 4 ? w0 : w1, t & 3), sp, e);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(u4_as_f16x8(make_uint4(e[0], e[1], e[2], e[3])),
-                                                     u4_as_f16x8(xv[t]), acc, 0, 0, 0);
+        O::expand(dword_of(t < 4 ? w0 : w1, t & 3), sp, e);
+        acc = O::mfma16(O::vec(make_uint4(e[0], e[1], e[2], e[3])), O::vec(xv[t]), acc);
       }
       issue(d);
     }
@@ -247,13 +252,14 @@ struct GwStage {
   uint4 x[16 * 32];      //  8 KB: [m][32 slots]
 };
 
-template <bool kYBf16>
+template <bool kA16, bool kYBf16>
 __global__ __launch_bounds__(512) void gemv_shared_kernel(const uint8_t* __restrict__ x16, uint32_t ld_x16_bytes,
                                                           int M, const uint8_t* __restrict__ wc,
                                                           const uint8_t* __restrict__ ws, int N, int K,
                                                           const float* __restrict__ gsx_p,
                                                           const float* __restrict__ gsw_p,
                                                           uint8_t* __restrict__ y, size_t ld_y_bytes) {
+  using O = Op<kA16>;
   __shared__ GwStage st0, st1, st2;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, l16 = lane & 15, g = lane >> 4;
   const int tile = blockIdx.x * kGwWaves + wave;  // 16-row tile of this wave
@@ -313,15 +319,14 @@ __global__ __launch_bounds__(512) void gemv_shared_kernel(const uint8_t* __restr
 #pragma unroll
       for (int t = 0; t < 8; ++t) xv[t] = xr[(uint32_t)t ^ xg];
     }
-    const half2_t s0 = scale_f16x2(sd), s1 = scale_f16x2(sd >> 8), s2 = scale_f16x2(sd >> 16),
-                  s3 = scale_f16x2(sd >> 24);
+    const uint32_t s0 = O::scale_bits(sd), s1 = O::scale_bits(sd >> 8), s2 = O::scale_bits(sd >> 16),
+                   s3 = O::scale_bits(sd >> 24);
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
-      const half2_t sp = t < 2 ? s0 : (t < 4 ? s1 : (t < 6 ? s2 : s3));
+      const uint32_t sp = t < 2 ? s0 : (t < 4 ? s1 : (t < 6 ? s2 : s3));
       uint32_t e[4];
-      expand8(dword_of(t < 4 ? w0 : w1, t & 3), sp, e);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(u4_as_f16x8(make_uint4(e[0], e[1], e[2], e[3])),
-                                                   u4_as_f16x8(xv[t]), acc, 0, 0, 0);
+      O::expand(dword_of(t < 4 ? w0 : w1, t & 3), sp, e);
+      acc = O::mfma16(O::vec(make_uint4(e[0], e[1], e[2], e[3])), O::vec(xv[t]), acc);
     }
   };
   // Step kt: wait for this wave's transfers of step kt (those of kt+1 may
@@ -341,7 +346,7 @@ __global__ __launch_bounds__(512) void gemv_shared_kernel(const uint8_t* __restr
     if (kt + 2 < nk) step(kt + 2, st2, 1);
   }
   wait_vmcnt<0>();
-  const float scale = (*gsx_p) * (*gsw_p);
+  const float scale = kA16 ? *gsw_p : (*gsx_p) * (*gsw_p);
   if (mvalid)
     store4<kYBf16>(y + (size_t)l16 * ld_y_bytes, tile * 16 + 4 * g, N, acc[0] * scale, acc[1] * scale,
                    acc[2] * scale, acc[3] * scale);
@@ -367,13 +372,14 @@ constexpr int kKsMaxWaves = 10;     // K <= 5120
 constexpr int kKsMaxResults = 4;    // tiles a wave reduces (bounded by the grid)
 constexpr uint32_t kKsSlot = 4096 + 512;  // codes + scales of one wave and tile
 
-template <bool kYBf16>
+template <bool kA16, bool kYBf16>
 __global__ __launch_bounds__(640) void gemv_ksplit_kernel(const uint8_t* __restrict__ x16, uint32_t ld_x16_bytes,
                                                           int M, const uint8_t* __restrict__ wc,
                                                           const uint8_t* __restrict__ ws, int N, int K,
                                                           int tiles, const float* __restrict__ gsx_p,
                                                           const float* __restrict__ gsw_p,
                                                           uint8_t* __restrict__ y, size_t ld_y_bytes) {
+  using O = Op<kA16>;
   __shared__ __attribute__((aligned(16))) uint8_t ring[3][kKsMaxWaves][kKsSlot];
   __shared__ floatx4 part[2][kKsMaxWaves][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, l16 = lane & 15, g = lane >> 4;
@@ -424,7 +430,7 @@ __global__ __launch_bounds__(640) void gemv_ksplit_kernel(const uint8_t* __restr
     }
   };
 
-  const float scale = (*gsx_p) * (*gsw_p);
+  const float scale = kA16 ? *gsw_p : (*gsx_p) * (*gsw_p);
   const uint32_t sw = (uint32_t)(l16 & 7);
   floatx4 res[kKsMaxResults];
   int res_tile[kKsMaxResults];
@@ -444,9 +450,8 @@ __global__ __launch_bounds__(640) void gemv_ksplit_kernel(const uint8_t* __restr
     for (int s = 0; s < 16; ++s) {
       const uint32_t sb = (s < 8 ? sc.x : sc.y) >> (8 * ((s >> 1) & 3));
       uint32_t e[4];
-      expand8(dword_of(w[s >> 2], s & 3), scale_f16x2(sb), e);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(u4_as_f16x8(make_uint4(e[0], e[1], e[2], e[3])),
-                                                   u4_as_f16x8(xv[s]), acc, 0, 0, 0);
+      O::expand(dword_of(w[s >> 2], s & 3), O::scale_bits(sb), e);
+      acc = O::mfma16(O::vec(make_uint4(e[0], e[1], e[2], e[3])), O::vec(xv[s]), acc);
     }
     part[pb][wave][lane] = acc;
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
@@ -532,23 +537,26 @@ static GvPlan plan_gemv_stream(int64_t M, int64_t N, int64_t K) {
   return p;
 }
 
-template <int NT>
-static void gemv_nt(const void* x16, int64_t M, int64_t Kp, const uint8_t* wc, const uint8_t* ws, int64_t N,
+template <int NT, bool kA16>
+static void gemv_nt(const void* x, size_t ld_x_bytes, int64_t M, const uint8_t* wc, const uint8_t* ws, int64_t N,
                     int64_t K, const float* gsx, const float* gsw, void* y, bool y_bf16, int64_t ld_y,
                     hipStream_t s) {
   const int grid = (int)((N + NT * 16 - 1) / (NT * 16));
   const size_t ldb = (size_t)ld_y * (y_bf16 ? 2u : 4u);
-  const uint32_t kpc = (uint32_t)(Kp / 8);
+  const uint32_t kpc = (uint32_t)(ld_x_bytes / 16);
   if (y_bf16)
-    gemv_kernel<NT, true><<<grid, 256, 0, s>>>((const uint4*)x16, kpc, (int)M, wc, ws, (int)N, (int)K, gsx, gsw,
-                                               (uint8_t*)y, ldb);
+    gemv_kernel<NT, kA16, true><<<grid, 256, 0, s>>>((const uint4*)x, kpc, (int)M, wc, ws, (int)N, (int)K, gsx,
+                                                     gsw, (uint8_t*)y, ldb);
   else
-    gemv_kernel<NT, false><<<grid, 256, 0, s>>>((const uint4*)x16, kpc, (int)M, wc, ws, (int)N, (int)K, gsx, gsw,
-                                                (uint8_t*)y, ldb);
+    gemv_kernel<NT, kA16, false><<<grid, 256, 0, s>>>((const uint4*)x, kpc, (int)M, wc, ws, (int)N, (int)K, gsx,
+                                                      gsw, (uint8_t*)y, ldb);
 }
 
-void launch_gemv(const void* x16, int64_t M, int64_t Kp, const uint8_t* wc, const uint8_t* ws, int64_t N, int64_t K,
-                 const float* gsx, const float* gsw, void* y, bool y_bf16, int64_t ld_y, hipStream_t s) {
+template <bool kA16>
+static void gemv_go(const void* x16, size_t ld_x_bytes, int64_t M, const uint8_t* wc, const uint8_t* ws, int64_t N,
+                    int64_t K, const float* gsx, const float* gsw, void* y, bool y_bf16, int64_t ld_y,
+                    hipStream_t s) {
+  const uint32_t ldx = (uint32_t)ld_x_bytes;
   if (M > 4 && M <= 16 && K >= 512 && K <= 512 * kKsMaxWaves && K % 512 == 0 &&
       (uint64_t)N * (uint64_t)K / 2 < (1ull << 32)) {
     static int cus = 0;
@@ -568,13 +576,12 @@ void launch_gemv(const void* x16, int64_t M, int64_t Kp, const uint8_t* wc, cons
       grid = grid > need ? grid : need;
       const int threads = waves * 64;
       const size_t ldb = (size_t)ld_y * (y_bf16 ? 2u : 4u);
-      const uint32_t ldx = (uint32_t)(Kp * 2);
       if (y_bf16)
-        gemv_ksplit_kernel<true><<<grid, threads, 0, s>>>((const uint8_t*)x16, ldx, (int)M, wc, ws, (int)N, (int)K,
-                                                         tiles, gsx, gsw, (uint8_t*)y, ldb);
+        gemv_ksplit_kernel<kA16, true><<<grid, threads, 0, s>>>((const uint8_t*)x16, ldx, (int)M, wc, ws, (int)N,
+                                                               (int)K, tiles, gsx, gsw, (uint8_t*)y, ldb);
       else
-        gemv_ksplit_kernel<false><<<grid, threads, 0, s>>>((const uint8_t*)x16, ldx, (int)M, wc, ws, (int)N,
-                                                          (int)K, tiles, gsx, gsw, (uint8_t*)y, ldb);
+        gemv_ksplit_kernel<kA16, false><<<grid, threads, 0, s>>>((const uint8_t*)x16, ldx, (int)M, wc, ws, (int)N,
+                                                                (int)K, tiles, gsx, gsw, (uint8_t*)y, ldb);
       return;
     }
   }
@@ -582,15 +589,15 @@ void launch_gemv(const void* x16, int64_t M, int64_t Kp, const uint8_t* wc, cons
   if (gp.depth) {
     const int tiles = (int)((N + 15) / 16);
     const size_t ldb = (size_t)ld_y * (y_bf16 ? 2u : 4u);
-    const uint32_t ldx = (uint32_t)(Kp * 2);
     auto go = [&](auto dc, auto xc) {
       constexpr int D = decltype(dc)::value, XI = decltype(xc)::value;
       if (y_bf16)
-        gemv_stream_kernel<D, XI, true><<<tiles, 64, gp.lds, s>>>((const uint8_t*)x16, ldx, (int)M, wc, ws, (int)N,
-                                                                  (int)K, gsx, gsw, (uint8_t*)y, ldb);
+        gemv_stream_kernel<D, XI, kA16, true><<<tiles, 64, gp.lds, s>>>((const uint8_t*)x16, ldx, (int)M, wc, ws,
+                                                                        (int)N, (int)K, gsx, gsw, (uint8_t*)y, ldb);
       else
-        gemv_stream_kernel<D, XI, false><<<tiles, 64, gp.lds, s>>>((const uint8_t*)x16, ldx, (int)M, wc, ws,
-                                                                   (int)N, (int)K, gsx, gsw, (uint8_t*)y, ldb);
+        gemv_stream_kernel<D, XI, kA16, false><<<tiles, 64, gp.lds, s>>>((const uint8_t*)x16, ldx, (int)M, wc, ws,
+                                                                         (int)N, (int)K, gsx, gsw, (uint8_t*)y,
+                                                                         ldb);
     };
     using I1 = std::integral_constant<int, 1>;
     using I2 = std::integral_constant<int, 2>;
@@ -605,22 +612,30 @@ void launch_gemv(const void* x16, int64_t M, int64_t Kp, const uint8_t* wc, cons
   if (M > 4 && M <= 16 && K >= 256 && K % 256 == 0 && (uint64_t)N * (uint64_t)K / 2 < (1ull << 32)) {
     const int grid = (int)((N + 16 * kGwWaves - 1) / (16 * kGwWaves));
     const size_t ldb = (size_t)ld_y * (y_bf16 ? 2u : 4u);
-    const uint32_t ldx = (uint32_t)(Kp * 2);
     if (y_bf16)
-      gemv_shared_kernel<true><<<grid, kGwWaves * 64, 0, s>>>((const uint8_t*)x16, ldx, (int)M, wc, ws, (int)N,
-                                                               (int)K, gsx, gsw, (uint8_t*)y, ldb);
+      gemv_shared_kernel<kA16, true><<<grid, kGwWaves * 64, 0, s>>>((const uint8_t*)x16, ldx, (int)M, wc, ws,
+                                                                     (int)N, (int)K, gsx, gsw, (uint8_t*)y, ldb);
     else
-      gemv_shared_kernel<false><<<grid, kGwWaves * 64, 0, s>>>((const uint8_t*)x16, ldx, (int)M, wc, ws, (int)N,
-                                                                (int)K, gsx, gsw, (uint8_t*)y, ldb);
+      gemv_shared_kernel<kA16, false><<<grid, kGwWaves * 64, 0, s>>>((const uint8_t*)x16, ldx, (int)M, wc, ws,
+                                                                      (int)N, (int)K, gsx, gsw, (uint8_t*)y, ldb);
     return;
   }
   // One 16-row tile per workgroup keeps the grid fine-grained when the
   // activations are few; more rows per workgroup amortise the activation
   // reads when M is larger.
   if (M <= 4)
-    gemv_nt<1>(x16, M, Kp, wc, ws, N, K, gsx, gsw, y, y_bf16, ld_y, s);
+    gemv_nt<1, kA16>(x16, ld_x_bytes, M, wc, ws, N, K, gsx, gsw, y, y_bf16, ld_y, s);
   else
-    gemv_nt<4>(x16, M, Kp, wc, ws, N, K, gsx, gsw, y, y_bf16, ld_y, s);
+    gemv_nt<4, kA16>(x16, ld_x_bytes, M, wc, ws, N, K, gsx, gsw, y, y_bf16, ld_y, s);
+}
+
+void launch_gemv(bool a16, const void* x, size_t ld_x_bytes, int64_t M, int64_t K, const uint8_t* wc,
+                 const uint8_t* ws, int64_t N, const float* gsx, const float* gsw, void* y, bool y_bf16,
+                 int64_t ld_y, hipStream_t s) {
+  if (a16)
+    gemv_go<true>(x, ld_x_bytes, M, wc, ws, N, K, gsx, gsw, y, y_bf16, ld_y, s);
+  else
+    gemv_go<false>(x, ld_x_bytes, M, wc, ws, N, K, gsx, gsw, y, y_bf16, ld_y, s);
 }
 
 }  // namespace nvfp4

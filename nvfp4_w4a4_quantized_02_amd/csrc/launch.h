@@ -81,12 +81,16 @@ void launch_dequant(const uint8_t* codes, const uint8_t* scales, const float* gs
                     void* out, bool out_bf16, int64_t ld_out, hipStream_t s);
 void launch_fuse_rescale(const RescaleArgs& a, hipStream_t s);
 
-// C[m, n] = (sum_k X16[m, k] * W[n, k]) * gs_x * gs_w for the prefill tile
-// kernel (M > kGemvMaxM) and the small-M kernel.
-void launch_gemm(const void* x16, int64_t M, int64_t Kp, const uint8_t* wc, const uint8_t* ws, int64_t N, int64_t K,
-                 const float* gsx, const float* gsw, void* y, bool y_bf16, int64_t ld_y, float* partials,
-                 hipStream_t s);
-void launch_gemv(const void* x16, int64_t M, int64_t Kp, const uint8_t* wc, const uint8_t* ws, int64_t N, int64_t K,
-                 const float* gsx, const float* gsw, void* y, bool y_bf16, int64_t ld_y, hipStream_t s);
+// C[m, n] = (sum_k X[m, k] * W[n, k]) * scale for the prefill tile kernel
+// (M > kGemvMaxM) and the small-M kernels; K % 64 == 0.  a16 = false: X is
+// the fp16 expansion of the quantized activations and scale = gs_x * gs_w
+// (W4A4); a16 = true: X is the caller's bf16 tensor and scale = gs_w (W4A16,
+// gsx unused).  ld_x_bytes: bytes between rows of X, a multiple of 16.
+void launch_gemm(bool a16, const void* x, size_t ld_x_bytes, int64_t M, int64_t K, const uint8_t* wc,
+                 const uint8_t* ws, int64_t N, const float* gsx, const float* gsw, void* y, bool y_bf16,
+                 int64_t ld_y, float* partials, hipStream_t s);
+void launch_gemv(bool a16, const void* x, size_t ld_x_bytes, int64_t M, int64_t K, const uint8_t* wc,
+                 const uint8_t* ws, int64_t N, const float* gsx, const float* gsw, void* y, bool y_bf16,
+                 int64_t ld_y, hipStream_t s);
 
 }  // namespace nvfp4

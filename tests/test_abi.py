@@ -178,3 +178,31 @@ def test_gemm_static_rejects(nv):
     assert L.nvfp4_gemm_prepare_static(A, BF16, 32, 64, 64, A, A + 16, BIG, None) == E_WS
     assert L.nvfp4_gemm_prepare_static(A, BF16, 32, 64, 64, A, A, 100, None) == E_WS
     assert L.nvfp4_gemm_prepare_static(A, BF16, 0, 64, 64, A, A, BIG, None) == OK
+
+
+def w16(nv, x=A, dt=BF16, M=32, K=64, ld=64, wc=A, wsc=A, wg=A, N=64, y=A, ydt=BF16, ldy=64, ws=A, nws=BIG):
+    return nv.lib.nvfp4_gemm_w4a16(x, dt, M, K, ld, wc, wsc, wg, N, y, ydt, ldy, ws, nws, None)
+
+
+def test_gemm_w4a16_rejects(nv):
+    L = nv.lib
+    assert w16(nv, dt=F32) == E_DTYPE                  # 16-bit activations only
+    assert w16(nv, dt=2) == E_DTYPE
+    assert w16(nv, ydt=7) == E_DTYPE
+    assert w16(nv, K=48, ld=48) == E_SHAPE
+    assert w16(nv, N=-1) == E_SHAPE
+    assert w16(nv, ldy=32) == E_SHAPE
+    assert w16(nv, x=None) == E_NULL
+    assert w16(nv, wg=None) == E_NULL
+    assert w16(nv, wc=None) == E_NULL
+    assert w16(nv, y=A + 8) == E_ALIGN
+    assert w16(nv, x=A + 8) == E_ALIGN
+    assert w16(nv, wc=A + 8) == E_ALIGN
+    assert w16(nv, M=0) == OK
+    assert w16(nv, N=0) == OK
+    # decode sizes need no workspace; the tile GEMM needs one for its split-K tail
+    assert L.nvfp4_gemm_w4a16_workspace_size(16, 34816, 5120) == 0
+    need = L.nvfp4_gemm_w4a16_workspace_size(4096, 17408, 5120)
+    assert need == L.nvfp4_gemm_workspace_size(4096, 17408, 5120) - L.nvfp4_gemm_workspace_size(4096, 0, 5120)
+    assert w16(nv, M=4096, K=5120, ld=5120, N=17408, ldy=17408, ws=None, nws=0) == E_WS
+    assert w16(nv, M=4096, K=5120, ld=5120, N=17408, ldy=17408, nws=need - 1) == E_WS

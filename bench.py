@@ -14,7 +14,9 @@ last-level cache cannot hold them), the standalone activation quantize at
 long prefill (X[32768x5120], GB/s on the two-pass byte count), the fused
 q/k/v repair + GEMM and the offline weight quantize.  The decode and quantize
 lines also time the calibrated-scale form (the activation tensor scale given,
-no absmax pass) under "calibrated_scale".
+no absmax pass) under "calibrated_scale", and the decode lines the W4A16 form
+(bf16 activations as given, one GEMV launch) under "w4a16"; a separate line
+times W4A16 at the prefill shape.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 """
@@ -44,6 +46,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--headline-only", action="store_true",
                     help="skip the secondary workloads (profiling runs)")
+    ap.add_argument("--no-numerics", action="store_true",
+                    help="skip the input statistics and fake-quantization errors")
     ap.add_argument("--no-box-peaks", action="store_true",
                     help="skip the box-measured reference rates (device copy, torch fp16 GEMM)")
     ap.add_argument("--copy-ref", action="store_true",
@@ -191,9 +195,37 @@ def main():
                      "frac": round(gemm_tflops / PEAK_FP16_TFLOPS, 4), "traffic": traffic,
                      "algorithmic": "2*M*N*K = %.4g flop per launch" % flops},
     }
+    also = []
+    if not args.headline_only:
+        # W4A16: the same weights against the bf16 activations as given
+        wsz16 = nv.lib.nvfp4_gemm_w4a16_workspace_size(M, N, K)
+        ws16 = torch.empty(max(wsz16, 256), dtype=torch.uint8, device=dev)
+
+        def step16(i, mark):
+            mark(0)
+            st = nv.lib.nvfp4_gemm_w4a16(x.data_ptr(), 1, M, K, K, wc.data_ptr(), ws.data_ptr(), wg.data_ptr(), N,
+                                         y.data_ptr(), 1, N, ws16.data_ptr(), ws16.numel(),
+                                         torch.cuda.current_stream().cuda_stream)
+            assert st == 0
+            mark(1)
+
+        _, (w16_ms,) = time_steps(torch, args.steps, args.warmup, step16, 1)
+        t16 = flops / (mean(w16_ms) * 1e-3) / 1e12
+        also.append({"metric": "W4A16 GEMM TFLOP/s at M=4096", "value": round(t16, 2), "unit": "TFLOP/s",
+                     "ms_per_step": round(mean(w16_ms), 4),
+                     "config": {"workload": "prefill W4A16 linear: X[4096x5120] bf16 Student-t(3) as given x "
+                                            "W[17408x5120] NVFP4 -> Y bf16"},
+                     "roofline": {"bound": "mfma", "kernel": "nvfp4_gemm_w4a16: gemm_kernel (bf16 MFMA 32x32x16) "
+                                                              "+ split-K reduce",
+                                  "achieved": round(t16, 2), "peak": PEAK_FP16_TFLOPS, "unit": "TFLOP/s",
+                                  "frac": round(t16 / PEAK_FP16_TFLOPS, 4),
+                                  "traffic": traffic_for("gemm_prefill_w4a16", sha_gemm)}})
+        log("W4A16 prefill: %.1f TFLOP/s" % t16)
+        del ws16
+        if not args.no_numerics:
+            out["numerics"] = numerics(torch, nv, workloads, to_gpu, dev, p, x, wc, ws, wg)
     del y, x
 
-    also = []
     if not args.headline_only:
         also += secondary(torch, np, nv, workloads, to_gpu, dev, args)
 
@@ -252,6 +284,15 @@ def secondary(torch, np, nv, workloads, to_gpu, dev, args):
             mark(2)
 
         _, (sprep_ms, srun_ms) = time_steps(torch, max(steps, 40), warmup + 8, sstep, 2)
+
+        # W4A16: one GEMV launch on the bf16 activations as given
+        def w16step(i, mark, x=x, y=y):
+            c, s = copies[i % R]
+            mark(0)
+            nv.nvfp4_gemm_w4a16(x, c, s, shared, out=y)
+            mark(1)
+
+        _, (w16_ms,) = time_steps(torch, max(steps, 40), warmup + 8, w16step, 1)
         nbytes = wbytes + M * K * 2 + M * N * 2
         step_ms = mean(prep_ms) + mean(run_ms)
         gbs = nbytes / (step_ms * 1e-3) / 1e9
@@ -260,6 +301,11 @@ def secondary(torch, np, nv, workloads, to_gpu, dev, args):
                     "ms_per_step": round(step_ms, 5), "wall_ms_per_step": round(wall, 5),
                     "phases_ms": {"activation_quantize": round(mean(prep_ms), 5),
                                   "gemv": round(mean(run_ms), 5)},
+                    "w4a16": {"ms_per_step": round(mean(w16_ms), 5),
+                              "GBs": round(nbytes / (mean(w16_ms) * 1e-3) / 1e9, 1),
+                              "frac": round(nbytes / (mean(w16_ms) * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                              "traffic": traffic_for("gemv_m%d_w4a16" % M, source_sha("gemv.hip", "encode.h",
+                                                                                      "common.h", "mfma_util.h"))},
                     "calibrated_scale": {"ms_per_step": round(mean(sprep_ms) + mean(srun_ms), 5),
                                          "activation_quantize_ms": round(mean(sprep_ms), 5),
                                          "GBs": round(nbytes / ((mean(sprep_ms) + mean(srun_ms)) * 1e-3) / 1e9,
@@ -272,7 +318,8 @@ def secondary(torch, np, nv, workloads, to_gpu, dev, args):
                                                                                    "common.h", "mfma_util.h")),
                                  "algorithmic": "W codes+scales %d B + X + Y = %d B per launch" % (wbytes,
                                                                                                   nbytes)}})
-        log("decode M=%d: %.1f GB/s step, %.1f GB/s kernel" % (M, gbs, kgbs))
+        log("decode M=%d: %.1f GB/s step, %.1f GB/s kernel, W4A16 %.1f GB/s" %
+            (M, gbs, kgbs, nbytes / (mean(w16_ms) * 1e-3) / 1e9))
     del copies
 
     # ------------------------------------------------ fused q/k/v repair + GEMM
@@ -373,6 +420,9 @@ def secondary(torch, np, nv, workloads, to_gpu, dev, args):
                              "algorithmic": "2 reads of X + codes + scales = %d B per call" % two_pass}})
     log("quantize: %.1f GB/s (two-pass count); calibrated scale %.1f GB/s (one read)"
         % (qgbs, single / (mean(sq_ms) * 1e-3) / 1e9))
+    if not args.no_numerics:
+        from nvfp4_w4a4_quantized_02_amd import stats
+        res[-1]["input_stats"] = {**stats.tensor_stats(xl), "a4": stats.fake_quant_error(xl)}
     del xl, codes, scl
 
     # ------------------------------------------------ offline weight quantize (fp32 in)
@@ -389,6 +439,33 @@ def secondary(torch, np, nv, workloads, to_gpu, dev, args):
                 "value": round(wb / (mean(w_ms) * 1e-3) / 1e9, 1), "unit": "GB/s",
                 "ms_per_step": round(mean(w_ms), 4),
                 "config": {"workload": "offline weight quantize W[17408x5120] fp32 N(0,0.02)"}})
+    return res
+
+
+# Paper "Why Gated DeltaNet Survives 4-Bit Quantization", section 5.1, Table 2
+# (medians over layers of captured activations; weights near-Gaussian).
+PAPER_MEDIANS = {"max_over_rms": 63.5, "kurtosis": 1560, "hot_channel_ratio": 100,
+                 "one_hot_block_share": [0.10, 0.32], "a4_rel_error": [0.075, 0.092],
+                 "w4_rel_error": [0.105, 0.119]}
+
+
+def numerics(torch, nv, workloads, to_gpu, dev, p, x, wc, ws, wg):
+    """Where the synthetic inputs sit against the paper's statistics, and
+    the fake-quantization and GEMM errors they give."""
+    from nvfp4_w4a4_quantized_02_amd import stats
+    log("numerics: input statistics and fake-quantization errors")
+    res = {"paper_medians": PAPER_MEDIANS}
+    w32 = torch.from_numpy(p.w_parts[0]).to(dev)
+    res["prefill_x"] = {**stats.tensor_stats(x), "a4": stats.fake_quant_error(x)}
+    res["prefill_w"] = {**stats.tensor_stats(w32), "w4": stats.fake_quant_error(w32)}
+    yref = x.float() @ w32.t()
+    y44 = nv.nvfp4_gemm(x, wc, ws, wg, out_dtype=torch.float32)
+    y416 = nv.nvfp4_gemm_w4a16(x, wc, ws, wg, out_dtype=torch.float32)
+    res["prefill_gemm_rel_error"] = {"w4a4": stats.gemm_error(y44, yref), "w4a16": stats.gemm_error(y416, yref),
+                                     "reference": "fp32 X.W^T of the unquantized bf16 X and fp32 W"}
+    del yref, y44, y416, w32
+    xd = to_gpu(workloads.decode(M=16, N_each=1).x)
+    res["decode_x_m16"] = {**stats.tensor_stats(xd), "a4": stats.fake_quant_error(xd)}
     return res
 
 

@@ -2,7 +2,8 @@
 
 A plain CPU statement of the NVFP4 W4A4 linear layer (quantize, dequantize,
 fused-module repair, exact block-scaled GEMM) and of the W4A16 form of the
-same weights against 16-bit activations, written in C
+same weights against 16-bit activations, plus FP8 E4M3 with one per-tensor
+scale (quantize, dequantize, W8A16 and W8A8 products), written in C
 (``nvfp4_oracle.c``) and wrapped here with ctypes over numpy arrays.  Only the
 tests, ``__graft_entry__.smoke()`` and the CPU-baseline leg of ``bench.py`` may
 import it.  It shares nothing with the HIP library in
@@ -79,6 +80,12 @@ def lib() -> ctypes.CDLL:
         L.orc_num_threads.restype = ctypes.c_int
         L.orc_gemm_w4a16.argtypes = [P, ctypes.c_int, I64, I64, I64, P, P, ctypes.c_float, I64, P]
         L.orc_gemm_w4a16_sampled.argtypes = [P, ctypes.c_int, I64, I64, P, P, ctypes.c_float, I64, P, P, P]
+        L.orc_fp8_tensor_scale.argtypes = [P, ctypes.c_int, I64, I64, I64]
+        L.orc_fp8_tensor_scale.restype = ctypes.c_float
+        L.orc_fp8_quantize_with_scale.argtypes = [P, ctypes.c_int, I64, I64, I64, ctypes.c_float, P]
+        L.orc_fp8_dequantize.argtypes = [P, ctypes.c_float, I64, I64, P]
+        L.orc_gemm_w8a16.argtypes = [P, ctypes.c_int, I64, I64, I64, P, ctypes.c_float, I64, P]
+        L.orc_gemm_w8a8.argtypes = [P, ctypes.c_float, P, ctypes.c_float, I64, I64, I64, P]
         _lib = L
     return _lib
 
@@ -252,6 +259,54 @@ def gemm_w4a16_sampled(x, wc, ws, gsw, m_idx, n_idx) -> np.ndarray:
     y = np.empty(m_idx.shape, dtype=np.float64)
     lib().orc_gemm_w4a16_sampled(_ptr(xa), is_bf16, K, K, _ptr(wc), _ptr(ws), float(np.float32(gsw)),
                                  m_idx.size, _ptr(m_idx), _ptr(n_idx), _ptr(y))
+    return y
+
+
+def fp8_tensor_scale(x) -> np.float32:
+    xa, is_bf16 = _as_input(x)
+    rows, K = xa.shape
+    return np.float32(lib().orc_fp8_tensor_scale(_ptr(xa), is_bf16, rows, K, K))
+
+
+def fp8_quantize(x, scale: float | None = None):
+    """FP8 E4M3 with one per-tensor scale: returns (bytes uint8 [rows, K],
+    scale float32); the scale is RN(amax / 448) unless given."""
+    xa, is_bf16 = _as_input(x)
+    rows, K = xa.shape
+    s = fp8_tensor_scale(xa) if scale is None else np.float32(scale)
+    q = np.zeros((rows, K), dtype=np.uint8)
+    lib().orc_fp8_quantize_with_scale(_ptr(xa), is_bf16, rows, K, K, float(s), _ptr(q))
+    return q, s
+
+
+def fp8_dequantize(q, scale) -> np.ndarray:
+    q = np.ascontiguousarray(q)
+    rows, K = q.shape
+    out = np.empty((rows, K), dtype=np.float32)
+    lib().orc_fp8_dequantize(_ptr(q), float(np.float32(scale)), rows, K, _ptr(out))
+    return out
+
+
+def gemm_w8a16(x, wq, sw) -> np.ndarray:
+    """y = x . (E4M3(wq) * sw)^T as fp64 [M, N]; x float32 or bf16 bits."""
+    xa, is_bf16 = _as_input(x)
+    wq = np.ascontiguousarray(wq)
+    M, K = xa.shape
+    N = wq.shape[0]
+    assert wq.shape[1] == K
+    y = np.empty((M, N), dtype=np.float64)
+    lib().orc_gemm_w8a16(_ptr(xa), is_bf16, M, K, K, _ptr(wq), float(np.float32(sw)), N, _ptr(y))
+    return y
+
+
+def gemm_w8a8(xq, sx, wq, sw) -> np.ndarray:
+    """Exact y = (E4M3(xq) * sx) . (E4M3(wq) * sw)^T as fp64 [M, N]."""
+    xq, wq = np.ascontiguousarray(xq), np.ascontiguousarray(wq)
+    M, K = xq.shape
+    N = wq.shape[0]
+    assert wq.shape[1] == K
+    y = np.empty((M, N), dtype=np.float64)
+    lib().orc_gemm_w8a8(_ptr(xq), float(np.float32(sx)), _ptr(wq), float(np.float32(sw)), M, N, K, _ptr(y))
     return y
 
 

@@ -431,6 +431,106 @@ void orc_gemm_w4a16_sampled(const void *x, int is_bf16, int64_t K, int64_t ld, c
                          K, gsw);
 }
 
+/* ---------------------------------------------------------------------- */
+/* FP8 E4M3 with one per-tensor scale (model card                          */
+/* "Gemma-4-31B-IT-NVFP4-FP8attn-text", section "What was quantized,        */
+/* exactly": per-tensor scale, float8_e4m3, weights only, served W8A16;    */
+/* paper section 7 "KV-cache precision": FP8 KV cache with static           */
+/* per-tensor scales).                                                      */
+/*                                                                          */
+/* Readings where the pages are silent:                                     */
+/*   F1 dynamic scale s = RN(amax / 448), the dequant form (largest byte    */
+/*      0x7E), as R1 for NVFP4; a static scale is given by the caller.      */
+/*   F2 byte = signbit(x) << 7 | E4M3_RNE_sat(RN(|x| / s)) (a divide, as    */
+/*      R3); s == 0 gives magnitude 0.                                      */
+/*   F3 dequant x = RN(E4M3(byte) * s).                                     */
+/* ---------------------------------------------------------------------- */
+
+float orc_fp8_tensor_scale(const void *x, int is_bf16, int64_t rows, int64_t K, int64_t ld)
+{
+    float amax = 0.0f;
+    int64_t r;
+#pragma omp parallel for schedule(static) reduction(max : amax)
+    for (r = 0; r < rows; ++r) {
+        int64_t k;
+        for (k = 0; k < K; ++k) {
+            float a = fabsf(load_elem(x, is_bf16, ld, r, k));
+            if (a > amax)
+                amax = a;
+        }
+    }
+    return amax / 448.0f; /* F1 */
+}
+
+void orc_fp8_quantize_with_scale(const void *x, int is_bf16, int64_t rows, int64_t K, int64_t ld, float s,
+                                 uint8_t *q)
+{
+    int64_t r;
+#pragma omp parallel for schedule(static)
+    for (r = 0; r < rows; ++r) {
+        int64_t k;
+        for (k = 0; k < K; ++k) {
+            float xv = load_elem(x, is_bf16, ld, r, k);
+            unsigned mag = 0;
+            if (s != 0.0f)
+                mag = orc_e4m3_encode(fabsf(xv) / s); /* F2 */
+            q[r * K + k] = (uint8_t)((signbit(xv) ? 0x80u : 0u) | mag);
+        }
+    }
+}
+
+void orc_fp8_dequantize(const uint8_t *q, float s, int64_t rows, int64_t K, float *out)
+{
+    int64_t i;
+#pragma omp parallel for schedule(static)
+    for (i = 0; i < rows * K; ++i)
+        out[i] = (float)(orc_e4m3_decode(q[i]) * (double)s); /* F3: one rounding of the exact product */
+}
+
+/* W8A16: y[m, n] = s_w * sum_k x[m, k] * E4M3(wq[n, k]); products exact in
+ * fp64 (24 + 4 significant bits), summed in fp64 in k order. */
+static double dot_w8a16(const void *x, int is_bf16, int64_t ld, int64_t m, const uint8_t *wq, int64_t K,
+                        float sw)
+{
+    int64_t k;
+    double acc = 0.0;
+    for (k = 0; k < K; ++k)
+        acc += (double)load_elem(x, is_bf16, ld, m, k) * orc_e4m3_decode(wq[k]);
+    return acc * (double)sw;
+}
+
+void orc_gemm_w8a16(const void *x, int is_bf16, int64_t M, int64_t K, int64_t ld, const uint8_t *wq, float sw,
+                    int64_t N, double *y)
+{
+    int64_t m;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (m = 0; m < M; ++m) {
+        int64_t n;
+        for (n = 0; n < N; ++n)
+            y[m * N + n] = dot_w8a16(x, is_bf16, ld, m, wq + n * K, K, sw);
+    }
+}
+
+/* W8A8, exact: every E4M3 value is an integer times 2^-9 below 2^18 in
+ * magnitude, so a K-long sum of products is exact in int64 for K < 2^27;
+ * y = sum * 2^-18 * s_x * s_w in fp64. */
+void orc_gemm_w8a8(const uint8_t *xq, float sx, const uint8_t *wq, float sw, int64_t M, int64_t N, int64_t K,
+                   double *y)
+{
+    int64_t m;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (m = 0; m < M; ++m) {
+        int64_t n, k;
+        for (n = 0; n < N; ++n) {
+            int64_t acc = 0;
+            for (k = 0; k < K; ++k)
+                acc += (int64_t)(512.0 * orc_e4m3_decode(xq[m * K + k])) *
+                       (int64_t)(512.0 * orc_e4m3_decode(wq[n * K + k]));
+            y[m * N + n] = ldexp((double)acc, -18) * (double)sx * (double)sw;
+        }
+    }
+}
+
 int orc_num_threads(void)
 {
 #ifdef _OPENMP

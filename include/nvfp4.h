@@ -263,6 +263,38 @@ nvfp4_status_t nvfp4_gemm_w4a16(const void *x, nvfp4_dtype_t x_dtype, int64_t M,
                                 int64_t N, void *y, nvfp4_dtype_t y_dtype, int64_t ld_y, void *workspace,
                                 size_t workspace_bytes, void *stream);
 
+/* ----------------------------------------------------------------------
+ * FP8 E4M3 with one per-tensor scale.  The model card
+ * "Gemma-4-31B-IT-NVFP4-FP8attn-text", section "What was quantized,
+ * exactly", stores attention weights as float8_e4m3 with one scale per
+ * tensor; the paper's section 7 "KV-cache precision" stores the KV cache in
+ * FP8 with static (calibrated) per-tensor scales.
+ *
+ * Byte = sign(x) << 7 | E4M3(RN(|x| / s)), E4M3 rounding to nearest even and
+ * saturating at 448 (0x7E); s == 0 keeps only sign bits.  Dequant value =
+ * RN(E4M3(byte) * s).  Bytes are [rows, K] contiguous (row stride K), q
+ * 16-byte aligned; K % 16 == 0.  x as in nvfp4_quantize.
+ *
+ * nvfp4_fp8_quantize: s = RN(amax / 448) over the whole tensor, written to
+ *   *scale (device float); workspace of nvfp4_fp8_quantize_workspace_size
+ *   bytes, 256-byte aligned.  rows == 0 or K == 0 writes scale 0.
+ * nvfp4_fp8_quantize_static: s = *scale (device float, finite and >= 0),
+ *   e.g. a calibrated KV-cache scale; no workspace, nothing else written.
+ * nvfp4_fp8_dequantize: out [rows, ld_out] fp32, or bf16 (the RNE of the
+ *   fp32 value), 16-byte aligned rows.
+ * ---------------------------------------------------------------------- */
+size_t nvfp4_fp8_quantize_workspace_size(int64_t rows, int64_t K);
+
+nvfp4_status_t nvfp4_fp8_quantize(const void *x, nvfp4_dtype_t x_dtype, int64_t rows, int64_t K, int64_t ld_x,
+                                  uint8_t *q, float *scale, void *workspace, size_t workspace_bytes,
+                                  void *stream);
+
+nvfp4_status_t nvfp4_fp8_quantize_static(const void *x, nvfp4_dtype_t x_dtype, int64_t rows, int64_t K,
+                                         int64_t ld_x, const float *scale, uint8_t *q, void *stream);
+
+nvfp4_status_t nvfp4_fp8_dequantize(const uint8_t *q, const float *scale, int64_t rows, int64_t K, void *out,
+                                    nvfp4_dtype_t out_dtype, int64_t ld_out, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

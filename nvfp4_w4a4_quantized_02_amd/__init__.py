@@ -42,6 +42,7 @@ EXPORTS = (
     "nvfp4_dequantize", "nvfp4_fuse_rescale", "nvfp4_gemm_workspace_size", "nvfp4_gemm",
     "nvfp4_gemm_prepare", "nvfp4_gemm_run", "nvfp4_quantize_static", "nvfp4_gemm_prepare_static",
     "nvfp4_gemm_static", "nvfp4_gemm_w4a16_workspace_size", "nvfp4_gemm_w4a16",
+    "nvfp4_fp8_quantize_workspace_size", "nvfp4_fp8_quantize", "nvfp4_fp8_quantize_static", "nvfp4_fp8_dequantize",
 )
 
 
@@ -87,6 +88,14 @@ def _load() -> ctypes.CDLL:
     L.nvfp4_gemm_w4a16_workspace_size.restype = SZ
     L.nvfp4_gemm_w4a16.argtypes = [P, I, I64, I64, I64, P, P, P, I64, P, I, I64, P, SZ, P]
     L.nvfp4_gemm_w4a16.restype = I
+    L.nvfp4_fp8_quantize_workspace_size.argtypes = [I64, I64]
+    L.nvfp4_fp8_quantize_workspace_size.restype = SZ
+    L.nvfp4_fp8_quantize.argtypes = [P, I, I64, I64, I64, P, P, P, SZ, P]
+    L.nvfp4_fp8_quantize.restype = I
+    L.nvfp4_fp8_quantize_static.argtypes = [P, I, I64, I64, I64, P, P, P]
+    L.nvfp4_fp8_quantize_static.restype = I
+    L.nvfp4_fp8_dequantize.argtypes = [P, P, I64, I64, P, I, I64, P]
+    L.nvfp4_fp8_dequantize.restype = I
     _check_single_hip_runtime()
     return L
 
@@ -312,7 +321,32 @@ def nvfp4_gemm_w4a16(x: torch.Tensor, w_codes: torch.Tensor, w_scales: torch.Ten
     return out
 
 
+def nvfp4_fp8_quantize(x: torch.Tensor, scale: torch.Tensor | None = None):
+    """FP8 E4M3 with one per-tensor scale.  Returns (bytes uint8 [rows, K],
+    scale float32 [1]): the scale is RN(amax / 448) unless a device scale
+    (float32 [1], e.g. a calibrated KV-cache scale) is given."""
+    rows, K, ld = _rows_view(x)
+    q = torch.empty((rows, K), dtype=torch.uint8, device=x.device)
+    if scale is None:
+        s = torch.empty(1, dtype=torch.float32, device=x.device)
+        ws = workspace(lib.nvfp4_fp8_quantize_workspace_size(rows, K), x.device)
+        _check(lib.nvfp4_fp8_quantize(x.data_ptr(), _dtype_code(x.dtype), rows, K, ld, q.data_ptr(), s.data_ptr(),
+                                      ws.data_ptr(), ws.numel(), _stream_ptr(x.device)), "nvfp4_fp8_quantize")
+        return q, s
+    _check(lib.nvfp4_fp8_quantize_static(x.data_ptr(), _dtype_code(x.dtype), rows, K, ld, scale.data_ptr(),
+                                         q.data_ptr(), _stream_ptr(x.device)), "nvfp4_fp8_quantize_static")
+    return q, scale
+
+
+def nvfp4_fp8_dequantize(q: torch.Tensor, scale: torch.Tensor, out_dtype: torch.dtype = torch.float32):
+    rows, K = q.shape
+    out = torch.empty((rows, K), dtype=out_dtype, device=q.device)
+    _check(lib.nvfp4_fp8_dequantize(q.data_ptr(), scale.data_ptr(), rows, K, out.data_ptr(), _dtype_code(out_dtype),
+                                    K, _stream_ptr(q.device)), "nvfp4_fp8_dequantize")
+    return out
+
+
 __all__ = ["nvfp4_quantize", "nvfp4_quantize_static", "nvfp4_dequantize", "nvfp4_fuse_rescale", "nvfp4_gemm",
-           "nvfp4_gemm_w4a16",
+           "nvfp4_gemm_w4a16", "nvfp4_fp8_quantize", "nvfp4_fp8_dequantize",
            "nvfp4_gemm_prepare", "nvfp4_gemm_run", "PreparedActivations", "Nvfp4Error",
            "status_string", "lib", "EXPORTS", "LIB_PATH", "workspace"]

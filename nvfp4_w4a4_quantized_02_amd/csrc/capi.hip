@@ -278,6 +278,55 @@ nvfp4_status_t nvfp4_gemm_static(const void* x, nvfp4_dtype_t x_dtype, int64_t M
   return nvfp4_gemm_run(M, K, w_codes, w_scales, w_gs, N, y, y_dtype, ld_y, workspace, workspace_bytes, stream);
 }
 
+size_t nvfp4_fp8_quantize_workspace_size(int64_t rows, int64_t K) { return nvfp4_quantize_workspace_size(rows, K); }
+
+nvfp4_status_t nvfp4_fp8_quantize(const void* x, nvfp4_dtype_t x_dtype, int64_t rows, int64_t K, int64_t ld_x,
+                                  uint8_t* q, float* scale, void* workspace, size_t workspace_bytes, void* stream) {
+  nvfp4_status_t st = check_input(x, x_dtype, rows, K, ld_x);
+  if (st != NVFP4_OK) return st;
+  if (!scale) return NVFP4_ERR_NULL;
+  hipStream_t s = (hipStream_t)stream;
+  if (rows == 0 || K == 0) {
+    launch_fill_f32(scale, 0.0f, s);
+    return launched();
+  }
+  if (!q) return NVFP4_ERR_NULL;
+  if (!aligned(q, 16)) return NVFP4_ERR_ALIGN;
+  if (!workspace || !aligned(workspace, 256) || workspace_bytes < nvfp4_fp8_quantize_workspace_size(rows, K))
+    return NVFP4_ERR_WORKSPACE;
+  uint32_t* partials = (uint32_t*)((char*)workspace + kWsPartials);
+  const bool xb = x_dtype == NVFP4_BF16;
+  const int np = launch_amax(x, xb, rows, K, ld_x, partials, s);
+  launch_fp8_quantize(x, xb, rows, K, ld_x, partials, np, nullptr, q, scale, s);
+  return launched();
+}
+
+nvfp4_status_t nvfp4_fp8_quantize_static(const void* x, nvfp4_dtype_t x_dtype, int64_t rows, int64_t K,
+                                         int64_t ld_x, const float* scale, uint8_t* q, void* stream) {
+  nvfp4_status_t st = check_input(x, x_dtype, rows, K, ld_x);
+  if (st != NVFP4_OK) return st;
+  if (!scale) return NVFP4_ERR_NULL;
+  if (rows == 0 || K == 0) return NVFP4_OK;
+  if (!q) return NVFP4_ERR_NULL;
+  if (!aligned(q, 16)) return NVFP4_ERR_ALIGN;
+  launch_fp8_quantize(x, x_dtype == NVFP4_BF16, rows, K, ld_x, nullptr, 0, scale, q, nullptr, (hipStream_t)stream);
+  return launched();
+}
+
+nvfp4_status_t nvfp4_fp8_dequantize(const uint8_t* q, const float* scale, int64_t rows, int64_t K, void* out,
+                                    nvfp4_dtype_t out_dtype, int64_t ld_out, void* stream) {
+  if (!dtype_ok(out_dtype)) return NVFP4_ERR_DTYPE;
+  if (rows < 0 || K < 0 || rows >= kMaxDim || K >= kMaxDim || K % 16 != 0) return NVFP4_ERR_SHAPE;
+  if (rows == 0 || K == 0) return NVFP4_OK;
+  if (!q || !scale || !out) return NVFP4_ERR_NULL;
+  if (ld_out < K) return NVFP4_ERR_SHAPE;
+  if ((uint64_t)rows * (uint64_t)(K / 16) >= kMaxBlocks) return NVFP4_ERR_SHAPE;
+  if (!aligned(q, 16) || !aligned(out, 16) || ((uint64_t)ld_out * esize(out_dtype)) % 16 != 0)
+    return NVFP4_ERR_ALIGN;
+  launch_fp8_dequant(q, scale, rows, K, out, out_dtype == NVFP4_BF16, ld_out, (hipStream_t)stream);
+  return launched();
+}
+
 nvfp4_status_t nvfp4_gemm_w4a16(const void* x, nvfp4_dtype_t x_dtype, int64_t M, int64_t K, int64_t ld_x,
                                 const uint8_t* w_codes, const uint8_t* w_scales, const float* w_gs, int64_t N,
                                 void* y, nvfp4_dtype_t y_dtype, int64_t ld_y, void* workspace,

@@ -81,6 +81,15 @@ void launch_dequant(const uint8_t* codes, const uint8_t* scales, const float* gs
                     void* out, bool out_bf16, int64_t ld_out, hipStream_t s);
 void launch_fuse_rescale(const RescaleArgs& a, hipStream_t s);
 
+// FP8 E4M3 per-tensor quantize: s_in given (static scale), else the absmax
+// partials of launch_amax (npartials > 0) or, when that launched nothing, a
+// one-launch kernel that takes the absmax itself.  s_out may be null.  K % 16
+// == 0; q is [rows, K] contiguous.
+void launch_fp8_quantize(const void* x, bool bf16, int64_t rows, int64_t K, int64_t ld, const uint32_t* partials,
+                         int npartials, const float* s_in, uint8_t* q, float* s_out, hipStream_t s);
+void launch_fp8_dequant(const uint8_t* q, const float* scale, int64_t rows, int64_t K, void* out, bool out_bf16,
+                        int64_t ld_out, hipStream_t s);
+
 // C[m, n] = (sum_k X[m, k] * W[n, k]) * scale for the prefill tile kernel
 // (M > kGemvMaxM) and the small-M kernels; K % 64 == 0.  a16 = false: X is
 // the fp16 expansion of the quantized activations and scale = gs_x * gs_w

@@ -206,3 +206,22 @@ def test_gemm_w4a16_rejects(nv):
     assert need == L.nvfp4_gemm_workspace_size(4096, 17408, 5120) - L.nvfp4_gemm_workspace_size(4096, 0, 5120)
     assert w16(nv, M=4096, K=5120, ld=5120, N=17408, ldy=17408, ws=None, nws=0) == E_WS
     assert w16(nv, M=4096, K=5120, ld=5120, N=17408, ldy=17408, nws=need - 1) == E_WS
+
+
+def test_fp8_rejects(nv):
+    L = nv.lib
+    assert L.nvfp4_fp8_quantize(A, 5, 4, 32, 32, A, A, A, BIG, None) == E_DTYPE
+    assert L.nvfp4_fp8_quantize(A, BF16, 4, 24, 24, A, A, A, BIG, None) == E_SHAPE
+    assert L.nvfp4_fp8_quantize(A, BF16, 4, 32, 32, None, A, A, BIG, None) == E_NULL
+    assert L.nvfp4_fp8_quantize(A, BF16, 4, 32, 32, A, None, A, BIG, None) == E_NULL
+    assert L.nvfp4_fp8_quantize(A, BF16, 4, 32, 32, A + 8, A, A, BIG, None) == E_ALIGN
+    assert L.nvfp4_fp8_quantize(A, BF16, 4, 32, 32, A, A, None, BIG, None) == E_WS
+    assert L.nvfp4_fp8_quantize(A, BF16, 4, 32, 32, A, A, A, 8, None) == E_WS
+    assert L.nvfp4_fp8_quantize_static(A, BF16, 4, 32, 32, None, A, None) == E_NULL
+    assert L.nvfp4_fp8_quantize_static(A, BF16, 4, 32, 32, A, A + 4, None) == E_ALIGN
+    assert L.nvfp4_fp8_quantize_static(A, BF16, 0, 32, 32, A, None, None) == OK
+    assert L.nvfp4_fp8_dequantize(A, A, 4, 32, A, 9, 32, None) == E_DTYPE
+    assert L.nvfp4_fp8_dequantize(A, A, 4, 40, A, F32, 40, None) == E_SHAPE
+    assert L.nvfp4_fp8_dequantize(None, A, 4, 32, A, F32, 32, None) == E_NULL
+    assert L.nvfp4_fp8_dequantize(A, A, 4, 32, A + 4, F32, 32, None) == E_ALIGN
+    assert L.nvfp4_fp8_dequantize(A, A, 0, 32, A, F32, 32, None) == OK

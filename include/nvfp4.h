@@ -250,6 +250,7 @@ nvfp4_status_t nvfp4_gemm_static(const void *x, nvfp4_dtype_t x_dtype, int64_t M
  *            rows; no activation quantization, so no tensor scale for X.
  *   K        a multiple of 64.
  *   w_codes, w_scales, w_gs, N, y, y_dtype, ld_y: as in nvfp4_gemm.
+ *   ld_x     below 2^23 elements (rows are addressed with 32-bit offsets).
  *   workspace: nvfp4_gemm_w4a16_workspace_size(M, N, K) bytes, 256-byte
  *            aligned; it may be NULL when that size is 0 (always for
  *            M <= 16).
@@ -294,6 +295,40 @@ nvfp4_status_t nvfp4_fp8_quantize_static(const void *x, nvfp4_dtype_t x_dtype, i
 
 nvfp4_status_t nvfp4_fp8_dequantize(const uint8_t *q, const float *scale, int64_t rows, int64_t K, void *out,
                                     nvfp4_dtype_t out_dtype, int64_t ld_out, void *stream);
+
+/* ----------------------------------------------------------------------
+ * Linears with FP8 E4M3 weights (one per-tensor scale, as produced by
+ * nvfp4_fp8_quantize).  The model card "Gemma-4-31B-IT-NVFP4-FP8attn-text",
+ * section "What was quantized, exactly", serves its float8_e4m3 attention
+ * weights against bf16 activations (W8A16); W8A8 quantizes the activations
+ * to FP8 as well, with one per-tensor scale.
+ *
+ *   w_q      [N, K] E4M3 bytes, row stride K, 16-byte aligned; N * K < 2^32.
+ *   w_scale  device float: the weight tensor scale s_w.
+ *   K        a multiple of 64.  y, y_dtype, ld_y as in nvfp4_gemm.
+ *
+ * nvfp4_gemm_w8a16: Y = s_w * X . E4M3(W)^T with FP32 accumulation, X
+ *   [M, ld_x] bf16 as given, ld_x below 2^23.  Workspace nvfp4_gemm_w8a16_workspace_size
+ *   bytes (0 for M <= 16; NULL allowed then).
+ * nvfp4_gemm_w8a8: X is quantized to E4M3 with one per-tensor scale s_x
+ *   (x_scale: a device float, e.g. calibrated, or NULL for RN(amax / 448),
+ *   exactly as nvfp4_fp8_quantize), then Y = RN(s_x * s_w) * sum of
+ *   E4M3(X) E4M3(W) products with FP32 accumulation; x bf16 or fp32.
+ *   Workspace nvfp4_gemm_w8a8_workspace_size bytes, 256-byte aligned.
+ * Errors as in nvfp4_gemm.
+ * ---------------------------------------------------------------------- */
+size_t nvfp4_gemm_w8a16_workspace_size(int64_t M, int64_t N, int64_t K);
+size_t nvfp4_gemm_w8a8_workspace_size(int64_t M, int64_t N, int64_t K);
+
+nvfp4_status_t nvfp4_gemm_w8a16(const void *x, nvfp4_dtype_t x_dtype, int64_t M, int64_t K, int64_t ld_x,
+                                const uint8_t *w_q, const float *w_scale, int64_t N, void *y,
+                                nvfp4_dtype_t y_dtype, int64_t ld_y, void *workspace, size_t workspace_bytes,
+                                void *stream);
+
+nvfp4_status_t nvfp4_gemm_w8a8(const void *x, nvfp4_dtype_t x_dtype, int64_t M, int64_t K, int64_t ld_x,
+                               const float *x_scale, const uint8_t *w_q, const float *w_scale, int64_t N, void *y,
+                               nvfp4_dtype_t y_dtype, int64_t ld_y, void *workspace, size_t workspace_bytes,
+                               void *stream);
 
 #ifdef __cplusplus
 }

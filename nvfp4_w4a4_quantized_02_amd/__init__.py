@@ -43,6 +43,7 @@ EXPORTS = (
     "nvfp4_gemm_prepare", "nvfp4_gemm_run", "nvfp4_quantize_static", "nvfp4_gemm_prepare_static",
     "nvfp4_gemm_static", "nvfp4_gemm_w4a16_workspace_size", "nvfp4_gemm_w4a16",
     "nvfp4_fp8_quantize_workspace_size", "nvfp4_fp8_quantize", "nvfp4_fp8_quantize_static", "nvfp4_fp8_dequantize",
+    "nvfp4_gemm_w8a16_workspace_size", "nvfp4_gemm_w8a8_workspace_size", "nvfp4_gemm_w8a16", "nvfp4_gemm_w8a8",
 )
 
 
@@ -96,6 +97,13 @@ def _load() -> ctypes.CDLL:
     L.nvfp4_fp8_quantize_static.restype = I
     L.nvfp4_fp8_dequantize.argtypes = [P, P, I64, I64, P, I, I64, P]
     L.nvfp4_fp8_dequantize.restype = I
+    for n in ("nvfp4_gemm_w8a16_workspace_size", "nvfp4_gemm_w8a8_workspace_size"):
+        getattr(L, n).argtypes = [I64, I64, I64]
+        getattr(L, n).restype = SZ
+    L.nvfp4_gemm_w8a16.argtypes = [P, I, I64, I64, I64, P, P, I64, P, I, I64, P, SZ, P]
+    L.nvfp4_gemm_w8a16.restype = I
+    L.nvfp4_gemm_w8a8.argtypes = [P, I, I64, I64, I64, P, P, P, I64, P, I, I64, P, SZ, P]
+    L.nvfp4_gemm_w8a8.restype = I
     _check_single_hip_runtime()
     return L
 
@@ -346,7 +354,47 @@ def nvfp4_fp8_dequantize(q: torch.Tensor, scale: torch.Tensor, out_dtype: torch.
     return out
 
 
+def _check_fp8_weight(w_q: torch.Tensor, K: int) -> int:
+    if w_q.dtype != torch.uint8 or w_q.dim() != 2 or w_q.shape[1] != K or not w_q.is_contiguous():
+        raise ValueError("FP8 weights must be contiguous uint8 [N, K=%d], got %s %s" % (K, w_q.dtype,
+                                                                                       tuple(w_q.shape)))
+    return w_q.shape[0]
+
+
+def nvfp4_gemm_w8a16(x: torch.Tensor, w_q: torch.Tensor, w_scale: torch.Tensor,
+                     out_dtype: torch.dtype = torch.bfloat16, out: torch.Tensor | None = None) -> torch.Tensor:
+    """W8A16: Y = X (E4M3(W) * s_w)^T, X [M, K] bf16 as given, W [N, K] E4M3
+    bytes with one per-tensor scale (float32 [1])."""
+    M, K, ld = _rows_view(x)
+    N = _check_fp8_weight(w_q, K)
+    if out is None:
+        out = _out_tensor(M, N, out_dtype, x.device)
+    nws = lib.nvfp4_gemm_w8a16_workspace_size(M, N, K)
+    ws = workspace(nws, x.device) if nws else None
+    _check(lib.nvfp4_gemm_w8a16(x.data_ptr(), _dtype_code(x.dtype), M, K, ld, w_q.data_ptr(), w_scale.data_ptr(), N,
+                                out.data_ptr(), _dtype_code(out.dtype), _ld_out(out, M, N),
+                                ws.data_ptr() if ws is not None else None, ws.numel() if ws is not None else 0,
+                                _stream_ptr(x.device)), "nvfp4_gemm_w8a16")
+    return out
+
+
+def nvfp4_gemm_w8a8(x: torch.Tensor, w_q: torch.Tensor, w_scale: torch.Tensor, x_scale: torch.Tensor | None = None,
+                    out_dtype: torch.dtype = torch.bfloat16, out: torch.Tensor | None = None) -> torch.Tensor:
+    """W8A8: X quantized to E4M3 with one per-tensor scale (RN(amax/448), or
+    the calibrated x_scale), then Y = RN(s_x s_w) * E4M3(X) E4M3(W)^T."""
+    M, K, ld = _rows_view(x)
+    N = _check_fp8_weight(w_q, K)
+    if out is None:
+        out = _out_tensor(M, N, out_dtype, x.device)
+    ws = workspace(lib.nvfp4_gemm_w8a8_workspace_size(M, N, K), x.device)
+    _check(lib.nvfp4_gemm_w8a8(x.data_ptr(), _dtype_code(x.dtype), M, K, ld,
+                               x_scale.data_ptr() if x_scale is not None else None, w_q.data_ptr(),
+                               w_scale.data_ptr(), N, out.data_ptr(), _dtype_code(out.dtype), _ld_out(out, M, N),
+                               ws.data_ptr(), ws.numel(), _stream_ptr(x.device)), "nvfp4_gemm_w8a8")
+    return out
+
+
 __all__ = ["nvfp4_quantize", "nvfp4_quantize_static", "nvfp4_dequantize", "nvfp4_fuse_rescale", "nvfp4_gemm",
-           "nvfp4_gemm_w4a16", "nvfp4_fp8_quantize", "nvfp4_fp8_dequantize",
+           "nvfp4_gemm_w4a16", "nvfp4_fp8_quantize", "nvfp4_fp8_dequantize", "nvfp4_gemm_w8a16", "nvfp4_gemm_w8a8",
            "nvfp4_gemm_prepare", "nvfp4_gemm_run", "PreparedActivations", "Nvfp4Error",
            "status_string", "lib", "EXPORTS", "LIB_PATH", "workspace"]

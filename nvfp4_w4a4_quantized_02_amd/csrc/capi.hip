@@ -13,6 +13,9 @@ namespace {
 
 constexpr int64_t kMaxDim = (int64_t)1 << 31;  // per-dimension limit
 constexpr uint64_t kMaxBlocks = (uint64_t)1 << 31;
+// Kernels that read the caller's activations tile by tile address up to 256
+// rows from a tile base with 32-bit offsets.
+constexpr uint64_t kMaxTileRowBytes = (uint64_t)1 << 24;
 
 inline bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 inline int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
@@ -327,6 +330,94 @@ nvfp4_status_t nvfp4_fp8_dequantize(const uint8_t* q, const float* scale, int64_
   return launched();
 }
 
+// FP8-weight linears.  Workspace: absmax partials | s_x | X in E4M3 [M, K]
+// (W8A8 only) | fp32 K-part sums of the split tiles.
+static size_t x8_bytes(int64_t M, int64_t K) {
+  if (M <= 0 || K <= 0) return 0;
+  return (size_t)round_up(M * K, 256);
+}
+
+size_t nvfp4_gemm_w8a16_workspace_size(int64_t M, int64_t N, int64_t K) {
+  return nvfp4_gemm_w4a16_workspace_size(M, N, K);
+}
+
+size_t nvfp4_gemm_w8a8_workspace_size(int64_t M, int64_t N, int64_t K) {
+  if (M < 0 || N < 0 || K < 0 || M >= kMaxDim || N >= kMaxDim || K >= kMaxDim) return 0;
+  return kWsX16 + x8_bytes(M, K) + partial_bytes(M, N, round_up(K, kGemmBK));
+}
+
+// Checks shared by the FP8-weight entry points (besides those of X).
+static nvfp4_status_t fp8w_args_ok(int64_t M, int64_t K, const uint8_t* w_q, const float* w_scale, int64_t N,
+                                   const void* y, nvfp4_dtype_t y_dtype, int64_t ld_y) {
+  if (!dtype_ok(y_dtype)) return NVFP4_ERR_DTYPE;
+  if (N < 0 || N >= kMaxDim || K % 64 != 0) return NVFP4_ERR_SHAPE;
+  if (M == 0 || N == 0) return NVFP4_OK;
+  if (!y || !w_scale) return NVFP4_ERR_NULL;
+  if (ld_y < N) return NVFP4_ERR_SHAPE;
+  if (!aligned(y, 16) || ((uint64_t)ld_y * esize(y_dtype)) % 16 != 0) return NVFP4_ERR_ALIGN;
+  if (K > 0) {
+    if (!w_q) return NVFP4_ERR_NULL;
+    if (!aligned(w_q, 16)) return NVFP4_ERR_ALIGN;
+    if ((uint64_t)N * (uint64_t)K >= ((uint64_t)1 << 32)) return NVFP4_ERR_SHAPE;
+  }
+  return NVFP4_OK;
+}
+
+static void fp8w_run(bool a8, const void* x, size_t ld_x_bytes, int64_t M, int64_t K, const uint8_t* w_q,
+                     const float* sx, const float* sw, int64_t N, void* y, bool yb, int64_t ld_y, float* partials,
+                     hipStream_t s) {
+  if (M <= kGemvMaxM && K <= kFp8GemvMaxK && K > 0)
+    launch_gemv_fp8w(a8, x, ld_x_bytes, M, K, w_q, N, sx, sw, y, yb, ld_y, s);
+  else
+    launch_gemm_fp8w(a8, x, ld_x_bytes, M, K, w_q, N, sx, sw, y, yb, ld_y, partials, s);
+}
+
+nvfp4_status_t nvfp4_gemm_w8a16(const void* x, nvfp4_dtype_t x_dtype, int64_t M, int64_t K, int64_t ld_x,
+                                const uint8_t* w_q, const float* w_scale, int64_t N, void* y, nvfp4_dtype_t y_dtype,
+                                int64_t ld_y, void* workspace, size_t workspace_bytes, void* stream) {
+  nvfp4_status_t st = check_input(x, x_dtype, M, K, ld_x);
+  if (st != NVFP4_OK) return st;
+  if (x_dtype != NVFP4_BF16) return NVFP4_ERR_DTYPE;
+  if ((uint64_t)ld_x * 2u >= kMaxTileRowBytes) return NVFP4_ERR_SHAPE;
+  st = fp8w_args_ok(M, K, w_q, w_scale, N, y, y_dtype, ld_y);
+  if (st != NVFP4_OK || M == 0 || N == 0) return st;
+  const size_t need = nvfp4_gemm_w8a16_workspace_size(M, N, K);
+  if (need && (!workspace || !aligned(workspace, 256) || workspace_bytes < need)) return NVFP4_ERR_WORKSPACE;
+  fp8w_run(false, x, (size_t)ld_x * 2, M, K, w_q, nullptr, w_scale, N, y, y_dtype == NVFP4_BF16, ld_y,
+           (float*)workspace, (hipStream_t)stream);
+  return launched();
+}
+
+nvfp4_status_t nvfp4_gemm_w8a8(const void* x, nvfp4_dtype_t x_dtype, int64_t M, int64_t K, int64_t ld_x,
+                               const float* x_scale, const uint8_t* w_q, const float* w_scale, int64_t N, void* y,
+                               nvfp4_dtype_t y_dtype, int64_t ld_y, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+  nvfp4_status_t st = check_input(x, x_dtype, M, K, ld_x);
+  if (st != NVFP4_OK) return st;
+  st = fp8w_args_ok(M, K, w_q, w_scale, N, y, y_dtype, ld_y);
+  if (st != NVFP4_OK || M == 0 || N == 0) return st;
+  if (!workspace || !aligned(workspace, 256) || workspace_bytes < nvfp4_gemm_w8a8_workspace_size(M, N, K))
+    return NVFP4_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  const bool xb = x_dtype == NVFP4_BF16;
+  uint32_t* amax_partials = (uint32_t*)((char*)workspace + kWsPartials);
+  float* sx = (float*)((char*)workspace + kWsGs);
+  uint8_t* x8 = (uint8_t*)workspace + kWsX16;
+  float* split_partials = (float*)((char*)workspace + kWsX16 + x8_bytes(M, K));
+  if (K > 0) {
+    if (x_scale) {
+      launch_fp8_quantize(x, xb, M, K, ld_x, nullptr, 0, x_scale, x8, sx, s);
+    } else {
+      const int np = launch_amax(x, xb, M, K, ld_x, amax_partials, s);
+      launch_fp8_quantize(x, xb, M, K, ld_x, amax_partials, np, nullptr, x8, sx, s);
+    }
+  } else {
+    launch_fill_f32(sx, 0.0f, s);
+  }
+  fp8w_run(true, x8, (size_t)K, M, K, w_q, sx, w_scale, N, y, y_dtype == NVFP4_BF16, ld_y, split_partials, s);
+  return launched();
+}
+
 nvfp4_status_t nvfp4_gemm_w4a16(const void* x, nvfp4_dtype_t x_dtype, int64_t M, int64_t K, int64_t ld_x,
                                 const uint8_t* w_codes, const uint8_t* w_scales, const float* w_gs, int64_t N,
                                 void* y, nvfp4_dtype_t y_dtype, int64_t ld_y, void* workspace,
@@ -336,6 +427,7 @@ nvfp4_status_t nvfp4_gemm_w4a16(const void* x, nvfp4_dtype_t x_dtype, int64_t M,
   if (x_dtype != NVFP4_BF16) return NVFP4_ERR_DTYPE;
   if (!dtype_ok(y_dtype)) return NVFP4_ERR_DTYPE;
   if (N < 0 || N >= kMaxDim || K % 64 != 0) return NVFP4_ERR_SHAPE;
+  if ((uint64_t)ld_x * 2u >= kMaxTileRowBytes) return NVFP4_ERR_SHAPE;
   if (M == 0 || N == 0) return NVFP4_OK;
   if (!y || !w_gs) return NVFP4_ERR_NULL;
   if (ld_y < N) return NVFP4_ERR_SHAPE;

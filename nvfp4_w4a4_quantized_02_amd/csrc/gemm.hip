@@ -309,6 +309,204 @@ __global__ __launch_bounds__(256) void gemm_split_reduce_kernel(const float* __r
   store4<kYBf16>(y + (size_t)m * ld_y_bytes, n, N, a.x * scale, a.y * scale, a.z * scale, a.w * scale);
 }
 
+// ================================================================ FP8 weights
+// W8A16 and W8A8 (model card "Gemma-4-31B-IT-NVFP4-FP8attn-text", section
+// "What was quantized, exactly": float8_e4m3 weights with one per-tensor
+// scale, served against bf16 activations; W8A8 with FP8 activations): W is
+// [N, K] E4M3 bytes.  The tile, the wave grid, the three-buffer ring of
+// direct transfers and the split-K tail are those of the kernel above.
+//   kA8 = false: X bf16 as given; each W byte pair becomes a bf16 pair
+//     (exact, one conversion) and the MFMA is 32x32x16 bf16.
+//   kA8 = true: X is E4M3 bytes; both operands go to the 32x32x64 FP8 MFMA
+//     unconverted (unit block scales), 32 consecutive k per lane.
+// Epilogue: y = acc * s_w (W8A16) or acc * RN(s_x * s_w) (W8A8).
+//
+// LDS rows of 64 bytes (W, and X in FP8) hold chunk c of row r in 16-byte
+// slot c ^ ((r >> 2) & 3), so 16 consecutive rows read at one chunk hit 16
+// distinct 16-byte bank groups.
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+template <bool kA8>
+struct Fp8wBuf {
+  uint4 x[kGemmBM * (kA8 ? 4 : 8)];  // X: 256 rows x 64 k (fp8: 16 KB, bf16: 32 KB)
+  uint4 w[kGemmBN * 4];              // W: 256 rows x 64 k fp8 (16 KB)
+};
+
+__device__ __forceinline__ uint32_t row64_slot(int row, int chunk) { return (uint32_t)(chunk ^ ((row >> 2) & 3)); }
+
+template <bool kA8, bool kYBf16>
+__global__ __launch_bounds__(512, 1) void gemm_fp8w_kernel(const uint8_t* __restrict__ x, uint32_t ld_x_bytes,
+                                                            const uint8_t* __restrict__ wq, int N, int K, int M,
+                                                            const float* __restrict__ sx_p,
+                                                            const float* __restrict__ sw_p,
+                                                            uint8_t* __restrict__ y, size_t ld_y_bytes, int tiles_n,
+                                                            int nk, int full_tiles, int split,
+                                                            float* __restrict__ partials) {
+  using B = Fp8wBuf<kA8>;
+  __shared__ B b0, b1, b2;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wave_n = wave >> 1, wave_m = wave & 1;  // W rows 64 wave_n.., X rows 128 wave_m..
+  int tile = blockIdx.x, part = -1, kb = 0, ke = nk;
+  if (tile >= full_tiles) {
+    const int i = tile - full_tiles;
+    tile = full_tiles + i / split;
+    part = i % split;
+    kb = part * nk / split;
+    ke = (part + 1) * nk / split;
+  }
+  const int tn = tile % tiles_n, tm = tile / tiles_n;
+  const int n0 = tn * kGemmBN, m0 = tm * kGemmBM;
+  const int l32 = lane & 31, h = lane >> 5;
+
+  // ---- transfers: per step W 2 x 1 KB and X 2 x 1 KB (fp8) or 4 x 1 KB
+  // (bf16) per wave.  64-byte rows: instruction j of wave w fills slots
+  // (2w + j) * 64 + lane = row (2w + j) * 16 + lane / 4, slot lane % 4.
+  const uint8_t* wbase = wq + (size_t)n0 * (size_t)K;
+  const uint8_t* xbase = x + (size_t)m0 * ld_x_bytes;
+  uint32_t woff[2], x8off[2], x16off[4];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int r = (2 * wave + j) * 16 + (lane >> 2);
+    const int logical = (lane & 3) ^ ((r >> 2) & 3);
+    int rn = n0 + r < N ? r : N - 1 - n0;   // rows past N / M repeat the last one (not stored)
+    int rm = m0 + r < M ? r : M - 1 - m0;
+    woff[j] = (uint32_t)rn * (uint32_t)K + 16u * (uint32_t)logical;
+    x8off[j] = (uint32_t)rm * ld_x_bytes + 16u * (uint32_t)logical;
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {  // bf16 X: 128-byte rows, as in the NVFP4 kernel
+    int r = (wave * 4 + j) * 8 + (lane >> 3);
+    r = m0 + r < M ? r : M - 1 - m0;
+    x16off[j] = (uint32_t)r * ld_x_bytes + ((uint32_t)((lane & 7) ^ ((lane >> 3) & 7) ^ (j & 1))) * 16u;
+  }
+  constexpr int kXDma = kA8 ? 2 : 4;
+  auto lx = [&](const B& bf) { return lds_addr(&bf.x[wave * (kA8 ? 128 : 256)]); };
+  auto lw = [&](const B& bf) { return lds_addr(&bf.w[wave * 128]); };
+  const uint32_t lx0 = lx(b0), lx1 = lx(b1), lx2 = lx(b2), lw0 = lw(b0), lw1 = lw(b1), lw2 = lw(b2);
+  auto issue = [&](int kt, uint32_t ldx, uint32_t ldw) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) lds_dma16(wbase + (size_t)kt * 64, woff[j], ldw + j * 1024);
+    if constexpr (kA8) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) lds_dma16(xbase + (size_t)kt * 64, x8off[j], ldx + j * 1024);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) lds_dma16(xbase + (size_t)kt * 128, x16off[j], ldx + j * 1024);
+    }
+  };
+
+  floatx16 acc[2][4];
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[t][u][r] = 0.0f;
+
+  // 32 bytes of a 64-byte row at k 32h .. 32h+31
+  auto read32 = [&](const uint4* base, int row, uint4 (&v)[2]) {
+    v[0] = base[row * 4 + row64_slot(row, 2 * h)];
+    v[1] = base[row * 4 + row64_slot(row, 2 * h + 1)];
+  };
+  auto compute = [&](const B& cur) {
+    uint4 w32[2][2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) read32(cur.w, wave_n * 64 + t * 32 + l32, w32[t]);
+    if constexpr (kA8) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        uint4 x32[2];
+        read32(cur.x, wave_m * 128 + u * 32 + l32, x32);
+        const i32x8 xb = __builtin_bit_cast(i32x8, x32);
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+          acc[t][u] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(__builtin_bit_cast(i32x8, w32[t]), xb,
+                                                                       acc[t][u], 0, 0, 0, 127, 0, 127);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        bf16x8 aw[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const uint32_t d0 = dword_of(w32[t][j >> 1], 2 * (j & 1)), d1 = dword_of(w32[t][j >> 1], 2 * (j & 1) + 1);
+          const uint4 e = make_uint4(
+              __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d0, 1.0f, false)),
+              __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d0, 1.0f, true)),
+              __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d1, 1.0f, false)),
+              __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d1, 1.0f, true)));
+          aw[t] = __builtin_bit_cast(bf16x8, e);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int row = wave_m * 128 + u * 32 + l32;
+          const bf16x8 bx = __builtin_bit_cast(bf16x8, cur.x[row * 8 + ((4 * h + j) ^ (row & 7) ^ ((row >> 3) & 1))]);
+#pragma unroll
+          for (int t = 0; t < 2; ++t)
+            acc[t][u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aw[t], bx, acc[t][u], 0, 0, 0);
+        }
+      }
+    }
+  };
+  constexpr int kDma = 2 + kXDma;
+  // Step kt computes buffer kt % 3 while the transfers of kt + 1 and kt + 2
+  // fly; the wait before the barrier leaves only kt + 2's (kDma) in flight.
+  auto step = [&](int kt, const B& cur, uint32_t ldx, uint32_t ldw) {
+    if constexpr (kA8)
+      asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(6) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    const int last = ke - 1;
+    issue(kt + 2 < last ? kt + 2 : last, ldx, ldw);
+    compute(cur);
+  };
+  static_assert(kDma == (kA8 ? 4 : 6), "the wait counts above must match the transfers per step");
+
+  if (ke > kb) {
+    issue(kb, lx0, lw0);
+    issue(kb + 1 < ke ? kb + 1 : kb, lx1, lw1);
+    for (int kt = kb; kt < ke; kt += 3) {
+      step(kt, b0, lx2, lw2);
+      if (kt + 1 < ke) step(kt + 1, b1, lx0, lw0);
+      if (kt + 2 < ke) step(kt + 2, b2, lx1, lw1);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  }
+
+  if (part >= 0) {
+    float* pp = partials + ((size_t)(tile - full_tiles) * split + part) * (kGemmBM * kGemmBN);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int ml = wave_m * 128 + u * 32 + l32;
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int nl = wave_n * 64 + t * 32 + 8 * q + 4 * h;
+          *reinterpret_cast<float4*>(pp + ml * kGemmBN + nl) =
+              make_float4(acc[t][u][4 * q], acc[t][u][4 * q + 1], acc[t][u][4 * q + 2], acc[t][u][4 * q + 3]);
+        }
+    }
+    return;
+  }
+  const float scale = kA8 ? (*sx_p) * (*sw_p) : *sw_p;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int m = m0 + wave_m * 128 + u * 32 + l32;
+    if (m >= M) continue;
+    uint8_t* yrow = y + (size_t)m * ld_y_bytes;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int n = n0 + wave_n * 64 + t * 32 + 8 * q + 4 * h;
+        store4<kYBf16>(yrow, n, N, acc[t][u][4 * q] * scale, acc[t][u][4 * q + 1] * scale,
+                       acc[t][u][4 * q + 2] * scale, acc[t][u][4 * q + 3] * scale);
+      }
+    }
+  }
+}
+
 // ====================================================================== launch
 template <bool kA16>
 static void gemm_go(const void* x, uint32_t ld_x_chunks, int64_t M, int64_t K, const uint8_t* wc, const uint8_t* ws,
@@ -335,6 +533,43 @@ static void gemm_go(const void* x, uint32_t ld_x_chunks, int64_t M, int64_t K, c
       gemm_split_reduce_kernel<kA16, false><<<rgrid, 256, 0, s>>>(partials, p.full_tiles, p.split, p.tiles_n,
                                                                   (int)M, (int)N, gsx, gsw, (uint8_t*)y, ldb);
   }
+}
+
+template <bool kA8>
+static void gemm_fp8w_go(const void* x, uint32_t ld_x_bytes, int64_t M, int64_t K, const uint8_t* wq, int64_t N,
+                         const float* sx, const float* sw, void* y, bool y_bf16, int64_t ld_y, float* partials,
+                         hipStream_t s) {
+  const GemmPlan p = plan_gemm(M, N, K);
+  const int rem = p.tiles_m * p.tiles_n - p.full_tiles;
+  const size_t ldb = (size_t)ld_y * (y_bf16 ? 2u : 4u);
+  dim3 grid(p.full_tiles + rem * p.split);
+  if (y_bf16)
+    gemm_fp8w_kernel<kA8, true><<<grid, kGemmWaves * 64, 0, s>>>((const uint8_t*)x, ld_x_bytes, wq, (int)N, (int)K,
+                                                                (int)M, sx, sw, (uint8_t*)y, ldb, p.tiles_n, p.nk,
+                                                                p.full_tiles, p.split, partials);
+  else
+    gemm_fp8w_kernel<kA8, false><<<grid, kGemmWaves * 64, 0, s>>>((const uint8_t*)x, ld_x_bytes, wq, (int)N, (int)K,
+                                                                 (int)M, sx, sw, (uint8_t*)y, ldb, p.tiles_n, p.nk,
+                                                                 p.full_tiles, p.split, partials);
+  if (p.split > 1) {
+    // the reduce applies s_w (W8A16: kA16 form) or s_x * s_w (W8A8: W4A4 form)
+    dim3 rgrid(kGemmBM * kGemmBN / 4 / 256, rem);
+    if (y_bf16)
+      gemm_split_reduce_kernel<!kA8, true><<<rgrid, 256, 0, s>>>(partials, p.full_tiles, p.split, p.tiles_n, (int)M,
+                                                                 (int)N, sx, sw, (uint8_t*)y, ldb);
+    else
+      gemm_split_reduce_kernel<!kA8, false><<<rgrid, 256, 0, s>>>(partials, p.full_tiles, p.split, p.tiles_n,
+                                                                  (int)M, (int)N, sx, sw, (uint8_t*)y, ldb);
+  }
+}
+
+void launch_gemm_fp8w(bool a8, const void* x, size_t ld_x_bytes, int64_t M, int64_t K, const uint8_t* wq, int64_t N,
+                      const float* sx, const float* sw, void* y, bool y_bf16, int64_t ld_y, float* partials,
+                      hipStream_t s) {
+  if (a8)
+    gemm_fp8w_go<true>(x, (uint32_t)ld_x_bytes, M, K, wq, N, sx, sw, y, y_bf16, ld_y, partials, s);
+  else
+    gemm_fp8w_go<false>(x, (uint32_t)ld_x_bytes, M, K, wq, N, sx, sw, y, y_bf16, ld_y, partials, s);
 }
 
 void launch_gemm(bool a16, const void* x, size_t ld_x_bytes, int64_t M, int64_t K, const uint8_t* wc,

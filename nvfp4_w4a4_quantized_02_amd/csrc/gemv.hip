@@ -499,6 +499,149 @@ __global__ __launch_bounds__(640) void gemv_ksplit_kernel(const uint8_t* __restr
   }
 }
 
+// ------------------------------------------------------------ FP8 weights
+// W8A16 / W8A8 GEMV (M <= 16; model card "Gemma-4-31B-IT-NVFP4-FP8attn-
+// text", section "What was quantized, exactly": float8_e4m3 weights with one
+// per-tensor scale, served against bf16 activations).  W is [N, K] E4M3
+// bytes.  A workgroup of ceil(K / 512) waves covers all of K for a run of
+// 16-row tiles (as the K-split kernel above; K <= 5120): wave w owns k [512w, 512w+512)
+// and keeps the activations of that slice in registers; lane (r, g) takes
+// k 128g .. 128g+127 of row r.  The weights of a tile (128 bytes a lane) go
+// straight to registers, the next tile's while the current one is computed
+// (two register sets, used alternately).  Past K the activations are zero.  The
+// partial tiles of the waves are added in LDS in wave order (one barrier a
+// tile, double-buffered), so the result does not depend on scheduling.
+//   kA8 = false: bf16 activations; W bytes become bf16 pairs (exact) for
+//     16 MFMA 16x16x32 bf16 steps of 8 k.
+//   kA8 = true: FP8 activations; 4 MFMA 16x16x128 FP8 steps of 32 k, both
+//     operands unconverted (unit block scales).
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+constexpr int kF8MaxWaves = 10;    // K <= 5120 (wider K takes the tile kernel)
+
+template <bool kA8, bool kYBf16>
+__global__ __launch_bounds__(640) void gemv_fp8w_kernel(const uint8_t* __restrict__ x, uint32_t ld_x_bytes, int M,
+                                                         const uint8_t* __restrict__ wq, int N, int K, int tiles,
+                                                         const float* __restrict__ sx_p,
+                                                         const float* __restrict__ sw_p, uint8_t* __restrict__ y,
+                                                         size_t ld_y_bytes) {
+  __shared__ floatx4 part[2][kF8MaxWaves][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, l16 = lane & 15, g = lane >> 4;
+  const int waves = blockDim.x >> 6;
+  const int k0 = wave * 512 + 128 * g;  // this lane's first k
+  const bool mvalid = l16 < M;
+
+  // activations of the slice: 128 k of row l16 (zeros past K and for m >= M)
+  constexpr int kXq = kA8 ? 8 : 16;  // uint4 per lane
+  uint4 xv[kXq];
+  {
+    const uint8_t* xr = x + (size_t)(mvalid ? l16 : 0) * ld_x_bytes + (size_t)k0 * (kA8 ? 1u : 2u);
+#pragma unroll
+    for (int q = 0; q < kXq; ++q) {
+      const int kq = k0 + q * (kA8 ? 16 : 8);
+      xv[q] = (mvalid && kq < K) ? reinterpret_cast<const uint4*>(xr)[q] : make_uint4(0, 0, 0, 0);
+    }
+  }
+
+  auto load_w = [&](int t, uint4 (&w)[8]) {
+    t = t < tiles ? t : tiles - 1;  // past the end: a valid tile whose sums are never used
+    int n = t * 16 + l16;
+    n = n < N ? n : N - 1;
+    // k past K re-reads the row's last 16 bytes: finite weights that meet
+    // zero activations, so every load is unconditional
+    const uint8_t* wr = wq + (size_t)n * (size_t)K;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int kq = k0 + 16 * q < K ? k0 + 16 * q : K - 16;
+      w[q] = *reinterpret_cast<const uint4*>(wr + kq);
+    }
+  };
+  auto mma = [&](const uint4 (&w)[8]) {
+    floatx4 acc = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+    if constexpr (kA8) {
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const uint4 wa[2] = {w[2 * s], w[2 * s + 1]};
+        const uint4 xa[2] = {xv[2 * s], xv[2 * s + 1]};
+        acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(__builtin_bit_cast(i32x8, wa),
+                                                                __builtin_bit_cast(i32x8, xa), acc, 0, 0, 0, 127, 0,
+                                                                127);
+      }
+    } else {
+#pragma unroll
+      for (int s = 0; s < 16; ++s) {
+        const uint32_t d0 = dword_of(w[s >> 1], 2 * (s & 1)), d1 = dword_of(w[s >> 1], 2 * (s & 1) + 1);
+        const uint4 e = make_uint4(
+            __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d0, 1.0f, false)),
+            __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d0, 1.0f, true)),
+            __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d1, 1.0f, false)),
+            __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d1, 1.0f, true)));
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, e),
+                                                      __builtin_bit_cast(bf16x8, xv[s]), acc, 0, 0, 0);
+      }
+    }
+    return acc;
+  };
+
+  const float scale = kA8 ? (*sx_p) * (*sw_p) : *sw_p;
+  int local = 0;
+  // the wave whose turn it is adds the partial tiles in wave order and
+  // stores the tile's outputs
+  auto finish = [&](int t, const floatx4& acc) {
+    const int pb = local & 1;
+    part[pb][wave][lane] = acc;
+    __syncthreads();
+    if (wave == local % waves && mvalid) {
+      floatx4 sum = part[pb][0][lane];
+      for (int v = 1; v < waves; ++v) sum = sum + part[pb][v][lane];
+      store4<kYBf16>(y + (size_t)l16 * ld_y_bytes, t * 16 + 4 * g, N, sum[0] * scale, sum[1] * scale,
+                     sum[2] * scale, sum[3] * scale);
+    }
+    ++local;
+  };
+
+  const int first = blockIdx.x, step = gridDim.x;
+  uint4 wa[8], wb[8];
+  load_w(first, wa);
+  for (int t = first; t < tiles; t += 2 * step) {
+    load_w(t + step, wb);
+    finish(t, mma(wa));
+    if (t + step >= tiles) break;
+    load_w(t + 2 * step, wa);
+    finish(t + step, mma(wb));
+  }
+}
+
+void launch_gemv_fp8w(bool a8, const void* x, size_t ld_x_bytes, int64_t M, int64_t K, const uint8_t* wq, int64_t N,
+                      const float* sx, const float* sw, void* y, bool y_bf16, int64_t ld_y, hipStream_t s) {
+  static int cus = 0;
+  if (!cus) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      cus = 256;
+  }
+  const int tiles = (int)((N + 15) / 16);
+  const int waves = (int)((K + 511) / 512);
+  const int grid = tiles < cus ? tiles : cus;
+  const size_t ldb = (size_t)ld_y * (y_bf16 ? 2u : 4u);
+  const uint32_t ldx = (uint32_t)ld_x_bytes;
+  if (a8) {
+    if (y_bf16)
+      gemv_fp8w_kernel<true, true><<<grid, waves * 64, 0, s>>>((const uint8_t*)x, ldx, (int)M, wq, (int)N, (int)K,
+                                                              tiles, sx, sw, (uint8_t*)y, ldb);
+    else
+      gemv_fp8w_kernel<true, false><<<grid, waves * 64, 0, s>>>((const uint8_t*)x, ldx, (int)M, wq, (int)N, (int)K,
+                                                               tiles, sx, sw, (uint8_t*)y, ldb);
+  } else {
+    if (y_bf16)
+      gemv_fp8w_kernel<false, true><<<grid, waves * 64, 0, s>>>((const uint8_t*)x, ldx, (int)M, wq, (int)N, (int)K,
+                                                               tiles, sx, sw, (uint8_t*)y, ldb);
+    else
+      gemv_fp8w_kernel<false, false><<<grid, waves * 64, 0, s>>>((const uint8_t*)x, ldx, (int)M, wq, (int)N,
+                                                                (int)K, tiles, sx, sw, (uint8_t*)y, ldb);
+  }
+}
+
 // LDS of one streaming workgroup, and the depth that keeps every tile in one
 // round of the machine; 0 when the streaming kernel does not apply.
 struct GvPlan {

@@ -98,6 +98,16 @@ void launch_fp8_dequant(const uint8_t* q, const float* scale, int64_t rows, int6
 void launch_gemm(bool a16, const void* x, size_t ld_x_bytes, int64_t M, int64_t K, const uint8_t* wc,
                  const uint8_t* ws, int64_t N, const float* gsx, const float* gsw, void* y, bool y_bf16,
                  int64_t ld_y, float* partials, hipStream_t s);
+// FP8 E4M3 weights [N, K] with one per-tensor scale: a8 = false (W8A16): X
+// bf16, y = acc * sw; a8 = true (W8A8): X E4M3 bytes, y = acc * sx * sw.
+// K % 64 == 0.  The GEMV form needs M <= 16 and K <= 5120.
+void launch_gemm_fp8w(bool a8, const void* x, size_t ld_x_bytes, int64_t M, int64_t K, const uint8_t* wq, int64_t N,
+                      const float* sx, const float* sw, void* y, bool y_bf16, int64_t ld_y, float* partials,
+                      hipStream_t s);
+void launch_gemv_fp8w(bool a8, const void* x, size_t ld_x_bytes, int64_t M, int64_t K, const uint8_t* wq, int64_t N,
+                      const float* sx, const float* sw, void* y, bool y_bf16, int64_t ld_y, hipStream_t s);
+constexpr int64_t kFp8GemvMaxK = 5120;
+
 void launch_gemv(bool a16, const void* x, size_t ld_x_bytes, int64_t M, int64_t K, const uint8_t* wc,
                  const uint8_t* ws, int64_t N, const float* gsx, const float* gsw, void* y, bool y_bf16,
                  int64_t ld_y, hipStream_t s);

@@ -225,3 +225,31 @@ def test_fp8_rejects(nv):
     assert L.nvfp4_fp8_dequantize(None, A, 4, 32, A, F32, 32, None) == E_NULL
     assert L.nvfp4_fp8_dequantize(A, A, 4, 32, A + 4, F32, 32, None) == E_ALIGN
     assert L.nvfp4_fp8_dequantize(A, A, 0, 32, A, F32, 32, None) == OK
+
+
+def test_fp8_linear_rejects(nv):
+    L = nv.lib
+
+    def w816(x=A, dt=BF16, M=32, K=64, ld=64, wq=A, wsc=A, N=64, y=A, ydt=BF16, ldy=64, ws=A, nws=BIG):
+        return L.nvfp4_gemm_w8a16(x, dt, M, K, ld, wq, wsc, N, y, ydt, ldy, ws, nws, None)
+
+    def w88(x=A, dt=BF16, M=32, K=64, ld=64, xs=None, wq=A, wsc=A, N=64, y=A, ydt=BF16, ldy=64, ws=A, nws=BIG):
+        return L.nvfp4_gemm_w8a8(x, dt, M, K, ld, xs, wq, wsc, N, y, ydt, ldy, ws, nws, None)
+
+    assert w816(dt=F32) == E_DTYPE
+    assert w816(K=48, ld=48) == E_SHAPE
+    assert w816(wsc=None) == E_NULL
+    assert w816(wq=None) == E_NULL
+    assert w816(wq=A + 8) == E_ALIGN
+    assert w816(M=0) == OK
+    assert L.nvfp4_gemm_w8a16_workspace_size(16, 34816, 5120) == 0
+    assert w88(dt=5) == E_DTYPE
+    assert w88(K=48, ld=48) == E_SHAPE
+    assert w88(y=None) == E_NULL
+    assert w88(y=A + 8) == E_ALIGN
+    assert w88(ws=None) == E_WS
+    assert w88(nws=L.nvfp4_gemm_w8a8_workspace_size(32, 64, 64) - 1) == E_WS
+    assert w88(N=0) == OK
+    # X in FP8 (M x K bytes) plus the split-K sums of the tile GEMM
+    assert L.nvfp4_gemm_w8a8_workspace_size(4096, 17408, 5120) >= 4096 * 5120 + \
+        L.nvfp4_gemm_w8a16_workspace_size(4096, 17408, 5120)

@@ -1,0 +1,129 @@
+"""GPU parity of the FP8-weight linears with the oracle (model card
+"Gemma-4-31B-IT-NVFP4-FP8attn-text", section "What was quantized, exactly":
+float8_e4m3 weights with one per-tensor scale, served W8A16; W8A8 with FP8
+activations).  The weights are the oracle's bytes, uploaded.  Every form is
+hit: the K-split GEMV (M <= 16, K <= 5120, including a partial last slice),
+the tile GEMM with and without its split-K tail, and small M with K > 5120;
+full decode and prefill sizes on sampled outputs.  Gate: the GEMM gate of
+the W4A4 tests."""
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from parity import check_gemm, to_gpu, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def nv():
+    import nvfp4_w4a4_quantized_02_amd as m
+    return m
+
+
+def _sc(v):
+    return torch.tensor([np.float32(v)], dtype=torch.float32, device="cuda:0")
+
+
+SHAPES = [(1, 300, 512), (4, 520, 5120), (16, 129, 768), (9, 100, 320), (3, 40, 6144),
+          (17, 64, 64), (100, 200, 320), (300, 257, 1088), (513, 300, 256)]
+
+
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+@pytest.mark.parametrize("M,N,K", SHAPES)
+def test_w8a16_matches_oracle(nv, orc, M, N, K, out):
+    x = workloads.to_bf16_bits(workloads.student_t(25, 1, M, K, 3.0))
+    wq, sw = orc.fp8_quantize(workloads.gaussian(25, 2, N, K, 0.02))
+    print("case: w8a16 %dx%dx%d %s" % (M, N, K, out), flush=True)
+    od = torch.bfloat16 if out == "bf16" else torch.float32
+    y = to_np(nv.nvfp4_gemm_w8a16(to_gpu(x), to_gpu(wq), _sc(sw), out_dtype=od))
+    torch.cuda.synchronize()
+    check_gemm(y, orc.gemm_w8a16(x, wq, sw), out == "bf16", "w8a16 %dx%dx%d" % (M, N, K))
+
+
+@pytest.mark.parametrize("mode", ["dynamic", "static"])
+@pytest.mark.parametrize("M,N,K", SHAPES)
+def test_w8a8_matches_oracle(nv, orc, M, N, K, mode):
+    x = workloads.to_bf16_bits(workloads.student_t(25, 3, M, K, 3.0))
+    wq, sw = orc.fp8_quantize(workloads.gaussian(25, 4, N, K, 0.02))
+    if mode == "dynamic":
+        xq, sx = orc.fp8_quantize(x)
+        xs = None
+    else:
+        sx = np.float32(orc.fp8_tensor_scale(x) * np.float32(0.6))    # a calibrated scale: saturates the largest
+        xq, _ = orc.fp8_quantize(x, scale=sx)
+        xs = _sc(sx)
+    print("case: w8a8 %s %dx%dx%d" % (mode, M, N, K), flush=True)
+    y = to_np(nv.nvfp4_gemm_w8a8(to_gpu(x), to_gpu(wq), _sc(sw), x_scale=xs, out_dtype=torch.float32))
+    torch.cuda.synchronize()
+    check_gemm(y, orc.gemm_w8a8(xq, sx, wq, sw), False, "w8a8 %s %dx%dx%d" % (mode, M, N, K))
+
+
+def test_w8a8_fp32_activations_and_strided_rows(nv, orc):
+    M, N, K = 40, 96, 512
+    x = workloads.gaussian(25, 5, M, K, 1.0)
+    wq, sw = orc.fp8_quantize(workloads.gaussian(25, 6, N, K, 0.02))
+    big = torch.zeros((M, K + 64), dtype=torch.float32, device="cuda:0")
+    big[:, :K] = to_gpu(x)
+    y = to_np(nv.nvfp4_gemm_w8a8(big[:, :K], to_gpu(wq), _sc(sw), out_dtype=torch.float32))
+    xq, sx = orc.fp8_quantize(x)
+    check_gemm(y, orc.gemm_w8a8(xq, sx, wq, sw), False, "w8a8 fp32 strided")
+
+
+def test_fp8_linears_empty_and_k_zero(nv):
+    wq = torch.zeros((8, 0), dtype=torch.uint8, device="cuda:0")
+    for M in (3, 40):
+        for f in (nv.nvfp4_gemm_w8a16, nv.nvfp4_gemm_w8a8):
+            x = torch.zeros((M, 0), dtype=torch.bfloat16, device="cuda:0")
+            y = torch.full((M, 8), 7.0, device="cuda:0")
+            f(x, wq, _sc(1.0), out=y)
+            torch.cuda.synchronize()
+            assert torch.count_nonzero(y).item() == 0
+
+
+def _sampled(nv, orc, x, w, a8, nsamp, seed):
+    sw = orc.fp8_tensor_scale(w)
+    q, s = nv.nvfp4_fp8_quantize(to_gpu(w))       # byte-exact with the oracle (FP8 quantize tests)
+    torch.cuda.synchronize()
+    assert np.float32(s.item()) == sw
+    xg = to_gpu(x)
+    if a8:
+        y = to_np(nv.nvfp4_gemm_w8a8(xg, q, s, out_dtype=torch.bfloat16))
+    else:
+        y = to_np(nv.nvfp4_gemm_w8a16(xg, q, s, out_dtype=torch.bfloat16))
+    torch.cuda.synchronize()
+    del q
+    M, N = x.shape[0], w.shape[0]
+    g = np.random.default_rng(seed)
+    mi, ni = g.integers(0, M, nsamp), g.integers(0, N, nsamp)
+    mi[:2], ni[:2] = [0, M - 1], [0, N - 1]
+    rows_w, rows_x = np.unique(ni), np.unique(mi)
+    wq, _ = orc.fp8_quantize(np.ascontiguousarray(w[rows_w]), scale=sw)
+    xs = np.ascontiguousarray(x[rows_x])
+    if a8:
+        sx = orc.fp8_tensor_scale(x)
+        xq, _ = orc.fp8_quantize(xs, scale=sx)
+        full = orc.gemm_w8a8(xq, sx, wq, sw)
+    else:
+        full = orc.gemm_w8a16(xs, wq, sw)
+    ref = full[np.searchsorted(rows_x, mi), np.searchsorted(rows_w, ni)]
+    return y[mi, ni], ref
+
+
+@pytest.mark.parametrize("a8", [False, True])
+@pytest.mark.parametrize("M", [1, 16])
+def test_fp8_linear_full_decode(nv, orc, M, a8):
+    p = workloads.decode(M=M)
+    w = np.concatenate(p.w_parts)
+    print("case: %s full decode M=%d N=34816 K=5120" % ("w8a8" if a8 else "w8a16", M), flush=True)
+    got, ref = _sampled(nv, orc, p.x, w, a8, 1500, 3)
+    check_gemm(got, ref, True, "fp8 full decode M=%d" % M)
+
+
+@pytest.mark.parametrize("a8", [False, True])
+def test_fp8_linear_full_prefill(nv, orc, a8):
+    p = workloads.prefill()
+    print("case: %s full prefill 4096x17408x5120" % ("w8a8" if a8 else "w8a16"), flush=True)
+    got, ref = _sampled(nv, orc, p.x, p.w_parts[0], a8, 1500, 4)
+    check_gemm(got, ref, True, "fp8 full prefill")

@@ -425,6 +425,9 @@ def secondary(torch, np, nv, workloads, to_gpu, dev, args):
         res[-1]["input_stats"] = {**stats.tensor_stats(xl), "a4": stats.fake_quant_error(xl)}
     del xl, codes, scl
 
+    # ------------------------------------------------ FP8-weight linears (W8A16, W8A8)
+    res += fp8_lines(torch, nv, workloads, to_gpu, dev, args)
+
     # ------------------------------------------------ offline weight quantize (fp32 in)
     w = torch.from_numpy(workloads.gaussian(3, 1, 17408, 5120, 0.02)).to(dev)
 
@@ -439,6 +442,71 @@ def secondary(torch, np, nv, workloads, to_gpu, dev, args):
                 "value": round(wb / (mean(w_ms) * 1e-3) / 1e9, 1), "unit": "GB/s",
                 "ms_per_step": round(mean(w_ms), 4),
                 "config": {"workload": "offline weight quantize W[17408x5120] fp32 N(0,0.02)"}})
+    return res
+
+
+PEAK_FP8_TFLOPS = 5000.0       # MI355X dense fp8 MFMA, published
+
+
+def fp8_lines(torch, nv, workloads, to_gpu, dev, args):
+    """W8A16 / W8A8 on FP8 E4M3 weights: decode GB/s (M = 1, 16, weights of the
+    fused gate/up shape, 4 rotated copies) and prefill TFLOP/s (M = 4096)."""
+    res = []
+    steps, warmup = args.steps, args.warmup
+    log("FP8 linears: quantizing weights to E4M3")
+    d = workloads.decode(M=1)
+    w32 = torch.cat([torch.from_numpy(w).to(dev) for w in d.w_parts])
+    wq0, sw = nv.nvfp4_fp8_quantize(w32)
+    del w32
+    R = 4
+    copies = [wq0.clone() for _ in range(R)]
+    del wq0
+    N, K = d.N, d.K
+    for M in (1, 16):
+        x = to_gpu(workloads.decode(M=M, N_each=1).x)
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        nbytes = N * K + M * K * 2 + M * N * 2
+        line = {"metric": "FP8-weight decode GB/s at M=%d" % M, "unit": "GB/s",
+                "config": {"workload": "decode: X[%dx5120] bf16 x W[34816x5120] E4M3 per-tensor scale "
+                                       "(4 rotated copies) -> Y bf16" % M},
+                "algorithmic": "W %d B + X + Y = %d B per call" % (N * K, nbytes)}
+        for name, fn in (("w8a16", nv.nvfp4_gemm_w8a16), ("w8a8", nv.nvfp4_gemm_w8a8)):
+            def st(i, mark, fn=fn, x=x, y=y):
+                mark(0)
+                fn(x, copies[i % R], sw, out=y)
+                mark(1)
+            _, (ms,) = time_steps(torch, max(steps, 40), warmup + 8, st, 1)
+            gbs = nbytes / (mean(ms) * 1e-3) / 1e9
+            line[name] = {"ms_per_call": round(mean(ms), 5), "GBs": round(gbs, 1),
+                          "frac": round(gbs / PEAK_HBM_GBS, 4)}
+        line["value"] = line["w8a16"]["GBs"]
+        res.append(line)
+        log("FP8 decode M=%d: W8A16 %.1f GB/s, W8A8 %.1f GB/s" % (M, line["w8a16"]["GBs"], line["w8a8"]["GBs"]))
+    del copies
+    p = workloads.prefill()
+    M, N, K = p.M, p.N, p.K
+    w32 = torch.from_numpy(p.w_parts[0]).to(dev)
+    wq, sw = nv.nvfp4_fp8_quantize(w32)
+    del w32
+    x = to_gpu(p.x)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    flops = 2.0 * M * N * K
+    line = {"metric": "FP8-weight GEMM TFLOP/s at M=4096", "unit": "TFLOP/s",
+            "config": {"workload": "prefill: X[4096x5120] bf16 x W[17408x5120] E4M3 per-tensor scale -> Y bf16; "
+                                   "W8A8 includes the dynamic activation quantize"}}
+    for name, fn, peak in (("w8a16", nv.nvfp4_gemm_w8a16, PEAK_FP16_TFLOPS),
+                           ("w8a8", nv.nvfp4_gemm_w8a8, PEAK_FP8_TFLOPS)):
+        def st(i, mark, fn=fn):
+            mark(0)
+            fn(x, wq, sw, out=y)
+            mark(1)
+        _, (ms,) = time_steps(torch, steps, warmup, st, 1)
+        tf = flops / (mean(ms) * 1e-3) / 1e12
+        line[name] = {"ms_per_call": round(mean(ms), 4), "TFLOPs": round(tf, 2), "peak": peak,
+                      "frac": round(tf / peak, 4)}
+    line["value"] = line["w8a8"]["TFLOPs"]
+    res.append(line)
+    log("FP8 prefill: W8A16 %.1f TFLOP/s, W8A8 %.1f TFLOP/s" % (line["w8a16"]["TFLOPs"], line["w8a8"]["TFLOPs"]))
     return res
 
 

@@ -611,6 +611,154 @@ __global__ __launch_bounds__(640) void gemv_fp8w_kernel(const uint8_t* __restric
   }
 }
 
+// FP8 weights, M <= 4: one wave per 16-row tile over all of K, as the NVFP4
+// streaming kernel.  Chunks of 256 k reach LDS through a ring of D slots by
+// direct transfers with explicit waits: the weights (16 rows x 256 B, four
+// transfers of 4 rows; piece p of row r in slot p ^ r of its row) and the
+// activations (bf16: M rows x 512 B, two transfers of 2 rows, piece 8a + b in
+// slot 8a + (b ^ a); FP8: M rows x 256 B, one transfer of 4 rows).  Lane
+// (r, g) takes k 64g .. 64g+63 of weight row r: eight bf16 MFMA steps of 8 k
+// (W8A16) or two FP8 steps of 32 k (W8A8), the activation operand read with
+// the same k.  Partial sums stay in the wave.
+constexpr uint32_t kF8Chunk = 4096;
+
+template <int D, bool kA8, bool kYBf16>
+__global__ __launch_bounds__(64) void gemv_fp8w_stream_kernel(const uint8_t* __restrict__ x, uint32_t ld_x_bytes,
+                                                               int M, const uint8_t* __restrict__ wq, int N, int K,
+                                                               const float* __restrict__ sx_p,
+                                                               const float* __restrict__ sw_p,
+                                                               uint8_t* __restrict__ y, size_t ld_y_bytes) {
+  extern __shared__ uint4 smem[];
+  constexpr int kXI = kA8 ? 1 : 2;                       // activation transfers per chunk
+  constexpr uint32_t kSlot = kF8Chunk + 1024u * kXI;
+  uint8_t* lds = reinterpret_cast<uint8_t*>(smem);
+  const int lane = threadIdx.x, l16 = lane & 15, g = lane >> 4;
+  const int tile = blockIdx.x;
+  const int nck = K >> 8;  // a multiple of D
+  const uint32_t ring0 = lds_addr(lds);
+
+  uint32_t woff[4];
+#pragma unroll
+  for (int h = 0; h < 4; ++h) {
+    const int r = 4 * h + (lane >> 4);
+    int n = tile * 16 + r;
+    n = n < N ? n : N - 1;
+    woff[h] = (uint32_t)n * (uint32_t)K + 16u * (uint32_t)((lane & 15) ^ r);
+  }
+  uint32_t xoff[kXI];
+#pragma unroll
+  for (int v = 0; v < kXI; ++v) {
+    if constexpr (kA8) {
+      int m = lane >> 4;
+      m = m < M ? m : M - 1;
+      xoff[v] = (uint32_t)m * ld_x_bytes + 16u * (uint32_t)(lane & 15);
+    } else {
+      int m = 2 * v + (lane >> 5);
+      m = m < M ? m : M - 1;
+      const uint32_t p = (uint32_t)(lane & 31), piece = (p & ~7u) | ((p & 7u) ^ (p >> 3));
+      xoff[v] = (uint32_t)m * ld_x_bytes + 16u * piece;
+    }
+  }
+  int next = 0;
+  auto issue = [&](int d) {
+    const int c = next < nck ? next : nck - 1;  // past the end: repeat the last chunk into a slot not read again
+    const uint32_t slot = ring0 + (uint32_t)d * kSlot;
+#pragma unroll
+    for (int h = 0; h < 4; ++h) lds_dma16(wq, woff[h] + (uint32_t)c * 256u, slot + 1024u * h);
+#pragma unroll
+    for (int v = 0; v < kXI; ++v)
+      lds_dma16(x, xoff[v] + (uint32_t)c * (kA8 ? 256u : 512u), slot + kF8Chunk + 1024u * v);
+    ++next;
+  };
+#pragma unroll
+  for (int d = 0; d < D; ++d) issue(d);
+
+  const bool mvalid = l16 < M;
+  const float scale = kA8 ? (*sx_p) * (*sw_p) : *sw_p;
+  floatx4 acc = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int c0 = 0; c0 < nck; c0 += D) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      wait_vmcnt<(D - 1) * (4 + kXI)>();
+      const uint8_t* slot = lds + d * kSlot;
+      uint4 w[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        w[j] = *reinterpret_cast<const uint4*>(slot + l16 * 256 + 16 * ((4 * g + j) ^ l16));
+      if constexpr (kA8) {
+        uint4 xa[4] = {make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0),
+                       make_uint4(0, 0, 0, 0)};
+        if (mvalid) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            xa[j] = *reinterpret_cast<const uint4*>(slot + kF8Chunk + l16 * 256 + 16 * (4 * g + j));
+        }
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const uint4 wa[2] = {w[2 * t], w[2 * t + 1]};
+          const uint4 xb[2] = {xa[2 * t], xa[2 * t + 1]};
+          acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(__builtin_bit_cast(i32x8, wa),
+                                                                  __builtin_bit_cast(i32x8, xb), acc, 0, 0, 0, 127, 0,
+                                                                  127);
+        }
+      } else {
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          uint4 xv = make_uint4(0, 0, 0, 0);
+          if (mvalid)
+            xv = *reinterpret_cast<const uint4*>(slot + kF8Chunk + l16 * 512 + 128 * g + 16 * (t ^ g));
+          const uint32_t d0 = dword_of(w[t >> 1], 2 * (t & 1)), d1 = dword_of(w[t >> 1], 2 * (t & 1) + 1);
+          const uint4 e = make_uint4(
+              __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d0, 1.0f, false)),
+              __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d0, 1.0f, true)),
+              __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d1, 1.0f, false)),
+              __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d1, 1.0f, true)));
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, e), __builtin_bit_cast(bf16x8, xv),
+                                                        acc, 0, 0, 0);
+        }
+      }
+      issue(d);
+    }
+  }
+  wait_vmcnt<0>();
+  if (mvalid)
+    store4<kYBf16>(y + (size_t)l16 * ld_y_bytes, tile * 16 + 4 * g, N, acc[0] * scale, acc[1] * scale,
+                   acc[2] * scale, acc[3] * scale);
+}
+
+template <bool kA8>
+static bool gemv_fp8w_stream_go(const void* x, uint32_t ldx, int64_t M, int64_t K, const uint8_t* wq, int64_t N,
+                                const float* sx, const float* sw, void* y, bool y_bf16, size_t ldb, int cus,
+                                hipStream_t s) {
+  // the deepest ring (4 or 2 slots, dividing the chunk count) whose
+  // workgroups all fit on the machine at once
+  const int tiles = (int)((N + 15) / 16);
+  const int nck = (int)(K / 256);
+  const size_t slot = kF8Chunk + 1024u * (kA8 ? 1 : 2);
+  int depth = 0;
+  for (int d : {4, 2}) {
+    if (nck % d) continue;
+    const int64_t per_cu = (int64_t)(160 * 1024) / (int64_t)(d * slot);
+    if (per_cu * cus < tiles && d > 2) continue;
+    depth = d;
+    break;
+  }
+  if (!depth) return false;
+  const size_t lds = (size_t)depth * slot;
+  auto go = [&](auto dc) {
+    constexpr int D = decltype(dc)::value;
+    if (y_bf16)
+      gemv_fp8w_stream_kernel<D, kA8, true><<<tiles, 64, lds, s>>>((const uint8_t*)x, ldx, (int)M, wq, (int)N, (int)K,
+                                                                  sx, sw, (uint8_t*)y, ldb);
+    else
+      gemv_fp8w_stream_kernel<D, kA8, false><<<tiles, 64, lds, s>>>((const uint8_t*)x, ldx, (int)M, wq, (int)N,
+                                                                   (int)K, sx, sw, (uint8_t*)y, ldb);
+  };
+  if (depth == 4) go(std::integral_constant<int, 4>());
+  else go(std::integral_constant<int, 2>());
+  return true;
+}
+
 void launch_gemv_fp8w(bool a8, const void* x, size_t ld_x_bytes, int64_t M, int64_t K, const uint8_t* wq, int64_t N,
                       const float* sx, const float* sw, void* y, bool y_bf16, int64_t ld_y, hipStream_t s) {
   static int cus = 0;
@@ -619,6 +767,14 @@ void launch_gemv_fp8w(bool a8, const void* x, size_t ld_x_bytes, int64_t M, int6
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
       cus = 256;
+  }
+  if (M <= 4 && K >= 256 && K % 256 == 0) {
+    const size_t ldb4 = (size_t)ld_y * (y_bf16 ? 2u : 4u);
+    const bool done = a8 ? gemv_fp8w_stream_go<true>(x, (uint32_t)ld_x_bytes, M, K, wq, N, sx, sw, y, y_bf16, ldb4,
+                                                     cus, s)
+                         : gemv_fp8w_stream_go<false>(x, (uint32_t)ld_x_bytes, M, K, wq, N, sx, sw, y, y_bf16, ldb4,
+                                                      cus, s);
+    if (done) return;
   }
   const int tiles = (int)((N + 15) / 16);
   const int waves = (int)((K + 511) / 512);

@@ -163,7 +163,9 @@ nvfp4_status_t nvfp4_fuse_rescale(int n, uint8_t *const *scales, const int64_t *
  *   x        device [M, ld_x] row-major, F32 or BF16; 16-byte aligned,
  *            ld_x * element size a multiple of 16 bytes, ld_x >= K.
  *   M, K, N  >= 0; K % 64 == 0 (the GEMM advances K 64 at a time, which
- *            is 4 scale bytes, one aligned dword, per weight row).
+ *            is 4 scale bytes, one aligned dword, per weight row); for
+ *            M > 16, K below 2^23 (activation tiles are addressed with
+ *            32-bit offsets), else NVFP4_ERR_SHAPE.
  *   w_codes  device [N, K/2] uint8 dense, 16-byte aligned.
  *   w_scales device [N, K/16] uint8 dense, 4-byte aligned.
  *   w_gs     device, one float.  For a fused weight: the gs_shared of

@@ -144,6 +144,12 @@ nvfp4_status_t nvfp4_fuse_rescale(int n, uint8_t* const* scales, const int64_t* 
   return launched();
 }
 
+// The tile GEMM (M > 16) addresses the fp16 activations of a 256-row tile
+// with 32-bit offsets.
+static bool tile_rows_ok(int64_t M, int64_t K) {
+  return M <= kGemvMaxM || (uint64_t)round_up(K, kGemmBK) * 2u < kMaxTileRowBytes;
+}
+
 // Workspace: absmax partials | gs_x | fp16 activations [Mp, Kp] | fp32 K-part
 // sums of the split tiles (see plan_gemm).
 static size_t x16_bytes(int64_t M, int64_t K) {
@@ -207,7 +213,7 @@ nvfp4_status_t nvfp4_gemm_run(int64_t M, int64_t K, const uint8_t* w_codes, cons
                               void* workspace, size_t workspace_bytes, void* stream) {
   if (!dtype_ok(y_dtype)) return NVFP4_ERR_DTYPE;
   if (M < 0 || K < 0 || N < 0 || M >= kMaxDim || K >= kMaxDim || N >= kMaxDim) return NVFP4_ERR_SHAPE;
-  if (K % 64 != 0) return NVFP4_ERR_SHAPE;
+  if (K % 64 != 0 || !tile_rows_ok(M, K)) return NVFP4_ERR_SHAPE;
   if (M == 0 || N == 0) return NVFP4_OK;
   if (!y || !w_gs) return NVFP4_ERR_NULL;
   if (ld_y < N) return NVFP4_ERR_SHAPE;
@@ -238,7 +244,7 @@ static nvfp4_status_t run_args_ok(int64_t M, int64_t K, const uint8_t* w_codes, 
                                   int64_t ld_y, const void* workspace, size_t workspace_bytes) {
   if (!dtype_ok(y_dtype)) return NVFP4_ERR_DTYPE;
   if (N < 0 || N >= kMaxDim) return NVFP4_ERR_SHAPE;
-  if (K % 64 != 0) return NVFP4_ERR_SHAPE;
+  if (K % 64 != 0 || !tile_rows_ok(M, K)) return NVFP4_ERR_SHAPE;
   if (M == 0 || N == 0) return NVFP4_OK;
   if (!y || !w_gs) return NVFP4_ERR_NULL;
   if (ld_y < N) return NVFP4_ERR_SHAPE;

@@ -135,15 +135,6 @@ __device__ __forceinline__ FastScale fast_scale(float gs) {
   return f;
 }
 
-// Branch-free form of e4m3_encode_sat for v >= 0.
-__device__ __forceinline__ uint32_t e4m3_encode_sat_sel(float v) {
-  const uint32_t u = __float_as_uint(v);
-  const uint32_t nrm = ((u + 0x7FFFFu + ((u >> 20) & 1u)) >> 20) - (120u << 3);
-  const uint32_t sub = (uint32_t)__builtin_rintf(v * 512.0f);
-  const uint32_t r = (v < 0.015625f) ? sub : nrm;
-  return (v < 448.0f) ? r : 0x7Eu;
-}
-
 __device__ __forceinline__ uint32_t cvt_fp4x8(const float (&x)[16], int base, float y) {
   uint32_t r = 0;
   r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, x[base + 0] * y, x[base + 1] * y, 1.0f, 0);
@@ -192,10 +183,15 @@ __device__ __forceinline__ uint32_t resolve_codes8(const float (&x)[16], int bas
 // exact path.
 __device__ __forceinline__ bool encode_block_fast(const float (&x)[16], uint32_t bm, const FastScale& f,
                                                   uint32_t& sb, uint32_t& code_lo, uint32_t& code_hi) {
+  // Both scale bracket ends in one hardware E4M3 conversion (OCP E4M3FN,
+  // round to nearest even, subnormals kept; clamped first so it saturates
+  // at 448 = 0x7E), and the hardware decode of the lower end's byte.
   const float bmf = __uint_as_float(bm);
-  sb = e4m3_encode_sat_sel(bmf * f.rlo);
-  const uint32_t sb_hi = e4m3_encode_sat_sel(bmf * f.rhi);
-  const float es = e4m3_value(sb) * f.gs;
+  const uint32_t pk = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(fminf(bmf * f.rlo, 448.0f),
+                                                                fminf(bmf * f.rhi, 448.0f), 0, false);
+  sb = pk & 0xFFu;
+  const uint32_t sb_hi = (pk >> 8) & 0xFFu;
+  const float es = __builtin_amdgcn_cvt_f32_fp8((int)pk, 0) * f.gs;
   const float y = (es == 0.0f) ? 0.0f : __builtin_amdgcn_rcpf(es);
   const float ylo = y * 0.99999904632568359375f;
   const float yhi = y * 1.00000095367431640625f;

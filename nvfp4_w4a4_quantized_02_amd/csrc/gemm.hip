@@ -29,27 +29,49 @@ namespace nvfp4 {
 // accumulation registers).  K advances 64 per step.
 //
 // Every operand byte reaches LDS by direct global->LDS transfers
-// (global_load_lds): the X tile (256 rows x 64 k fp16 = 32 KB), the W codes
-// (256 rows x 32 B) and the W scale bytes (256 rows x 4 B).  Three buffers
-// form a ring: step kt computes from buffer kt%3 while the transfers of step
-// kt+2 are in flight, so one barrier per step suffices and no staging
-// registers are needed.  Because all memory traffic is of this one kind and
-// completes in issue order, the wait before each barrier is exact.
+// (global_load_lds), six per wave per step, so every step issues the same
+// number and the wait before each barrier is exact:
+//   X: the 256 x 64 fp16 tile of the step (32 KB), four transfers per wave;
+//   W codes: 64 B of every W row, i.e. two steps at once (16 KB per group),
+//     one transfer per wave per step, each covering 16 rows x 64 B;
+//   W scale bytes: 16 B of every W row, i.e. four steps at once (4 KB per
+//     group), one 32-lane transfer per wave per step covering 8 rows x 16 B.
+// A transfer costs roughly in proportion to the 128-byte lines it touches,
+// so wide groups for the strided W rows matter: a per-step 32 B code slice
+// and 4 B scale slice of each row would touch twice and four times as many
+// lines.  Each operand has a ring of three buffers: step i computes from
+// X buffer i%3, code group (i/2)%3 and scale group (i/4)%3, while the
+// transfers for X step i+2, half (i%2) of code group i/2+2 and quarter (i%4)
+// of scale group i/4+2 are in flight; steps are counted from the first step
+// of the workgroup's K range.  The main loop is unrolled by three, so the X
+// buffer is a constant and the W buffers are picked per step.
 //
-// LDS layouts (16-byte slots): X chunk (row, c) sits in slot
-// c ^ (row & 7) ^ ((row >> 3) & 1) of its row; W code half (row, h) in slot
-// h ^ (((row >> 2) ^ (row >> 3)) & 1).  Any 8 or 16 consecutive rows then hit
-// distinct 16-byte bank groups, so the 128-bit operand reads are free of
-// bank conflicts whether the LDS serves 8 or 16 lanes per pass.
+// LDS layouts (16-byte slots unless noted):
+//   X chunk (row, c) in slot c ^ (row & 7) ^ ((row >> 3) & 1) of its row;
+//   W code piece p (16 B = 32 k; pieces 0, 1 = first step of the group) of
+//     row r in slot p ^ swz(r), swz(r) = ((r>>2 ^ r>>3) & 1) << 1 | ((r>>1 ^ r>>2) & 1);
+//   W scale dword d (the four block scales of one step) of row r in dword
+//     slot d ^ ((r >> 3) & 3) of the row's 16 bytes.
+// Any 8 or 16 consecutive rows then hit distinct 16-byte bank groups for the
+// 128-bit operand reads, and 32 consecutive rows distinct banks for the
+// scale dwords.
 
-struct GemmBuf {
-  uint4 x[kGemmBM * 8];        // 32 KB
-  uint4 wc[kGemmBN * 2];       // 8 KB
-  uint32_t ws[8 * 64];         // 2 KB: wave w's 32 rows at [64w, 64w+32), repeated in [64w+32, 64w+64)
+struct GemmSmem {
+  uint4 x[3][kGemmBM * 8];      // 3 x 32 KB
+  uint4 wc[3][kGemmBN * 4];     // 3 x 16 KB
+  uint32_t ws[3][kGemmBN * 4];  // 3 x 4 KB
 };
 
 constexpr int kGemmWaves = 8;
 constexpr int kDmaPerStep = 6;  // per wave: 4 (X) + 1 (W codes) + 1 (W scales)
+
+// sched_barrier mask: everything but MFMAs (and the transfers themselves)
+// may still be scheduled across the barrier (VALU, SALU, LDS, transcendental).
+constexpr int kSchedKeepMfma = 0x0002 | 0x0004 | 0x0080 | 0x0100 | 0x0200 | 0x0400;
+
+__device__ __forceinline__ uint32_t wc_swz(uint32_t r) {
+  return ((((r >> 2) ^ (r >> 3)) & 1u) << 1) | (((r >> 1) ^ (r >> 2)) & 1u);
+}
 
 template <bool kA16, bool kYBf16>
 __global__ __launch_bounds__(512, 1) void gemm_kernel(const uint4* __restrict__ x16, uint32_t kp_chunks,
@@ -59,11 +81,9 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const uint4* __restrict__ 
                                                        const float* __restrict__ gsw_p, uint8_t* __restrict__ y,
                                                        size_t ld_y_bytes, int tiles_n, int nk, int full_tiles,
                                                        int split, float* __restrict__ partials) {
-  // Three distinct buffers (not one indexed array) so the compiler can see
-  // that a transfer into one buffer never feeds reads of another.
   using O = Op<kA16>;
   using V = typename O::vec8;
-  __shared__ GemmBuf b0, b1, b2;
+  __shared__ GemmSmem sm;
   __shared__ uint32_t scale_lut[128];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wave_n = wave >> 1, wave_m = wave & 1;  // W rows 64 wave_n.., X rows 128 wave_m..
@@ -80,13 +100,14 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const uint4* __restrict__ 
   const int tn = tile % tiles_n, tm = tile / tiles_n;
   const int n0 = tn * kGemmBN, m0 = tm * kGemmBM;
   const int l32 = lane & 31, h = lane >> 5;
-  const size_t kh = (size_t)K / 2, ks = (size_t)K / 16;
+  const uint32_t kh = (uint32_t)K / 2, ks = (uint32_t)K / 16;
+  const int n = ke - kb;  // steps of this workgroup
 
-  // ---- transfer sources: a wave-uniform base per step plus per-lane byte
-  // offsets fixed for the whole loop.
-  const uint8_t* xbase = reinterpret_cast<const uint8_t*>(x16 + (size_t)m0 * kp_chunks);  // + 128 B per step
-  const uint8_t* wcbase = wc + (size_t)n0 * kh;                                          // + 32 B per step
-  const uint8_t* wsbase = ws + (size_t)n0 * ks;                                          // + 4 B per step
+  // ---- transfer sources: a wave-uniform base per step or group plus per-lane
+  // byte offsets fixed for the whole loop.
+  const uint8_t* xbase = reinterpret_cast<const uint8_t*>(x16 + (size_t)m0 * kp_chunks) + (size_t)kb * 128;
+  const uint8_t* wcbase = wc + (size_t)n0 * kh;
+  const uint8_t* wsbase = ws + (size_t)n0 * ks;
   uint32_t xoff[4];  // X: instruction j fills slots (wave*4+j)*64 + lane (row (wave*4+j)*8 + lane/8)
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -94,32 +115,37 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const uint4* __restrict__ 
     row = m0 + row < M ? row : M - 1 - m0;   // rows past M repeat the last one (not stored)
     xoff[j] = ((uint32_t)row * kp_chunks + ((lane & 7) ^ ((lane >> 3) & 7) ^ (j & 1))) * 16u;
   }
-  uint32_t wcoff;  // W codes: the instruction fills slots wave*64 + lane = row*2 + physical half
-  {
-    int row = wave * 32 + (lane >> 1);
-    row = n0 + row < N ? row : N - 1 - n0;   // rows past N repeat the last one (not stored)
-    wcoff = (uint32_t)row * (uint32_t)kh + (uint32_t)(((lane & 1) ^ (((lane >> 3) ^ (lane >> 4)) & 1)) * 16);
-  }
-  uint32_t wsoff;  // W scales: one dword (4 blocks) per row; lanes 32..63 repeat lanes 0..31
-  {
-    int row = wave * 32 + (lane & 31);
-    row = n0 + row < N ? row : N - 1 - n0;
-    wsoff = (uint32_t)row * (uint32_t)ks;
-  }
-  // LDS byte addresses of this wave's transfer slots in each buffer
-  const uint32_t lx0 = lds_addr(&b0.x[wave * 256]), lx1 = lds_addr(&b1.x[wave * 256]),
-                 lx2 = lds_addr(&b2.x[wave * 256]);
-  const uint32_t lc0 = lds_addr(&b0.wc[wave * 64]), lc1 = lds_addr(&b1.wc[wave * 64]),
-                 lc2 = lds_addr(&b2.wc[wave * 64]);
-  const uint32_t ls0 = lds_addr(&b0.ws[wave * 64]), ls1 = lds_addr(&b1.ws[wave * 64]),
-                 ls2 = lds_addr(&b2.ws[wave * 64]);
+  // W codes: the transfer of half hh fills rows 128 hh + 16 wave + lane/4,
+  // slot lane%4 of the row, with piece (lane%4) ^ swz(row).  Pieces past the
+  // end of a row (a group reaching past K) re-read the row's last 16 bytes.
+  // W scales: the transfer of quarter qq fills (lanes 0..31) rows
+  // 64 qq + 8 wave + lane/4, dword slot lane%4 of the row, with dword
+  // (lane%4) ^ ((row >> 3) & 3) = (lane%4) ^ (wave & 3).  Rows past N repeat
+  // the last one (never stored).  These offsets are recomputed per transfer
+  // (a few integer operations) rather than held in registers.
+  const int nrows = N - n0;
+  const int last = n - 1;
+  const int glast = last >> 1, Glast = last >> 2;
 
-  auto issue = [&](int kt, uint32_t lx, uint32_t lc, uint32_t ls) {
-    const uint8_t* xb = xbase + (size_t)kt * 128;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) lds_dma16(xb, xoff[j], lx + j * 1024);
-    lds_dma16(wcbase + (size_t)kt * 32, wcoff, lc);
-    lds_dma4(wsbase + (size_t)kt * 4, wsoff, ls);
+  // Transfers into buffer b of each ring.  Sources past the range repeat
+  // the last step or group (into buffers that are no longer read).
+  auto issue_x = [&](int i, int j, int b) {
+    const uint8_t* xb = xbase + (size_t)(i < last ? i : last) * 128;
+    lds_dma16(xb, xoff[j], lds_addr(&sm.x[b][wave * 256 + j * 64]));
+  };
+  auto issue_wc = [&](int g, int hh, int b) {
+    const uint32_t goff = (uint32_t)(kb + 2 * (g < glast ? g : glast)) * 32u;
+    const int row = 128 * hh + 16 * wave + (lane >> 2);
+    const uint32_t piece = (((uint32_t)lane & 3u) ^ wc_swz((uint32_t)row)) * 16u;
+    const uint32_t off = (uint32_t)(row < nrows ? row : nrows - 1) * kh + min(goff + piece, kh - 16u);
+    lds_dma16(wcbase, off, lds_addr(&sm.wc[b][(128 * hh + 16 * wave) * 4]));
+  };
+  auto issue_ws = [&](int G, int qq, int b) {
+    const uint32_t goff = (uint32_t)(kb + 4 * (G < Glast ? G : Glast)) * 4u;
+    const int row = 64 * qq + 8 * wave + (l32 >> 2);
+    const uint32_t dw = (((uint32_t)lane & 3u) ^ ((uint32_t)wave & 3u)) * 4u;
+    const uint32_t off = (uint32_t)(row < nrows ? row : nrows - 1) * ks + min(goff + dw, ks - 4u);
+    if (lane < 32) lds_dma4(wsbase, off, lds_addr(&sm.ws[b][(64 * qq + 8 * wave) * 4]));
   };
 
   floatx16 acc[2][4];
@@ -135,21 +161,25 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const uint4* __restrict__ 
   // is ignored).
   if (tid < 128) scale_lut[tid] = O::scale_bits((uint32_t)tid);
 
-  // Operand fragments of sub-step j from buffer `cur`.
-  auto read_x = [&](const GemmBuf& cur, int j, V (&bx)[4]) {
+  // Operand fragments of sub-step j from X buffer b.
+  auto read_x = [&](int b, int j, V (&bx)[4]) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int row = wave_m * 128 + u * 32 + l32;
-      bx[u] = O::vec(cur.x[row * 8 + ((4 * h + j) ^ (row & 7) ^ ((row >> 3) & 1))]);
+      bx[u] = O::vec(sm.x[b][row * 8 + ((4 * h + j) ^ (row & 7) ^ ((row >> 3) & 1))]);
     }
   };
-  // W codes (one dword per sub-step) and the two block scales of this lane.
-  auto read_w = [&](const GemmBuf& cur, uint4 (&wv)[2], uint32_t (&sw)[2]) {
+  // W codes of one step (one 16-byte piece per row and lane) and the two
+  // block scales of this lane: step s of code group buffer bc (s%2 = its
+  // position in the group) and scale group buffer bs (s%4).
+  auto read_w = [&](int bc, int sp2, int bs, int sp4, uint4 (&wv)[2], uint32_t (&sw)[2]) {
+    const uint4* cb = sm.wc[bc];
+    const uint32_t* sb = sm.ws[bs];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      const int row = wave_n * 64 + t * 32 + l32;
-      wv[t] = cur.wc[row * 2 + (h ^ (((row >> 2) ^ (row >> 3)) & 1))];
-      sw[t] = cur.ws[(wave_n * 2 + t) * 64 + l32] >> (16 * h);
+      const uint32_t row = wave_n * 64 + t * 32 + l32;
+      wv[t] = cb[row * 4 + ((uint32_t)(2 * sp2 + h) ^ wc_swz(row))];
+      sw[t] = sb[row * 4 + ((uint32_t)sp4 ^ ((row >> 3) & 3u))] >> (16 * h);
     }
   };
   auto split_w = [&](const uint32_t (&sw)[2], uint32_t (&sp)[2][2]) {
@@ -167,11 +197,13 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const uint4* __restrict__ 
       aw[t] = O::vec(make_uint4(e[0], e[1], e[2], e[3]));
     }
   };
+  auto mfma4 = [&](int t, const V (&aw)[2], const V (&bx)[4]) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) acc[t][u] = O::mfma32(aw[t], bx[u], acc[t][u]);
+  };
   auto mfma8 = [&](const V (&aw)[2], const V (&bx)[4]) {
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int u = 0; u < 4; ++u) acc[t][u] = O::mfma32(aw[t], bx[u], acc[t][u]);
+    mfma4(0, aw, bx);
+    mfma4(1, aw, bx);
   };
 
   // Register-resident operands carried across sub-steps and steps: the W
@@ -181,66 +213,95 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const uint4* __restrict__ 
   uint32_t sp[2][2];
   V bx[4], aw[2];
 
-  // One main-loop step.  Sub-steps 0..2 of step kt run from `cur`, each
-  // overlapping the LDS reads and expansion of the following sub-step.  Then
-  // the wave waits for the transfers of step kt+1 and meets the barrier with
-  // the operands of sub-step 3 in registers; its 16 MFMAs run after the
-  // barrier and cover the LDS reads, scale lookups and first expansion of
-  // step kt+1 (from `nxt`).  The transfers of step kt+2 (into `nxt2`) are
-  // issued at the start; every step issues the same transfers (near the end
-  // they repeat the last step into a buffer that is no longer read), so the
-  // wait count is the same in every step.
-  auto step = [&](int kt, const GemmBuf& cur, const GemmBuf& nxt, uint32_t lx, uint32_t lc, uint32_t ls) {
-    const int last = ke - 1;
-    issue(kt + 2 < last ? kt + 2 : last, lx, lc, ls);
+  // Ring buffer of code group g and scale group G (wave-uniform).
+  auto mod3 = [](int v) { return (int)((uint32_t)v % 3u); };
+
+  // One main-loop step, i = I (mod 3).  Sub-steps 0..2 run from X buffer I,
+  // each overlapping the LDS reads and expansion of the following sub-step.
+  // Then the wave waits for its transfers issued one step earlier and meets
+  // the barrier with the operands of sub-step 3 in registers; its 16 MFMAs
+  // run after the barrier and cover the LDS reads, scale lookups and first
+  // expansion of step i+1.  Step i+1's operands are prepared even after the
+  // last step (the buffers then hold repeated, finite data), which keeps
+  // this branch-free.
+  // The six transfers are spread over the sub-steps, one after every four
+  // MFMAs, and pinned there: issued back to back, all waves of the
+  // workgroup would queue their transfers at once right after the barrier
+  // and stall their MFMA issue behind them.
+  auto pinned = [&](auto&& f) {
+    __builtin_amdgcn_sched_barrier(kSchedKeepMfma);
+    f();
+    __builtin_amdgcn_sched_barrier(kSchedKeepMfma);
+  };
+  auto step = [&](auto ic, int i) {
+    constexpr int I = decltype(ic)::value;
+    const int bw = mod3((i >> 1) + 2), bs = mod3((i >> 2) + 2);
 #pragma unroll
     for (int j = 0; j < 3; ++j) {
       V bxn[4], awn[2];
-      read_x(cur, j + 1, bxn);
-      mfma8(aw, bx);
+      read_x(I, j + 1, bxn);
+      mfma4(0, aw, bx);
+      if (j == 0) pinned([&] { issue_wc((i >> 1) + 2, i & 1, bw); });
+      if (j == 1) pinned([&] { issue_x(i + 2, 1, (I + 2) % 3); });
+      if (j == 2) pinned([&] { issue_x(i + 2, 3, (I + 2) % 3); });
+      mfma4(1, aw, bx);
+      if (j == 0) pinned([&] { issue_ws((i >> 2) + 2, i & 3, bs); });
+      if (j == 1) pinned([&] { issue_x(i + 2, 0, (I + 2) % 3); });
+      if (j == 2) pinned([&] { issue_x(i + 2, 2, (I + 2) % 3); });
       expand_w(wv, sp, j + 1, awn);
 #pragma unroll
       for (int q = 0; q < 4; ++q) bx[q] = bxn[q];
 #pragma unroll
       for (int q = 0; q < 2; ++q) aw[q] = awn[q];
     }
-    // All LDS reads of `cur` have completed and this wave's transfers of step
-    // kt+1 have landed (only step kt+2's 6 may be in flight); after the
-    // barrier every wave's have.  The barrier is a bare s_barrier: a
-    // workgroup fence would also wait for the transfers still in flight.
+    // All LDS reads of this step have completed and this wave's transfers of
+    // the previous step have landed (only this step's 6 may be in flight);
+    // after the barrier every wave's have.  The barrier is a bare s_barrier:
+    // a workgroup fence would also wait for the transfers still in flight.
     asm volatile("s_waitcnt vmcnt(6) lgkmcnt(0)\n\ts_barrier" ::: "memory");
     V bx3[4], aw3[2];
 #pragma unroll
     for (int q = 0; q < 4; ++q) bx3[q] = bx[q];
 #pragma unroll
     for (int q = 0; q < 2; ++q) aw3[q] = aw[q];
-    // Step kt+1's operands are prepared even after the last step (the
-    // buffer then holds a repeated, finite copy), which keeps this branch-free.
+    const int i1 = i + 1;
     uint32_t sw[2];
-    read_w(nxt, wv, sw);
-    read_x(nxt, 0, bx);
+    read_w(mod3(i1 >> 1), i1 & 1, mod3(i1 >> 2), i1 & 3, wv, sw);
+    read_x((I + 1) % 3, 0, bx);
     mfma8(aw3, bx3);
     split_w(sw, sp);
     expand_w(wv, sp, 0, aw);
   };
   static_assert(kDmaPerStep == 6, "the wait count above must match the transfers per step");
 
-  if (ke > kb) {
-    issue(kb, lx0, lc0, ls0);
-    issue(kb + 1 < ke ? kb + 1 : kb, lx1, lc1, ls1);
+  if (n > 0) {
+    // Steps 0 and 1 of X, code groups 0 and 1 (steps 0..3), scale groups 0
+    // and 1 (steps 0..7): ten transfers for step 0, then ten more.
+#pragma unroll
+    for (int j = 0; j < 4; ++j) issue_x(0, j, 0);
+    issue_wc(0, 0, 0);
+    issue_wc(0, 1, 0);
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq) issue_ws(0, qq, 0);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) issue_x(1, j, 1);
+    issue_wc(1, 0, 1);
+    issue_wc(1, 1, 1);
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq) issue_ws(1, qq, 1);
     // the scale table above is written with ordinary LDS stores
-    asm volatile("s_waitcnt vmcnt(6) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    asm volatile("s_waitcnt vmcnt(10) lgkmcnt(0)\n\ts_barrier" ::: "memory");
     {
       uint32_t sw[2];
-      read_w(b0, wv, sw);
-      read_x(b0, 0, bx);
+      read_w(0, 0, 0, 0, wv, sw);
+      read_x(0, 0, bx);
       split_w(sw, sp);
       expand_w(wv, sp, 0, aw);
     }
-    for (int kt = kb; kt < ke; kt += 3) {
-      step(kt, b0, b1, lx2, lc2, ls2);
-      if (kt + 1 < ke) step(kt + 1, b1, b2, lx0, lc0, ls0);
-      if (kt + 2 < ke) step(kt + 2, b2, b0, lx1, lc1, ls1);
+    for (int i = 0; i < n; i += 3) {
+      step(std::integral_constant<int, 0>{}, i);
+      if (i + 1 < n) step(std::integral_constant<int, 1>{}, i + 1);
+      if (i + 2 < n) step(std::integral_constant<int, 2>{}, i + 2);
     }
     // drain the repeated transfers before the workgroup can exit
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -273,8 +334,8 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const uint4* __restrict__ 
     for (int t = 0; t < 2; ++t) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int n = n0 + wave_n * 64 + t * 32 + 8 * q + 4 * h;
-        store4<kYBf16>(yrow, n, N, acc[t][u][4 * q] * scale, acc[t][u][4 * q + 1] * scale,
+        const int nn = n0 + wave_n * 64 + t * 32 + 8 * q + 4 * h;
+        store4<kYBf16>(yrow, nn, N, acc[t][u][4 * q] * scale, acc[t][u][4 * q + 1] * scale,
                        acc[t][u][4 * q + 2] * scale, acc[t][u][4 * q + 3] * scale);
       }
     }

@@ -101,8 +101,24 @@ __device__ __forceinline__ void load_block(const uint8_t* __restrict__ p, float 
   }
 }
 
-// fp32 bits of the largest |x| of a block.  For bf16 input the max runs on
-// the packed 16-bit patterns (same order as the values for |x|).
+// fp32 bits of the largest |x| of a bf16 block from its eight raw words: the
+// max runs on the packed 16-bit magnitude patterns (integer order is value
+// order for non-negative floats), two per instruction.
+typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t bf16_absmax_bits(const uint32_t (&w)[8]) {
+  u16x2_t m[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) m[j] = __builtin_bit_cast(u16x2_t, w[j] & 0x7FFF7FFFu);
+  const u16x2_t a = __builtin_elementwise_max(__builtin_elementwise_max(m[0], m[1]),
+                                              __builtin_elementwise_max(m[2], m[3]));
+  const u16x2_t b = __builtin_elementwise_max(__builtin_elementwise_max(m[4], m[5]),
+                                              __builtin_elementwise_max(m[6], m[7]));
+  const u16x2_t c = __builtin_elementwise_max(a, b);
+  const uint32_t lo = c[0], hi = c[1];
+  return (hi > lo ? hi : lo) << 16;
+}
+
+// fp32 bits of the largest |x| of a block.
 template <bool kBf16>
 __device__ __forceinline__ uint32_t block_absmax_bits(const float (&x)[16]) {
   uint32_t bm = 0;
@@ -192,16 +208,11 @@ __global__ __launch_bounds__(256) void quantize_kernel(const uint8_t* __restrict
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   };
 
-  // Raw input words of one block.  The next block's words are fetched
-  // before the current block is encoded, so every wave keeps two blocks in
-  // flight; blocks past the end or in padding fetch a valid block (the last
-  // one, or the row's last real one) that is never encoded, so every fetch is
-  // unconditional.
+  // Raw input words of the block at row r, block kb of the row.  Blocks in
+  // the padding (kb >= kblocks) read the row's last real block instead,
+  // which is never encoded, so every load is unconditional.
   constexpr int kWords = kBf16 ? 8 : 16;
-  auto fetch = [&](uint32_t b, uint32_t (&w)[kWords]) {
-    const uint32_t bb = b < total_blocks ? b : total_blocks - 1u;
-    const uint32_t r = fastdiv(bb, fd);
-    uint32_t kb = bb - r * out_kblocks;
+  auto load_at = [&](uint32_t r, uint32_t kb, uint32_t (&w)[kWords]) {
     kb = kb < kblocks ? kb : kblocks - 1u;
     const uint4* q = reinterpret_cast<const uint4*>(x + (size_t)r * ld_bytes + (size_t)kb * (kBf16 ? 32u : 64u));
 #pragma unroll
@@ -215,13 +226,29 @@ __global__ __launch_bounds__(256) void quantize_kernel(const uint8_t* __restrict
   };
   const int32_t last = (int32_t)((chunks - 1u - wave_id) / waves);
   auto block_of = [&](int32_t it) { return (wave_id + (uint32_t)it * waves) * 64u + lane; };
+  // A lane visits blocks b, b - stride, b - 2 stride, ... (stride = the
+  // wave's chunk step).  Their (row, block-in-row) positions are stepped down
+  // by the stride's quotient and remainder rather than divided out per block.
+  const uint32_t stride = waves * 64u;
+  const uint32_t sq = fastdiv(stride, fd), sr = stride - sq * out_kblocks;
+  uint32_t pr, pk;  // position of the block fetched last
+  {
+    const uint32_t b = block_of(last);
+    pr = fastdiv(b, fd);
+    pk = b - pr * out_kblocks;
+  }
+  auto step_back = [&]() {
+    const bool borrow = pk < sr;
+    pk = pk - sr + (borrow ? out_kblocks : 0u);
+    pr = pr - sq - (borrow ? 1u : 0u);
+  };
 
   uint32_t queued = 0;  // wave-uniform
-  auto encode = [&](uint32_t b, const uint32_t (&w)[kWords]) {
+  // kb: the block's position in its row.
+  auto encode = [&](uint32_t b, uint32_t kb, const uint32_t (&w)[kWords]) {
     bool settled = true;
     if (b < total_blocks) {
-      const uint32_t r = fastdiv(b, fd);
-      if (kF16 && b - r * out_kblocks >= kblocks) {
+      if (kF16 && kb >= kblocks) {
         x16[(size_t)b * 2u] = make_uint4(0, 0, 0, 0);
         x16[(size_t)b * 2u + 1u] = make_uint4(0, 0, 0, 0);
       } else {
@@ -235,8 +262,14 @@ __global__ __launch_bounds__(256) void quantize_kernel(const uint8_t* __restrict
             xv[i] = __uint_as_float(w[i]);
           }
         }
+        uint32_t bm;
+        if constexpr (kBf16) {
+          bm = bf16_absmax_bits(w);
+        } else {
+          bm = block_absmax_bits<false>(xv);
+        }
         uint32_t sb, lo, hi;
-        settled = encode_block_fast(xv, block_absmax_bits<kBf16>(xv), fsc, sb, lo, hi);
+        settled = encode_block_fast(xv, bm, fsc, sb, lo, hi);
         if (settled) store(b, sb, lo, hi);
       }
     }
@@ -253,15 +286,29 @@ __global__ __launch_bounds__(256) void quantize_kernel(const uint8_t* __restrict
     }
   };
 
-  // Two register sets alternate (no copies, which would wait for the fetch).
+  // Two register sets alternate (no copies, which would wait for the fetch):
+  // the next block's words are fetched before the current block is encoded,
+  // so every wave keeps two blocks in flight.  The first block of the last
+  // chunk may lie past the end; it then reads the tensor's last block.
   uint32_t wa[kWords], wb[kWords];
-  fetch(block_of(last), wa);
+  uint32_t ka = pk, kbb = 0;  // positions of the blocks held in wa, wb
+  {
+    const bool in = block_of(last) < total_blocks;
+    const uint32_t rl = fastdiv(total_blocks - 1u, fd);
+    load_at(in ? pr : rl, in ? pk : total_blocks - 1u - rl * out_kblocks, wa);
+  }
+  // Past the wave's first block the position stays put, so the surplus
+  // loads at the end re-read a valid block.
   for (int32_t it = last;; it -= 2) {
-    fetch(block_of(it >= 1 ? it - 1 : 0), wb);
-    encode(block_of(it), wa);
+    if (it >= 1) step_back();
+    load_at(pr, pk, wb);
+    kbb = pk;
+    encode(block_of(it), ka, wa);
     if (it < 1) break;
-    fetch(block_of(it >= 2 ? it - 2 : 0), wa);
-    encode(block_of(it - 1), wb);
+    if (it >= 2) step_back();
+    load_at(pr, pk, wa);
+    ka = pk;
+    encode(block_of(it - 1), kbb, wb);
     if (it < 2) break;
   }
   if (queued) flush(queued);

@@ -94,6 +94,8 @@ def test_gemm_rejects(nv):
     assert g(nv, ydt=7) == E_DTYPE
     assert g(nv, K=48, ld=48) == E_SHAPE              # K % 64
     assert g(nv, K=96, ld=96) == E_SHAPE
+    assert g(nv, K=1 << 23, ld=1 << 23) == E_SHAPE    # tile rows past 32-bit offsets (M > 16)
+    assert nv.lib.nvfp4_gemm_run(32, 1 << 23, A, A, A, 64, A, BF16, 64, A, BIG, None) == E_SHAPE
     assert g(nv, N=-3) == E_SHAPE
     assert g(nv, ldy=32) == E_SHAPE
     assert g(nv, y=None) == E_NULL

@@ -60,14 +60,16 @@ __device__ __forceinline__ Bounds make_bounds(float es) {
 }
 
 // Magnitude code of a = |x| (fp32 bits compared as integers: both are
-// non-negative, so integer and float order agree).
+// non-negative, so integer and float order agree): the number of bounds
+// passed, the bounds being increasing.  A count rather than a binary search:
+// a search picks bounds by computed index, which turns the bound array into
+// addressable memory (the compiler then places it in LDS and reads the
+// dispatch packet at every wave's start to index it), and this path is rare.
 __device__ __forceinline__ uint32_t mag_from_bounds(uint32_t a, const uint32_t (&b)[7]) {
-  uint32_t c4 = a > b[3];
-  uint32_t mid = c4 ? b[5] : b[1];
-  uint32_t c2 = a > mid;
-  uint32_t lo = c4 ? (c2 ? b[6] : b[4]) : (c2 ? b[2] : b[0]);
-  uint32_t c1 = a > lo;
-  return (c4 << 2) | (c2 << 1) | c1;
+  uint32_t c = 0;
+#pragma unroll
+  for (int k = 0; k < 7; ++k) c += a > b[k] ? 1u : 0u;
+  return c;
 }
 
 // Encode one block.  absbits[j] = fp32 bits of |x_j|, signs = bit j set when

@@ -132,12 +132,12 @@ __device__ __forceinline__ uint32_t block_absmax_bits(const float (&x)[16]) {
 
 // ------------------------------------------------------------------ encode
 // One lane per 16-element block, 64 consecutive blocks per wave and step.
-// The fast encoder settles almost every block; the few whose bracket
-// straddles a decision point (values on or next to a rounding tie, which
-// short bf16 and E4M3 significands make common enough to hit most waves)
-// are queued in the wave's slice of LDS and encoded exactly in batches of
-// up to 64, so the exact path runs with full waves instead of stalling the
-// fast path of every wave that holds one such block.
+// The fast encoder settles every block whose scale is in its range,
+// rounding ties included; the rest (a subnormal es, a reciprocal that
+// overflows, a tensor scale out of range) are queued in the wave's slice of
+// LDS and encoded exactly in batches of up to 64, so the exact path runs
+// with full waves instead of stalling the fast path of every wave that
+// holds one such block.
 //
 // The steps walk the tensor from its end back to its start, the reverse of
 // the absmax pass, so the part read last by that pass is read first here,

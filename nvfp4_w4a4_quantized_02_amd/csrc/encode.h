@@ -101,6 +101,85 @@ __device__ __forceinline__ uint32_t encode_block(const uint32_t (&absbits)[16], 
   return s.sb;
 }
 
+// fp32 bits of the largest |x| of a bf16 block from its eight raw words: the
+// max runs on the packed 16-bit magnitude patterns (integer order is value
+// order for non-negative floats), two per instruction.
+typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t bf16_absmax_bits(const uint32_t (&w)[8]) {
+  u16x2_t m[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) m[j] = __builtin_bit_cast(u16x2_t, w[j] & 0x7FFF7FFFu);
+  const u16x2_t a = __builtin_elementwise_max(__builtin_elementwise_max(m[0], m[1]),
+                                              __builtin_elementwise_max(m[2], m[3]));
+  const u16x2_t b = __builtin_elementwise_max(__builtin_elementwise_max(m[4], m[5]),
+                                              __builtin_elementwise_max(m[6], m[7]));
+  const u16x2_t c = __builtin_elementwise_max(a, b);
+  const uint32_t lo = c[0], hi = c[1];
+  return (hi > lo ? hi : lo) << 16;
+}
+
+// fp32 bits of the largest |x| of a block.
+template <bool kBf16>
+__device__ __forceinline__ uint32_t block_absmax_bits(const float (&x)[16]) {
+  uint32_t bm = 0;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const uint32_t a = __float_as_uint(x[j]) & 0x7FFFFFFFu;
+    bm = bm > a ? bm : a;
+  }
+  return bm;
+}
+
+// Raw words of one block: bf16 eight dwords (two elements each), fp32
+// sixteen.
+template <bool kBf16>
+struct BlockWords {
+  static constexpr int n = kBf16 ? 8 : 16;
+};
+
+template <bool kBf16>
+__device__ __forceinline__ void load_words(const uint8_t* __restrict__ p, uint32_t (&w)[BlockWords<kBf16>::n]) {
+  const uint4* q = reinterpret_cast<const uint4*>(p);
+#pragma unroll
+  for (int c = 0; c < BlockWords<kBf16>::n / 4; ++c) {
+    const uint4 v = q[c];
+    w[4 * c] = v.x;
+    w[4 * c + 1] = v.y;
+    w[4 * c + 2] = v.z;
+    w[4 * c + 3] = v.w;
+  }
+}
+
+// The block as fp32 (bf16 widened exactly).
+template <bool kBf16>
+__device__ __forceinline__ void words_to_floats(const uint32_t (&w)[BlockWords<kBf16>::n], float (&xv)[16]) {
+#pragma unroll
+  for (int i = 0; i < BlockWords<kBf16>::n; ++i) {
+    if (kBf16) {
+      xv[2 * i] = __uint_as_float(w[i] << 16);
+      xv[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+    } else {
+      xv[i] = __uint_as_float(w[i]);
+    }
+  }
+}
+
+// fp32 bits of the block's largest |x|.
+template <bool kBf16>
+__device__ __forceinline__ uint32_t words_absmax_bits(const uint32_t (&w)[BlockWords<kBf16>::n]) {
+  if constexpr (kBf16) {
+    return bf16_absmax_bits(w);
+  } else {
+    uint32_t bm = 0;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const uint32_t a = w[j] & 0x7FFFFFFFu;
+      bm = bm > a ? bm : a;
+    }
+    return bm;
+  }
+}
+
 // Fast block encoder.  Every rounding decision is bracketed: a decision is
 // taken by the fast path only when both ends of a bracket around the exact
 // operand give the same result, and a block whose bracket straddles a
@@ -149,41 +228,25 @@ __device__ __forceinline__ uint32_t cvt_fp4x8(const float (&x)[16], int base, fl
   return r;
 }
 
-// Exact code of one element whose bracket straddles a decision point.  The
-// bracket ends differ by one step (decision points are at least 0.5 apart in
-// quotient space, the bracket is 2^-19 wide), so the magnitude is k or k + 1
-// with k the lower end's, and the one bound between them decides it exactly
-// (the same bound make_bounds gives).  ca: the lower end's code (sign kept).
-__device__ __forceinline__ uint32_t resolve_code(float x, float es, uint32_t ca) {
-  const uint32_t k = ca & 7u;
-  const double T = k == 0 ? e2m1_decision(0)
-                 : k == 1 ? e2m1_decision(1)
-                 : k == 2 ? e2m1_decision(2)
-                 : k == 3 ? e2m1_decision(3)
-                 : k == 4 ? e2m1_decision(4)
-                 : k == 5 ? e2m1_decision(5) : e2m1_decision(6);
-  const float b = bound_from(T * (double)es, (k & 1u) == 0u);
-  const uint32_t a = __float_as_uint(x) & 0x7FFFFFFFu;  // |x| and b are non-negative: integer order is float order
-  return (ca & 8u) | (k + (a > __float_as_uint(b) ? 1u : 0u));
-}
-
-// Replace every code nibble of `a` that differs from `b` by its exact value.
-__device__ __forceinline__ uint32_t resolve_codes8(const float (&x)[16], int base, float es, uint32_t a,
-                                                   uint32_t b) {
-  const uint32_t d = a ^ b;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    if ((d >> (4 * j)) & 15u) {
-      const uint32_t c = resolve_code(x[base + j], es, (a >> (4 * j)) & 15u);
-      a = (a & ~(15u << (4 * j))) | (c << (4 * j));
-    }
-  }
-  return a;
+// Exact codes of 8 elements: the hardware FP4 conversion (round to nearest
+// even, saturating, sign kept) of the correctly rounded quotients
+// RN(x / es), which is the rule itself.  Used for a half-block whose bracket
+// straddles a decision point somewhere: eight divisions, branch-free, cost
+// less than settling the straddling elements one by one with their own
+// bounds (a divergent loop over the nibbles).  Requires es > 0.
+__device__ __forceinline__ uint32_t exact_codes8(const float (&x)[16], int base, float es) {
+  uint32_t r = 0;
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, __fdiv_rn(x[base + 0], es), __fdiv_rn(x[base + 1], es), 1.0f, 0);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, __fdiv_rn(x[base + 2], es), __fdiv_rn(x[base + 3], es), 1.0f, 1);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, __fdiv_rn(x[base + 4], es), __fdiv_rn(x[base + 5], es), 1.0f, 2);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, __fdiv_rn(x[base + 6], es), __fdiv_rn(x[base + 7], es), 1.0f, 3);
+  return r;
 }
 
 // x: the 16 values as fp32 (bf16 widened exactly); bm: fp32 bits of the
-// largest |x|.  On success writes the scale byte and the codes; elements on
-// or next to a decision point are settled one by one.  Returns false only
+// largest |x|.  On success writes the scale byte and the codes; a half-block
+// with an element on or next to a decision point is settled by division.
+// Returns false only
 // for a tensor scale out of the fast range, a subnormal es or a reciprocal
 // that overflows (see above); the block then takes the exact path.
 __device__ __forceinline__ bool encode_block_fast(const float (&x)[16], uint32_t bm, const FastScale& f,
@@ -212,10 +275,8 @@ __device__ __forceinline__ bool encode_block_fast(const float (&x)[16], uint32_t
   const uint32_t hi_b = cvt_fp4x8(x, 8, yhi);
   const bool es_ok = (es == 0.0f) || (es >= 0x1p-126f && y < 0x1p+126f);
   if (!(f.ok && es_ok)) return false;
-  if (__builtin_expect(((lo_a ^ lo_b) | (hi_a ^ hi_b)) != 0u, 0)) {
-    lo_a = resolve_codes8(x, 0, es, lo_a, lo_b);
-    hi_a = resolve_codes8(x, 8, es, hi_a, hi_b);
-  }
+  if (__builtin_expect(lo_a != lo_b, 0)) lo_a = exact_codes8(x, 0, es);
+  if (__builtin_expect(hi_a != hi_b, 0)) hi_a = exact_codes8(x, 8, es);
   code_lo = lo_a;
   code_hi = hi_a;
   return true;

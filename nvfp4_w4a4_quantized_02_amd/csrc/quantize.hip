@@ -101,35 +101,6 @@ __device__ __forceinline__ void load_block(const uint8_t* __restrict__ p, float 
   }
 }
 
-// fp32 bits of the largest |x| of a bf16 block from its eight raw words: the
-// max runs on the packed 16-bit magnitude patterns (integer order is value
-// order for non-negative floats), two per instruction.
-typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ uint32_t bf16_absmax_bits(const uint32_t (&w)[8]) {
-  u16x2_t m[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) m[j] = __builtin_bit_cast(u16x2_t, w[j] & 0x7FFF7FFFu);
-  const u16x2_t a = __builtin_elementwise_max(__builtin_elementwise_max(m[0], m[1]),
-                                              __builtin_elementwise_max(m[2], m[3]));
-  const u16x2_t b = __builtin_elementwise_max(__builtin_elementwise_max(m[4], m[5]),
-                                              __builtin_elementwise_max(m[6], m[7]));
-  const u16x2_t c = __builtin_elementwise_max(a, b);
-  const uint32_t lo = c[0], hi = c[1];
-  return (hi > lo ? hi : lo) << 16;
-}
-
-// fp32 bits of the largest |x| of a block.
-template <bool kBf16>
-__device__ __forceinline__ uint32_t block_absmax_bits(const float (&x)[16]) {
-  uint32_t bm = 0;
-#pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    const uint32_t a = __float_as_uint(x[j]) & 0x7FFFFFFFu;
-    bm = bm > a ? bm : a;
-  }
-  return bm;
-}
-
 // ------------------------------------------------------------------ encode
 // One lane per 16-element block, 64 consecutive blocks per wave and step.
 // The fast encoder settles every block whose scale is in its range,
@@ -253,23 +224,9 @@ __global__ __launch_bounds__(256) void quantize_kernel(const uint8_t* __restrict
         x16[(size_t)b * 2u + 1u] = make_uint4(0, 0, 0, 0);
       } else {
         float xv[16];
-#pragma unroll
-        for (int i = 0; i < kWords; ++i) {
-          if (kBf16) {
-            xv[2 * i] = __uint_as_float(w[i] << 16);
-            xv[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
-          } else {
-            xv[i] = __uint_as_float(w[i]);
-          }
-        }
-        uint32_t bm;
-        if constexpr (kBf16) {
-          bm = bf16_absmax_bits(w);
-        } else {
-          bm = block_absmax_bits<false>(xv);
-        }
+        words_to_floats<kBf16>(w, xv);
         uint32_t sb, lo, hi;
-        settled = encode_block_fast(xv, bm, fsc, sb, lo, hi);
+        settled = encode_block_fast(xv, words_absmax_bits<kBf16>(w), fsc, sb, lo, hi);
         if (settled) store(b, sb, lo, hi);
       }
     }

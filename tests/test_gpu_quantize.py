@@ -110,6 +110,35 @@ def test_quantize_decision_points(nv, orc, gs0):
     _compare_quantize(nv, orc, _tie_tensor(orc, gs0), "ties gs0=%g" % gs0)
 
 
+def _scale_tie_tensor(orc, gs0):
+    """Blocks whose absmax over RN(6 gs) is exactly the midpoint between two
+    consecutive E4M3 values (a scale-byte tie, settled to the even byte), and
+    one ulp either side, for every pair of consecutive finite bytes.  Block 0
+    is the anchor (absmax 2688 gs0, so gs == gs0 exactly; gs0 a power of two
+    keeps every product exact)."""
+    e4 = orc.e4m3_table().astype(np.float64)
+    t = 6.0 * gs0
+    g = np.random.default_rng(11)
+    blocks = [np.concatenate([[2688.0 * gs0], g.uniform(-1, 1, 15) * 2688.0 * gs0])]
+    for b in range(0x7E):
+        mid = np.float32((e4[b] + e4[b + 1]) / 2.0 * t)
+        for bmax in (mid, np.nextafter(mid, np.float32(np.inf)), np.nextafter(mid, np.float32(0))):
+            rest = (g.uniform(-1, 1, 15) * float(bmax)).astype(np.float32)
+            rest = np.clip(rest, -np.float32(bmax), np.float32(bmax))
+            sign = -1.0 if b % 2 else 1.0
+            blocks.append(np.concatenate([[sign * float(bmax)], rest]))
+    x = np.concatenate(blocks).astype(np.float32)
+    pad = (-x.size) % 64
+    return np.concatenate([x, np.zeros(pad, np.float32)]).reshape(-1, 64)
+
+
+@pytest.mark.parametrize("gs0", [1.0, 2.0 ** -9, 2.0 ** 12])
+def test_quantize_scale_byte_ties(nv, orc, gs0):
+    x = _scale_tie_tensor(orc, gs0)
+    _compare_quantize(nv, orc, x, "scale ties gs0=%g" % gs0)
+    _compare_quantize(nv, orc, workloads.to_bf16_bits(x), "scale ties bf16 gs0=%g" % gs0)
+
+
 def test_quantize_random_rescales(nv, orc):
     """Random magnitudes over the whole binade range of bf16, many tensors."""
     g = np.random.default_rng(77)

@@ -56,6 +56,33 @@ namespace nvfp4 {
 // 128-bit operand reads, and 32 consecutive rows distinct banks for the
 // scale dwords.
 
+// Tile coordinates of a workgroup.  Workgroups go to the eight compute dies
+// (XCDs, each with its own L2) round-robin by index, so workgroup b runs on
+// die b % 8.  Whole tiles are renumbered so that the tiles one die holds at
+// a time are consecutive in an order that walks groups of four tile rows
+// column by column: the 32 concurrent tiles of a die then share 4 activation
+// tiles and 8 weight tiles.  The renumbering is a bijection on the whole
+// tiles (row-major indices below full_tiles), so the split tail keeps its
+// tiles.  Measured under sustained load: about 0.7% faster.
+__device__ __forceinline__ void tile_coords(int tile, int full_tiles, int tiles_n, int& tm, int& tn) {
+  constexpr int kDies = 8, kGroupRows = 4;
+  int p = tile;
+  const int f8 = full_tiles - full_tiles % kDies;
+  if (tile < f8) p = (tile % kDies) * (f8 / kDies) + tile / kDies;
+  const int rows = full_tiles / tiles_n;  // complete tile rows among the whole tiles
+  if (p < rows * tiles_n) {
+    const int span = kGroupRows * tiles_n;
+    const int first = (p / span) * kGroupRows;
+    const int gm = rows - first < kGroupRows ? rows - first : kGroupRows;
+    const int local = p - (p / span) * span;
+    tm = first + local % gm;
+    tn = local / gm;
+  } else {
+    tm = p / tiles_n;
+    tn = p % tiles_n;
+  }
+}
+
 struct GemmSmem {
   uint4 x[3][kGemmBM * 8];      // 3 x 32 KB
   uint4 wc[3][kGemmBN * 4];     // 3 x 16 KB
@@ -64,10 +91,6 @@ struct GemmSmem {
 
 constexpr int kGemmWaves = 8;
 constexpr int kDmaPerStep = 6;  // per wave: 4 (X) + 1 (W codes) + 1 (W scales)
-
-// sched_barrier mask: everything but MFMAs (and the transfers themselves)
-// may still be scheduled across the barrier (VALU, SALU, LDS, transcendental).
-constexpr int kSchedKeepMfma = 0x0002 | 0x0004 | 0x0080 | 0x0100 | 0x0200 | 0x0400;
 
 __device__ __forceinline__ uint32_t wc_swz(uint32_t r) {
   return ((((r >> 2) ^ (r >> 3)) & 1u) << 1) | (((r >> 1) ^ (r >> 2)) & 1u);
@@ -97,7 +120,8 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const uint4* __restrict__ 
     kb = part * nk / split;
     ke = (part + 1) * nk / split;
   }
-  const int tn = tile % tiles_n, tm = tile / tiles_n;
+  int tm, tn;
+  tile_coords(tile, full_tiles, tiles_n, tm, tn);
   const int n0 = tn * kGemmBN, m0 = tm * kGemmBM;
   const int l32 = lane & 31, h = lane >> 5;
   const uint32_t kh = (uint32_t)K / 2, ks = (uint32_t)K / 16;
@@ -129,9 +153,11 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const uint4* __restrict__ 
 
   // Transfers into buffer b of each ring.  Sources past the range repeat
   // the last step or group (into buffers that are no longer read).
-  auto issue_x = [&](int i, int j, int b) {
+  auto issue_x = [&](int i, int b) {
     const uint8_t* xb = xbase + (size_t)(i < last ? i : last) * 128;
-    lds_dma16(xb, xoff[j], lds_addr(&sm.x[b][wave * 256 + j * 64]));
+    const uint32_t lx = lds_addr(&sm.x[b][wave * 256]);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) lds_dma16(xb, xoff[j], lx + j * 1024);
   };
   auto issue_wc = [&](int g, int hh, int b) {
     const uint32_t goff = (uint32_t)(kb + 2 * (g < glast ? g : glast)) * 32u;
@@ -197,13 +223,11 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const uint4* __restrict__ 
       aw[t] = O::vec(make_uint4(e[0], e[1], e[2], e[3]));
     }
   };
-  auto mfma4 = [&](int t, const V (&aw)[2], const V (&bx)[4]) {
-#pragma unroll
-    for (int u = 0; u < 4; ++u) acc[t][u] = O::mfma32(aw[t], bx[u], acc[t][u]);
-  };
   auto mfma8 = [&](const V (&aw)[2], const V (&bx)[4]) {
-    mfma4(0, aw, bx);
-    mfma4(1, aw, bx);
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) acc[t][u] = O::mfma32(aw[t], bx[u], acc[t][u]);
   };
 
   // Register-resident operands carried across sub-steps and steps: the W
@@ -224,30 +248,16 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const uint4* __restrict__ 
   // expansion of step i+1.  Step i+1's operands are prepared even after the
   // last step (the buffers then hold repeated, finite data), which keeps
   // this branch-free.
-  // The six transfers are spread over the sub-steps, one after every four
-  // MFMAs, and pinned there: issued back to back, all waves of the
-  // workgroup would queue their transfers at once right after the barrier
-  // and stall their MFMA issue behind them.
-  auto pinned = [&](auto&& f) {
-    __builtin_amdgcn_sched_barrier(kSchedKeepMfma);
-    f();
-    __builtin_amdgcn_sched_barrier(kSchedKeepMfma);
-  };
   auto step = [&](auto ic, int i) {
     constexpr int I = decltype(ic)::value;
-    const int bw = mod3((i >> 1) + 2), bs = mod3((i >> 2) + 2);
+    issue_x(i + 2, (I + 2) % 3);
+    issue_wc((i >> 1) + 2, i & 1, mod3((i >> 1) + 2));
+    issue_ws((i >> 2) + 2, i & 3, mod3((i >> 2) + 2));
 #pragma unroll
     for (int j = 0; j < 3; ++j) {
       V bxn[4], awn[2];
       read_x(I, j + 1, bxn);
-      mfma4(0, aw, bx);
-      if (j == 0) pinned([&] { issue_wc((i >> 1) + 2, i & 1, bw); });
-      if (j == 1) pinned([&] { issue_x(i + 2, 1, (I + 2) % 3); });
-      if (j == 2) pinned([&] { issue_x(i + 2, 3, (I + 2) % 3); });
-      mfma4(1, aw, bx);
-      if (j == 0) pinned([&] { issue_ws((i >> 2) + 2, i & 3, bs); });
-      if (j == 1) pinned([&] { issue_x(i + 2, 0, (I + 2) % 3); });
-      if (j == 2) pinned([&] { issue_x(i + 2, 2, (I + 2) % 3); });
+      mfma8(aw, bx);
       expand_w(wv, sp, j + 1, awn);
 #pragma unroll
       for (int q = 0; q < 4; ++q) bx[q] = bxn[q];
@@ -277,14 +287,12 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const uint4* __restrict__ 
   if (n > 0) {
     // Steps 0 and 1 of X, code groups 0 and 1 (steps 0..3), scale groups 0
     // and 1 (steps 0..7): ten transfers for step 0, then ten more.
-#pragma unroll
-    for (int j = 0; j < 4; ++j) issue_x(0, j, 0);
+    issue_x(0, 0);
     issue_wc(0, 0, 0);
     issue_wc(0, 1, 0);
 #pragma unroll
     for (int qq = 0; qq < 4; ++qq) issue_ws(0, qq, 0);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) issue_x(1, j, 1);
+    issue_x(1, 1);
     issue_wc(1, 0, 1);
     issue_wc(1, 1, 1);
 #pragma unroll
@@ -415,7 +423,8 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8w_kernel(const uint8_t* __rest
     kb = part * nk / split;
     ke = (part + 1) * nk / split;
   }
-  const int tn = tile % tiles_n, tm = tile / tiles_n;
+  int tm, tn;
+  tile_coords(tile, full_tiles, tiles_n, tm, tn);
   const int n0 = tn * kGemmBN, m0 = tm * kGemmBM;
   const int l32 = lane & 31, h = lane >> 5;
 

@@ -118,18 +118,6 @@ __device__ __forceinline__ uint32_t bf16_absmax_bits(const uint32_t (&w)[8]) {
   return (hi > lo ? hi : lo) << 16;
 }
 
-// fp32 bits of the largest |x| of a block.
-template <bool kBf16>
-__device__ __forceinline__ uint32_t block_absmax_bits(const float (&x)[16]) {
-  uint32_t bm = 0;
-#pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    const uint32_t a = __float_as_uint(x[j]) & 0x7FFFFFFFu;
-    bm = bm > a ? bm : a;
-  }
-  return bm;
-}
-
 // Raw words of one block: bf16 eight dwords (two elements each), fp32
 // sixteen.
 template <bool kBf16>

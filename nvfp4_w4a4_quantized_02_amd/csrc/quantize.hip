@@ -305,23 +305,31 @@ __global__ __launch_bounds__(1024) void quantize_small_kernel(const uint8_t* __r
     return x + (size_t)r * ld_bytes + (size_t)kc * (kBf16 ? 32u : 64u);
   };
 
+  // This thread's own block, fetched first so that it is in registers by
+  // the time the tensor scale is known (lanes past the end fetch the last
+  // block and encode nothing).
+  const uint32_t b = blockIdx.x * kSmallThreads + threadIdx.x;
+  uint32_t kb_own;
+  uint32_t own[BlockWords<kBf16>::n];
+  load_words<kBf16>(block_ptr(b < total_blocks ? b : total_blocks - 1u, kb_own), own);
+
   float gs;
   if constexpr (kGiven) {
     gs = *gs_in;
   } else {
     uint32_t m = 0;
     for (uint32_t b0 = threadIdx.x; b0 < total_blocks; b0 += 4u * kSmallThreads) {
-      float xv[4][16];
+      uint32_t wv[4][BlockWords<kBf16>::n];
       uint32_t kb[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        uint32_t b = b0 + (uint32_t)u * kSmallThreads;
-        b = b < total_blocks ? b : total_blocks - 1u;
-        load_block<kBf16>(block_ptr(b, kb[u]), xv[u]);
+        uint32_t bu = b0 + (uint32_t)u * kSmallThreads;
+        bu = bu < total_blocks ? bu : total_blocks - 1u;
+        load_words<kBf16>(block_ptr(bu, kb[u]), wv[u]);
       }
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const uint32_t a = kb[u] < kblocks ? block_absmax_bits<kBf16>(xv[u]) : 0u;  // padding blocks are zeros
+        const uint32_t a = kb[u] < kblocks ? words_absmax_bits<kBf16>(wv[u]) : 0u;  // padding blocks are zeros
         m = m > a ? m : a;
       }
     }
@@ -335,19 +343,16 @@ __global__ __launch_bounds__(1024) void quantize_small_kernel(const uint8_t* __r
   }
   if (gs_out && blockIdx.x == 0 && threadIdx.x == 0) *gs_out = gs;
 
-  const uint32_t b = blockIdx.x * kSmallThreads + threadIdx.x;
   if (b >= total_blocks) return;
-  uint32_t kb;
-  const uint8_t* p = block_ptr(b, kb);
-  if (kF16 && kb >= kblocks) {
+  if (kF16 && kb_own >= kblocks) {
     x16[(size_t)b * 2u] = make_uint4(0, 0, 0, 0);
     x16[(size_t)b * 2u + 1u] = make_uint4(0, 0, 0, 0);
     return;
   }
   float xv[16];
-  load_block<kBf16>(p, xv);
+  words_to_floats<kBf16>(own, xv);
   uint32_t sb, lo, hi;
-  if (!encode_block_fast(xv, block_absmax_bits<kBf16>(xv), fast_scale(gs), sb, lo, hi))
+  if (!encode_block_fast(xv, words_absmax_bits<kBf16>(own), fast_scale(gs), sb, lo, hi))
     sb = encode_block_exact(xv, gs, lo, hi);
   if (kF16) {
     const half2_t q2 = scale_f16x2(sb);

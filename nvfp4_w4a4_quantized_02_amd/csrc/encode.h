@@ -3,16 +3,21 @@
 //
 // The code of an element is E2M1(RN(|x| / es)) with ties to the even code
 // (paper "Why Gated DeltaNet Survives 4-Bit Quantization", section 2
-// "NVFP4"; the exact rounding rule is this library's reading).  Instead of
-// one correctly rounded division per element, every decision point of that
-// rule is moved into |x|-space once per block: RN(q) > c holds exactly when
-// q lies above the midpoint between c and its fp32 successor (c even, so a
-// tie there rounds to c), and RN(q) >= c exactly when q reaches the midpoint
-// between c's predecessor and c.  With q = |x| / es and es > 0 this becomes
-// |x| > T * es or |x| >= T * es, where T (at most 25 significant bits) times
-// es (24 bits) is exact in fp64.  A directed rounding of that product to
-// fp32 turns both forms into one strict fp32 comparison |x| > B, so the
-// per-element work is a three-step binary search over seven block bounds.
+// "NVFP4"; the exact rounding rule is this library's reading).
+//
+// Two encoders give the same bytes.  The fast one (encode_block_fast) brackets
+// every rounding decision between two cheap estimates and falls back to exact
+// arithmetic only where the bracket straddles a decision point.  The exact
+// one (encode_block, for the rare blocks the fast one cannot take) moves every
+// decision point of the rule into |x|-space once per block: RN(q) > c holds
+// exactly when q lies above the midpoint between c and its fp32 successor
+// (c even, so a tie there rounds to c), and RN(q) >= c exactly when q
+// reaches the midpoint between c's predecessor and c.  With q = |x| / es and
+// es > 0 this becomes |x| > T * es or |x| >= T * es, where T (at most 25
+// significant bits) times es (24 bits) is exact in fp64.  A directed rounding
+// of that product to fp32 turns both forms into one strict fp32 comparison
+// |x| > B, so an element's magnitude code is the number of the seven block
+// bounds it exceeds.
 #pragma once
 
 #include "common.h"

@@ -19,6 +19,11 @@ no absmax pass) under "calibrated_scale", and the decode lines the W4A16 form
 times W4A16 at the prefill shape.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+Defaults: 100 warm-up steps, then 100 timed steps.  From idle the GPU clock
+takes a few tens of milliseconds of sustained load to settle (the first 20
+prefill steps run about a quarter slower than the settled rate), so the
+warm-up is long enough to time the settled, sustained rate.
 """
 from __future__ import annotations
 
@@ -41,8 +46,8 @@ PROFILE_DIR = os.path.join(ROOT, "profiles")
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--headline-only", action="store_true",
                     help="skip the secondary workloads (profiling runs)")

@@ -616,13 +616,17 @@ def cpu_baseline(np, p):
     t0 = time.perf_counter()
     oracle.linear(np.ascontiguousarray(p.x[:1]), wc, ws, wg)
     t1 = time.perf_counter() - t0
-    m = int(max(1, min(64, round(15.0 / max(t1, 1e-3)))))
-    log("cpu baseline: 1 row took %.2f s, timing %d rows" % (t1, m))
+    # The oracle spreads rows over its threads, one row per thread at a time:
+    # a whole number of rows per thread keeps every thread busy for ~15 s.
+    nt = oracle.num_threads()
+    rounds = int(max(1, round(15.0 / max(t1, 1e-3))))
+    m = int(min(p.M, nt * rounds))
+    log("cpu baseline: 1 row took %.2f s, timing %d rows on %d threads" % (t1, m, nt))
     t0 = time.perf_counter()
     oracle.linear(np.ascontiguousarray(p.x[:m]), wc, ws, wg)
     dt = time.perf_counter() - t0
     flops = 2.0 * m * N * K
-    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.num_threads(),
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": min(nt, m),
             "kind": "oracle", "seconds": round(dt, 2),
             "sample": "W4A4 linear of the first %d of 4096 activation rows (on-the-fly quantize of those rows "
                       "+ exact int64 GEMM) against the full W[17408x5120]" % m}

@@ -43,7 +43,9 @@
  *    error nothing is launched and a non-zero status is returned.  No call
  *    allocates device memory: scratch space comes from the caller's
  *    workspace, whose size the *_workspace_size functions give.  The library
- *    keeps no state between calls.
+ *    keeps no state between calls apart from a per-device cache of two device
+ *    attributes (compute units, LDS per compute unit), safe to fill from
+ *    several host threads at once.
  *  - Inputs must be finite (no NaN or infinity); this is not checked.
  *  - Calls that share a workspace, or whose outputs overlap their inputs,
  *    must be ordered by the caller (same stream, or events).

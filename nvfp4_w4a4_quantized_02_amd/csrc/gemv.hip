@@ -761,13 +761,8 @@ static bool gemv_fp8w_stream_go(const void* x, uint32_t ldx, int64_t M, int64_t 
 
 void launch_gemv_fp8w(bool a8, const void* x, size_t ld_x_bytes, int64_t M, int64_t K, const uint8_t* wq, int64_t N,
                       const float* sx, const float* sw, void* y, bool y_bf16, int64_t ld_y, hipStream_t s) {
-  static int cus = 0;
-  if (!cus) {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-      cus = 256;
-  }
+  int cus = 0, lds_cu = 0;
+  if (!device_caps(cus, lds_cu)) cus = 256;
   if (M <= 4 && K >= 256 && K % 256 == 0) {
     const size_t ldb4 = (size_t)ld_y * (y_bf16 ? 2u : 4u);
     const bool done = a8 ? gemv_fp8w_stream_go<true>(x, (uint32_t)ld_x_bytes, M, K, wq, N, sx, sw, y, y_bf16, ldb4,
@@ -808,16 +803,8 @@ struct GvPlan {
 static GvPlan plan_gemv_stream(int64_t M, int64_t N, int64_t K) {
   GvPlan p{0, 0, 0};
   if (M < 1 || M > 4 || K < 256 || K % 256 != 0 || (uint64_t)N * (uint64_t)K / 2 >= (1ull << 32)) return p;
-  static int cus = 0, lds_cu = 0;
-  if (!cus) {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        hipDeviceGetAttribute(&lds_cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) != hipSuccess) {
-      cus = 0;
-      return p;
-    }
-  }
+  int cus = 0, lds_cu = 0;
+  if (!device_caps(cus, lds_cu)) return p;
   const int xi = M <= 2 ? 1 : 2;
   const int64_t tiles = (N + 15) / 16;
   const size_t sc = (size_t)((16 * (K / 16) + 1023) / 1024) * 1024;
@@ -858,14 +845,8 @@ static void gemv_go(const void* x16, size_t ld_x_bytes, int64_t M, const uint8_t
   const uint32_t ldx = (uint32_t)ld_x_bytes;
   if (M > 4 && M <= 16 && K >= 512 && K <= 512 * kKsMaxWaves && K % 512 == 0 &&
       (uint64_t)N * (uint64_t)K / 2 < (1ull << 32)) {
-    static int cus = 0;
-    if (!cus) {
-      int dev = 0;
-      if (hipGetDevice(&dev) != hipSuccess ||
-          hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-        cus = 0;
-    }
-    if (cus) {
+    int cus = 0, lds_cu = 0;
+    if (device_caps(cus, lds_cu)) {
       const int tiles = (int)((N + 15) / 16);
       const int waves = (int)(K / 512);
       // one workgroup per compute unit, but enough of them that no wave

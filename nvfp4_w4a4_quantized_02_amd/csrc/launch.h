@@ -5,7 +5,38 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace nvfp4 {
+
+// Compute units and LDS bytes per compute unit of the current device, for
+// launch shapes.  Each device's values are queried once and kept in atomics:
+// concurrent first calls from several host threads store the same values.
+// False when the runtime cannot report them.
+inline bool device_caps(int& cus, int& lds_per_cu) {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> cached_cus[kMaxDevices], cached_lds[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return false;
+  const bool cache = dev >= 0 && dev < kMaxDevices;
+  if (cache) {
+    cus = cached_cus[dev].load(std::memory_order_relaxed);
+    lds_per_cu = cached_lds[dev].load(std::memory_order_relaxed);
+    if (cus > 0 && lds_per_cu > 0) return true;
+  }
+  int a = 0, b = 0;
+  if (hipDeviceGetAttribute(&a, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipDeviceGetAttribute(&b, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) != hipSuccess || a <= 0 ||
+      b <= 0)
+    return false;
+  if (cache) {
+    cached_cus[dev].store(a, std::memory_order_relaxed);
+    cached_lds[dev].store(b, std::memory_order_relaxed);
+  }
+  cus = a;
+  lds_per_cu = b;
+  return true;
+}
 
 constexpr int kMaxFused = 16;
 constexpr int kMaxPartials = 2048;  // absmax partials (one per workgroup)

@@ -277,7 +277,9 @@ __global__ __launch_bounds__(256) void quantize_kernel(const uint8_t* __restrict
 // is at most 256 KB and sits in cache after the first workgroup reads it;
 // surplus lanes re-read the last block, which cannot change a max, so every
 // load is unconditional), then encodes its own 1024 blocks, one per thread,
-// the rare bracket misses inline.
+// the rare bracket misses inline.  A tensor of at most 1024 blocks has one
+// workgroup, whose own blocks are the whole tensor: the absmax then comes
+// from the blocks already in registers, with no second read.
 constexpr int kSmallThreads = 1024;
 
 // Tensors of at most this many blocks take the one-launch kernel.
@@ -318,19 +320,25 @@ __global__ __launch_bounds__(1024) void quantize_small_kernel(const uint8_t* __r
     gs = *gs_in;
   } else {
     uint32_t m = 0;
-    for (uint32_t b0 = threadIdx.x; b0 < total_blocks; b0 += 4u * kSmallThreads) {
-      uint32_t wv[4][BlockWords<kBf16>::n];
-      uint32_t kb[4];
+    if (gridDim.x == 1) {
+      // One workgroup: the threads' own blocks are the whole tensor, and
+      // they are already in registers (padding blocks count as zeros).
+      if (b < total_blocks && kb_own < kblocks) m = words_absmax_bits<kBf16>(own);
+    } else {
+      for (uint32_t b0 = threadIdx.x; b0 < total_blocks; b0 += 4u * kSmallThreads) {
+        uint32_t wv[4][BlockWords<kBf16>::n];
+        uint32_t kb[4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        uint32_t bu = b0 + (uint32_t)u * kSmallThreads;
-        bu = bu < total_blocks ? bu : total_blocks - 1u;
-        load_words<kBf16>(block_ptr(bu, kb[u]), wv[u]);
-      }
+        for (int u = 0; u < 4; ++u) {
+          uint32_t bu = b0 + (uint32_t)u * kSmallThreads;
+          bu = bu < total_blocks ? bu : total_blocks - 1u;
+          load_words<kBf16>(block_ptr(bu, kb[u]), wv[u]);
+        }
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const uint32_t a = kb[u] < kblocks ? words_absmax_bits<kBf16>(wv[u]) : 0u;  // padding blocks are zeros
-        m = m > a ? m : a;
+        for (int u = 0; u < 4; ++u) {
+          const uint32_t a = kb[u] < kblocks ? words_absmax_bits<kBf16>(wv[u]) : 0u;  // padding blocks are zeros
+          m = m > a ? m : a;
+        }
       }
     }
     m = wave_max_u32(m);

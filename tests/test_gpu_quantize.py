@@ -93,6 +93,12 @@ def _cases():
     yield "one_launch_8192_blocks_bf16", workloads.to_bf16_bits(workloads.student_t(7, 6, 512, 256, 3.0))
     yield "two_launches_8193_blocks_bf16", workloads.to_bf16_bits(workloads.student_t(7, 7, 8193, 16, 3.0))
     yield "one_launch_8_workgroups_f32", workloads.gaussian(7, 8, 16, 8192, 1.0)
+    # one workgroup (its own blocks give the absmax) against two, with the
+    # absmax in the very last block
+    for name, (r, k) in (("one_workgroup_1024_blocks", (64, 256)), ("two_workgroups_1025_blocks", (1025, 16))):
+        g = workloads.gaussian(7, 9, r, k, 1.0)
+        g[-1, -1] = np.float32(-50.0)
+        yield name, workloads.to_bf16_bits(g)
 
 
 @pytest.mark.parametrize("name,x", list(_cases()), ids=[n for n, _ in _cases()])

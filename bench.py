@@ -266,7 +266,18 @@ def main():
 
     # ------------------------------------------------------------ box-measured peaks
     if not args.headline_only and not args.no_box_peaks:
-        out["box_peaks"] = box_peaks(torch, dev, M, N, K)
+        bp = box_peaks(torch, dev, M, N, K)
+        out["box_peaks"] = bp
+        # the same achieved rates against what this machine sustains on plain work
+        out["roofline"]["frac_of_box"] = round(out["roofline"]["achieved"] / bp["fp16_gemm_TFLOPs"], 4)
+        for line in also:
+            r = line.get("roofline")
+            if not r or r.get("achieved") is None:
+                continue
+            if r.get("unit") == "GB/s":
+                r["frac_of_box"] = round(r["achieved"] / bp["hbm_copy_GBs"], 4)
+            elif r.get("unit") == "TFLOP/s" and r.get("peak") == PEAK_FP16_TFLOPS:
+                r["frac_of_box"] = round(r["achieved"] / bp["fp16_gemm_TFLOPs"], 4)
 
     # ------------------------------------------------------------ CPU oracle
     if not args.no_cpu_baseline:

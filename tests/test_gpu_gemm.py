@@ -161,14 +161,17 @@ def test_unrepaired_fusion_is_misscaled(nv, orc):
 
 # --------------------------------------------------------- full sizes, sampled
 
-def _sampled(nv, orc, p, out_dtype, nsamp=1500, seed=0):
+def _sampled(nv, orc, p, out_dtype, nsamp=1500, seed=0, idx=None):
     wc, ws, wg = _gpu_weight(nv, p.w_parts)
     y = to_np(nv.nvfp4_gemm(to_gpu(p.x), wc, ws, wg, out_dtype=out_dtype))
     torch.cuda.synchronize()
-    g = np.random.default_rng(seed)
-    mi = g.integers(0, p.M, nsamp)
-    ni = g.integers(0, p.N, nsamp)
-    mi[:2], ni[:2] = [0, p.M - 1], [0, p.N - 1]
+    if idx is None:
+        g = np.random.default_rng(seed)
+        mi = g.integers(0, p.M, nsamp)
+        ni = g.integers(0, p.N, nsamp)
+        mi[:2], ni[:2] = [0, p.M - 1], [0, p.N - 1]
+    else:
+        mi, ni = idx
     rows_w = np.unique(ni)
     owc, ows, owg = _oracle_weight(orc, p.w_parts, rows=rows_w)
     rows_x = np.unique(mi)
@@ -177,6 +180,37 @@ def _sampled(nv, orc, p, out_dtype, nsamp=1500, seed=0):
     ref = orc.gemm_exact_sampled(oxc, oxs, gx, owc, ows, owg, np.searchsorted(rows_x, mi),
                                  np.searchsorted(rows_w, ni))
     return y[mi, ni], ref
+
+
+# Split-K tail: when the tiles do not fill whole rounds of the 256 compute
+# units, the remaining tiles (the last ones in row-major order) are split
+# along K and a second kernel adds the parts.
+def test_split_tail_every_output(nv, orc):
+    # 2 x 129 tiles = 258: the last 2 (tile row 1, tile columns 127 and 128,
+    # both ragged) are split in 2 (K = 128 is 2 steps).  Every output of
+    # those two tiles is checked, plus samples of the whole tiles.
+    M, N, K = 500, 33000, 128
+    p = workloads.prefill(M=M, K=K, N=N)
+    print("case: split tail gemm M=%d N=%d K=%d" % (M, N, K), flush=True)
+    tm, tn = np.meshgrid(np.arange(256, M), np.arange(127 * 256, N), indexing="ij")
+    g = np.random.default_rng(4)
+    mi = np.concatenate([tm.ravel(), g.integers(0, M, 1000)])
+    ni = np.concatenate([tn.ravel(), g.integers(0, N, 1000)])
+    got, ref = _sampled(nv, orc, p, torch.float32, idx=(mi, ni))
+    check_gemm(got, ref, False, "split tail %dx%dx%d" % (M, N, K))
+
+
+def test_split_tail_16_parts_sampled(nv, orc):
+    # 2 x 257 tiles = 514: the last 2 (tile row 1, tile columns 255 and 256)
+    # are split in 16 (K = 1024 is 16 steps); most samples fall in them
+    M, N, K = 300, 65600, 1024
+    p = workloads.prefill(M=M, K=K, N=N)
+    print("case: split tail sampled M=%d N=%d K=%d" % (M, N, K), flush=True)
+    g = np.random.default_rng(5)
+    mi = np.concatenate([g.integers(256, M, 1500), g.integers(0, M, 500), [256, M - 1]])
+    ni = np.concatenate([g.integers(255 * 256, N, 1500), g.integers(0, N, 500), [255 * 256, N - 1]])
+    got, ref = _sampled(nv, orc, p, torch.float32, idx=(mi, ni))
+    check_gemm(got, ref, False, "split tail sampled")
 
 
 @pytest.mark.parametrize("M", [1, 4, 16])

@@ -82,7 +82,7 @@ def test_fp8_linears_empty_and_k_zero(nv):
             assert torch.count_nonzero(y).item() == 0
 
 
-def _sampled(nv, orc, x, w, a8, nsamp, seed):
+def _sampled(nv, orc, x, w, a8, nsamp, seed, idx=None):
     sw = orc.fp8_tensor_scale(w)
     q, s = nv.nvfp4_fp8_quantize(to_gpu(w))       # byte-exact with the oracle (FP8 quantize tests)
     torch.cuda.synchronize()
@@ -95,9 +95,12 @@ def _sampled(nv, orc, x, w, a8, nsamp, seed):
     torch.cuda.synchronize()
     del q
     M, N = x.shape[0], w.shape[0]
-    g = np.random.default_rng(seed)
-    mi, ni = g.integers(0, M, nsamp), g.integers(0, N, nsamp)
-    mi[:2], ni[:2] = [0, M - 1], [0, N - 1]
+    if idx is None:
+        g = np.random.default_rng(seed)
+        mi, ni = g.integers(0, M, nsamp), g.integers(0, N, nsamp)
+        mi[:2], ni[:2] = [0, M - 1], [0, N - 1]
+    else:
+        mi, ni = idx
     rows_w, rows_x = np.unique(ni), np.unique(mi)
     wq, _ = orc.fp8_quantize(np.ascontiguousarray(w[rows_w]), scale=sw)
     xs = np.ascontiguousarray(x[rows_x])
@@ -127,3 +130,19 @@ def test_fp8_linear_full_prefill(nv, orc, a8):
     print("case: %s full prefill 4096x17408x5120" % ("w8a8" if a8 else "w8a16"), flush=True)
     got, ref = _sampled(nv, orc, p.x, p.w_parts[0], a8, 1500, 4)
     check_gemm(got, ref, True, "fp8 full prefill")
+
+
+@pytest.mark.parametrize("a8", [False, True])
+def test_fp8_linear_split_tail(nv, orc, a8):
+    # 2 x 129 tiles = 258 of the shared tile plan: the last 2 (tile row 1,
+    # tile columns 127 and 128, both ragged) are split along K (K = 128 is 2
+    # steps).  Every output of those tiles, plus samples elsewhere.
+    M, N, K = 500, 33000, 128
+    p = workloads.prefill(M=M, K=K, N=N)
+    print("case: %s split tail M=%d N=%d K=%d" % ("w8a8" if a8 else "w8a16", M, N, K), flush=True)
+    tm, tn = np.meshgrid(np.arange(256, M), np.arange(127 * 256, N), indexing="ij")
+    g = np.random.default_rng(6)
+    mi = np.concatenate([tm.ravel(), g.integers(0, M, 1000)])
+    ni = np.concatenate([tn.ravel(), g.integers(0, N, 1000)])
+    got, ref = _sampled(nv, orc, p.x, p.w_parts[0], a8, 0, 0, idx=(mi, ni))
+    check_gemm(got, ref, True, "fp8 split tail")

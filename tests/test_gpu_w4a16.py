@@ -87,7 +87,7 @@ def test_w4a16_rejects_fp32_activations(nv):
         nv.nvfp4_gemm_w4a16(x, wc, ws, torch.ones(1, device="cuda:0"))
 
 
-def _sampled(nv, orc, x, w_parts, nsamp, seed):
+def _sampled(nv, orc, x, w_parts, nsamp, seed, idx=None):
     """Fused weight quantized member by member and repaired on the GPU; the
     oracle recomputes the sampled rows from the same member scales."""
     q = [nv.nvfp4_quantize(to_gpu(w)) for w in w_parts]
@@ -100,9 +100,12 @@ def _sampled(nv, orc, x, w_parts, nsamp, seed):
     y = to_np(nv.nvfp4_gemm_w4a16(to_gpu(x), wc, ws, shared, out_dtype=torch.bfloat16))
     torch.cuda.synchronize()
     M, N = x.shape[0], wc.shape[0]
-    g = np.random.default_rng(seed)
-    mi, ni = g.integers(0, M, nsamp), g.integers(0, N, nsamp)
-    mi[:2], ni[:2] = [0, M - 1], [0, N - 1]
+    if idx is None:
+        g = np.random.default_rng(seed)
+        mi, ni = g.integers(0, M, nsamp), g.integers(0, N, nsamp)
+        mi[:2], ni[:2] = [0, M - 1], [0, N - 1]
+    else:
+        mi, ni = idx
     rows_w = np.unique(ni)
     gss = [orc.tensor_scale(w) for w in w_parts]
     offs = np.cumsum([0] + [w.shape[0] for w in w_parts])
@@ -135,3 +138,18 @@ def test_w4a16_full_prefill(nv, orc):
     print("case: w4a16 full prefill 4096x17408x5120", flush=True)
     got, ref = _sampled(nv, orc, p.x, p.w_parts, 3000, 2)
     check_gemm(got, ref, True, "w4a16 full prefill")
+
+
+def test_w4a16_split_tail(nv, orc):
+    # 2 x 129 tiles = 258: the last 2 (tile row 1, tile columns 127 and 128,
+    # both ragged) are split along K (K = 128 is 2 steps).  Every output of
+    # those tiles, plus samples elsewhere.
+    M, N, K = 500, 33000, 128
+    p = workloads.prefill(M=M, K=K, N=N)
+    print("case: w4a16 split tail M=%d N=%d K=%d" % (M, N, K), flush=True)
+    tm, tn = np.meshgrid(np.arange(256, M), np.arange(127 * 256, N), indexing="ij")
+    g = np.random.default_rng(7)
+    mi = np.concatenate([tm.ravel(), g.integers(0, M, 1000)])
+    ni = np.concatenate([tn.ravel(), g.integers(0, N, 1000)])
+    got, ref = _sampled(nv, orc, p.x, p.w_parts, 0, 0, idx=(mi, ni))
+    check_gemm(got, ref, True, "w4a16 split tail")

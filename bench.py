@@ -64,11 +64,17 @@ def log(msg):
     print("[bench] " + msg, file=sys.stderr, flush=True)
 
 
-def source_sha(*names):
+def source_sha():
+    """Hash of every source the library is built from (kernels, launchers,
+    the ABI layer and its header): counters taken on other sources are not
+    reported as the current kernels' traffic."""
     h = hashlib.sha256()
-    for n in names:
-        with open(os.path.join(ROOT, "nvfp4_w4a4_quantized_02_amd", "csrc", n), "rb") as f:
-            h.update(f.read())
+    csrc = os.path.join(ROOT, "nvfp4_w4a4_quantized_02_amd", "csrc")
+    for path in [os.path.join(csrc, n) for n in sorted(os.listdir(csrc))] + \
+            [os.path.join(ROOT, "include", "nvfp4.h")]:
+        if os.path.isfile(path):
+            with open(path, "rb") as f:
+                h.update(os.path.basename(path).encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
 
 
@@ -180,7 +186,7 @@ def main():
             return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
         return torch.from_numpy(a).to(dev)
 
-    # ------------------------------------------------------------ headline
+    # ------------------------------------------------------------ headline workload
     log("generating prefill workload X[4096x5120] bf16, W[17408x5120]")
     p = workloads.prefill()
     M, K, N = p.M, p.K, p.N
@@ -190,6 +196,18 @@ def main():
     x = to_gpu(p.x)
     y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
     ws_buf = torch.empty(nv.lib.nvfp4_gemm_workspace_size(M, N, K), dtype=torch.uint8, device=dev)
+    flops = 2.0 * M * N * K
+    sha = source_sha()
+
+    # The secondary lines and the machine's reference rates run first, so the
+    # headline's warm-up starts on a GPU that is already under load (from
+    # idle, the clock takes tens of milliseconds of sustained load to settle).
+    also = []
+    bp = None
+    if not args.headline_only:
+        also += secondary(torch, np, nv, workloads, to_gpu, dev, args)
+        if not args.no_box_peaks:
+            bp = box_peaks(torch, dev, M, N, K)
 
     def step(i, mark):
         mark(0)
@@ -201,11 +219,9 @@ def main():
     log("timing prefill GEMM: %d warmup, %d steps" % (args.warmup, args.steps))
     wall_ms, (prep_ms, run_ms) = time_steps(torch, args.steps, args.warmup, step, 2)
     step_ms = wall_ms                      # timed region / steps, synchronized on both sides
-    flops = 2.0 * M * N * K
     value = flops / (step_ms * 1e-3) / 1e12
     gemm_tflops = flops / (mean(run_ms) * 1e-3) / 1e12
-    sha_gemm = source_sha("gemm.hip", "encode.h", "common.h", "mfma_util.h")
-    traffic = traffic_for("gemm_prefill", sha_gemm)
+    traffic = traffic_for("gemm_prefill", sha)
     out = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -224,14 +240,21 @@ def main():
         "config": {"workload": "prefill W4A4 linear: X[4096x5120] bf16 Student-t(3) quantized on the fly "
                                "x W[17408x5120] NVFP4 from N(0,0.02) -> Y bf16",
                    "M": M, "N": N, "K": K, "x_dtype": "bf16", "y_dtype": "bf16"},
+        "timed_after": ("the secondary lines and the box peaks (the GPU is under load when the warm-up starts)"
+                        if not args.headline_only else "nothing (headline only)"),
         "phases_ms": {"activation_quantize": round(mean(prep_ms), 4), "gemm": round(mean(run_ms), 4)},
         "roofline": {"bound": "mfma", "kernel": "nvfp4_gemm_run: gemm_kernel (fp16 MFMA 32x32x16) + split-K reduce",
                      "achieved": round(gemm_tflops, 2), "peak": PEAK_FP16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(gemm_tflops / PEAK_FP16_TFLOPS, 4), "traffic": traffic,
                      "algorithmic": "2*M*N*K = %.4g flop per launch" % flops},
     }
-    also = []
     if not args.headline_only:
+        # the same step again with 100 warm-up and 100 timed steps: the
+        # sustained rate, whatever warm-up the headline was given
+        wall2, (prep2, run2) = time_steps(torch, 100, 100, step, 2)
+        out["settled"] = {"warmup": 100, "steps": 100, "ms_per_step": round(wall2, 4),
+                          "TFLOPs": round(flops / (wall2 * 1e-3) / 1e12, 2),
+                          "gemm_TFLOPs": round(flops / (mean(run2) * 1e-3) / 1e12, 2)}
         # W4A16: the same weights against the bf16 activations as given
         wsz16 = nv.lib.nvfp4_gemm_w4a16_workspace_size(M, N, K)
         ws16 = torch.empty(max(wsz16, 256), dtype=torch.uint8, device=dev)
@@ -246,27 +269,23 @@ def main():
 
         _, (w16_ms,) = time_steps(torch, args.steps, args.warmup, step16, 1)
         t16 = flops / (mean(w16_ms) * 1e-3) / 1e12
-        also.append({"metric": "W4A16 GEMM TFLOP/s at M=4096", "value": round(t16, 2), "unit": "TFLOP/s",
-                     "ms_per_step": round(mean(w16_ms), 4),
-                     "config": {"workload": "prefill W4A16 linear: X[4096x5120] bf16 Student-t(3) as given x "
-                                            "W[17408x5120] NVFP4 -> Y bf16"},
-                     "roofline": {"bound": "mfma", "kernel": "nvfp4_gemm_w4a16: gemm_kernel (bf16 MFMA 32x32x16) "
-                                                              "+ split-K reduce",
-                                  "achieved": round(t16, 2), "peak": PEAK_FP16_TFLOPS, "unit": "TFLOP/s",
-                                  "frac": round(t16 / PEAK_FP16_TFLOPS, 4),
-                                  "traffic": traffic_for("gemm_prefill_w4a16", sha_gemm)}})
+        also.insert(0, {"metric": "W4A16 GEMM TFLOP/s at M=4096", "value": round(t16, 2), "unit": "TFLOP/s",
+                        "ms_per_step": round(mean(w16_ms), 4),
+                        "config": {"workload": "prefill W4A16 linear: X[4096x5120] bf16 Student-t(3) as given x "
+                                               "W[17408x5120] NVFP4 -> Y bf16"},
+                        "roofline": {"bound": "mfma", "kernel": "nvfp4_gemm_w4a16: gemm_kernel (bf16 MFMA 32x32x16) "
+                                                                 "+ split-K reduce",
+                                     "achieved": round(t16, 2), "peak": PEAK_FP16_TFLOPS, "unit": "TFLOP/s",
+                                     "frac": round(t16 / PEAK_FP16_TFLOPS, 4),
+                                     "traffic": traffic_for("gemm_prefill_w4a16", sha)}})
         log("W4A16 prefill: %.1f TFLOP/s" % t16)
         del ws16
         if not args.no_numerics:
             out["numerics"] = numerics(torch, nv, workloads, to_gpu, dev, p, x, wc, ws, wg)
     del y, x
 
-    if not args.headline_only:
-        also += secondary(torch, np, nv, workloads, to_gpu, dev, args)
-
     # ------------------------------------------------------------ box-measured peaks
-    if not args.headline_only and not args.no_box_peaks:
-        bp = box_peaks(torch, dev, M, N, K)
+    if bp is not None:
         out["box_peaks"] = bp
         # the same achieved rates against what this machine sustains on plain work
         out["roofline"]["frac_of_box"] = round(out["roofline"]["achieved"] / bp["fp16_gemm_TFLOPs"], 4)
@@ -275,7 +294,7 @@ def main():
             if not r or r.get("achieved") is None:
                 continue
             if r.get("unit") == "GB/s":
-                r["frac_of_box"] = round(r["achieved"] / bp["hbm_copy_GBs"], 4)
+                r["frac_of_box"] = round(r["achieved"] / bp["hbm_read_GBs"], 4)
             elif r.get("unit") == "TFLOP/s" and r.get("peak") == PEAK_FP16_TFLOPS:
                 r["frac_of_box"] = round(r["achieved"] / bp["fp16_gemm_TFLOPs"], 4)
 
@@ -349,16 +368,14 @@ def secondary(torch, np, nv, workloads, to_gpu, dev, args):
                     "w4a16": {"ms_per_step": round(t["w4a16"], 5),
                               "GBs": round(nbytes / (t["w4a16"] * 1e-3) / 1e9, 1),
                               "frac": round(nbytes / (t["w4a16"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-                              "traffic": traffic_for("gemv_m%d_w4a16" % M, source_sha("gemv.hip", "encode.h",
-                                                                                      "common.h", "mfma_util.h"))},
+                              "traffic": traffic_for("gemv_m%d_w4a16" % M, source_sha())},
                     "calibrated_scale": {"ms_per_step": round(t["w4a4_static"], 5),
                                          "GBs": round(nbytes / (t["w4a4_static"] * 1e-3) / 1e9, 1)},
                     "config": {"workload": "decode: X[%dx5120] bf16 x fused gate/up W[34816x5120] NVFP4 "
                                            "(4 rotated copies) -> Y bf16" % M},
                     "roofline": {"bound": "hbm", "kernel": "nvfp4_gemm_run: gemv kernel", "achieved": round(kgbs, 1),
                                  "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(kgbs / PEAK_HBM_GBS, 4),
-                                 "traffic": traffic_for("gemv_m%d" % M, source_sha("gemv.hip", "encode.h",
-                                                                                   "common.h", "mfma_util.h")),
+                                 "traffic": traffic_for("gemv_m%d" % M, source_sha()),
                                  "algorithmic": "W codes+scales %d B + X + Y = %d B per launch" % (wbytes,
                                                                                                   nbytes)}})
         log("decode M=%d: step %.2f us (%.1f GB/s), gemv %.2f us (%.1f GB/s), prep %.2f us, W4A16 %.2f us" %
@@ -451,15 +468,13 @@ def secondary(torch, np, nv, workloads, to_gpu, dev, args):
                                      "GBs": round(single / (mean(sq_ms) * 1e-3) / 1e9, 1),
                                      "frac": round(single / (mean(sq_ms) * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
                                      "algorithmic": "1 read of X + codes + scales = %d B per call" % single,
-                                     "traffic": traffic_for("quantize_long_static",
-                                                            source_sha("quantize.hip", "encode.h", "common.h"))},
+                                     "traffic": traffic_for("quantize_long_static", source_sha())},
                 "config": {"workload": "long-prefill quantize: X[32768x5120] bf16 Student-t(2.5), 16 hot "
                                        "channels x200 -> packed E2M1 + E4M3 scales + FP32 scale"},
                 "roofline": {"bound": "hbm", "kernel": "nvfp4_quantize: amax_partials_kernel + quantize_kernel",
                              "achieved": round(qgbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                              "frac": round(qgbs / PEAK_HBM_GBS, 4),
-                             "traffic": traffic_for("quantize_long", source_sha("quantize.hip", "encode.h",
-                                                                                "common.h")),
+                             "traffic": traffic_for("quantize_long", source_sha()),
                              "algorithmic": "2 reads of X + codes + scales = %d B per call" % two_pass}})
     log("quantize: %.1f GB/s (two-pass count); calibrated scale %.1f GB/s (one read)"
         % (qgbs, single / (mean(sq_ms) * 1e-3) / 1e9))
@@ -578,13 +593,58 @@ def numerics(torch, nv, workloads, to_gpu, dev, p, x, wc, ws, wg):
     return res
 
 
+def _read_probe():
+    import ctypes
+    path = os.path.join(ROOT, "nvfp4_w4a4_quantized_02_amd", "libnvfp4_probe.so")
+    if not os.path.exists(path):
+        return None
+    L = ctypes.CDLL(path)
+    L.nvfp4_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_uint32,
+                                   ctypes.c_int, ctypes.c_void_p]
+    L.nvfp4_probe_read.restype = ctypes.c_int
+    return L
+
+
+def read_rate(torch, dev, nbytes, copies, reps=20):
+    """GB/s of a plain streaming read (the reference kernel of
+    libnvfp4_probe.so) over `copies` buffers of nbytes read in turn, best of
+    five timed rounds; None when the probe library is not built."""
+    L = _read_probe()
+    if L is None:
+        return None, None
+    bufs = [torch.full((nbytes // 4,), i + 1, dtype=torch.int32, device=dev) for i in range(copies)]
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream().cuda_stream
+    best = {}
+    for grid in (1024, 2048, 4096):
+        ms = []
+        for r in range(6):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for i in range(reps):
+                assert L.nvfp4_probe_read(bufs[i % copies].data_ptr(), nbytes, sink.data_ptr(), 0x9E3779B9,
+                                          grid, stream) == 0
+            e1.record()
+            torch.cuda.synchronize()
+            if r:
+                ms.append(e0.elapsed_time(e1) / reps)
+        best[grid] = min(ms)
+    del bufs
+    grid = min(best, key=best.get)
+    return nbytes / (best[grid] * 1e-3) / 1e9, grid
+
+
 def box_peaks(torch, dev, M, N, K):
     """What this machine sustains on plain work, measured beside the
-    nominal peaks: a 1 GiB device-to-device copy (HBM read + write) and
-    torch's own fp16 GEMM (hipBLASLt) at the prefill shape with fp32
-    accumulation, the same MFMA arithmetic the W4A4 GEMM runs after its exact
-    expansion.  Context for the roofline fractions, not part of any step."""
-    log("box peaks: 1 GiB copy, fp16 GEMM %dx%dx%d" % (M, N, K))
+    nominal peaks: a streaming read of 100 MB (the decode weight size, four
+    buffers read in turn so the 256 MB last-level cache cannot hold them) and
+    of 1 GiB, a 1 GiB device-to-device copy (HBM read + write) and torch's own
+    fp16 GEMM (hipBLASLt) at the prefill shape with fp32 accumulation, the
+    same MFMA arithmetic the W4A4 GEMM runs after its exact expansion.
+    Context for the roofline fractions, not part of any step."""
+    log("box peaks: streaming read 100 MB and 1 GiB, 1 GiB copy, fp16 GEMM %dx%dx%d" % (M, N, K))
+    read100, g100 = read_rate(torch, dev, 100 << 20, 4)
+    read1g, g1g = read_rate(torch, dev, 1 << 30, 2, reps=5)
     a = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
     b = torch.empty_like(a)
     ms = []
@@ -611,16 +671,52 @@ def box_peaks(torch, dev, M, N, K):
             ms.append(e0.elapsed_time(e1))
     gemm_tf = 2.0 * M * N * K / (min(ms) * 1e-3) / 1e12
     del x, w
-    return {"hbm_copy_GBs": round(copy_gbs, 1),
-            "fp16_gemm_TFLOPs": round(gemm_tf, 1),
-            "note": "best of 5 timed runs; copy counts read + write bytes; torch fp16 GEMM at the prefill shape"}
+    res = {"hbm_copy_GBs": round(copy_gbs, 1),
+           "fp16_gemm_TFLOPs": round(gemm_tf, 1),
+           "note": "best of 5 timed runs; copy counts read + write bytes; torch fp16 GEMM at the prefill shape; "
+                   "reads: a plain streaming-read kernel (libnvfp4_probe.so), best grid of 1024/2048/4096 "
+                   "workgroups"}
+    if read100 is not None:
+        res["hbm_read_GBs"] = round(read100, 1)
+        res["hbm_read_100MB_grid"] = g100
+        res["hbm_read_1GiB_GBs"] = round(read1g, 1)
+    else:
+        res["hbm_read_GBs"] = res["hbm_copy_GBs"]
+        res["note"] += "; the read probe library is not built, hbm_read_GBs repeats the copy rate"
+    log("box peaks: read %s GB/s (100 MB), %s GB/s (1 GiB), copy %.0f GB/s, fp16 GEMM %.0f TFLOP/s" % (
+        res.get("hbm_read_GBs"), res.get("hbm_read_1GiB_GBs"), copy_gbs, gemm_tf))
+    return res
+
+
+def _cpu_info():
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:
+        usable = os.cpu_count()
+    return {"cpu_model": model, "nproc": usable, "os_cpu_count": os.cpu_count()}
 
 
 def cpu_baseline(np, p):
-    """The oracle, untuned, on a bounded sample of the headline workload: the
-    W4A4 linear for the first m rows of X against the whole weight (weights
-    quantized beforehand, untimed, as on the GPU)."""
+    """The oracle, untuned, on bounded samples of the benchmark workloads, on
+    the host cores: the headline W4A4 linear for the first m rows of X
+    against the whole weight (weights quantized beforehand, untimed, as on
+    the GPU); the decode GEMV at M = 1 (the oracle spreads rows over its
+    threads, so one row runs on one thread); and the long-prefill activation
+    quantize on its first rows (the two-pass byte count, as on the GPU)."""
     import oracle
+    import workloads
+    info = _cpu_info()
+    nt = oracle.num_threads()
+    log("cpu baseline on %s (%d usable CPUs, %d oracle threads)" % (info["cpu_model"], info["nproc"], nt))
     log("cpu baseline: oracle weight quantize (untimed)")
     wc, ws, wg = oracle.quantize(p.w_parts[0])
     N, K = p.N, p.K
@@ -629,7 +725,6 @@ def cpu_baseline(np, p):
     t1 = time.perf_counter() - t0
     # The oracle spreads rows over its threads, one row per thread at a time:
     # a whole number of rows per thread keeps every thread busy for ~15 s.
-    nt = oracle.num_threads()
     rounds = int(max(1, round(15.0 / max(t1, 1e-3))))
     m = int(min(p.M, nt * rounds))
     log("cpu baseline: 1 row took %.2f s, timing %d rows on %d threads" % (t1, m, nt))
@@ -637,10 +732,48 @@ def cpu_baseline(np, p):
     oracle.linear(np.ascontiguousarray(p.x[:m]), wc, ws, wg)
     dt = time.perf_counter() - t0
     flops = 2.0 * m * N * K
-    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": min(nt, m),
-            "kind": "oracle", "seconds": round(dt, 2),
-            "sample": "W4A4 linear of the first %d of 4096 activation rows (on-the-fly quantize of those rows "
-                      "+ exact int64 GEMM) against the full W[17408x5120]" % m}
+    del wc, ws
+    res = {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": min(nt, m),
+           "kind": "oracle", "seconds": round(dt, 2), **info,
+           "sample": "W4A4 linear of the first %d of 4096 activation rows (on-the-fly quantize of those rows "
+                     "+ exact int64 GEMM) against the full W[17408x5120]" % m}
+
+    # decode GEMV, M = 1: one row against the fused gate/up weight
+    d = workloads.decode(M=1)
+    gss = [oracle.tensor_scale(w) for w in d.w_parts]
+    q = [oracle.quantize(w, gs=g) for w, g in zip(d.w_parts, gss)]
+    scales, S = oracle.fuse_rescale([s for _, s, _ in q], gss)
+    dwc = np.concatenate([c for c, _, _ in q])
+    dws = np.concatenate(scales)
+    del q
+    t0 = time.perf_counter()
+    oracle.linear(d.x, dwc, dws, S)
+    dt = time.perf_counter() - t0
+    nbytes = dwc.nbytes + dws.nbytes + d.x.nbytes + dwc.shape[0] * 2
+    res["decode_gemv_m1"] = {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1,
+                             "seconds": round(dt, 2),
+                             "sample": "decode W4A4 linear X[1x5120] x fused W[34816x5120] (whole call)"}
+    del dwc, dws
+
+    # long-prefill quantize on the first rows, sized for ~5 s
+    # (the generator gives the same first rows whatever the row count)
+    rows = 256
+    t0 = time.perf_counter()
+    oracle.quantize(workloads.long_prefill_activations(M=rows))
+    t1 = time.perf_counter() - t0
+    rows = int(min(32768, max(rows, rows * 5.0 / max(t1, 1e-3))))
+    xs = workloads.long_prefill_activations(M=rows)
+    t0 = time.perf_counter()
+    oracle.quantize(xs)
+    dt = time.perf_counter() - t0
+    two_pass = 2 * xs.nbytes + xs.size // 2 + xs.size // 16
+    res["quantize_long_prefill"] = {"value": round(two_pass / dt / 1e9, 4), "unit": "GB/s",
+                                    "cores": min(nt, rows), "seconds": round(dt, 2),
+                                    "sample": "NVFP4 quantize of the first %d of 32768 long-prefill rows "
+                                              "(two-pass byte count)" % rows}
+    log("cpu baseline: GEMM %.2e TFLOP/s, decode GEMV %.3f GB/s, quantize %.3f GB/s" % (
+        res["value"], res["decode_gemv_m1"]["value"], res["quantize_long_prefill"]["value"]))
+    return res
 
 
 if __name__ == "__main__":

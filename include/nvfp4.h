@@ -165,9 +165,9 @@ nvfp4_status_t nvfp4_fuse_rescale(int n, uint8_t *const *scales, const int64_t *
  *   x        device [M, ld_x] row-major, F32 or BF16; 16-byte aligned,
  *            ld_x * element size a multiple of 16 bytes, ld_x >= K.
  *   M, K, N  >= 0; K % 64 == 0 (the GEMM advances K 64 at a time, which
- *            is 4 scale bytes, one aligned dword, per weight row); for
- *            M > 16, K below 2^23 (activation tiles are addressed with
- *            32-bit offsets), else NVFP4_ERR_SHAPE.
+ *            is 4 scale bytes, one aligned dword, per weight row); K below
+ *            2^23 (the quantized activations are addressed with 32-bit
+ *            offsets), else NVFP4_ERR_SHAPE.
  *   w_codes  device [N, K/2] uint8 dense, 16-byte aligned.
  *   w_scales device [N, K/16] uint8 dense, 4-byte aligned.
  *   w_gs     device, one float.  For a fused weight: the gs_shared of
@@ -198,6 +198,11 @@ nvfp4_status_t nvfp4_gemm(const void *x, nvfp4_dtype_t x_dtype, int64_t M, int64
  * nvfp4_gemm_workspace_size(M, N, K), whose part past the prepared
  * activations it uses as scratch (so runs sharing one workspace must be
  * ordered).  The pair is equivalent to one nvfp4_gemm call.
+ *
+ * A prepared workspace holds, at byte 8192, gs_x (one float) and, from byte
+ * 8448, the quantized activations as fp16 values E2M1(code) * E4M3(scale)
+ * (exact; gs_x not applied), row-major [M, K] with a row stride of 2K bytes.
+ * The layout is stable, so callers and tests may inspect the operand.
  * ---------------------------------------------------------------------- */
 nvfp4_status_t nvfp4_gemm_prepare(const void *x, nvfp4_dtype_t x_dtype, int64_t M, int64_t K,
                                   int64_t ld_x, void *workspace, size_t workspace_bytes,
@@ -317,7 +322,8 @@ nvfp4_status_t nvfp4_fp8_dequantize(const uint8_t *q, const float *scale, int64_
  * nvfp4_gemm_w8a8: X is quantized to E4M3 with one per-tensor scale s_x
  *   (x_scale: a device float, e.g. calibrated, or NULL for RN(amax / 448),
  *   exactly as nvfp4_fp8_quantize), then Y = RN(s_x * s_w) * sum of
- *   E4M3(X) E4M3(W) products with FP32 accumulation; x bf16 or fp32.
+ *   E4M3(X) E4M3(W) products with FP32 accumulation; x bf16 or fp32;
+ *   K below 2^24.
  *   Workspace nvfp4_gemm_w8a8_workspace_size bytes, 256-byte aligned.
  * Errors as in nvfp4_gemm.
  * ---------------------------------------------------------------------- */

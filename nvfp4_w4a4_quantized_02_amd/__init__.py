@@ -149,24 +149,53 @@ _workspaces: dict = {}
 
 
 def workspace(nbytes: int, device) -> torch.Tensor:
-    """A per-device scratch buffer of at least nbytes (256-byte aligned).
-    Calls that use it are ordered on the current stream."""
+    """A scratch buffer of at least nbytes (256-byte aligned), one per
+    (device, current stream): calls that use it are ordered on that stream,
+    so calls on different streams never share one, and a buffer replaced by a
+    larger one was only ever used on the stream it was allocated on (torch's
+    allocator then reuses its memory in that stream's order).  Code under
+    graph capture should pass its own workspace where an entry point takes
+    one, or run once eagerly on the capture stream first."""
     dev = torch.device(device)
-    key = (dev.type, dev.index)
+    if dev.type != "cuda":
+        raise ValueError("workspaces live on a GPU, got device %s" % dev)
+    idx = dev.index if dev.index is not None else torch.cuda.current_device()
+    key = (idx, torch.cuda.current_stream(idx).cuda_stream)
     ws = _workspaces.get(key)
     if ws is None or ws.numel() < nbytes:
-        ws = torch.empty(max(nbytes, 1 << 16), dtype=torch.uint8, device=dev)
+        ws = torch.empty(max(nbytes, 1 << 16), dtype=torch.uint8, device=torch.device("cuda", idx))
         assert ws.data_ptr() % 256 == 0
         _workspaces[key] = ws
     return ws
 
 
 def _rows_view(x: torch.Tensor) -> tuple:
+    """(rows, K, ld) of a 2-D float32/bfloat16 tensor on a GPU whose last
+    dimension is contiguous."""
+    if not isinstance(x, torch.Tensor) or x.device.type != "cuda":
+        raise ValueError("expected a tensor on a GPU")
     if x.dim() != 2:
         raise ValueError("expected a 2-D tensor, got shape %s" % (tuple(x.shape),))
-    if x.stride(1) != 1:
+    if x.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("supported dtypes are float32 and bfloat16, got %s" % x.dtype)
+    if x.stride(1) != 1 and x.shape[1] > 1:
         raise ValueError("the last dimension must be contiguous")
     return x.shape[0], x.shape[1], x.stride(0) if x.shape[0] > 1 else max(x.shape[1], x.stride(0))
+
+
+def _check_u8(t: torch.Tensor, shape: tuple, device, what: str):
+    if not isinstance(t, torch.Tensor) or t.dtype != torch.uint8 or tuple(t.shape) != tuple(shape) \
+            or t.device != device or not t.is_contiguous():
+        raise ValueError("%s must be a contiguous uint8 tensor of shape %s on %s, got %s" % (
+            what, tuple(shape), device, "%s %s on %s" % (t.dtype, tuple(t.shape), t.device)
+            if isinstance(t, torch.Tensor) else type(t).__name__))
+
+
+def _check_scalar(t: torch.Tensor, device, what: str):
+    """A float32 device scalar (the first element is used)."""
+    if not isinstance(t, torch.Tensor) or t.dtype != torch.float32 or t.numel() < 1 or t.device != device \
+            or not t.is_contiguous():
+        raise ValueError("%s must be a contiguous float32 tensor with at least one element on %s" % (what, device))
 
 
 def nvfp4_quantize(x: torch.Tensor):
@@ -189,6 +218,7 @@ def nvfp4_quantize_static(x: torch.Tensor, gs: torch.Tensor):
     """Quantize with a given (calibrated) tensor scale gs (float32 [1] on the
     device).  Returns (codes uint8 [rows, K/2], scales uint8 [rows, K/16])."""
     rows, K, ld = _rows_view(x)
+    _check_scalar(gs, x.device, "gs")
     codes = torch.empty((rows, K // 2), dtype=torch.uint8, device=x.device)
     scales = torch.empty((rows, K // 16), dtype=torch.uint8, device=x.device)
     _check(lib.nvfp4_quantize_static(x.data_ptr(), _dtype_code(x.dtype), rows, K, ld, gs.data_ptr(),
@@ -199,8 +229,13 @@ def nvfp4_quantize_static(x: torch.Tensor, gs: torch.Tensor):
 
 def nvfp4_dequantize(codes: torch.Tensor, scales: torch.Tensor, gs: torch.Tensor,
                      out_dtype: torch.dtype = torch.float32) -> torch.Tensor:
+    if not isinstance(codes, torch.Tensor) or codes.dim() != 2 or codes.device.type != "cuda":
+        raise ValueError("codes must be a 2-D uint8 tensor [rows, K/2] on a GPU")
     rows, half = codes.shape
     K = 2 * half
+    _check_u8(codes, (rows, half), codes.device, "codes")
+    _check_u8(scales, (rows, K // 16), codes.device, "scales")
+    _check_scalar(gs, codes.device, "gs")
     out = torch.empty((rows, K), dtype=out_dtype, device=codes.device)
     _check(lib.nvfp4_dequantize(codes.data_ptr(), scales.data_ptr(), gs.data_ptr(), rows, K, out.data_ptr(),
                                 _dtype_code(out_dtype), K, _stream_ptr(codes.device)), "nvfp4_dequantize")
@@ -213,10 +248,15 @@ def nvfp4_fuse_rescale(scales_list, gs_list) -> torch.Tensor:
     if not 1 <= n <= MAX_FUSED or len(gs_list) != n:
         raise ValueError("need 1..%d members with one tensor scale each" % MAX_FUSED)
     kb = scales_list[0].shape[1]
-    for s in scales_list:
-        if s.dim() != 2 or s.shape[1] != kb or not s.is_contiguous() or s.dtype != torch.uint8:
-            raise ValueError("member scales must be contiguous uint8 [rows, K/16] with one K")
     dev = scales_list[0].device
+    if dev.type != "cuda":
+        raise ValueError("member scales must be on a GPU")
+    for s in scales_list:
+        if s.dim() != 2 or s.shape[1] != kb:
+            raise ValueError("member scales must be uint8 [rows, K/16] with one K")
+        _check_u8(s, tuple(s.shape), dev, "member scales")
+    for g in gs_list:
+        _check_scalar(g, dev, "member tensor scale")
     shared = torch.empty(1, dtype=torch.float32, device=dev)
     ptrs = (ctypes.c_void_p * n)(*[s.data_ptr() for s in scales_list])
     rows = (ctypes.c_int64 * n)(*[s.shape[0] for s in scales_list])
@@ -228,21 +268,38 @@ def nvfp4_fuse_rescale(scales_list, gs_list) -> torch.Tensor:
 
 def _out_tensor(M, N, out_dtype, device):
     # rows padded to a 16-byte multiple, as the kernels store 16-byte aligned
+    _dtype_code(out_dtype)
     per16 = 16 // torch.empty((), dtype=out_dtype).element_size()
     ld_pad = (N + per16 - 1) // per16 * per16
     return torch.empty((M, ld_pad), dtype=out_dtype, device=device)[:, :N]
 
 
-def _check_weight(w_codes, w_scales, K):
+def _check_out(out: torch.Tensor, M: int, N: int, device) -> torch.Tensor:
+    """A caller-supplied output: [M, N] float32/bfloat16 on the device, unit
+    inner stride and rows at least N apart (the library checks alignment)."""
+    if not isinstance(out, torch.Tensor) or tuple(out.shape) != (M, N) or out.device != device:
+        raise ValueError("out must be a tensor of shape %s on %s" % ((M, N), device))
+    if out.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("out must be float32 or bfloat16, got %s" % out.dtype)
+    if N > 1 and out.stride(1) != 1:
+        raise ValueError("out rows must be contiguous")
+    if M > 1 and out.stride(0) < N:
+        raise ValueError("out rows overlap (row stride %d < N = %d)" % (out.stride(0), N))
+    return out
+
+
+def _output(out, M, N, out_dtype, device):
+    return _out_tensor(M, N, out_dtype, device) if out is None else _check_out(out, M, N, device)
+
+
+def _check_weight(w_codes, w_scales, w_gs, K, device):
+    if not isinstance(w_codes, torch.Tensor) or w_codes.dim() != 2:
+        raise ValueError("w_codes must be a 2-D uint8 tensor [N, K/2]")
     N = w_codes.shape[0]
-    if w_codes.shape[1] * 2 != K or tuple(w_scales.shape) != (N, K // 16):
-        raise ValueError("weight shapes %s / %s do not match K=%d" % (tuple(w_codes.shape),
-                                                                       tuple(w_scales.shape), K))
+    _check_u8(w_codes, (N, K // 2), device, "w_codes")
+    _check_u8(w_scales, (N, K // 16), device, "w_scales")
+    _check_scalar(w_gs, device, "w_gs")
     return N
-
-
-def _ld_out(out, M, N):
-    return out.stride(0) if M > 1 else max(N, out.stride(0))
 
 
 def nvfp4_gemm(x: torch.Tensor, w_codes: torch.Tensor, w_scales: torch.Tensor, w_gs: torch.Tensor,
@@ -253,9 +310,10 @@ def nvfp4_gemm(x: torch.Tensor, w_codes: torch.Tensor, w_scales: torch.Tensor, w
     activation tensor scale (float32 [1] on the device) instead of the
     absmax one."""
     M, K, ld = _rows_view(x)
-    N = _check_weight(w_codes, w_scales, K)
-    if out is None:
-        out = _out_tensor(M, N, out_dtype, x.device)
+    N = _check_weight(w_codes, w_scales, w_gs, K, x.device)
+    out = _output(out, M, N, out_dtype, x.device)
+    if x_gs is not None:
+        _check_scalar(x_gs, x.device, "x_gs")
     nws = lib.nvfp4_gemm_workspace_size(M, N, K)
     ws = workspace(nws, x.device)
     if x_gs is None:
@@ -287,7 +345,11 @@ def nvfp4_gemm_prepare(x: torch.Tensor, ws: torch.Tensor | None = None, max_n: i
     nws = lib.nvfp4_gemm_workspace_size(M, max_n, K)
     if ws is None or ws.numel() < nws:
         ws = torch.empty(max(nws, 256), dtype=torch.uint8, device=x.device)
-    assert ws.data_ptr() % 256 == 0
+    _check_u8(ws, (ws.numel(),), x.device, "ws")
+    if ws.data_ptr() % 256:
+        raise ValueError("the workspace must be 256-byte aligned")
+    if x_gs is not None:
+        _check_scalar(x_gs, x.device, "x_gs")
     if x_gs is None:
         _check(lib.nvfp4_gemm_prepare(x.data_ptr(), _dtype_code(x.dtype), M, K, ld, ws.data_ptr(), ws.numel(),
                                       _stream_ptr(x.device)), "nvfp4_gemm_prepare")
@@ -302,9 +364,8 @@ def nvfp4_gemm_run(prep: PreparedActivations, w_codes: torch.Tensor, w_scales: t
                    w_gs: torch.Tensor, out_dtype: torch.dtype = torch.bfloat16,
                    out: torch.Tensor | None = None) -> torch.Tensor:
     M, K = prep.M, prep.K
-    N = _check_weight(w_codes, w_scales, K)
-    if out is None:
-        out = _out_tensor(M, N, out_dtype, prep.ws.device)
+    N = _check_weight(w_codes, w_scales, w_gs, K, prep.ws.device)
+    out = _output(out, M, N, out_dtype, prep.ws.device)
     _check(lib.nvfp4_gemm_run(M, K, w_codes.data_ptr(), w_scales.data_ptr(), w_gs.data_ptr(), N, out.data_ptr(),
                               _dtype_code(out.dtype), _ld_out(out, M, N), prep.ws.data_ptr(), prep.ws.numel(),
                               _stream_ptr(prep.ws.device)), "nvfp4_gemm_run")
@@ -317,9 +378,8 @@ def nvfp4_gemm_w4a16(x: torch.Tensor, w_codes: torch.Tensor, w_scales: torch.Ten
     quantization) and W given as NVFP4 (codes [N, K/2], scales [N, K/16],
     w_gs [1])."""
     M, K, ld = _rows_view(x)
-    N = _check_weight(w_codes, w_scales, K)
-    if out is None:
-        out = _out_tensor(M, N, out_dtype, x.device)
+    N = _check_weight(w_codes, w_scales, w_gs, K, x.device)
+    out = _output(out, M, N, out_dtype, x.device)
     nws = lib.nvfp4_gemm_w4a16_workspace_size(M, N, K)
     ws = workspace(nws, x.device) if nws else None
     _check(lib.nvfp4_gemm_w4a16(x.data_ptr(), _dtype_code(x.dtype), M, K, ld, w_codes.data_ptr(),
@@ -341,23 +401,29 @@ def nvfp4_fp8_quantize(x: torch.Tensor, scale: torch.Tensor | None = None):
         _check(lib.nvfp4_fp8_quantize(x.data_ptr(), _dtype_code(x.dtype), rows, K, ld, q.data_ptr(), s.data_ptr(),
                                       ws.data_ptr(), ws.numel(), _stream_ptr(x.device)), "nvfp4_fp8_quantize")
         return q, s
+    _check_scalar(scale, x.device, "scale")
     _check(lib.nvfp4_fp8_quantize_static(x.data_ptr(), _dtype_code(x.dtype), rows, K, ld, scale.data_ptr(),
                                          q.data_ptr(), _stream_ptr(x.device)), "nvfp4_fp8_quantize_static")
     return q, scale
 
 
 def nvfp4_fp8_dequantize(q: torch.Tensor, scale: torch.Tensor, out_dtype: torch.dtype = torch.float32):
+    if not isinstance(q, torch.Tensor) or q.dim() != 2 or q.device.type != "cuda":
+        raise ValueError("q must be a 2-D uint8 tensor on a GPU")
     rows, K = q.shape
+    _check_u8(q, (rows, K), q.device, "q")
+    _check_scalar(scale, q.device, "scale")
     out = torch.empty((rows, K), dtype=out_dtype, device=q.device)
     _check(lib.nvfp4_fp8_dequantize(q.data_ptr(), scale.data_ptr(), rows, K, out.data_ptr(), _dtype_code(out_dtype),
                                     K, _stream_ptr(q.device)), "nvfp4_fp8_dequantize")
     return out
 
 
-def _check_fp8_weight(w_q: torch.Tensor, K: int) -> int:
-    if w_q.dtype != torch.uint8 or w_q.dim() != 2 or w_q.shape[1] != K or not w_q.is_contiguous():
-        raise ValueError("FP8 weights must be contiguous uint8 [N, K=%d], got %s %s" % (K, w_q.dtype,
-                                                                                       tuple(w_q.shape)))
+def _check_fp8_weight(w_q: torch.Tensor, w_scale: torch.Tensor, K: int, device) -> int:
+    if not isinstance(w_q, torch.Tensor) or w_q.dim() != 2:
+        raise ValueError("FP8 weights must be a 2-D uint8 tensor [N, K=%d]" % K)
+    _check_u8(w_q, (w_q.shape[0], K), device, "FP8 weights")
+    _check_scalar(w_scale, device, "w_scale")
     return w_q.shape[0]
 
 
@@ -366,9 +432,8 @@ def nvfp4_gemm_w8a16(x: torch.Tensor, w_q: torch.Tensor, w_scale: torch.Tensor,
     """W8A16: Y = X (E4M3(W) * s_w)^T, X [M, K] bf16 as given, W [N, K] E4M3
     bytes with one per-tensor scale (float32 [1])."""
     M, K, ld = _rows_view(x)
-    N = _check_fp8_weight(w_q, K)
-    if out is None:
-        out = _out_tensor(M, N, out_dtype, x.device)
+    N = _check_fp8_weight(w_q, w_scale, K, x.device)
+    out = _output(out, M, N, out_dtype, x.device)
     nws = lib.nvfp4_gemm_w8a16_workspace_size(M, N, K)
     ws = workspace(nws, x.device) if nws else None
     _check(lib.nvfp4_gemm_w8a16(x.data_ptr(), _dtype_code(x.dtype), M, K, ld, w_q.data_ptr(), w_scale.data_ptr(), N,
@@ -383,9 +448,10 @@ def nvfp4_gemm_w8a8(x: torch.Tensor, w_q: torch.Tensor, w_scale: torch.Tensor, x
     """W8A8: X quantized to E4M3 with one per-tensor scale (RN(amax/448), or
     the calibrated x_scale), then Y = RN(s_x s_w) * E4M3(X) E4M3(W)^T."""
     M, K, ld = _rows_view(x)
-    N = _check_fp8_weight(w_q, K)
-    if out is None:
-        out = _out_tensor(M, N, out_dtype, x.device)
+    N = _check_fp8_weight(w_q, w_scale, K, x.device)
+    out = _output(out, M, N, out_dtype, x.device)
+    if x_scale is not None:
+        _check_scalar(x_scale, x.device, "x_scale")
     ws = workspace(lib.nvfp4_gemm_w8a8_workspace_size(M, N, K), x.device)
     _check(lib.nvfp4_gemm_w8a8(x.data_ptr(), _dtype_code(x.dtype), M, K, ld,
                                x_scale.data_ptr() if x_scale is not None else None, w_q.data_ptr(),

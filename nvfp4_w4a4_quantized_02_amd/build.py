@@ -1,7 +1,8 @@
 """Build the HIP library ``libnvfp4.so`` for gfx950 with hipcc.
 
 Every ``csrc/*.hip`` file is compiled to an object under ``_build/`` and the
-objects are linked into ``nvfp4_w4a4_quantized_02_amd/libnvfp4.so``.  Run as
+objects are linked into ``nvfp4_w4a4_quantized_02_amd/libnvfp4.so``; the
+benchmark's reference kernels (``probe/*.hip``) go into ``libnvfp4_probe.so``.  Run as
 ``python nvfp4_w4a4_quantized_02_amd/build.py`` (a script: importing the
 package itself needs the built library).
 """
@@ -18,6 +19,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libnvfp4.so")
+PROBE = os.path.join(PKG, "probe")
+PROBE_LIB = os.path.join(PKG, "libnvfp4_probe.so")
 ARCH = "gfx950"
 
 # -ffp-contract=off keeps every fp32 step of the quantizer a separately
@@ -47,19 +50,27 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
-    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = LIB + ".tmp%d" % os.getpid()
+def _link(objs, lib):
+    tmp = lib + ".tmp%d" % os.getpid()
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n%s\n%s" % (r.stdout, r.stderr))
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    """Build libnvfp4.so and the benchmark's reference-kernel library
+    libnvfp4_probe.so (a plain HBM read, not part of the NVFP4 path)."""
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    probe_srcs = sorted(glob.glob(os.path.join(PROBE, "*.hip")))
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs) + len(probe_srcs))) as ex:
+        objs = list(ex.map(_compile, srcs + probe_srcs))
+    _link(objs[:len(srcs)], LIB)
+    _link(objs[len(srcs):], PROBE_LIB)
     if verbose:
-        print("built", LIB)
+        print("built", LIB, "and", PROBE_LIB)
     return LIB
 
 

@@ -144,11 +144,10 @@ nvfp4_status_t nvfp4_fuse_rescale(int n, uint8_t* const* scales, const int64_t* 
   return launched();
 }
 
-// The tile GEMM (M > 16) addresses the fp16 activations of a 256-row tile
-// with 32-bit offsets.
-static bool tile_rows_ok(int64_t M, int64_t K) {
-  return M <= kGemvMaxM || (uint64_t)round_up(K, kGemmBK) * 2u < kMaxTileRowBytes;
-}
+// The contraction kernels address up to 256 rows of the fp16 activations
+// (the tile GEMM) or up to 16 (the GEMV forms) from a base with 32-bit
+// offsets, so a row may not reach 2^24 bytes.
+static bool tile_rows_ok(int64_t K) { return (uint64_t)round_up(K, kGemmBK) * 2u < kMaxTileRowBytes; }
 
 // Workspace: absmax partials | gs_x | fp16 activations [Mp, Kp] | fp32 K-part
 // sums of the split tiles (see plan_gemm).
@@ -213,7 +212,7 @@ nvfp4_status_t nvfp4_gemm_run(int64_t M, int64_t K, const uint8_t* w_codes, cons
                               void* workspace, size_t workspace_bytes, void* stream) {
   if (!dtype_ok(y_dtype)) return NVFP4_ERR_DTYPE;
   if (M < 0 || K < 0 || N < 0 || M >= kMaxDim || K >= kMaxDim || N >= kMaxDim) return NVFP4_ERR_SHAPE;
-  if (K % 64 != 0 || !tile_rows_ok(M, K)) return NVFP4_ERR_SHAPE;
+  if (K % 64 != 0 || !tile_rows_ok(K)) return NVFP4_ERR_SHAPE;
   if (M == 0 || N == 0) return NVFP4_OK;
   if (!y || !w_gs) return NVFP4_ERR_NULL;
   if (ld_y < N) return NVFP4_ERR_SHAPE;
@@ -244,7 +243,7 @@ static nvfp4_status_t run_args_ok(int64_t M, int64_t K, const uint8_t* w_codes, 
                                   int64_t ld_y, const void* workspace, size_t workspace_bytes) {
   if (!dtype_ok(y_dtype)) return NVFP4_ERR_DTYPE;
   if (N < 0 || N >= kMaxDim) return NVFP4_ERR_SHAPE;
-  if (K % 64 != 0 || !tile_rows_ok(M, K)) return NVFP4_ERR_SHAPE;
+  if (K % 64 != 0 || !tile_rows_ok(K)) return NVFP4_ERR_SHAPE;
   if (M == 0 || N == 0) return NVFP4_OK;
   if (!y || !w_gs) return NVFP4_ERR_NULL;
   if (ld_y < N) return NVFP4_ERR_SHAPE;
@@ -400,6 +399,9 @@ nvfp4_status_t nvfp4_gemm_w8a8(const void* x, nvfp4_dtype_t x_dtype, int64_t M, 
                                void* stream) {
   nvfp4_status_t st = check_input(x, x_dtype, M, K, ld_x);
   if (st != NVFP4_OK) return st;
+  // the E4M3 activations (row stride K bytes) are addressed like the
+  // activations of the other linears
+  if ((uint64_t)K >= kMaxTileRowBytes) return NVFP4_ERR_SHAPE;
   st = fp8w_args_ok(M, K, w_q, w_scale, N, y, y_dtype, ld_y);
   if (st != NVFP4_OK || M == 0 || N == 0) return st;
   if (!workspace || !aligned(workspace, 256) || workspace_bytes < nvfp4_gemm_w8a8_workspace_size(M, N, K))

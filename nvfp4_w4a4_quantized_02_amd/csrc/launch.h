@@ -55,8 +55,13 @@ constexpr int kGemvMaxM = 16;  // M at or below this uses the GEMV kernel
 // Tiling of one GEMM.  Whole 256 x 256 tiles fill complete rounds of the
 // machine; when the last round would leave most compute units idle, its
 // tiles are split along K into `split` parts that write fp32 partial sums,
-// which a second kernel adds in a fixed order.
-constexpr int kGemmCUs = 256;  // compute units of an MI355X
+// which a second kernel adds in a fixed order.  A round is one tile per
+// compute unit of the current device (256 on a whole MI355X, the value
+// taken when the runtime cannot report it).
+inline int gemm_cus() {
+  int cus = 0, lds = 0;
+  return device_caps(cus, lds) ? cus : 256;
+}
 
 struct GemmPlan {
   int tiles_m, tiles_n, nk;
@@ -71,8 +76,9 @@ inline GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K) {
   p.tiles_n = (int)((N + kGemmBN - 1) / kGemmBN);
   p.nk = (int)((K + kGemmBK - 1) / kGemmBK);
   const int tiles = p.tiles_m * p.tiles_n;
-  const int rem = tiles % kGemmCUs;
-  int split = rem ? kGemmCUs / rem : 1;
+  const int cus = gemm_cus();
+  const int rem = tiles % cus;
+  int split = rem ? cus / rem : 1;
   if (split > p.nk) split = p.nk;
   if (split < 2 || M <= kGemvMaxM) {
     p.full_tiles = tiles;

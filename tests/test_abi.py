@@ -95,7 +95,9 @@ def test_gemm_rejects(nv):
     assert g(nv, K=48, ld=48) == E_SHAPE              # K % 64
     assert g(nv, K=96, ld=96) == E_SHAPE
     assert g(nv, K=1 << 23, ld=1 << 23) == E_SHAPE    # tile rows past 32-bit offsets (M > 16)
+    assert g(nv, M=16, K=1 << 23, ld=1 << 23) == E_SHAPE  # and the GEMV forms' (M <= 16)
     assert nv.lib.nvfp4_gemm_run(32, 1 << 23, A, A, A, 64, A, BF16, 64, A, BIG, None) == E_SHAPE
+    assert nv.lib.nvfp4_gemm_run(4, 1 << 23, A, A, A, 64, A, BF16, 64, A, BIG, None) == E_SHAPE
     assert g(nv, N=-3) == E_SHAPE
     assert g(nv, ldy=32) == E_SHAPE
     assert g(nv, y=None) == E_NULL
@@ -252,6 +254,8 @@ def test_fp8_linear_rejects(nv):
     assert w88(ws=None) == E_WS
     assert w88(nws=L.nvfp4_gemm_w8a8_workspace_size(32, 64, 64) - 1) == E_WS
     assert w88(N=0) == OK
+    assert w88(M=32, K=1 << 24, ld=1 << 24) == E_SHAPE    # E4M3 rows past 32-bit tile offsets
+    assert w88(M=4, K=1 << 24, ld=1 << 24) == E_SHAPE
     # X in FP8 (M x K bytes) plus the split-K sums of the tile GEMM
     assert L.nvfp4_gemm_w8a8_workspace_size(4096, 17408, 5120) >= 4096 * 5120 + \
         L.nvfp4_gemm_w8a16_workspace_size(4096, 17408, 5120)

@@ -115,17 +115,14 @@ def test_fp8_dequantize(nv, orc, out):
         assert np.array_equal(d, workloads.to_bf16_bits(ref))
 
 
-def test_fp8_long_sampled(nv, orc):
+def test_fp8_long_every_byte(nv, orc):
     x = workloads.long_prefill_activations()
-    print("case: fp8 long prefill 32768x5120", flush=True)
+    print("case: fp8 long prefill 32768x5120, every byte", flush=True)
     q, s = nv.nvfp4_fp8_quantize(to_gpu(x))
     torch.cuda.synchronize()
-    os_ = orc.fp8_tensor_scale(x)
+    oq, os_ = orc.fp8_quantize(x)
     assert np.float32(s.item()) == os_
-    rows = np.unique(np.concatenate([np.random.default_rng(9).choice(x.shape[0], 256, replace=False),
-                                     [0, x.shape[0] - 1]]))
-    oq, _ = orc.fp8_quantize(np.ascontiguousarray(x[rows]), scale=os_)
-    assert np.array_equal(to_np(q)[rows], oq)
+    assert np.array_equal(to_np(q), oq)
 
 
 def test_fp8_empty(nv):

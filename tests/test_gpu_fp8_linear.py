@@ -4,14 +4,14 @@ float8_e4m3 weights with one per-tensor scale, served W8A16; W8A8 with FP8
 activations).  The weights are the oracle's bytes, uploaded.  Every form is
 hit: the K-split GEMV (M <= 16, K <= 5120, including a partial last slice),
 the tile GEMM with and without its split-K tail, and small M with K > 5120;
-full decode and prefill sizes on sampled outputs.  Gate: the GEMM gate of
+full decode and prefill sizes on whole output rows.  Gate: the GEMM gate of
 the W4A4 tests."""
 import numpy as np
 import pytest
 import torch
 
 import workloads
-from parity import check_gemm, to_gpu, to_np
+from parity import check_gemm, sample_rows, to_gpu, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -82,9 +82,11 @@ def test_fp8_linears_empty_and_k_zero(nv):
             assert torch.count_nonzero(y).item() == 0
 
 
-def _sampled(nv, orc, x, w, a8, nsamp, seed, idx=None):
+def _rows(nv, orc, x, w, a8, rows):
+    """GPU linear on FP8 weights (quantized on the GPU, byte-exact with the
+    oracle by the FP8 quantize tests); the oracle recomputes whole rows."""
     sw = orc.fp8_tensor_scale(w)
-    q, s = nv.nvfp4_fp8_quantize(to_gpu(w))       # byte-exact with the oracle (FP8 quantize tests)
+    q, s = nv.nvfp4_fp8_quantize(to_gpu(w))
     torch.cuda.synchronize()
     assert np.float32(s.item()) == sw
     xg = to_gpu(x)
@@ -94,24 +96,15 @@ def _sampled(nv, orc, x, w, a8, nsamp, seed, idx=None):
         y = to_np(nv.nvfp4_gemm_w8a16(xg, q, s, out_dtype=torch.bfloat16))
     torch.cuda.synchronize()
     del q
-    M, N = x.shape[0], w.shape[0]
-    if idx is None:
-        g = np.random.default_rng(seed)
-        mi, ni = g.integers(0, M, nsamp), g.integers(0, N, nsamp)
-        mi[:2], ni[:2] = [0, M - 1], [0, N - 1]
-    else:
-        mi, ni = idx
-    rows_w, rows_x = np.unique(ni), np.unique(mi)
-    wq, _ = orc.fp8_quantize(np.ascontiguousarray(w[rows_w]), scale=sw)
-    xs = np.ascontiguousarray(x[rows_x])
+    wq, _ = orc.fp8_quantize(w, scale=sw)
+    xs = np.ascontiguousarray(x[rows])
     if a8:
         sx = orc.fp8_tensor_scale(x)
         xq, _ = orc.fp8_quantize(xs, scale=sx)
-        full = orc.gemm_w8a8(xq, sx, wq, sw)
+        ref = orc.gemm_w8a8(xq, sx, wq, sw)
     else:
-        full = orc.gemm_w8a16(xs, wq, sw)
-    ref = full[np.searchsorted(rows_x, mi), np.searchsorted(rows_w, ni)]
-    return y[mi, ni], ref
+        ref = orc.gemm_w8a16(xs, wq, sw)
+    return y[rows], ref
 
 
 @pytest.mark.parametrize("a8", [False, True])
@@ -120,7 +113,7 @@ def test_fp8_linear_full_decode(nv, orc, M, a8):
     p = workloads.decode(M=M)
     w = np.concatenate(p.w_parts)
     print("case: %s full decode M=%d N=34816 K=5120" % ("w8a8" if a8 else "w8a16", M), flush=True)
-    got, ref = _sampled(nv, orc, p.x, w, a8, 1500, 3)
+    got, ref = _rows(nv, orc, p.x, w, a8, np.arange(M))
     check_gemm(got, ref, True, "fp8 full decode M=%d" % M)
 
 
@@ -128,7 +121,7 @@ def test_fp8_linear_full_decode(nv, orc, M, a8):
 def test_fp8_linear_full_prefill(nv, orc, a8):
     p = workloads.prefill()
     print("case: %s full prefill 4096x17408x5120" % ("w8a8" if a8 else "w8a16"), flush=True)
-    got, ref = _sampled(nv, orc, p.x, p.w_parts[0], a8, 1500, 4)
+    got, ref = _rows(nv, orc, p.x, p.w_parts[0], a8, sample_rows(p.M, 10, 4, must=[3840, 4000]))
     check_gemm(got, ref, True, "fp8 full prefill")
 
 
@@ -136,13 +129,9 @@ def test_fp8_linear_full_prefill(nv, orc, a8):
 def test_fp8_linear_split_tail(nv, orc, a8):
     # 2 x 129 tiles = 258 of the shared tile plan: the last 2 (tile row 1,
     # tile columns 127 and 128, both ragged) are split along K (K = 128 is 2
-    # steps).  Every output of those tiles, plus samples elsewhere.
+    # steps).  Every output.
     M, N, K = 500, 33000, 128
     p = workloads.prefill(M=M, K=K, N=N)
     print("case: %s split tail M=%d N=%d K=%d" % ("w8a8" if a8 else "w8a16", M, N, K), flush=True)
-    tm, tn = np.meshgrid(np.arange(256, M), np.arange(127 * 256, N), indexing="ij")
-    g = np.random.default_rng(6)
-    mi = np.concatenate([tm.ravel(), g.integers(0, M, 1000)])
-    ni = np.concatenate([tn.ravel(), g.integers(0, N, 1000)])
-    got, ref = _sampled(nv, orc, p.x, p.w_parts[0], a8, 0, 0, idx=(mi, ni))
+    got, ref = _rows(nv, orc, p.x, p.w_parts[0], a8, np.arange(M))
     check_gemm(got, ref, True, "fp8 split tail")

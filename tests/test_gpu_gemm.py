@@ -1,6 +1,6 @@
 """GPU parity of nvfp4_gemm (W4A4 linear with on-the-fly activation
 quantization) against the oracle's exact GEMM, at small sizes element by
-element and at the full workload sizes on sampled outputs.
+element and at the full workload sizes on whole sampled output rows.
 
 Weights are quantized independently on both sides (nvfp4_quantize on the
 GPU, the oracle on the CPU); the quantize tests establish that both give the
@@ -11,7 +11,7 @@ import pytest
 import torch
 
 import workloads
-from parity import check_gemm, to_gpu, to_np
+from parity import check_gemm, sample_rows, to_gpu, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -159,27 +159,21 @@ def test_unrepaired_fusion_is_misscaled(nv, orc):
     check_gemm(_run(nv, p, torch.float32), ref, False, "repaired")
 
 
-# --------------------------------------------------------- full sizes, sampled
+# --------------------------------------------------------- full sizes, whole rows
+# At the full workload sizes the oracle recomputes whole output rows (the
+# complete weight against a sample of activation rows, the tensor scale taken
+# over the whole activation tensor), so every element is gated against the
+# rms of its own row.
 
-def _sampled(nv, orc, p, out_dtype, nsamp=1500, seed=0, idx=None):
+def _rows(nv, orc, p, out_dtype, rows):
     wc, ws, wg = _gpu_weight(nv, p.w_parts)
     y = to_np(nv.nvfp4_gemm(to_gpu(p.x), wc, ws, wg, out_dtype=out_dtype))
     torch.cuda.synchronize()
-    if idx is None:
-        g = np.random.default_rng(seed)
-        mi = g.integers(0, p.M, nsamp)
-        ni = g.integers(0, p.N, nsamp)
-        mi[:2], ni[:2] = [0, p.M - 1], [0, p.N - 1]
-    else:
-        mi, ni = idx
-    rows_w = np.unique(ni)
-    owc, ows, owg = _oracle_weight(orc, p.w_parts, rows=rows_w)
-    rows_x = np.unique(mi)
+    del wc, ws
+    owc, ows, owg = _oracle_weight(orc, p.w_parts)
     gx = orc.tensor_scale(p.x)
-    oxc, oxs, _ = orc.quantize(np.ascontiguousarray(p.x[rows_x]), gs=gx)
-    ref = orc.gemm_exact_sampled(oxc, oxs, gx, owc, ows, owg, np.searchsorted(rows_x, mi),
-                                 np.searchsorted(rows_w, ni))
-    return y[mi, ni], ref
+    oxc, oxs, _ = orc.quantize(np.ascontiguousarray(p.x[rows]), gs=gx)
+    return y[rows], orc.gemm_exact(oxc, oxs, gx, owc, ows, owg)
 
 
 # Split-K tail: when the tiles do not fill whole rounds of the 256 compute
@@ -187,51 +181,47 @@ def _sampled(nv, orc, p, out_dtype, nsamp=1500, seed=0, idx=None):
 # along K and a second kernel adds the parts.
 def test_split_tail_every_output(nv, orc):
     # 2 x 129 tiles = 258: the last 2 (tile row 1, tile columns 127 and 128,
-    # both ragged) are split in 2 (K = 128 is 2 steps).  Every output of
-    # those two tiles is checked, plus samples of the whole tiles.
+    # both ragged) are split in 2 (K = 128 is 2 steps).  Every output.
     M, N, K = 500, 33000, 128
     p = workloads.prefill(M=M, K=K, N=N)
     print("case: split tail gemm M=%d N=%d K=%d" % (M, N, K), flush=True)
-    tm, tn = np.meshgrid(np.arange(256, M), np.arange(127 * 256, N), indexing="ij")
-    g = np.random.default_rng(4)
-    mi = np.concatenate([tm.ravel(), g.integers(0, M, 1000)])
-    ni = np.concatenate([tn.ravel(), g.integers(0, N, 1000)])
-    got, ref = _sampled(nv, orc, p, torch.float32, idx=(mi, ni))
+    got, ref = _rows(nv, orc, p, torch.float32, np.arange(M))
     check_gemm(got, ref, False, "split tail %dx%dx%d" % (M, N, K))
 
 
-def test_split_tail_16_parts_sampled(nv, orc):
+def test_split_tail_16_parts(nv, orc):
     # 2 x 257 tiles = 514: the last 2 (tile row 1, tile columns 255 and 256)
-    # are split in 16 (K = 1024 is 16 steps); most samples fall in them
+    # are split in 16 (K = 1024 is 16 steps): every row of the split tiles
+    # (256..299) and a sample of the others, whole
     M, N, K = 300, 65600, 1024
     p = workloads.prefill(M=M, K=K, N=N)
-    print("case: split tail sampled M=%d N=%d K=%d" % (M, N, K), flush=True)
-    g = np.random.default_rng(5)
-    mi = np.concatenate([g.integers(256, M, 1500), g.integers(0, M, 500), [256, M - 1]])
-    ni = np.concatenate([g.integers(255 * 256, N, 1500), g.integers(0, N, 500), [255 * 256, N - 1]])
-    got, ref = _sampled(nv, orc, p, torch.float32, idx=(mi, ni))
-    check_gemm(got, ref, False, "split tail sampled")
+    print("case: split tail 16 parts M=%d N=%d K=%d" % (M, N, K), flush=True)
+    rows = sample_rows(M, 8, 5, must=np.arange(256, M))
+    got, ref = _rows(nv, orc, p, torch.float32, rows)
+    check_gemm(got, ref, False, "split tail 16 parts")
 
 
 @pytest.mark.parametrize("M", [1, 4, 16])
 def test_full_decode(nv, orc, M):
     p = workloads.decode(M=M)
-    print("case: full decode M=%d N=34816 K=5120" % M, flush=True)
-    got, ref = _sampled(nv, orc, p, torch.bfloat16, nsamp=3000)
+    print("case: full decode M=%d N=34816 K=5120, every output" % M, flush=True)
+    got, ref = _rows(nv, orc, p, torch.bfloat16, np.arange(M))
     check_gemm(got, ref, True, "full decode M=%d" % M)
 
 
 def test_full_prefill(nv, orc):
     p = workloads.prefill()
-    print("case: full prefill 4096x17408x5120", flush=True)
-    got, ref = _sampled(nv, orc, p, torch.bfloat16, nsamp=3000)
+    print("case: full prefill 4096x17408x5120, whole rows", flush=True)
+    # rows of the first and last tile rows and of the split tail (tile row 15)
+    rows = sample_rows(p.M, 10, 0, must=[255, 256, 3840, 4000])
+    got, ref = _rows(nv, orc, p, torch.bfloat16, rows)
     check_gemm(got, ref, True, "full prefill")
 
 
 @pytest.mark.parametrize("out", ["f32", "bf16"])
 def test_full_fused_qkv(nv, orc, out):
     p = workloads.fused_qkv()
-    print("case: full fused qkv 2048x8192x5120 %s" % out, flush=True)
+    print("case: full fused qkv 2048x8192x5120 %s, whole rows" % out, flush=True)
     od = torch.bfloat16 if out == "bf16" else torch.float32
-    got, ref = _sampled(nv, orc, p, od, nsamp=3000)
+    got, ref = _rows(nv, orc, p, od, sample_rows(p.M, 12, 1 if out == "f32" else 2))
     check_gemm(got, ref, out == "bf16", "full fused qkv")

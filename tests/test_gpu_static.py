@@ -81,18 +81,16 @@ def test_static_quantize_extreme_scales(nv, orc, gs):
 
 
 def test_static_quantize_full_size_long_prefill(nv, orc):
-    """X[32768x5120] bf16 with a calibrated scale half the absmax one:
-    sampled rows bit-exact."""
+    """X[32768x5120] bf16 with a calibrated scale half the absmax one: every
+    code and scale byte."""
     x = workloads.long_prefill_activations()
     gs = np.float32(orc.tensor_scale(x) * np.float32(0.5))
-    print("case: static long prefill 32768x5120", flush=True)
+    print("case: static long prefill 32768x5120, every byte", flush=True)
     c, s = nv.nvfp4_quantize_static(to_gpu(x), _gs_tensor(gs))
     torch.cuda.synchronize()
-    rows = np.sort(np.random.default_rng(6).choice(x.shape[0], 512, replace=False))
-    rows = np.unique(np.concatenate([rows, [0, x.shape[0] - 1]]))
-    oc, os_, _ = orc.quantize(np.ascontiguousarray(x[rows]), gs=gs)
-    assert np.array_equal(to_np(s)[rows], os_)
-    assert np.array_equal(to_np(c)[rows], oc)
+    oc, os_, _ = orc.quantize(x, gs=gs)
+    assert np.array_equal(to_np(s), os_)
+    assert np.array_equal(to_np(c), oc)
 
 
 def test_static_quantize_empty(nv):
@@ -141,8 +139,9 @@ def test_static_prepare_then_run(nv, orc):
         check_gemm(y, orc.gemm_exact(xc, xs, gx, oc, os_, og), True, "prepared static N=%d" % N)
 
 
-def test_static_full_decode_sampled(nv, orc):
-    """Decode at the full fused gate/up size with a calibrated scale."""
+def test_static_full_decode(nv, orc):
+    """Decode at the full fused gate/up size with a calibrated scale: every
+    output."""
     p = workloads.decode(M=16)
     w = np.concatenate(p.w_parts)
     wc, ws, wg = nv.nvfp4_quantize(to_gpu(w))
@@ -150,10 +149,8 @@ def test_static_full_decode_sampled(nv, orc):
     print("case: static full decode M=16 N=34816 K=5120", flush=True)
     y = to_np(nv.nvfp4_gemm(to_gpu(p.x), wc, ws, wg, out_dtype=torch.bfloat16, x_gs=_gs_tensor(gx)))
     torch.cuda.synchronize()
-    g = np.random.default_rng(3)
-    ni = np.unique(np.concatenate([g.integers(0, w.shape[0], 300), [0, w.shape[0] - 1]]))
-    ogw = orc.tensor_scale(w)
-    oc, os_, _ = orc.quantize(np.ascontiguousarray(w[ni]), gs=ogw)
+    del wc, ws
+    oc, os_, ogw = orc.quantize(w)
     xc, xs, _ = orc.quantize(p.x, gs=gx)
     ref = orc.gemm_exact(xc, xs, gx, oc, os_, ogw)
-    check_gemm(y[:, ni], ref, True, "static full decode")
+    check_gemm(y, ref, True, "static full decode")

@@ -6,14 +6,14 @@ NVFP4 weights); weight format from the paper "Why Gated DeltaNet Survives
 
 The weights are the oracle's bytes, uploaded; every GEMV form (streaming,
 K-split, shared, general) and the tile GEMM with its split-K tail are hit at
-ragged shapes, and the full decode and prefill shapes on sampled outputs.
+ragged shapes, and the full decode and prefill shapes on whole output rows.
 Gate: the GEMM gate of the W4A4 tests (accumulation order is free)."""
 import numpy as np
 import pytest
 import torch
 
 import workloads
-from parity import check_gemm, to_gpu, to_np
+from parity import check_gemm, sample_rows, to_gpu, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -87,9 +87,9 @@ def test_w4a16_rejects_fp32_activations(nv):
         nv.nvfp4_gemm_w4a16(x, wc, ws, torch.ones(1, device="cuda:0"))
 
 
-def _sampled(nv, orc, x, w_parts, nsamp, seed, idx=None):
+def _rows(nv, orc, x, w_parts, rows):
     """Fused weight quantized member by member and repaired on the GPU; the
-    oracle recomputes the sampled rows from the same member scales."""
+    oracle recomputes whole output rows from the same member scales."""
     q = [nv.nvfp4_quantize(to_gpu(w)) for w in w_parts]
     if len(q) > 1:
         shared = nv.nvfp4_fuse_rescale([s for _, s, _ in q], [g for _, _, g in q])
@@ -99,57 +99,41 @@ def _sampled(nv, orc, x, w_parts, nsamp, seed, idx=None):
         wc, ws, shared = q[0]
     y = to_np(nv.nvfp4_gemm_w4a16(to_gpu(x), wc, ws, shared, out_dtype=torch.bfloat16))
     torch.cuda.synchronize()
-    M, N = x.shape[0], wc.shape[0]
-    if idx is None:
-        g = np.random.default_rng(seed)
-        mi, ni = g.integers(0, M, nsamp), g.integers(0, N, nsamp)
-        mi[:2], ni[:2] = [0, M - 1], [0, N - 1]
-    else:
-        mi, ni = idx
-    rows_w = np.unique(ni)
+    del q, wc, ws
     gss = [orc.tensor_scale(w) for w in w_parts]
-    offs = np.cumsum([0] + [w.shape[0] for w in w_parts])
     codes, scales = [], []
-    for i, w in enumerate(w_parts):
-        sel = rows_w[(rows_w >= offs[i]) & (rows_w < offs[i + 1])] - offs[i]
-        c, s, _ = orc.quantize(np.ascontiguousarray(w[sel]), gs=gss[i])
+    for w, g in zip(w_parts, gss):
+        c, s, _ = orc.quantize(w, gs=g)
         codes.append(c)
         scales.append(s)
     if len(w_parts) > 1:
         scales, S = orc.fuse_rescale(scales, gss)
     else:
         S = gss[0]
-    rows_x = np.unique(mi)
-    ref = orc.gemm_w4a16_sampled(np.ascontiguousarray(x[rows_x]), np.concatenate(codes), np.concatenate(scales),
-                                 S, np.searchsorted(rows_x, mi), np.searchsorted(rows_w, ni))
-    return y[mi, ni], ref
+    ref = orc.gemm_w4a16(np.ascontiguousarray(x[rows]), np.concatenate(codes), np.concatenate(scales), S)
+    return y[rows], ref
 
 
 @pytest.mark.parametrize("M", [1, 4, 16])
 def test_w4a16_full_decode(nv, orc, M):
     p = workloads.decode(M=M)
     print("case: w4a16 full decode M=%d N=34816 K=5120" % M, flush=True)
-    got, ref = _sampled(nv, orc, p.x, p.w_parts, 3000, 1)
+    got, ref = _rows(nv, orc, p.x, p.w_parts, np.arange(M))
     check_gemm(got, ref, True, "w4a16 full decode M=%d" % M)
 
 
 def test_w4a16_full_prefill(nv, orc):
     p = workloads.prefill()
     print("case: w4a16 full prefill 4096x17408x5120", flush=True)
-    got, ref = _sampled(nv, orc, p.x, p.w_parts, 3000, 2)
+    got, ref = _rows(nv, orc, p.x, p.w_parts, sample_rows(p.M, 10, 2, must=[3840, 4000]))
     check_gemm(got, ref, True, "w4a16 full prefill")
 
 
 def test_w4a16_split_tail(nv, orc):
     # 2 x 129 tiles = 258: the last 2 (tile row 1, tile columns 127 and 128,
-    # both ragged) are split along K (K = 128 is 2 steps).  Every output of
-    # those tiles, plus samples elsewhere.
+    # both ragged) are split along K (K = 128 is 2 steps).  Every output.
     M, N, K = 500, 33000, 128
     p = workloads.prefill(M=M, K=K, N=N)
     print("case: w4a16 split tail M=%d N=%d K=%d" % (M, N, K), flush=True)
-    tm, tn = np.meshgrid(np.arange(256, M), np.arange(127 * 256, N), indexing="ij")
-    g = np.random.default_rng(7)
-    mi = np.concatenate([tm.ravel(), g.integers(0, M, 1000)])
-    ni = np.concatenate([tn.ravel(), g.integers(0, N, 1000)])
-    got, ref = _sampled(nv, orc, p.x, p.w_parts, 0, 0, idx=(mi, ni))
+    got, ref = _rows(nv, orc, p.x, p.w_parts, np.arange(M))
     check_gemm(got, ref, True, "w4a16 split tail")

@@ -288,6 +288,10 @@ def _check_out(out: torch.Tensor, M: int, N: int, device) -> torch.Tensor:
     return out
 
 
+def _ld_out(out, M, N):
+    return out.stride(0) if M > 1 else max(N, out.stride(0))
+
+
 def _output(out, M, N, out_dtype, device):
     return _out_tensor(M, N, out_dtype, device) if out is None else _check_out(out, M, N, device)
 

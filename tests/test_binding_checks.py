@@ -74,3 +74,9 @@ def test_check_weight(nv):
         nv._check_weight(wc, ws, torch.ones(0), 64, CPU)
     with pytest.raises(ValueError):
         nv._check_fp8_weight(torch.zeros((8, 60), dtype=torch.uint8), g, 64, CPU)
+
+
+def test_ld_out(nv):
+    assert nv._ld_out(torch.empty((3, 8))[:, :5], 3, 5) == 8
+    assert nv._ld_out(torch.empty((1, 8))[:, :5], 1, 5) == 8
+    assert nv._ld_out(torch.empty((1, 5)), 1, 5) == 5

@@ -214,6 +214,28 @@ nvfp4_status_t nvfp4_gemm_run(int64_t M, int64_t K, const uint8_t *w_codes,
                               size_t workspace_bytes, void *stream);
 
 /* ------------------------------------------------------------------------
+ * nvfp4_gemm_noalloc -- nvfp4_gemm for callers that cannot allocate device
+ * memory or pass a workspace (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation).  Same arguments and result as
+ * nvfp4_gemm without the workspace: its scratch (absmax partials, gs_x, the
+ * quantized activations, split-K partial sums) lives in a fixed array of
+ * NVFP4_NOALLOC_SCRATCH_BYTES that the library holds on every device it runs
+ * on until the process ends.  Shapes whose nvfp4_gemm_workspace_size exceeds
+ * that size give NVFP4_ERR_WORKSPACE (the 4096 x 17408 x 5120 prefill needs
+ * about 109 MB, most of it the split-K partial sums of its last tiles).  Every call on one device shares the array: calls that
+ * overlap on a device (different streams, concurrent graphs) race and must
+ * be ordered by the caller.  Nothing of the array needs to start at zero.
+ * The first call on a device looks up the array's device address (no
+ * allocation).
+ * ---------------------------------------------------------------------- */
+#define NVFP4_NOALLOC_SCRATCH_BYTES (128u << 20)
+
+nvfp4_status_t nvfp4_gemm_noalloc(const void *x, nvfp4_dtype_t x_dtype, int64_t M, int64_t K,
+                                  int64_t ld_x, const uint8_t *w_codes, const uint8_t *w_scales,
+                                  const float *w_gs, int64_t N, void *y, nvfp4_dtype_t y_dtype,
+                                  int64_t ld_y, void *stream);
+
+/* ------------------------------------------------------------------------
  * Static (calibrated) activation scale.  The checkpoints of the paper are
  * produced by a calibration tool that fixes one FP32 global scale per
  * module (paper section 3 "Checkpoints", section 6 "Per-module calibration

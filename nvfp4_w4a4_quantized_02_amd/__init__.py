@@ -44,7 +44,11 @@ EXPORTS = (
     "nvfp4_gemm_static", "nvfp4_gemm_w4a16_workspace_size", "nvfp4_gemm_w4a16",
     "nvfp4_fp8_quantize_workspace_size", "nvfp4_fp8_quantize", "nvfp4_fp8_quantize_static", "nvfp4_fp8_dequantize",
     "nvfp4_gemm_w8a16_workspace_size", "nvfp4_gemm_w8a8_workspace_size", "nvfp4_gemm_w8a16", "nvfp4_gemm_w8a8",
+    "nvfp4_gemm_noalloc",
 )
+
+# Size of the library's fixed scratch array behind nvfp4_gemm_noalloc.
+NOALLOC_SCRATCH_BYTES = 128 << 20
 
 
 class Nvfp4Error(RuntimeError):
@@ -104,6 +108,8 @@ def _load() -> ctypes.CDLL:
     L.nvfp4_gemm_w8a16.restype = I
     L.nvfp4_gemm_w8a8.argtypes = [P, I, I64, I64, I64, P, P, P, I64, P, I, I64, P, SZ, P]
     L.nvfp4_gemm_w8a8.restype = I
+    L.nvfp4_gemm_noalloc.argtypes = [P, I, I64, I64, I64, P, P, P, I64, P, I, I64, P]
+    L.nvfp4_gemm_noalloc.restype = I
     _check_single_hip_runtime()
     return L
 
@@ -332,6 +338,21 @@ def nvfp4_gemm(x: torch.Tensor, w_codes: torch.Tensor, w_scales: torch.Tensor, w
     return out
 
 
+def nvfp4_gemm_noalloc(x: torch.Tensor, w_codes: torch.Tensor, w_scales: torch.Tensor, w_gs: torch.Tensor,
+                       out: torch.Tensor) -> torch.Tensor:
+    """nvfp4_gemm into a caller-given output with no workspace and no
+    allocation: the library's fixed scratch array (NOALLOC_SCRATCH_BYTES per
+    device) holds the intermediate data.  Calls that overlap on one device
+    race on that array."""
+    M, K, ld = _rows_view(x)
+    N = _check_weight(w_codes, w_scales, w_gs, K, x.device)
+    _check_out(out, M, N, x.device)
+    _check(lib.nvfp4_gemm_noalloc(x.data_ptr(), _dtype_code(x.dtype), M, K, ld, w_codes.data_ptr(),
+                                  w_scales.data_ptr(), w_gs.data_ptr(), N, out.data_ptr(), _dtype_code(out.dtype),
+                                  _ld_out(out, M, N), _stream_ptr(x.device)), "nvfp4_gemm_noalloc")
+    return out
+
+
 class PreparedActivations:
     """Result of nvfp4_gemm_prepare: X quantized into its own workspace,
     reusable by several nvfp4_gemm_run calls (same M and K)."""
@@ -466,5 +487,5 @@ def nvfp4_gemm_w8a8(x: torch.Tensor, w_q: torch.Tensor, w_scale: torch.Tensor, x
 
 __all__ = ["nvfp4_quantize", "nvfp4_quantize_static", "nvfp4_dequantize", "nvfp4_fuse_rescale", "nvfp4_gemm",
            "nvfp4_gemm_w4a16", "nvfp4_fp8_quantize", "nvfp4_fp8_dequantize", "nvfp4_gemm_w8a16", "nvfp4_gemm_w8a8",
-           "nvfp4_gemm_prepare", "nvfp4_gemm_run", "PreparedActivations", "Nvfp4Error",
+           "nvfp4_gemm_prepare", "nvfp4_gemm_run", "nvfp4_gemm_noalloc", "PreparedActivations", "Nvfp4Error",
            "status_string", "lib", "EXPORTS", "LIB_PATH", "workspace"]

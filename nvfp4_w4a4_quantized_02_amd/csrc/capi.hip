@@ -5,6 +5,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+
 #include "launch.h"
 
 using namespace nvfp4;
@@ -237,10 +239,11 @@ nvfp4_status_t nvfp4_gemm_run(int64_t M, int64_t K, const uint8_t* w_codes, cons
   return launched();
 }
 
-// The checks nvfp4_gemm makes besides those of the activations.
-static nvfp4_status_t run_args_ok(int64_t M, int64_t K, const uint8_t* w_codes, const uint8_t* w_scales,
-                                  const float* w_gs, int64_t N, const void* y, nvfp4_dtype_t y_dtype,
-                                  int64_t ld_y, const void* workspace, size_t workspace_bytes) {
+// The checks nvfp4_gemm makes besides those of the activations and the
+// workspace.
+static nvfp4_status_t linear_args_ok(int64_t M, int64_t K, const uint8_t* w_codes, const uint8_t* w_scales,
+                                     const float* w_gs, int64_t N, const void* y, nvfp4_dtype_t y_dtype,
+                                     int64_t ld_y) {
   if (!dtype_ok(y_dtype)) return NVFP4_ERR_DTYPE;
   if (N < 0 || N >= kMaxDim) return NVFP4_ERR_SHAPE;
   if (K % 64 != 0 || !tile_rows_ok(K)) return NVFP4_ERR_SHAPE;
@@ -252,6 +255,14 @@ static nvfp4_status_t run_args_ok(int64_t M, int64_t K, const uint8_t* w_codes, 
     if (!w_codes || !w_scales) return NVFP4_ERR_NULL;
     if (!aligned(w_codes, 16) || !aligned(w_scales, 4)) return NVFP4_ERR_ALIGN;
   }
+  return NVFP4_OK;
+}
+
+static nvfp4_status_t run_args_ok(int64_t M, int64_t K, const uint8_t* w_codes, const uint8_t* w_scales,
+                                  const float* w_gs, int64_t N, const void* y, nvfp4_dtype_t y_dtype,
+                                  int64_t ld_y, const void* workspace, size_t workspace_bytes) {
+  nvfp4_status_t st = linear_args_ok(M, K, w_codes, w_scales, w_gs, N, y, y_dtype, ld_y);
+  if (st != NVFP4_OK || M == 0 || N == 0) return st;
   if (!workspace || !aligned(workspace, 256) || workspace_bytes < nvfp4_gemm_workspace_size(M, N, K))
     return NVFP4_ERR_WORKSPACE;
   return NVFP4_OK;
@@ -284,6 +295,45 @@ nvfp4_status_t nvfp4_gemm_static(const void* x, nvfp4_dtype_t x_dtype, int64_t M
   st = nvfp4_gemm_prepare_static(x, x_dtype, M, K, ld_x, gs_x, workspace, workspace_bytes, stream);
   if (st != NVFP4_OK) return st;
   return nvfp4_gemm_run(M, K, w_codes, w_scales, w_gs, N, y, y_dtype, ld_y, workspace, workspace_bytes, stream);
+}
+
+// ---------------------------------------------------------------- no-alloc
+// nvfp4_gemm_noalloc: nvfp4_gemm with its workspace in a fixed array of the
+// library instead of a caller buffer, for callers that cannot allocate.
+// Each device holds its own copy of `scratch`; host code reaches it only
+// through the device address hipGetSymbolAddress returns on that device (the
+// array's name is a host-side stand-in there), taken on the first call on a
+// device and kept per device.
+static __device__ __align__(256) uint8_t scratch[NVFP4_NOALLOC_SCRATCH_BYTES];
+
+static void* scratch_address() {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<void*> cached[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  void* p = cached[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  void* q = nullptr;
+  if (hipGetSymbolAddress(&q, HIP_SYMBOL(scratch)) != hipSuccess || !q) return nullptr;
+  cached[dev].store(q, std::memory_order_release);  // every thread finds the same address
+  return q;
+}
+
+nvfp4_status_t nvfp4_gemm_noalloc(const void* x, nvfp4_dtype_t x_dtype, int64_t M, int64_t K, int64_t ld_x,
+                                  const uint8_t* w_codes, const uint8_t* w_scales, const float* w_gs, int64_t N,
+                                  void* y, nvfp4_dtype_t y_dtype, int64_t ld_y, void* stream) {
+  // the shape checks of nvfp4_gemm come first, so the workspace size below
+  // is computed for a valid shape
+  nvfp4_status_t st = check_input(x, x_dtype, M, K, ld_x);
+  if (st != NVFP4_OK) return st;
+  st = linear_args_ok(M, K, w_codes, w_scales, w_gs, N, y, y_dtype, ld_y);
+  if (st != NVFP4_OK || M == 0 || N == 0) return st;
+  const size_t need = nvfp4_gemm_workspace_size(M, N, K);
+  if (need > (size_t)NVFP4_NOALLOC_SCRATCH_BYTES) return NVFP4_ERR_WORKSPACE;
+  void* ws = scratch_address();
+  if (!ws) return NVFP4_ERR_DEVICE;
+  return nvfp4_gemm(x, x_dtype, M, K, ld_x, w_codes, w_scales, w_gs, N, y, y_dtype, ld_y, ws,
+                    (size_t)NVFP4_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 size_t nvfp4_fp8_quantize_workspace_size(int64_t rows, int64_t K) { return nvfp4_quantize_workspace_size(rows, K); }

@@ -113,6 +113,24 @@ def test_gemm_rejects(nv):
     assert g(nv, N=0) == OK
 
 
+def test_gemm_noalloc_rejects(nv):
+    L = nv.lib
+
+    def na(x=A, dt=BF16, M=32, K=64, ld=64, wc=A, wsc=A, wg=A, N=64, y=A, ydt=BF16, ldy=64):
+        return L.nvfp4_gemm_noalloc(x, dt, M, K, ld, wc, wsc, wg, N, y, ydt, ldy, None)
+
+    assert na(dt=2) == E_DTYPE
+    assert na(K=48, ld=48) == E_SHAPE
+    assert na(y=None) == E_NULL
+    assert na(y=A + 8) == E_ALIGN
+    # more scratch than the fixed array holds: refused before the device is touched
+    assert L.nvfp4_gemm_workspace_size(16384, 17408, 5120) > nv.NOALLOC_SCRATCH_BYTES
+    assert na(M=16384, K=5120, ld=5120, N=17408, ldy=17408) == E_WS
+    assert L.nvfp4_gemm_workspace_size(4096, 17408, 5120) <= nv.NOALLOC_SCRATCH_BYTES
+    assert na(M=0) == OK
+    assert na(N=0) == OK
+
+
 def test_dequantize_rejects(nv):
     L = nv.lib
     assert L.nvfp4_dequantize(A, A, A, 4, 32, A, 9, 32, None) == E_DTYPE

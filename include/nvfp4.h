@@ -46,6 +46,10 @@
  *    keeps no state between calls apart from a per-device cache of two device
  *    attributes (compute units, LDS per compute unit), safe to fill from
  *    several host threads at once.
+ *  - The *_workspace_size functions return 0 for shapes outside the range
+ *    their entry point accepts (negative sizes, a dimension of 2^31 or
+ *    more, K too long, more than 2^30 256 x 256 output tiles); the entry
+ *    point rejects those shapes with NVFP4_ERR_SHAPE.
  *  - Inputs must be finite (no NaN or infinity); this is not checked.
  *  - Calls that share a workspace, or whose outputs overlap their inputs,
  *    must be ordered by the caller (same stream, or events).
@@ -75,7 +79,14 @@ typedef enum nvfp4_status {
     NVFP4_ERR_DEVICE = 7     /* the HIP runtime reported a launch error        */
 } nvfp4_status_t;
 
+/* The dtype arguments are int-sized; any int may arrive from a caller and is
+ * checked (NVFP4_ERR_DTYPE).  C++ sees the int representation explicitly, so
+ * that no value is outside the enumeration's range there either. */
+#ifdef __cplusplus
+typedef enum nvfp4_dtype : int {
+#else
 typedef enum nvfp4_dtype {
+#endif
     NVFP4_F32 = 0,           /* IEEE binary32                                  */
     NVFP4_BF16 = 1           /* bfloat16 (upper half of a binary32)            */
 } nvfp4_dtype_t;

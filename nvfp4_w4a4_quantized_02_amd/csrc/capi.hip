@@ -151,6 +151,16 @@ nvfp4_status_t nvfp4_fuse_rescale(int n, uint8_t* const* scales, const int64_t* 
 // offsets, so a row may not reach 2^24 bytes.
 static bool tile_rows_ok(int64_t K) { return (uint64_t)round_up(K, kGemmBK) * 2u < kMaxTileRowBytes; }
 
+// The tile GEMM (M > 16, or the FP8 weights' long-K path) needs its tile
+// count in range.  Arguments already below 2^31.
+static bool tiles_ok(int64_t M, int64_t N) { return gemm_tiles(M, N) <= kMaxGemmTiles; }
+
+// Shapes every linear's size function accepts; anything else sizes to 0,
+// which the entry point then rejects with its own status.
+static bool dims_ok(int64_t M, int64_t N, int64_t K) {
+  return M >= 0 && N >= 0 && K >= 0 && M < kMaxDim && N < kMaxDim && K < kMaxDim && tiles_ok(M, N);
+}
+
 // Workspace: absmax partials | gs_x | fp16 activations [Mp, Kp] | fp32 K-part
 // sums of the split tiles (see plan_gemm).
 static size_t x16_bytes(int64_t M, int64_t K) {
@@ -165,12 +175,13 @@ static size_t partial_bytes(int64_t M, int64_t N, int64_t K) {
 }
 
 size_t nvfp4_gemm_workspace_size(int64_t M, int64_t N, int64_t K) {
+  if (!dims_ok(M, N, K) || !tile_rows_ok(K)) return 0;
   return kWsX16 + x16_bytes(M, K) + partial_bytes(M, N, K);
 }
 
 // W4A16 needs only the fp32 K-part sums of the split tiles.
 size_t nvfp4_gemm_w4a16_workspace_size(int64_t M, int64_t N, int64_t K) {
-  if (M < 0 || N < 0 || K < 0 || M >= kMaxDim || N >= kMaxDim || K >= kMaxDim) return 0;
+  if (!dims_ok(M, N, K)) return 0;
   return partial_bytes(M, N, round_up(K, kGemmBK));
 }
 
@@ -213,7 +224,7 @@ nvfp4_status_t nvfp4_gemm_run(int64_t M, int64_t K, const uint8_t* w_codes, cons
                               const float* w_gs, int64_t N, void* y, nvfp4_dtype_t y_dtype, int64_t ld_y,
                               void* workspace, size_t workspace_bytes, void* stream) {
   if (!dtype_ok(y_dtype)) return NVFP4_ERR_DTYPE;
-  if (M < 0 || K < 0 || N < 0 || M >= kMaxDim || K >= kMaxDim || N >= kMaxDim) return NVFP4_ERR_SHAPE;
+  if (!dims_ok(M, N, K)) return NVFP4_ERR_SHAPE;
   if (K % 64 != 0 || !tile_rows_ok(K)) return NVFP4_ERR_SHAPE;
   if (M == 0 || N == 0) return NVFP4_OK;
   if (!y || !w_gs) return NVFP4_ERR_NULL;
@@ -245,7 +256,7 @@ static nvfp4_status_t linear_args_ok(int64_t M, int64_t K, const uint8_t* w_code
                                      const float* w_gs, int64_t N, const void* y, nvfp4_dtype_t y_dtype,
                                      int64_t ld_y) {
   if (!dtype_ok(y_dtype)) return NVFP4_ERR_DTYPE;
-  if (N < 0 || N >= kMaxDim) return NVFP4_ERR_SHAPE;
+  if (N < 0 || N >= kMaxDim || !tiles_ok(M, N)) return NVFP4_ERR_SHAPE;
   if (K % 64 != 0 || !tile_rows_ok(K)) return NVFP4_ERR_SHAPE;
   if (M == 0 || N == 0) return NVFP4_OK;
   if (!y || !w_gs) return NVFP4_ERR_NULL;
@@ -397,7 +408,7 @@ size_t nvfp4_gemm_w8a16_workspace_size(int64_t M, int64_t N, int64_t K) {
 }
 
 size_t nvfp4_gemm_w8a8_workspace_size(int64_t M, int64_t N, int64_t K) {
-  if (M < 0 || N < 0 || K < 0 || M >= kMaxDim || N >= kMaxDim || K >= kMaxDim) return 0;
+  if (!dims_ok(M, N, K)) return 0;
   return kWsX16 + x8_bytes(M, K) + partial_bytes(M, N, round_up(K, kGemmBK));
 }
 
@@ -405,7 +416,7 @@ size_t nvfp4_gemm_w8a8_workspace_size(int64_t M, int64_t N, int64_t K) {
 static nvfp4_status_t fp8w_args_ok(int64_t M, int64_t K, const uint8_t* w_q, const float* w_scale, int64_t N,
                                    const void* y, nvfp4_dtype_t y_dtype, int64_t ld_y) {
   if (!dtype_ok(y_dtype)) return NVFP4_ERR_DTYPE;
-  if (N < 0 || N >= kMaxDim || K % 64 != 0) return NVFP4_ERR_SHAPE;
+  if (N < 0 || N >= kMaxDim || K % 64 != 0 || !tiles_ok(M, N)) return NVFP4_ERR_SHAPE;
   if (M == 0 || N == 0) return NVFP4_OK;
   if (!y || !w_scale) return NVFP4_ERR_NULL;
   if (ld_y < N) return NVFP4_ERR_SHAPE;
@@ -484,7 +495,7 @@ nvfp4_status_t nvfp4_gemm_w4a16(const void* x, nvfp4_dtype_t x_dtype, int64_t M,
   if (st != NVFP4_OK) return st;
   if (x_dtype != NVFP4_BF16) return NVFP4_ERR_DTYPE;
   if (!dtype_ok(y_dtype)) return NVFP4_ERR_DTYPE;
-  if (N < 0 || N >= kMaxDim || K % 64 != 0) return NVFP4_ERR_SHAPE;
+  if (N < 0 || N >= kMaxDim || K % 64 != 0 || !tiles_ok(M, N)) return NVFP4_ERR_SHAPE;
   if ((uint64_t)ld_x * 2u >= kMaxTileRowBytes) return NVFP4_ERR_SHAPE;
   if (M == 0 || N == 0) return NVFP4_OK;
   if (!y || !w_gs) return NVFP4_ERR_NULL;

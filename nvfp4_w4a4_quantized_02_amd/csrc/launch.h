@@ -70,12 +70,20 @@ struct GemmPlan {
   size_t partial_bytes;
 };
 
+// The tile GEMM takes at most this many 256 x 256 tiles (the ABI rejects
+// larger problems), so tile counts and grid sizes fit an int.
+constexpr int64_t kMaxGemmTiles = (int64_t)1 << 30;
+inline int64_t gemm_tiles(int64_t M, int64_t N) {
+  return ((M + kGemmBM - 1) / kGemmBM) * ((N + kGemmBN - 1) / kGemmBN);
+}
+
+// 0 <= M, N, K < 2^31 and gemm_tiles(M, N) <= kMaxGemmTiles.
 inline GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K) {
   GemmPlan p;
   p.tiles_m = (int)((M + kGemmBM - 1) / kGemmBM);
   p.tiles_n = (int)((N + kGemmBN - 1) / kGemmBN);
   p.nk = (int)((K + kGemmBK - 1) / kGemmBK);
-  const int tiles = p.tiles_m * p.tiles_n;
+  const int tiles = (int)gemm_tiles(M, N);
   const int cus = gemm_cus();
   const int rem = tiles % cus;
   int split = rem ? cus / rem : 1;

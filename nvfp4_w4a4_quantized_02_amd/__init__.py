@@ -314,18 +314,25 @@ def _check_weight(w_codes, w_scales, w_gs, K, device):
 
 def nvfp4_gemm(x: torch.Tensor, w_codes: torch.Tensor, w_scales: torch.Tensor, w_gs: torch.Tensor,
                out_dtype: torch.dtype = torch.bfloat16, out: torch.Tensor | None = None,
-               x_gs: torch.Tensor | None = None) -> torch.Tensor:
+               x_gs: torch.Tensor | None = None, ws: torch.Tensor | None = None) -> torch.Tensor:
     """Y = X W^T with X [M, K] quantized on the fly and W given as NVFP4
     (codes [N, K/2], scales [N, K/16], w_gs [1]).  x_gs: a calibrated
     activation tensor scale (float32 [1] on the device) instead of the
-    absmax one."""
+    absmax one.  ws: a uint8 workspace of the caller's (256-byte aligned, at
+    least nvfp4_gemm_workspace_size bytes), e.g. for graph capture; by
+    default the per-stream one."""
     M, K, ld = _rows_view(x)
     N = _check_weight(w_codes, w_scales, w_gs, K, x.device)
     out = _output(out, M, N, out_dtype, x.device)
     if x_gs is not None:
         _check_scalar(x_gs, x.device, "x_gs")
     nws = lib.nvfp4_gemm_workspace_size(M, N, K)
-    ws = workspace(nws, x.device)
+    if ws is None:
+        ws = workspace(nws, x.device)
+    else:
+        _check_u8(ws, (ws.numel(),), x.device, "ws")
+        if ws.data_ptr() % 256 or ws.numel() < nws:
+            raise ValueError("the workspace must be 256-byte aligned and hold %d bytes" % nws)
     if x_gs is None:
         _check(lib.nvfp4_gemm(x.data_ptr(), _dtype_code(x.dtype), M, K, ld, w_codes.data_ptr(),
                               w_scales.data_ptr(), w_gs.data_ptr(), N, out.data_ptr(), _dtype_code(out.dtype),

@@ -279,6 +279,18 @@ static nvfp4_status_t run_args_ok(int64_t M, int64_t K, const uint8_t* w_codes, 
   return NVFP4_OK;
 }
 
+// One bf16 activation row (decode): the quantize and the GEMV in one launch,
+// which also leaves the quantized row and gs_x in the workspace as
+// nvfp4_gemm_prepare would.  False when the shape has no such form
+// (nothing launched); arguments already validated.
+static bool fused_m1(const void* x, nvfp4_dtype_t x_dtype, int64_t M, int64_t K, const float* gs_x,
+                     const uint8_t* w_codes, const uint8_t* w_scales, const float* w_gs, int64_t N, void* y,
+                     nvfp4_dtype_t y_dtype, void* workspace, void* stream) {
+  if (M != 1 || x_dtype != NVFP4_BF16 || K == 0) return false;
+  return launch_gemv_fused_m1(x, true, K, gs_x, w_codes, w_scales, N, w_gs, y, y_dtype == NVFP4_BF16,
+                              (char*)workspace + kWsX16, (float*)((char*)workspace + kWsGs), (hipStream_t)stream);
+}
+
 nvfp4_status_t nvfp4_gemm(const void* x, nvfp4_dtype_t x_dtype, int64_t M, int64_t K, int64_t ld_x,
                           const uint8_t* w_codes, const uint8_t* w_scales, const float* w_gs, int64_t N, void* y,
                           nvfp4_dtype_t y_dtype, int64_t ld_y, void* workspace, size_t workspace_bytes,
@@ -288,6 +300,8 @@ nvfp4_status_t nvfp4_gemm(const void* x, nvfp4_dtype_t x_dtype, int64_t M, int64
   if (st != NVFP4_OK) return st;
   st = run_args_ok(M, K, w_codes, w_scales, w_gs, N, y, y_dtype, ld_y, workspace, workspace_bytes);
   if (st != NVFP4_OK || M == 0 || N == 0) return st;
+  if (fused_m1(x, x_dtype, M, K, nullptr, w_codes, w_scales, w_gs, N, y, y_dtype, workspace, stream))
+    return launched();
   st = nvfp4_gemm_prepare(x, x_dtype, M, K, ld_x, workspace, workspace_bytes, stream);
   if (st != NVFP4_OK) return st;
   return nvfp4_gemm_run(M, K, w_codes, w_scales, w_gs, N, y, y_dtype, ld_y, workspace, workspace_bytes, stream);
@@ -303,6 +317,8 @@ nvfp4_status_t nvfp4_gemm_static(const void* x, nvfp4_dtype_t x_dtype, int64_t M
   if (!gs_x) return NVFP4_ERR_NULL;
   st = run_args_ok(M, K, w_codes, w_scales, w_gs, N, y, y_dtype, ld_y, workspace, workspace_bytes);
   if (st != NVFP4_OK || M == 0 || N == 0) return st;
+  if (fused_m1(x, x_dtype, M, K, gs_x, w_codes, w_scales, w_gs, N, y, y_dtype, workspace, stream))
+    return launched();
   st = nvfp4_gemm_prepare_static(x, x_dtype, M, K, ld_x, gs_x, workspace, workspace_bytes, stream);
   if (st != NVFP4_OK) return st;
   return nvfp4_gemm_run(M, K, w_codes, w_scales, w_gs, N, y, y_dtype, ld_y, workspace, workspace_bytes, stream);

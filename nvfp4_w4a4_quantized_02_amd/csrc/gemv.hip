@@ -200,7 +200,8 @@ __global__ __launch_bounds__(64) void gemv_stream_kernel(const uint8_t* __restri
   uint4 xv[8];
 #pragma unroll
   for (int t = 0; t < 8; ++t) xv[t] = make_uint4(0, 0, 0, 0);
-  floatx4 acc = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+  // two accumulators: alternate MFMAs do not wait for each other's result
+  floatx4 acc[2] = {floatx4{0.0f, 0.0f, 0.0f, 0.0f}, floatx4{0.0f, 0.0f, 0.0f, 0.0f}};
   for (int c0 = 0; c0 < nck; c0 += D) {
 #pragma unroll
     for (int d = 0; d < D; ++d) {
@@ -216,6 +217,10 @@ __global__ __launch_bounds__(64) void gemv_stream_kernel(const uint8_t* __restri
 #pragma unroll
         for (int t = 0; t < 8; ++t) xv[t] = *reinterpret_cast<const uint4*>(xb + 16u * ((uint32_t)t ^ xg));
       }
+      // the slot's reads are complete: refill it before computing, so the
+      // transfer is not held back by this chunk's arithmetic
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      issue(d);
       const uint32_t s0 = O::scale_bits(sd), s1 = O::scale_bits(sd >> 8), s2 = O::scale_bits(sd >> 16),
                      s3 = O::scale_bits(sd >> 24);
 #pragma unroll
@@ -223,15 +228,219 @@ __global__ __launch_bounds__(64) void gemv_stream_kernel(const uint8_t* __restri
         const uint32_t sp = t < 2 ? s0 : (t < 4 ? s1 : (t < 6 ? s2 : s3));
         uint32_t e[4];
         O::expand(dword_of(t < 4 ? w0 : w1, t & 3), sp, e);
-        acc = O::mfma16(O::vec(make_uint4(e[0], e[1], e[2], e[3])), O::vec(xv[t]), acc);
+        acc[t & 1] = O::mfma16(O::vec(make_uint4(e[0], e[1], e[2], e[3])), O::vec(xv[t]), acc[t & 1]);
       }
-      issue(d);
     }
   }
   wait_vmcnt<0>();
+  const floatx4 a = acc[0] + acc[1];
   if (mvalid)
-    store4<kYBf16>(y + (size_t)l16 * ld_y_bytes, tile * 16 + 4 * g, N, acc[0] * scale, acc[1] * scale,
-                   acc[2] * scale, acc[3] * scale);
+    store4<kYBf16>(y + (size_t)l16 * ld_y_bytes, tile * 16 + 4 * g, N, a[0] * scale, a[1] * scale, a[2] * scale,
+                   a[3] * scale);
+}
+
+// --------------------------------------------------- M == 1, one launch
+// The whole decode step for one bf16 activation row: its quantization
+// (tensor scale, block scales, codes, exactly as the quantize kernels do it)
+// and the GEMV, in one kernel.  A separate quantize launch costs the step
+// more than its work; here every workgroup quantizes the row (at most 8192
+// elements) into its own LDS while its first weight transfers are already in
+// flight.
+//
+// A workgroup is kFuWaves waves, one 16-row weight tile each, sharing the
+// fp16 expansion of the quantized row in LDS.  Order of work in a wave:
+//   1. its tile's scale bytes (16 rows x K/16, contiguous) and the first D
+//      chunks of codes into LDS by direct transfers (codes: 16 rows x 128 B
+//      per chunk, two transfers filling 8 lines each);
+//   2. the activation row into registers (lane l: blocks l, l + 64, ...);
+//   3. the absmax of the row over the lane's blocks and the wave (exact,
+//      integer order), the tensor scale RN(amax / 2688) (or the given one),
+//      and the encode of this wave's share of the blocks, written to LDS as
+//      fp16 values E2M1 * E4M3;
+//   4. one barrier, then the streaming loop of the M <= 4 kernel above with
+//      the activation operand read from the shared LDS copy;
+//   5. workgroup 0 copies the quantized row and the tensor scale to the
+//      workspace, where nvfp4_gemm_prepare would leave them.  Stored last: a
+//      store can be acknowledged before older loads return, so stores issued
+//      while loads are in flight would let a compiler-counted wait for those
+//      loads pass early.
+// The accumulation order is the same as the two-launch path's.
+constexpr int kFuWaves = 3;
+constexpr int kFuDepth = 4;
+
+template <int NCK, bool kGiven, bool kYBf16>
+__global__ __launch_bounds__(64 * kFuWaves) void gemv_fused_m1_kernel(const uint8_t* __restrict__ x,
+                                                                      const float* __restrict__ gs_in,
+                                                                      const uint8_t* __restrict__ wc,
+                                                                      const uint8_t* __restrict__ ws, int N,
+                                                                      int tiles, const float* __restrict__ gsw_p,
+                                                                      uint8_t* __restrict__ y,
+                                                                      uint4* __restrict__ x16_out,
+                                                                      float* __restrict__ gsx_out) {
+  using O = Op<false>;
+  constexpr int K = NCK * 256, NB = K / 16, BPL = (NB + 63) / 64, D = kFuDepth;
+  constexpr uint32_t kh = K / 2, ks = K / 16;
+  constexpr uint32_t kScBytes = (16u * ks + 1023u) / 1024u * 1024u;
+  extern __shared__ uint4 smem[];  // X16 [K / 8] | ring [wave][D][2048 B] | scales [wave][kScBytes]
+  const int lane = threadIdx.x & 63, l16 = lane & 15, g = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));  // uniform: scalar bases
+  const int tile_raw = blockIdx.x * kFuWaves + wave;
+  const int tile = tile_raw < tiles ? tile_raw : tiles - 1;  // a surplus wave redoes the last tile, unstored
+  uint4* xs = smem;
+  uint8_t* ring = reinterpret_cast<uint8_t*>(smem + K / 8) + (size_t)wave * D * kGvChunkCodes;
+  uint8_t* sc_lds = reinterpret_cast<uint8_t*>(smem + K / 8) + (size_t)kFuWaves * D * kGvChunkCodes +
+                    (size_t)wave * kScBytes;
+
+  // 1. scale bytes (pieces past the end re-read the last piece; their LDS
+  //    bytes are never read) and the first D chunks of codes
+  const int n0 = tile * 16;
+  {
+    const uint32_t rows_here = (uint32_t)((N - n0) < 16 ? (N - n0) : 16);
+    const uint32_t bytes = rows_here * ks;  // a multiple of 16 (K % 256 == 0)
+    const uint32_t sc0 = lds_addr(sc_lds);
+#pragma unroll
+    for (uint32_t q = 0; q < kScBytes / 1024u; ++q) {
+      uint32_t off = q * 1024u + 16u * (uint32_t)lane;
+      off = off + 16u <= bytes ? off : bytes - 16u;
+      lds_dma16(ws + (size_t)n0 * ks, off, sc0 + q * 1024u);
+    }
+  }
+  const uint8_t* wtile = wc + (size_t)n0 * kh;
+  uint32_t coff[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int r = 8 * h + (lane >> 3);
+    const int n = n0 + r < N ? n0 + r : N - 1;
+    coff[h] = (uint32_t)(n - n0) * kh + 16u * (uint32_t)((lane & 7) ^ (r & 7));
+  }
+  const uint32_t ring0 = lds_addr(ring);
+  auto issue = [&](int c, int d) {  // chunk c (clamped) into ring slot d
+    c = c < NCK ? c : NCK - 1;
+    const uint32_t slot = ring0 + (uint32_t)d * kGvChunkCodes;
+    lds_dma16(wtile, coff[0] + (uint32_t)c * 128u, slot);
+    lds_dma16(wtile, coff[1] + (uint32_t)c * 128u, slot + 1024u);
+  };
+#pragma unroll
+  for (int d = 0; d < D; ++d) issue(d, d);
+
+  // 2. the activation row
+  uint32_t xw[BPL][BlockWords<true>::n];
+#pragma unroll
+  for (int j = 0; j < BPL; ++j) {
+    const int b = lane + 64 * j < NB ? lane + 64 * j : NB - 1;
+    load_words<true>(x + (size_t)b * 32u, xw[j]);
+  }
+
+  // 3. tensor scale and this wave's share of the blocks
+  float gs;
+  if constexpr (kGiven) {
+    gs = *gs_in;
+  } else {
+    uint32_t m = 0;
+#pragma unroll
+    for (int j = 0; j < BPL; ++j) {
+      const uint32_t a = words_absmax_bits<true>(xw[j]);
+      m = m > a ? m : a;
+    }
+    gs = tensor_scale(__uint_as_float(wave_max_u32(m)));
+  }
+  const FastScale fsc = fast_scale(gs);
+#pragma unroll
+  for (int j = 0; j < BPL; ++j) {
+    const int b = lane + 64 * j;
+    if (j % kFuWaves != wave || b >= NB) continue;  // wave-uniform except the last partial set
+    float xv[16];
+    words_to_floats<true>(xw[j], xv);
+    uint32_t sb, lo, hi;
+    if (!encode_block_fast(xv, words_absmax_bits<true>(xw[j]), fsc, sb, lo, hi))
+      sb = encode_block_exact(xv, gs, lo, hi);
+    const half2_t q2 = scale_f16x2(sb);
+    uint32_t e0[4], e1[4];
+    expand8(lo, q2, e0);
+    expand8(hi, q2, e1);
+    xs[2 * b] = make_uint4(e0[0], e0[1], e0[2], e0[3]);
+    xs[2 * b + 1] = make_uint4(e1[0], e1[1], e1[2], e1[3]);
+  }
+  // X16 complete and visible to every wave (the transfers in flight are not
+  // waited for: a bare barrier, no fence)
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+
+  // 4. the streaming loop
+  const uint32_t sw = (uint32_t)(l16 & 7);
+  const uint32_t cpos0 = (uint32_t)l16 * 128u + 16u * ((2u * g) ^ sw);
+  const uint32_t cpos1 = (uint32_t)l16 * 128u + 16u * ((2u * g + 1u) ^ sw);
+  const bool col0 = l16 == 0;
+  // two accumulators: alternate MFMAs do not wait for each other's result
+  floatx4 acc[2] = {floatx4{0.0f, 0.0f, 0.0f, 0.0f}, floatx4{0.0f, 0.0f, 0.0f, 0.0f}};
+#pragma unroll
+  for (int c = 0; c < NCK; ++c) {
+    const int d = c % D;
+    wait_vmcnt<(D - 1) * 2>();
+    const uint8_t* slot = ring + d * kGvChunkCodes;
+    const uint4 w0 = *reinterpret_cast<const uint4*>(slot + cpos0);
+    const uint4 w1 = *reinterpret_cast<const uint4*>(slot + cpos1);
+    uint4 xv[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) xv[t] = make_uint4(0, 0, 0, 0);
+    if (col0) {
+#pragma unroll
+      for (int t = 0; t < 8; ++t) xv[t] = xs[32 * c + 8 * g + t];
+    }
+    const uint32_t sd = *reinterpret_cast<const uint32_t*>(sc_lds + (uint32_t)l16 * ks + 4u * g + 16u * c);
+    // the slot's reads are complete: refill it before computing, so the
+    // transfer is not held back by this chunk's arithmetic
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    issue(c + D, d);
+    const uint32_t s0 = O::scale_bits(sd), s1 = O::scale_bits(sd >> 8), s2 = O::scale_bits(sd >> 16),
+                   s3 = O::scale_bits(sd >> 24);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const uint32_t sp = t < 2 ? s0 : (t < 4 ? s1 : (t < 6 ? s2 : s3));
+      uint32_t e[4];
+      O::expand(dword_of(t < 4 ? w0 : w1, t & 3), sp, e);
+      acc[t & 1] = O::mfma16(O::vec(make_uint4(e[0], e[1], e[2], e[3])), O::vec(xv[t]), acc[t & 1]);
+    }
+  }
+  wait_vmcnt<0>();
+  if (col0 && tile_raw < tiles) {
+    const float scale = gs * (*gsw_p);
+    const floatx4 a = acc[0] + acc[1];
+    store4<kYBf16>(y, n0 + 4 * g, N, a[0] * scale, a[1] * scale, a[2] * scale, a[3] * scale);
+  }
+  // 5. the quantized row for the workspace
+  if (blockIdx.x == 0) {
+    for (int i = (int)threadIdx.x; i < K / 8; i += 64 * kFuWaves) x16_out[i] = xs[i];
+    if (threadIdx.x == 0) *gsx_out = gs;
+  }
+}
+
+// One-launch decode step for M == 1 when the row is bf16 and its length has
+// an instantiation; false otherwise (nothing launched: the caller quantizes
+// and runs the GEMV in two launches).
+bool launch_gemv_fused_m1(const void* x, bool x_bf16, int64_t K, const float* gs_in, const uint8_t* wc,
+                          const uint8_t* ws, int64_t N, const float* gsw, void* y, bool y_bf16, void* x16_out,
+                          float* gsx_out, hipStream_t s) {
+  if (!x_bf16 || (K != 4096 && K != 5120)) return false;
+  const int tiles = (int)((N + 15) / 16);
+  const int grid = (tiles + kFuWaves - 1) / kFuWaves;
+  const size_t lds = (size_t)K * 2u + (size_t)kFuWaves * kFuDepth * kGvChunkCodes +
+                     (size_t)kFuWaves * (((size_t)K + 1023u) / 1024u * 1024u);  // 16 rows of K/16 scale bytes
+  auto go = [&](auto nc, auto gv, auto yb) {
+    gemv_fused_m1_kernel<decltype(nc)::value, decltype(gv)::value, decltype(yb)::value>
+        <<<grid, 64 * kFuWaves, lds, s>>>((const uint8_t*)x, gs_in, wc, ws, (int)N, tiles, gsw, (uint8_t*)y,
+                                          (uint4*)x16_out, gsx_out);
+  };
+  auto by_y = [&](auto nc, auto gv) {
+    if (y_bf16) go(nc, gv, std::true_type());
+    else go(nc, gv, std::false_type());
+  };
+  auto by_gs = [&](auto nc) {
+    if (gs_in) by_y(nc, std::true_type());
+    else by_y(nc, std::false_type());
+  };
+  if (K == 5120) by_gs(std::integral_constant<int, 20>());
+  else by_gs(std::integral_constant<int, 16>());
+  return true;
 }
 
 // ------------------------------------------------------------ 4 < M <= 16

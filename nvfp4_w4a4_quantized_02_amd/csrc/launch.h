@@ -153,6 +153,15 @@ void launch_gemv_fp8w(bool a8, const void* x, size_t ld_x_bytes, int64_t M, int6
                       const float* sx, const float* sw, void* y, bool y_bf16, int64_t ld_y, hipStream_t s);
 constexpr int64_t kFp8GemvMaxK = 5120;
 
+// The W4A4 decode step for one activation row in one launch: quantize x
+// ([1, K], bf16 or fp32; with gs_in given, that tensor scale) and contract
+// with W.  Also writes the fp16 operand and the tensor scale to x16_out /
+// gsx_out, as nvfp4_gemm_prepare would.  Returns false (nothing launched) for
+// a K it has no form for.
+bool launch_gemv_fused_m1(const void* x, bool x_bf16, int64_t K, const float* gs_in, const uint8_t* wc,
+                          const uint8_t* ws, int64_t N, const float* gsw, void* y, bool y_bf16, void* x16_out,
+                          float* gsx_out, hipStream_t s);
+
 void launch_gemv(bool a16, const void* x, size_t ld_x_bytes, int64_t M, int64_t K, const uint8_t* wc,
                  const uint8_t* ws, int64_t N, const float* gsx, const float* gsw, void* y, bool y_bf16,
                  int64_t ld_y, hipStream_t s);

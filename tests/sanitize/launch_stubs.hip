@@ -53,5 +53,9 @@ void launch_gemv(bool, const void*, size_t, int64_t, int64_t, const uint8_t*, co
                  const float*, const float*, void*, bool, int64_t, hipStream_t) {
   launched("gemv");
 }
+bool launch_gemv_fused_m1(const void*, bool, int64_t, const float*, const uint8_t*, const uint8_t*, int64_t,
+                          const float*, void*, bool, void*, float*, hipStream_t) {
+  launched("gemv_fused_m1");
+}
 
 }  // namespace nvfp4

@@ -124,10 +124,12 @@ def time_steps(torch, steps, warmup, body, nphase):
     return wall, [tm.phase_ms(j) for j in range(nphase)]
 
 
-def graph_step_ms(torch, fn, nsteps, out, reps=20):
-    """GPU ms per step of fn(i), i = 0..nsteps-1, captured as one graph and
-    replayed `reps` times between events.  The replay's `out` must equal the
-    eager result bit for bit (the kernels are deterministic)."""
+def graph_step_ms(torch, fn, nsteps, out, reps=20, batches=5, warm_ms=30.0):
+    """GPU ms per step of fn(i), i = 0..nsteps-1, captured as one graph:
+    replayed for at least warm_ms first (the clock settles under sustained
+    load), then `batches` batches of `reps` replays between events; the
+    median batch is returned.  The replay's `out` must equal the eager result
+    bit for bit (the kernels are deterministic)."""
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
@@ -145,13 +147,21 @@ def graph_step_ms(torch, fn, nsteps, out, reps=20):
     torch.cuda.synchronize()
     if not torch.equal(out, eager):
         raise RuntimeError("graph replay differs from the eager result")
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(reps):
-        g.replay()
-    e1.record()
-    torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / (reps * nsteps)
+    t0 = time.perf_counter()
+    while (time.perf_counter() - t0) * 1e3 < warm_ms:
+        for _ in range(reps):
+            g.replay()
+        torch.cuda.synchronize()
+    times = []
+    for _ in range(batches):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1) / (reps * nsteps))
+    return sorted(times)[len(times) // 2]
 
 
 def mean(v):
@@ -373,7 +383,8 @@ def secondary(torch, np, nv, workloads, to_gpu, dev, args):
             kname, kkey = "nvfp4_gemm_run: gemv kernel", "gemv_m%d" % M
         res.append({"metric": "decode GEMV GB/s at M=%d" % M, "value": round(gbs, 1), "unit": "GB/s",
                     "ms_per_step": round(t["w4a4"], 5),
-                    "timing": "graph replay of %d steps (one per weight copy), events around the replays" % R,
+                    "timing": "graph of %d steps (one per weight copy) replayed 30 ms to warm up, then the median of 5 "
+                              "batches of replays between events" % R,
                     "phases_ms": {"activation_quantize": round(t["prep"], 5), "gemv": round(t["gemv"], 5),
                                   "quantize_then_gemv": round(t["two_launch"], 5)},
                     "w4a16": {"ms_per_step": round(t["w4a16"], 5),

@@ -286,8 +286,11 @@ constexpr int kSmallThreads = 1024;
 static inline uint32_t small_block_limit(bool) { return 8u * kSmallThreads; }
 
 // kGiven: the tensor scale is *gs_in and no absmax is taken.  gs_out may be
-// nullptr.
-template <bool kBf16, bool kF16, bool kGiven>
+// nullptr.  With several workgroups, each takes the absmax of the whole
+// tensor itself: thread t reads blocks t, t + 1024, ... (kRounds of them,
+// indices past the end clamped onto the last block), all loads issued
+// together, so the absmax costs one round trip.
+template <bool kBf16, bool kF16, bool kGiven, int kRounds>
 __global__ __launch_bounds__(1024) void quantize_small_kernel(const uint8_t* __restrict__ x, size_t ld_bytes,
                                                                uint32_t kblocks, uint32_t out_kblocks,
                                                                uint32_t total_blocks, FastDiv fd,
@@ -325,17 +328,20 @@ __global__ __launch_bounds__(1024) void quantize_small_kernel(const uint8_t* __r
       // they are already in registers (padding blocks count as zeros).
       if (b < total_blocks && kb_own < kblocks) m = words_absmax_bits<kBf16>(own);
     } else {
-      for (uint32_t b0 = threadIdx.x; b0 < total_blocks; b0 += 4u * kSmallThreads) {
-        uint32_t wv[4][BlockWords<kBf16>::n];
-        uint32_t kb[4];
+      // fp32 blocks take twice the registers: at most four in flight
+      constexpr int kBatch = (kBf16 || kRounds < 4) ? kRounds : 4;
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          uint32_t bu = b0 + (uint32_t)u * kSmallThreads;
+      for (int r0 = 0; r0 < kRounds; r0 += kBatch) {
+        uint32_t wv[kBatch][BlockWords<kBf16>::n];
+        uint32_t kb[kBatch];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+          uint32_t bu = threadIdx.x + (uint32_t)(r0 + u) * kSmallThreads;
           bu = bu < total_blocks ? bu : total_blocks - 1u;
           load_words<kBf16>(block_ptr(bu, kb[u]), wv[u]);
         }
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
+        for (int u = 0; u < kBatch; ++u) {
           const uint32_t a = kb[u] < kblocks ? words_absmax_bits<kBf16>(wv[u]) : 0u;  // padding blocks are zeros
           m = m > a ? m : a;
         }
@@ -478,9 +484,15 @@ static void launch_encode(bool small, const uint8_t* xb, size_t ld_bytes, uint32
                           FastDiv fd, const uint32_t* partials, int npartials, const float* gs_in, uint8_t* codes,
                           uint8_t* scales, uint4* xo, float* gs, hipStream_t s) {
   if (small) {
-    const int grid = (int)((total + kSmallThreads - 1) / kSmallThreads);
-    quantize_small_kernel<kBf16, kF16, kGiven><<<grid, kSmallThreads, 0, s>>>(xb, ld_bytes, kb, okb, total, fd,
-                                                                              gs_in, codes, scales, xo, gs);
+    const int grid = (int)((total + kSmallThreads - 1) / kSmallThreads);  // at most 8 (small_block_limit)
+    auto go = [&](auto rounds) {
+      quantize_small_kernel<kBf16, kF16, kGiven, decltype(rounds)::value>
+          <<<grid, kSmallThreads, 0, s>>>(xb, ld_bytes, kb, okb, total, fd, gs_in, codes, scales, xo, gs);
+    };
+    if (kGiven || grid == 1) go(std::integral_constant<int, 1>());
+    else if (grid == 2) go(std::integral_constant<int, 2>());
+    else if (grid <= 4) go(std::integral_constant<int, 4>());
+    else go(std::integral_constant<int, 8>());
     return;
   }
   // Four workgroups per compute unit, all resident at once:

@@ -51,6 +51,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--headline-only", action="store_true",
                     help="skip the secondary workloads (profiling runs)")
+    ap.add_argument("--only", choices=["prefill", "decode", "qkv", "quantize", "fp8", "weight"],
+                    help="run one workload group alone and print its lines (profiling runs); prefill: the "
+                         "headline, its settled rerun and W4A16, without the secondary lines and box peaks")
     ap.add_argument("--no-numerics", action="store_true",
                     help="skip the input statistics and fake-quantization errors")
     ap.add_argument("--no-box-peaks", action="store_true",
@@ -209,12 +212,17 @@ def main():
     flops = 2.0 * M * N * K
     sha = source_sha()
 
+    if args.only and args.only != "prefill":
+        print(json.dumps({"only": args.only, "also": secondary(torch, np, nv, workloads, to_gpu, dev, args)}),
+              flush=True)
+        return
+
     # The secondary lines and the machine's reference rates run first, so the
     # headline's warm-up starts on a GPU that is already under load (from
     # idle, the clock takes tens of milliseconds of sustained load to settle).
     also = []
     bp = None
-    if not args.headline_only:
+    if not args.headline_only and args.only != "prefill":
         also += secondary(torch, np, nv, workloads, to_gpu, dev, args)
         if not args.no_box_peaks:
             bp = box_peaks(torch, dev, M, N, K)
@@ -319,210 +327,218 @@ def secondary(torch, np, nv, workloads, to_gpu, dev, args):
     res = []
     steps, warmup = args.steps, args.warmup
 
+    def want(group):
+        return args.only is None or args.only == group
+
     # ------------------------------------------------ decode GEMV, M = 1/4/16
-    log("generating decode workload (fused gate/up W[34816x5120])")
-    d = workloads.decode(M=1)
-    q = [nv.nvfp4_quantize(torch.from_numpy(w).to(dev)) for w in d.w_parts]
-    shared = nv.nvfp4_fuse_rescale([s for _, s, _ in q], [g for _, _, g in q])
-    wc0 = torch.cat([c for c, _, _ in q])
-    ws0 = torch.cat([s for _, s, _ in q])
-    del q
-    R = 4                                  # 4 x 100 MB > the 256 MB last-level cache
-    copies = [(wc0.clone(), ws0.clone()) for _ in range(R)]
-    del wc0, ws0
-    N, K = d.N, d.K
-    wbytes = copies[0][0].numel() + copies[0][1].numel()
-    for M in (1, 4, 16):
-        dm = workloads.decode(M=M, N_each=1)          # only X is used from it
-        x = to_gpu(dm.x)
-        y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-        wsb = torch.empty(nv.lib.nvfp4_gemm_workspace_size(M, N, K), dtype=torch.uint8, device=dev)
-        xgs = nv.nvfp4_quantize(x)[2]
+    if want("decode"):
+        log("generating decode workload (fused gate/up W[34816x5120])")
+        d = workloads.decode(M=1)
+        q = [nv.nvfp4_quantize(torch.from_numpy(w).to(dev)) for w in d.w_parts]
+        shared = nv.nvfp4_fuse_rescale([s for _, s, _ in q], [g for _, _, g in q])
+        wc0 = torch.cat([c for c, _, _ in q])
+        ws0 = torch.cat([s for _, s, _ in q])
+        del q
+        R = 4                                  # 4 x 100 MB > the 256 MB last-level cache
+        copies = [(wc0.clone(), ws0.clone()) for _ in range(R)]
+        del wc0, ws0
+        N, K = d.N, d.K
+        wbytes = copies[0][0].numel() + copies[0][1].numel()
+        for M in (1, 4, 16):
+            dm = workloads.decode(M=M, N_each=1)          # only X is used from it
+            x = to_gpu(dm.x)
+            y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+            wsb = torch.empty(nv.lib.nvfp4_gemm_workspace_size(M, N, K), dtype=torch.uint8, device=dev)
+            xgs = nv.nvfp4_quantize(x)[2]
 
-        # Each form is captured as one graph of R steps (one per weight copy)
-        # and replayed, so the time is the GPU's and not the launch overhead
-        # of the Python binding; the replay's output is checked against the
-        # eager call's.
-        # the whole call (M = 1: quantize and GEMV in one launch)
-        def w4a4(i, x=x, y=y, wsb=wsb):
-            c, s = copies[i]
-            nv.nvfp4_gemm(x, c, s, shared, out=y, ws=wsb)
+            # Each form is captured as one graph of R steps (one per weight copy)
+            # and replayed, so the time is the GPU's and not the launch overhead
+            # of the Python binding; the replay's output is checked against the
+            # eager call's.
+            # the whole call (M = 1: quantize and GEMV in one launch)
+            def w4a4(i, x=x, y=y, wsb=wsb):
+                c, s = copies[i]
+                nv.nvfp4_gemm(x, c, s, shared, out=y, ws=wsb)
 
-        def w4a4_static(i, x=x, y=y, wsb=wsb, xgs=xgs):
-            c, s = copies[i]
-            nv.nvfp4_gemm(x, c, s, shared, out=y, x_gs=xgs, ws=wsb)
+            def w4a4_static(i, x=x, y=y, wsb=wsb, xgs=xgs):
+                c, s = copies[i]
+                nv.nvfp4_gemm(x, c, s, shared, out=y, x_gs=xgs, ws=wsb)
 
-        # the same product as two launches (quantize, then the GEMV)
-        def two_launch(i, x=x, y=y, wsb=wsb):
-            c, s = copies[i]
-            nv.nvfp4_gemm_run(nv.nvfp4_gemm_prepare(x, ws=wsb), c, s, shared, out=y)
+            # the same product as two launches (quantize, then the GEMV)
+            def two_launch(i, x=x, y=y, wsb=wsb):
+                c, s = copies[i]
+                nv.nvfp4_gemm_run(nv.nvfp4_gemm_prepare(x, ws=wsb), c, s, shared, out=y)
 
-        prep = nv.nvfp4_gemm_prepare(x, ws=wsb)
+            prep = nv.nvfp4_gemm_prepare(x, ws=wsb)
 
-        def gemv_only(i, y=y, prep=prep):
-            c, s = copies[i]
-            nv.nvfp4_gemm_run(prep, c, s, shared, out=y)
+            def gemv_only(i, y=y, prep=prep):
+                c, s = copies[i]
+                nv.nvfp4_gemm_run(prep, c, s, shared, out=y)
 
-        def prep_only(i, x=x, wsb=wsb):
-            nv.nvfp4_gemm_prepare(x, ws=wsb)
+            def prep_only(i, x=x, wsb=wsb):
+                nv.nvfp4_gemm_prepare(x, ws=wsb)
 
-        def w4a16(i, x=x, y=y):
-            c, s = copies[i]
-            nv.nvfp4_gemm_w4a16(x, c, s, shared, out=y)
+            def w4a16(i, x=x, y=y):
+                c, s = copies[i]
+                nv.nvfp4_gemm_w4a16(x, c, s, shared, out=y)
 
-        t = {}
-        for name, fn in (("w4a4", w4a4), ("w4a4_static", w4a4_static), ("two_launch", two_launch),
-                         ("gemv", gemv_only), ("prep", prep_only), ("w4a16", w4a16)):
-            t[name] = graph_step_ms(torch, fn, R, y, reps=max(steps, 20))
-        nbytes = wbytes + M * K * 2 + M * N * 2
-        gbs = nbytes / (t["w4a4"] * 1e-3) / 1e9
-        kgbs = nbytes / (t["gemv"] * 1e-3) / 1e9
-        if M == 1:   # one launch does the whole step: that kernel is the one on the roofline
-            kname, kkey, kgbs = "nvfp4_gemm: gemv_fused_m1_kernel (quantize + GEMV)", "gemv_fused_m1", gbs
-        else:
-            kname, kkey = "nvfp4_gemm_run: gemv kernel", "gemv_m%d" % M
-        res.append({"metric": "decode GEMV GB/s at M=%d" % M, "value": round(gbs, 1), "unit": "GB/s",
-                    "ms_per_step": round(t["w4a4"], 5),
-                    "timing": "graph of %d steps (one per weight copy) replayed 30 ms to warm up, then the median of 5 "
-                              "batches of replays between events" % R,
-                    "phases_ms": {"activation_quantize": round(t["prep"], 5), "gemv": round(t["gemv"], 5),
-                                  "quantize_then_gemv": round(t["two_launch"], 5)},
-                    "w4a16": {"ms_per_step": round(t["w4a16"], 5),
-                              "GBs": round(nbytes / (t["w4a16"] * 1e-3) / 1e9, 1),
-                              "frac": round(nbytes / (t["w4a16"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-                              "traffic": traffic_for("gemv_m%d_w4a16" % M, source_sha())},
-                    "calibrated_scale": {"ms_per_step": round(t["w4a4_static"], 5),
-                                         "GBs": round(nbytes / (t["w4a4_static"] * 1e-3) / 1e9, 1)},
-                    "config": {"workload": "decode: X[%dx5120] bf16 x fused gate/up W[34816x5120] NVFP4 "
-                                           "(4 rotated copies) -> Y bf16" % M},
-                    "roofline": {"bound": "hbm", "kernel": kname, "achieved": round(kgbs, 1),
-                                 "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(kgbs / PEAK_HBM_GBS, 4),
-                                 "traffic": traffic_for(kkey, source_sha()),
-                                 "algorithmic": "W codes+scales %d B + X + Y = %d B per launch" % (wbytes,
-                                                                                                  nbytes)}})
-        log("decode M=%d: step %.2f us (%.1f GB/s), two launches %.2f us, gemv %.2f us (%.1f GB/s), "
-            "prep %.2f us, W4A16 %.2f us" % (M, t["w4a4"] * 1e3, gbs, t["two_launch"] * 1e3, t["gemv"] * 1e3,
-                                              kgbs, t["prep"] * 1e3, t["w4a16"] * 1e3))
-    del copies
+            t = {}
+            for name, fn in (("w4a4", w4a4), ("w4a4_static", w4a4_static), ("two_launch", two_launch),
+                             ("gemv", gemv_only), ("prep", prep_only), ("w4a16", w4a16)):
+                t[name] = graph_step_ms(torch, fn, R, y, reps=max(steps, 20))
+            nbytes = wbytes + M * K * 2 + M * N * 2
+            gbs = nbytes / (t["w4a4"] * 1e-3) / 1e9
+            kgbs = nbytes / (t["gemv"] * 1e-3) / 1e9
+            if M == 1:   # one launch does the whole step: that kernel is the one on the roofline
+                kname, kkey, kgbs = "nvfp4_gemm: gemv_fused_m1_kernel (quantize + GEMV)", "gemv_fused_m1", gbs
+            else:
+                kname, kkey = "nvfp4_gemm_run: gemv kernel", "gemv_m%d" % M
+            res.append({"metric": "decode GEMV GB/s at M=%d" % M, "value": round(gbs, 1), "unit": "GB/s",
+                        "ms_per_step": round(t["w4a4"], 5),
+                        "timing": "graph of %d steps (one per weight copy) replayed 30 ms to warm up, then the median of 5 "
+                                  "batches of replays between events" % R,
+                        "phases_ms": {"activation_quantize": round(t["prep"], 5), "gemv": round(t["gemv"], 5),
+                                      "quantize_then_gemv": round(t["two_launch"], 5)},
+                        "w4a16": {"ms_per_step": round(t["w4a16"], 5),
+                                  "GBs": round(nbytes / (t["w4a16"] * 1e-3) / 1e9, 1),
+                                  "frac": round(nbytes / (t["w4a16"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                                  "traffic": traffic_for("gemv_m%d_w4a16" % M, source_sha())},
+                        "calibrated_scale": {"ms_per_step": round(t["w4a4_static"], 5),
+                                             "GBs": round(nbytes / (t["w4a4_static"] * 1e-3) / 1e9, 1)},
+                        "config": {"workload": "decode: X[%dx5120] bf16 x fused gate/up W[34816x5120] NVFP4 "
+                                               "(4 rotated copies) -> Y bf16" % M},
+                        "roofline": {"bound": "hbm", "kernel": kname, "achieved": round(kgbs, 1),
+                                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(kgbs / PEAK_HBM_GBS, 4),
+                                     "traffic": traffic_for(kkey, source_sha()),
+                                     "algorithmic": "W codes+scales %d B + X + Y = %d B per launch" % (wbytes,
+                                                                                                      nbytes)}})
+            log("decode M=%d: step %.2f us (%.1f GB/s), two launches %.2f us, gemv %.2f us (%.1f GB/s), "
+                "prep %.2f us, W4A16 %.2f us" % (M, t["w4a4"] * 1e3, gbs, t["two_launch"] * 1e3, t["gemv"] * 1e3,
+                                                  kgbs, t["prep"] * 1e3, t["w4a16"] * 1e3))
+        del copies
 
     # ------------------------------------------------ fused q/k/v repair + GEMM
-    log("fused q/k/v workload")
-    f = workloads.fused_qkv()
-    parts = [torch.from_numpy(w).to(dev) for w in f.w_parts]
-    qs = [nv.nvfp4_quantize(w) for w in parts]
-    scales = [s for _, s, _ in qs]
-    gss = [g for _, _, g in qs]
-    sc_backup = [s.clone() for s in scales]
+    if want("qkv"):
+        log("fused q/k/v workload")
+        f = workloads.fused_qkv()
+        parts = [torch.from_numpy(w).to(dev) for w in f.w_parts]
+        qs = [nv.nvfp4_quantize(w) for w in parts]
+        scales = [s for _, s, _ in qs]
+        gss = [g for _, _, g in qs]
+        sc_backup = [s.clone() for s in scales]
 
-    def rstep(i, mark):
-        for s, b in zip(scales, sc_backup):
-            s.copy_(b)
-        mark(0)
-        nv.nvfp4_fuse_rescale(scales, gss)
-        mark(1)
+        def rstep(i, mark):
+            for s, b in zip(scales, sc_backup):
+                s.copy_(b)
+            mark(0)
+            nv.nvfp4_fuse_rescale(scales, gss)
+            mark(1)
 
-    _, (resc_ms,) = time_steps(torch, steps, warmup, rstep, 1)
-    shared = nv.nvfp4_fuse_rescale([s.copy_(b) for s, b in zip(scales, sc_backup)], gss)
-    fwc = torch.cat([c for c, _, _ in qs])
-    fws = torch.cat(scales)
-    x = to_gpu(f.x)
-    M, N, K = f.M, f.N, f.K
-    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-    wsb = torch.empty(nv.lib.nvfp4_gemm_workspace_size(M, N, K), dtype=torch.uint8, device=dev)
+        _, (resc_ms,) = time_steps(torch, steps, warmup, rstep, 1)
+        shared = nv.nvfp4_fuse_rescale([s.copy_(b) for s, b in zip(scales, sc_backup)], gss)
+        fwc = torch.cat([c for c, _, _ in qs])
+        fws = torch.cat(scales)
+        x = to_gpu(f.x)
+        M, N, K = f.M, f.N, f.K
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        wsb = torch.empty(nv.lib.nvfp4_gemm_workspace_size(M, N, K), dtype=torch.uint8, device=dev)
 
-    def fstep(i, mark):
-        mark(0)
-        prep = nv.nvfp4_gemm_prepare(x, ws=wsb)
-        mark(1)
-        nv.nvfp4_gemm_run(prep, fwc, fws, shared, out=y)
-        mark(2)
+        def fstep(i, mark):
+            mark(0)
+            prep = nv.nvfp4_gemm_prepare(x, ws=wsb)
+            mark(1)
+            nv.nvfp4_gemm_run(prep, fwc, fws, shared, out=y)
+            mark(2)
 
-    _, (prep_ms, run_ms) = time_steps(torch, steps, warmup, fstep, 2)
-    flops = 2.0 * M * N * K
-    step_ms = mean(prep_ms) + mean(run_ms)
-    rbytes = 2 * sum(s.numel() for s in scales)
-    res.append({"metric": "fused q/k/v W4A4 GEMM TFLOP/s at M=2048", "value": round(flops / step_ms / 1e9, 2),
-                "unit": "TFLOP/s", "ms_per_step": round(step_ms, 4),
-                "phases_ms": {"activation_quantize": round(mean(prep_ms), 4), "gemm": round(mean(run_ms), 4),
-                              "fuse_rescale_offline": round(mean(resc_ms), 5)},
-                "config": {"workload": "fused q/k/v: X[2048x5120] bf16 x [q 6144; k 1024; v 1024]x5120 NVFP4, "
-                                       "block scales repaired onto the shared tensor scale"},
-                "roofline": {"bound": "mfma", "kernel": "gemm_kernel",
-                             "achieved": round(flops / mean(run_ms) / 1e9, 2), "peak": PEAK_FP16_TFLOPS,
-                             "unit": "TFLOP/s", "frac": round(flops / mean(run_ms) / 1e9 / PEAK_FP16_TFLOPS, 4)},
-                "fuse_rescale_GBs": round(rbytes / mean(resc_ms) / 1e6, 1)})
-    del parts, qs, x, y, wsb, fwc, fws
+        _, (prep_ms, run_ms) = time_steps(torch, steps, warmup, fstep, 2)
+        flops = 2.0 * M * N * K
+        step_ms = mean(prep_ms) + mean(run_ms)
+        rbytes = 2 * sum(s.numel() for s in scales)
+        res.append({"metric": "fused q/k/v W4A4 GEMM TFLOP/s at M=2048", "value": round(flops / step_ms / 1e9, 2),
+                    "unit": "TFLOP/s", "ms_per_step": round(step_ms, 4),
+                    "phases_ms": {"activation_quantize": round(mean(prep_ms), 4), "gemm": round(mean(run_ms), 4),
+                                  "fuse_rescale_offline": round(mean(resc_ms), 5)},
+                    "config": {"workload": "fused q/k/v: X[2048x5120] bf16 x [q 6144; k 1024; v 1024]x5120 NVFP4, "
+                                           "block scales repaired onto the shared tensor scale"},
+                    "roofline": {"bound": "mfma", "kernel": "gemm_kernel",
+                                 "achieved": round(flops / mean(run_ms) / 1e9, 2), "peak": PEAK_FP16_TFLOPS,
+                                 "unit": "TFLOP/s", "frac": round(flops / mean(run_ms) / 1e9 / PEAK_FP16_TFLOPS, 4)},
+                    "fuse_rescale_GBs": round(rbytes / mean(resc_ms) / 1e6, 1)})
+        del parts, qs, x, y, wsb, fwc, fws
 
     # ------------------------------------------------ standalone quantize, long prefill
-    log("generating long-prefill activations X[32768x5120] bf16")
-    xl = to_gpu(workloads.long_prefill_activations())
-    rows, K = xl.shape
-    codes = torch.empty((rows, K // 2), dtype=torch.uint8, device=dev)
-    scl = torch.empty((rows, K // 16), dtype=torch.uint8, device=dev)
-    gs = torch.empty(1, dtype=torch.float32, device=dev)
-    qws = nv.workspace(nv.lib.nvfp4_quantize_workspace_size(rows, K), dev)
+    if want("quantize"):
+        log("generating long-prefill activations X[32768x5120] bf16")
+        xl = to_gpu(workloads.long_prefill_activations())
+        rows, K = xl.shape
+        codes = torch.empty((rows, K // 2), dtype=torch.uint8, device=dev)
+        scl = torch.empty((rows, K // 16), dtype=torch.uint8, device=dev)
+        gs = torch.empty(1, dtype=torch.float32, device=dev)
+        qws = nv.workspace(nv.lib.nvfp4_quantize_workspace_size(rows, K), dev)
 
-    def qstep(i, mark):
-        mark(0)
-        st = nv.lib.nvfp4_quantize(xl.data_ptr(), 1, rows, K, K, codes.data_ptr(), scl.data_ptr(), gs.data_ptr(),
-                                   qws.data_ptr(), qws.numel(), torch.cuda.current_stream().cuda_stream)
-        assert st == 0
-        mark(1)
+        def qstep(i, mark):
+            mark(0)
+            st = nv.lib.nvfp4_quantize(xl.data_ptr(), 1, rows, K, K, codes.data_ptr(), scl.data_ptr(), gs.data_ptr(),
+                                       qws.data_ptr(), qws.numel(), torch.cuda.current_stream().cuda_stream)
+            assert st == 0
+            mark(1)
 
-    _, (q_ms,) = time_steps(torch, steps, warmup, qstep, 1)
-    gcal = gs.clone()
+        _, (q_ms,) = time_steps(torch, steps, warmup, qstep, 1)
+        gcal = gs.clone()
 
-    def sqstep(i, mark):
-        mark(0)
-        st = nv.lib.nvfp4_quantize_static(xl.data_ptr(), 1, rows, K, K, gcal.data_ptr(), codes.data_ptr(),
-                                          scl.data_ptr(), torch.cuda.current_stream().cuda_stream)
-        assert st == 0
-        mark(1)
+        def sqstep(i, mark):
+            mark(0)
+            st = nv.lib.nvfp4_quantize_static(xl.data_ptr(), 1, rows, K, K, gcal.data_ptr(), codes.data_ptr(),
+                                              scl.data_ptr(), torch.cuda.current_stream().cuda_stream)
+            assert st == 0
+            mark(1)
 
-    _, (sq_ms,) = time_steps(torch, steps, warmup, sqstep, 1)
-    xbytes = rows * K * 2
-    two_pass = 2 * xbytes + rows * K // 2 + rows * K // 16
-    single = xbytes + rows * K // 2 + rows * K // 16
-    qgbs = two_pass / (mean(q_ms) * 1e-3) / 1e9
-    res.append({"metric": "activation quantize GB/s (two-pass bytes)", "value": round(qgbs, 1), "unit": "GB/s",
-                "ms_per_step": round(mean(q_ms), 4),
-                "single_read_GBs": round(single / (mean(q_ms) * 1e-3) / 1e9, 1),
-                "calibrated_scale": {"ms_per_step": round(mean(sq_ms), 4),
-                                     "GBs": round(single / (mean(sq_ms) * 1e-3) / 1e9, 1),
-                                     "frac": round(single / (mean(sq_ms) * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-                                     "algorithmic": "1 read of X + codes + scales = %d B per call" % single,
-                                     "traffic": traffic_for("quantize_long_static", source_sha())},
-                "config": {"workload": "long-prefill quantize: X[32768x5120] bf16 Student-t(2.5), 16 hot "
-                                       "channels x200 -> packed E2M1 + E4M3 scales + FP32 scale"},
-                "roofline": {"bound": "hbm", "kernel": "nvfp4_quantize: amax_partials_kernel + quantize_kernel",
-                             "achieved": round(qgbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                             "frac": round(qgbs / PEAK_HBM_GBS, 4),
-                             "traffic": traffic_for("quantize_long", source_sha()),
-                             "algorithmic": "2 reads of X + codes + scales = %d B per call" % two_pass}})
-    log("quantize: %.1f GB/s (two-pass count); calibrated scale %.1f GB/s (one read)"
-        % (qgbs, single / (mean(sq_ms) * 1e-3) / 1e9))
-    if not args.no_numerics:
-        from nvfp4_w4a4_quantized_02_amd import stats
-        res[-1]["input_stats"] = {**stats.tensor_stats(xl), "a4": stats.fake_quant_error(xl)}
-    del xl, codes, scl
+        _, (sq_ms,) = time_steps(torch, steps, warmup, sqstep, 1)
+        xbytes = rows * K * 2
+        two_pass = 2 * xbytes + rows * K // 2 + rows * K // 16
+        single = xbytes + rows * K // 2 + rows * K // 16
+        qgbs = two_pass / (mean(q_ms) * 1e-3) / 1e9
+        res.append({"metric": "activation quantize GB/s (two-pass bytes)", "value": round(qgbs, 1), "unit": "GB/s",
+                    "ms_per_step": round(mean(q_ms), 4),
+                    "single_read_GBs": round(single / (mean(q_ms) * 1e-3) / 1e9, 1),
+                    "calibrated_scale": {"ms_per_step": round(mean(sq_ms), 4),
+                                         "GBs": round(single / (mean(sq_ms) * 1e-3) / 1e9, 1),
+                                         "frac": round(single / (mean(sq_ms) * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                                         "algorithmic": "1 read of X + codes + scales = %d B per call" % single,
+                                         "traffic": traffic_for("quantize_long_static", source_sha())},
+                    "config": {"workload": "long-prefill quantize: X[32768x5120] bf16 Student-t(2.5), 16 hot "
+                                           "channels x200 -> packed E2M1 + E4M3 scales + FP32 scale"},
+                    "roofline": {"bound": "hbm", "kernel": "nvfp4_quantize: amax_partials_kernel + quantize_kernel",
+                                 "achieved": round(qgbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                 "frac": round(qgbs / PEAK_HBM_GBS, 4),
+                                 "traffic": traffic_for("quantize_long", source_sha()),
+                                 "algorithmic": "2 reads of X + codes + scales = %d B per call" % two_pass}})
+        log("quantize: %.1f GB/s (two-pass count); calibrated scale %.1f GB/s (one read)"
+            % (qgbs, single / (mean(sq_ms) * 1e-3) / 1e9))
+        if not args.no_numerics:
+            from nvfp4_w4a4_quantized_02_amd import stats
+            res[-1]["input_stats"] = {**stats.tensor_stats(xl), "a4": stats.fake_quant_error(xl)}
+        del xl, codes, scl
 
     # ------------------------------------------------ FP8-weight linears (W8A16, W8A8)
-    res += fp8_lines(torch, nv, workloads, to_gpu, dev, args)
+    if want("fp8"):
+        res += fp8_lines(torch, nv, workloads, to_gpu, dev, args)
 
     # ------------------------------------------------ offline weight quantize (fp32 in)
-    w = torch.from_numpy(workloads.gaussian(3, 1, 17408, 5120, 0.02)).to(dev)
+    if want("weight"):
+        w = torch.from_numpy(workloads.gaussian(3, 1, 17408, 5120, 0.02)).to(dev)
 
-    def wstep(i, mark):
-        mark(0)
-        nv.nvfp4_quantize(w)
-        mark(1)
+        def wstep(i, mark):
+            mark(0)
+            nv.nvfp4_quantize(w)
+            mark(1)
 
-    _, (w_ms,) = time_steps(torch, max(4, steps // 4), 2, wstep, 1)
-    wb = 2 * w.numel() * 4 + w.numel() // 2 + w.numel() // 16
-    res.append({"metric": "weight quantize GB/s (fp32 in, two-pass bytes)",
-                "value": round(wb / (mean(w_ms) * 1e-3) / 1e9, 1), "unit": "GB/s",
-                "ms_per_step": round(mean(w_ms), 4),
-                "config": {"workload": "offline weight quantize W[17408x5120] fp32 N(0,0.02)"}})
+        _, (w_ms,) = time_steps(torch, max(4, steps // 4), 2, wstep, 1)
+        wb = 2 * w.numel() * 4 + w.numel() // 2 + w.numel() // 16
+        res.append({"metric": "weight quantize GB/s (fp32 in, two-pass bytes)",
+                    "value": round(wb / (mean(w_ms) * 1e-3) / 1e9, 1), "unit": "GB/s",
+                    "ms_per_step": round(mean(w_ms), 4),
+                    "config": {"workload": "offline weight quantize W[17408x5120] fp32 N(0,0.02)"}})
     return res
 
 

@@ -462,7 +462,8 @@ def secondary(torch, np, nv, workloads, to_gpu, dev, args):
                                            "block scales repaired onto the shared tensor scale"},
                     "roofline": {"bound": "mfma", "kernel": "gemm_kernel",
                                  "achieved": round(flops / mean(run_ms) / 1e9, 2), "peak": PEAK_FP16_TFLOPS,
-                                 "unit": "TFLOP/s", "frac": round(flops / mean(run_ms) / 1e9 / PEAK_FP16_TFLOPS, 4)},
+                                 "unit": "TFLOP/s", "frac": round(flops / mean(run_ms) / 1e9 / PEAK_FP16_TFLOPS, 4),
+                                 "traffic": traffic_for("gemm_qkv", source_sha())},
                     "fuse_rescale_GBs": round(rbytes / mean(resc_ms) / 1e6, 1)})
         del parts, qs, x, y, wsb, fwc, fws
 

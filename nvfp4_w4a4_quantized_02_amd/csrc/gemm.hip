@@ -108,7 +108,8 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const uint4* __restrict__ 
   using V = typename O::vec8;
   __shared__ GemmSmem sm;
   __shared__ uint32_t scale_lut[128];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: LDS and global bases stay scalar
   const int wave_n = wave >> 1, wave_m = wave & 1;  // W rows 64 wave_n.., X rows 128 wave_m..
   // Whole tiles first; the workgroups past full_tiles each take one K part
   // (steps [kb, ke)) of a remaining tile.
@@ -147,6 +148,13 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const uint4* __restrict__ 
   // (lane%4) ^ ((row >> 3) & 3) = (lane%4) ^ (wave & 3).  Rows past N repeat
   // the last one (never stored).  These offsets are recomputed per transfer
   // (a few integer operations) rather than held in registers.
+  // LDS byte address of a place in sm: one address-space conversion for the
+  // whole kernel, then integer offsets (a conversion per use would also test
+  // the pointer for null every time)
+  const uint32_t sm0 = lds_addr(&sm);
+  auto soff = [&](const void* p) {
+    return sm0 + (uint32_t)(reinterpret_cast<const char*>(p) - reinterpret_cast<const char*>(&sm));
+  };
   const int nrows = N - n0;
   const int last = n - 1;
   const int glast = last >> 1, Glast = last >> 2;
@@ -155,7 +163,7 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const uint4* __restrict__ 
   // the last step or group (into buffers that are no longer read).
   auto issue_x = [&](int i, int b) {
     const uint8_t* xb = xbase + (size_t)(i < last ? i : last) * 128;
-    const uint32_t lx = lds_addr(&sm.x[b][wave * 256]);
+    const uint32_t lx = soff(&sm.x[b][wave * 256]);
 #pragma unroll
     for (int j = 0; j < 4; ++j) lds_dma16(xb, xoff[j], lx + j * 1024);
   };
@@ -164,14 +172,14 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const uint4* __restrict__ 
     const int row = 128 * hh + 16 * wave + (lane >> 2);
     const uint32_t piece = (((uint32_t)lane & 3u) ^ wc_swz((uint32_t)row)) * 16u;
     const uint32_t off = (uint32_t)(row < nrows ? row : nrows - 1) * kh + min(goff + piece, kh - 16u);
-    lds_dma16(wcbase, off, lds_addr(&sm.wc[b][(128 * hh + 16 * wave) * 4]));
+    lds_dma16(wcbase, off, soff(&sm.wc[b][(128 * hh + 16 * wave) * 4]));
   };
   auto issue_ws = [&](int G, int qq, int b) {
     const uint32_t goff = (uint32_t)(kb + 4 * (G < Glast ? G : Glast)) * 4u;
     const int row = 64 * qq + 8 * wave + (l32 >> 2);
     const uint32_t dw = (((uint32_t)lane & 3u) ^ ((uint32_t)wave & 3u)) * 4u;
     const uint32_t off = (uint32_t)(row < nrows ? row : nrows - 1) * ks + min(goff + dw, ks - 4u);
-    if (lane < 32) lds_dma4(wsbase, off, lds_addr(&sm.ws[b][(64 * qq + 8 * wave) * 4]));
+    if (lane < 32) lds_dma4(wsbase, off, soff(&sm.ws[b][(64 * qq + 8 * wave) * 4]));
   };
 
   floatx16 acc[2][4];

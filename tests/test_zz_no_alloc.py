@@ -30,8 +30,9 @@ def _noalloc_abi(nv, x, wc, ws, wg, y):
 
 
 # (M, N, K, seed): a tile GEMM with a split-K tail, then smaller shapes that
-# reuse the same array (a decode GEMV, then a one-tile GEMM).
-CASES = [(300, 520, 1024, 1), (4, 264, 512, 2), (40, 136, 256, 3)]
+# reuse the same array (a decode GEMV, the one-launch decode of one bf16 row,
+# then a one-tile GEMM).
+CASES = [(300, 520, 1024, 1), (4, 264, 512, 2), (1, 304, 4096, 4), (40, 136, 256, 3)]
 
 
 @pytest.mark.parametrize("out", [torch.float32, torch.bfloat16])

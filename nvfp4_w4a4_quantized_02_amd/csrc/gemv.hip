@@ -248,15 +248,21 @@ __global__ __launch_bounds__(64) void gemv_stream_kernel(const uint8_t* __restri
 // flight.
 //
 // A workgroup is kFuWaves waves, one 16-row weight tile each, sharing the
-// fp16 expansion of the quantized row in LDS.  Order of work in a wave:
-//   1. its tile's scale bytes (16 rows x K/16, contiguous) and the first D
-//      chunks of codes into LDS by direct transfers (codes: 16 rows x 128 B
-//      per chunk, two transfers filling 8 lines each);
-//   2. the activation row into registers (lane l: blocks l, l + 64, ...);
-//   3. the absmax of the row over the lane's blocks and the wave (exact,
-//      integer order), the tensor scale RN(amax / 2688) (or the given one),
-//      and the encode of this wave's share of the blocks, written to LDS as
-//      fp16 values E2M1 * E4M3;
+// fp16 expansion of the quantized row in LDS.  The row's 16-element blocks
+// are dealt to the waves in sets of 64 (set j to wave j % kFuWaves; lane l
+// takes block 64 j + l).  Order of work in a wave:
+//   1. direct transfers into LDS, in this order: the bf16 bytes of its own
+//      sets of blocks, into the LDS region of the fp16 copy at the offsets
+//      their expansion will take (a bf16 block and its fp16 expansion are
+//      both 32 B); its tile's scale bytes (16 rows x K/16, contiguous); the
+//      first D chunks of codes (16 rows x 128 B per chunk, two transfers
+//      filling 8 lines each).  Transfers complete in the order issued, so
+//      the wave then waits for its row bytes alone;
+//   2. the absmax of its blocks (exact: integer max of the magnitudes),
+//      combined over the wave and, through LDS and a barrier, over the
+//      workgroup; the tensor scale RN(amax / 2688) (or the given one);
+//   3. the encode of its blocks, each written over its own bf16 bytes as
+//      fp16 values E2M1 * E4M3 (only this lane reads or writes them);
 //   4. one barrier, then the streaming loop of the M <= 4 kernel above with
 //      the activation operand read from the shared LDS copy;
 //   5. workgroup 0 copies the quantized row and the tensor scale to the
@@ -279,9 +285,11 @@ __global__ __launch_bounds__(64 * kFuWaves) void gemv_fused_m1_kernel(const uint
                                                                       float* __restrict__ gsx_out) {
   using O = Op<false>;
   constexpr int K = NCK * 256, NB = K / 16, BPL = (NB + 63) / 64, D = kFuDepth;
+  static_assert(NB % 64 == 0, "whole sets of 64 blocks");
   constexpr uint32_t kh = K / 2, ks = K / 16;
   constexpr uint32_t kScBytes = (16u * ks + 1023u) / 1024u * 1024u;
-  extern __shared__ uint4 smem[];  // X16 [K / 8] | ring [wave][D][2048 B] | scales [wave][kScBytes]
+  // X16 [K / 8] | ring [wave][D][2048 B] | scales [wave][kScBytes] | wave maxima [4]
+  extern __shared__ uint4 smem[];
   const int lane = threadIdx.x & 63, l16 = lane & 15, g = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));  // uniform: scalar bases
   const int tile_raw = blockIdx.x * kFuWaves + wave;
@@ -290,9 +298,22 @@ __global__ __launch_bounds__(64 * kFuWaves) void gemv_fused_m1_kernel(const uint
   uint8_t* ring = reinterpret_cast<uint8_t*>(smem + K / 8) + (size_t)wave * D * kGvChunkCodes;
   uint8_t* sc_lds = reinterpret_cast<uint8_t*>(smem + K / 8) + (size_t)kFuWaves * D * kGvChunkCodes +
                     (size_t)wave * kScBytes;
+  uint32_t* wmax = reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(smem + K / 8) +
+                                               (size_t)kFuWaves * (D * kGvChunkCodes + kScBytes));
 
-  // 1. scale bytes (pieces past the end re-read the last piece; their LDS
-  //    bytes are never read) and the first D chunks of codes
+  // 1. transfers: this wave's sets of the row (set j = bytes 2048 j ..
+  //    2048 j + 2047, two 1 KB transfers), the scale bytes (pieces past the
+  //    end re-read the last piece; their LDS bytes are never read), the first
+  //    D chunks of codes
+  {
+    const uint32_t xs0 = lds_addr(xs);
+#pragma unroll
+    for (int j = 0; j < BPL; ++j) {
+      if (j % kFuWaves != wave) continue;
+      lds_dma16(x, 2048u * j + 16u * (uint32_t)lane, xs0 + 2048u * j);
+      lds_dma16(x, 2048u * j + 1024u + 16u * (uint32_t)lane, xs0 + 2048u * j + 1024u);
+    }
+  }
   const int n0 = tile * 16;
   {
     const uint32_t rows_here = (uint32_t)((N - n0) < 16 ? (N - n0) : 16);
@@ -322,16 +343,19 @@ __global__ __launch_bounds__(64 * kFuWaves) void gemv_fused_m1_kernel(const uint
   };
 #pragma unroll
   for (int d = 0; d < D; ++d) issue(d, d);
+  // this wave's row bytes have landed (the scale and code transfers after
+  // them may still be in flight)
+  wait_vmcnt<(int)(kScBytes / 1024u) + 2 * D>();
 
-  // 2. the activation row
+  // 2. this wave's blocks, their absmax, the tensor scale
   uint32_t xw[BPL][BlockWords<true>::n];
 #pragma unroll
   for (int j = 0; j < BPL; ++j) {
-    const int b = lane + 64 * j < NB ? lane + 64 * j : NB - 1;
-    load_words<true>(x + (size_t)b * 32u, xw[j]);
+    if (j % kFuWaves != wave) continue;
+    const uint4 a = xs[2 * (lane + 64 * j)], b = xs[2 * (lane + 64 * j) + 1];
+    xw[j][0] = a.x; xw[j][1] = a.y; xw[j][2] = a.z; xw[j][3] = a.w;
+    xw[j][4] = b.x; xw[j][5] = b.y; xw[j][6] = b.z; xw[j][7] = b.w;
   }
-
-  // 3. tensor scale and this wave's share of the blocks
   float gs;
   if constexpr (kGiven) {
     gs = *gs_in;
@@ -339,16 +363,24 @@ __global__ __launch_bounds__(64 * kFuWaves) void gemv_fused_m1_kernel(const uint
     uint32_t m = 0;
 #pragma unroll
     for (int j = 0; j < BPL; ++j) {
+      if (j % kFuWaves != wave) continue;
       const uint32_t a = words_absmax_bits<true>(xw[j]);
       m = m > a ? m : a;
     }
-    gs = tensor_scale(__uint_as_float(wave_max_u32(m)));
+    m = wave_max_u32(m);
+    if (lane == 0) wmax[wave] = m;
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+#pragma unroll
+    for (int w = 0; w < kFuWaves; ++w) m = m > wmax[w] ? m : wmax[w];
+    gs = tensor_scale(__uint_as_float(m));
   }
+
+  // 3. encode this wave's blocks over their bf16 bytes
   const FastScale fsc = fast_scale(gs);
 #pragma unroll
   for (int j = 0; j < BPL; ++j) {
+    if (j % kFuWaves != wave) continue;
     const int b = lane + 64 * j;
-    if (j % kFuWaves != wave || b >= NB) continue;  // wave-uniform except the last partial set
     float xv[16];
     words_to_floats<true>(xw[j], xv);
     uint32_t sb, lo, hi;
@@ -424,7 +456,8 @@ bool launch_gemv_fused_m1(const void* x, bool x_bf16, int64_t K, const float* gs
   const int tiles = (int)((N + 15) / 16);
   const int grid = (tiles + kFuWaves - 1) / kFuWaves;
   const size_t lds = (size_t)K * 2u + (size_t)kFuWaves * kFuDepth * kGvChunkCodes +
-                     (size_t)kFuWaves * (((size_t)K + 1023u) / 1024u * 1024u);  // 16 rows of K/16 scale bytes
+                     (size_t)kFuWaves * (((size_t)K + 1023u) / 1024u * 1024u) +  // 16 rows of K/16 scale bytes
+                     16u;                                                          // the waves' maxima
   auto go = [&](auto nc, auto gv, auto yb) {
     gemv_fused_m1_kernel<decltype(nc)::value, decltype(gv)::value, decltype(yb)::value>
         <<<grid, 64 * kFuWaves, lds, s>>>((const uint8_t*)x, gs_in, wc, ws, (int)N, tiles, gsw, (uint8_t*)y,

@@ -594,6 +594,27 @@ __global__ __launch_bounds__(512) void gemv_shared_kernel(const uint8_t* __restr
                    acc[2] * scale, acc[3] * scale);
 }
 
+// Cross-lane exchanges of gfx950, per 32-bit word of a 16-byte value:
+// swap_lanes32(u, v) swaps the upper 32 lanes of u with the lower 32 lanes
+// of v; swap_rows16(u, v) swaps the odd 16-lane rows of u with the even rows
+// of v.
+__device__ __forceinline__ void swap_lanes32(uint4& u, uint4& v) {
+  auto x = __builtin_amdgcn_permlane32_swap(u.x, v.x, false, false);
+  auto y = __builtin_amdgcn_permlane32_swap(u.y, v.y, false, false);
+  auto z = __builtin_amdgcn_permlane32_swap(u.z, v.z, false, false);
+  auto w = __builtin_amdgcn_permlane32_swap(u.w, v.w, false, false);
+  u = make_uint4(x[0], y[0], z[0], w[0]);
+  v = make_uint4(x[1], y[1], z[1], w[1]);
+}
+__device__ __forceinline__ void swap_rows16(uint4& u, uint4& v) {
+  auto x = __builtin_amdgcn_permlane16_swap(u.x, v.x, false, false);
+  auto y = __builtin_amdgcn_permlane16_swap(u.y, v.y, false, false);
+  auto z = __builtin_amdgcn_permlane16_swap(u.z, v.z, false, false);
+  auto w = __builtin_amdgcn_permlane16_swap(u.w, v.w, false, false);
+  u = make_uint4(x[0], y[0], z[0], w[0]);
+  v = make_uint4(x[1], y[1], z[1], w[1]);
+}
+
 // ---------------------------------------------------------- K split (M <= 16)
 // A workgroup of K/512 waves covers all of K for a run of 16-row tiles: wave
 // w owns k [512w, 512w + 512) and keeps the activations of that slice in
@@ -627,19 +648,41 @@ __global__ __launch_bounds__(640) void gemv_ksplit_kernel(const uint8_t* __restr
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, l16 = lane & 15, g = lane >> 4;
   const int waves = blockDim.x >> 6;
   const uint32_t ks0 = (uint32_t)wave * 512u;                 // slice start
-  const uint32_t k0 = ks0 + 128u * (uint32_t)g;               // this lane's first k
   const uint32_t kh = (uint32_t)K / 2, ks = (uint32_t)K / 16;
   const bool mvalid = l16 < M;
 
   // activations of the slice, loaded unconditionally (rows m >= M read row 0
-  // and are zeroed), all before the first transfer
+  // and are zeroed), all before the first transfer.  Lane (r, g) needs the
+  // 16-byte pieces 16g .. 16g+15 of row r's slice (xv[s] = piece 16g + s).
+  // Loaded that way, each load instruction would touch 64 lines; instead
+  // load q reads piece 4q + g, so the four lanes of a row read 64 contiguous
+  // bytes, and the pieces are then moved to their lanes in registers.
+  // Writing q = 4a + b, lane g holds piece (a, b, g) (= 16a + 4b + g) in
+  // register q; exchanging the lane index g with the register field a (a
+  // 4 x 4 transpose over the rows of 16 lanes: bit 1 by swapping the upper
+  // 32 lanes of one register with the lower 32 of another, bit 0 by swapping
+  // odd 16-lane rows with even ones) leaves piece (g, b, c) in register
+  // 4c + b of lane g, which is xv[4b + c].
   uint4 xv[16];
   {
-    const uint4* xr = reinterpret_cast<const uint4*>(x16 + (size_t)(mvalid ? l16 : 0) * ld_x16_bytes + k0 * 2u);
+    const uint8_t* xr = x16 + (size_t)(mvalid ? l16 : 0) * ld_x16_bytes + ks0 * 2u + 16u * (uint32_t)g;
+    uint4 L[16];
 #pragma unroll
-    for (int q = 0; q < 16; ++q) xv[q] = xr[q];
+    for (int q = 0; q < 16; ++q) L[q] = *reinterpret_cast<const uint4*>(xr + 64u * q);
 #pragma unroll
-    for (int q = 0; q < 16; ++q) xv[q] = mvalid ? xv[q] : make_uint4(0, 0, 0, 0);
+    for (int q = 0; q < 16; ++q) L[q] = mvalid ? L[q] : make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int a0 = 0; a0 < 2; ++a0)
+#pragma unroll
+      for (int b = 0; b < 4; ++b) swap_lanes32(L[4 * a0 + b], L[4 * (2 + a0) + b]);
+#pragma unroll
+    for (int a1 = 0; a1 < 2; ++a1)
+#pragma unroll
+      for (int b = 0; b < 4; ++b) swap_rows16(L[8 * a1 + b], L[8 * a1 + 4 + b]);
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) xv[4 * b + c] = L[4 * c + b];
   }
 
   // transfer offsets within a tile (+ 16 rows of W per tile)

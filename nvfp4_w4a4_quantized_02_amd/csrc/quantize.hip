@@ -273,32 +273,41 @@ __global__ __launch_bounds__(256) void quantize_kernel(const uint8_t* __restrict
 
 // Small tensors (decode-sized activations): one launch instead of the
 // absmax + encode pair, which is what decides the time at this size.  Each
-// workgroup of 1024 threads takes the absmax of the whole tensor itself (it
-// is at most 256 KB and sits in cache after the first workgroup reads it;
-// surplus lanes re-read the last block, which cannot change a max, so every
-// load is unconditional), then encodes its own 1024 blocks, one per thread,
-// the rare bracket misses inline.  A tensor of at most 1024 blocks has one
-// workgroup, whose own blocks are the whole tensor: the absmax then comes
-// from the blocks already in registers, with no second read.
-constexpr int kSmallThreads = 1024;
+// thread encodes one block, the rare bracket misses inline.  The encode is
+// VALU work, so the blocks are spread over several compute units, and with
+// a dynamic scale each workgroup also takes the absmax of the whole tensor
+// itself (it is at most 256 KB and sits in cache after the first workgroup
+// reads it; surplus lanes re-read the last block, which cannot change a max,
+// so every load is unconditional): the more workgroups, the more compute
+// units share the encode, but the more times the tensor is read.  Sizes:
+//   * at most kSmallOneWg blocks, dynamic scale: one workgroup of that many
+//     threads, whose own blocks are the whole tensor, so the absmax comes
+//     from the blocks already in registers, with no second read;
+//   * given scale (no absmax), or at most 16 * 256 blocks: workgroups of
+//     kSmallThreads = 256 threads (one wave per SIMD);
+//   * larger: workgroups of kSmallThreadsLarge = 512 threads (half as many
+//     reads of the tensor per block encoded).
+constexpr int kSmallThreads = 256;
+constexpr int kSmallThreadsLarge = 512;
+constexpr int kSmallOneWg = 1024;
 
 // Tensors of at most this many blocks take the one-launch kernel.
-static inline uint32_t small_block_limit(bool) { return 8u * kSmallThreads; }
+static inline uint32_t small_block_limit(bool) { return 32u * kSmallThreads; }
 
 // kGiven: the tensor scale is *gs_in and no absmax is taken.  gs_out may be
 // nullptr.  With several workgroups, each takes the absmax of the whole
-// tensor itself: thread t reads blocks t, t + 1024, ... (kRounds of them,
-// indices past the end clamped onto the last block), all loads issued
-// together, so the absmax costs one round trip.
-template <bool kBf16, bool kF16, bool kGiven, int kRounds>
-__global__ __launch_bounds__(1024) void quantize_small_kernel(const uint8_t* __restrict__ x, size_t ld_bytes,
+// tensor itself: thread t reads blocks t, t + kThreads, ... (kRounds of
+// them, indices past the end clamped onto the last block), in batches whose
+// loads are issued together.
+template <int kThreads, bool kBf16, bool kF16, bool kGiven, int kRounds>
+__global__ __launch_bounds__(kThreads) void quantize_small_kernel(const uint8_t* __restrict__ x, size_t ld_bytes,
                                                                uint32_t kblocks, uint32_t out_kblocks,
                                                                uint32_t total_blocks, FastDiv fd,
                                                                const float* __restrict__ gs_in,
                                                                uint8_t* __restrict__ codes,
                                                                uint8_t* __restrict__ scales,
                                                                uint4* __restrict__ x16, float* __restrict__ gs_out) {
-  __shared__ uint32_t red[kSmallThreads / 64];
+  __shared__ uint32_t red[kThreads / 64];
   if (total_blocks == 0) {  // (the launcher never sends one) no element to clamp onto
     if (gs_out && blockIdx.x == 0 && threadIdx.x == 0) *gs_out = kGiven ? *gs_in : 0.0f;
     return;
@@ -313,7 +322,7 @@ __global__ __launch_bounds__(1024) void quantize_small_kernel(const uint8_t* __r
   // This thread's own block, fetched first so that it is in registers by
   // the time the tensor scale is known (lanes past the end fetch the last
   // block and encode nothing).
-  const uint32_t b = blockIdx.x * kSmallThreads + threadIdx.x;
+  const uint32_t b = blockIdx.x * kThreads + threadIdx.x;
   uint32_t kb_own;
   uint32_t own[BlockWords<kBf16>::n];
   load_words<kBf16>(block_ptr(b < total_blocks ? b : total_blocks - 1u, kb_own), own);
@@ -328,15 +337,16 @@ __global__ __launch_bounds__(1024) void quantize_small_kernel(const uint8_t* __r
       // they are already in registers (padding blocks count as zeros).
       if (b < total_blocks && kb_own < kblocks) m = words_absmax_bits<kBf16>(own);
     } else {
-      // fp32 blocks take twice the registers: at most four in flight
-      constexpr int kBatch = (kBf16 || kRounds < 4) ? kRounds : 4;
+      // at most 16 bf16 blocks (128 registers) in flight, 4 fp32 ones
+      constexpr int kCap = kBf16 ? 16 : 4;
+      constexpr int kBatch = kRounds < kCap ? kRounds : kCap;
 #pragma unroll
       for (int r0 = 0; r0 < kRounds; r0 += kBatch) {
         uint32_t wv[kBatch][BlockWords<kBf16>::n];
         uint32_t kb[kBatch];
 #pragma unroll
         for (int u = 0; u < kBatch; ++u) {
-          uint32_t bu = threadIdx.x + (uint32_t)(r0 + u) * kSmallThreads;
+          uint32_t bu = threadIdx.x + (uint32_t)(r0 + u) * kThreads;
           bu = bu < total_blocks ? bu : total_blocks - 1u;
           load_words<kBf16>(block_ptr(bu, kb[u]), wv[u]);
         }
@@ -352,7 +362,7 @@ __global__ __launch_bounds__(1024) void quantize_small_kernel(const uint8_t* __r
     __syncthreads();
     uint32_t amax = red[0];
 #pragma unroll
-    for (int i = 1; i < kSmallThreads / 64; ++i) amax = amax > red[i] ? amax : red[i];
+    for (int i = 1; i < kThreads / 64; ++i) amax = amax > red[i] ? amax : red[i];
     gs = tensor_scale(__uint_as_float(amax));
   }
   if (gs_out && blockIdx.x == 0 && threadIdx.x == 0) *gs_out = gs;
@@ -463,7 +473,7 @@ static inline int grid_for(uint64_t work, uint64_t per_wg, int cap) {
 
 int launch_amax(const void* x, bool bf16, int64_t rows, int64_t K, int64_t ld, uint32_t* partials,
                 hipStream_t s) {
-  if (rows * (K / 16) <= (int64_t)small_block_limit(bf16)) return 0;  // one-workgroup quantize instead
+  if (rows * (K / 16) <= (int64_t)small_block_limit(bf16)) return 0;  // one-launch quantize instead
   uint32_t esize = bf16 ? 2u : 4u;
   uint32_t cpr = (uint32_t)(K * esize / 16);
   uint32_t ldc = (uint32_t)(ld * esize / 16);
@@ -484,15 +494,30 @@ static void launch_encode(bool small, const uint8_t* xb, size_t ld_bytes, uint32
                           FastDiv fd, const uint32_t* partials, int npartials, const float* gs_in, uint8_t* codes,
                           uint8_t* scales, uint4* xo, float* gs, hipStream_t s) {
   if (small) {
-    const int grid = (int)((total + kSmallThreads - 1) / kSmallThreads);  // at most 8 (small_block_limit)
+    if (!kGiven && total <= (uint32_t)kSmallOneWg) {
+      quantize_small_kernel<kSmallOneWg, kBf16, kF16, false, 1>
+          <<<1, kSmallOneWg, 0, s>>>(xb, ld_bytes, kb, okb, total, fd, gs_in, codes, scales, xo, gs);
+      return;
+    }
+    // the absmax reads every block: kRounds * threads >= total
+    if (kGiven || total <= 16u * kSmallThreads) {
+      const int grid = (int)((total + kSmallThreads - 1) / kSmallThreads);
+      auto go = [&](auto rounds) {
+        quantize_small_kernel<kSmallThreads, kBf16, kF16, kGiven, decltype(rounds)::value>
+            <<<grid, kSmallThreads, 0, s>>>(xb, ld_bytes, kb, okb, total, fd, gs_in, codes, scales, xo, gs);
+      };
+      if (kGiven) go(std::integral_constant<int, 1>());
+      else if (grid <= 8) go(std::integral_constant<int, 8>());
+      else go(std::integral_constant<int, 16>());
+      return;
+    }
+    const int grid = (int)((total + kSmallThreadsLarge - 1) / kSmallThreadsLarge);  // at most 16
     auto go = [&](auto rounds) {
-      quantize_small_kernel<kBf16, kF16, kGiven, decltype(rounds)::value>
-          <<<grid, kSmallThreads, 0, s>>>(xb, ld_bytes, kb, okb, total, fd, gs_in, codes, scales, xo, gs);
+      quantize_small_kernel<kSmallThreadsLarge, kBf16, kF16, false, decltype(rounds)::value>
+          <<<grid, kSmallThreadsLarge, 0, s>>>(xb, ld_bytes, kb, okb, total, fd, gs_in, codes, scales, xo, gs);
     };
-    if (kGiven || grid == 1) go(std::integral_constant<int, 1>());
-    else if (grid == 2) go(std::integral_constant<int, 2>());
-    else if (grid <= 4) go(std::integral_constant<int, 4>());
-    else go(std::integral_constant<int, 8>());
+    if (grid <= 12) go(std::integral_constant<int, 12>());
+    else go(std::integral_constant<int, 16>());
     return;
   }
   // Four workgroups per compute unit, all resident at once:

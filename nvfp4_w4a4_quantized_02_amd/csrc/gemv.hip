@@ -790,8 +790,12 @@ __global__ __launch_bounds__(640) void gemv_ksplit_kernel(const uint8_t* __restr
 // per-tensor scale, served against bf16 activations).  W is [N, K] E4M3
 // bytes.  A workgroup of ceil(K / 512) waves covers all of K for a run of
 // 16-row tiles (as the K-split kernel above; K <= 5120): wave w owns k [512w, 512w+512)
-// and keeps the activations of that slice in registers; lane (r, g) takes
-// k 128g .. 128g+127 of row r.  The weights of a tile (128 bytes a lane) go
+// and keeps the activations of that slice in registers.  Lane (r, g) takes
+// 128 k of row r, interleaved with the other three lanes of the row so that
+// each load instruction reads 64 contiguous bytes of W per row (16-byte
+// pieces: piece 4q + g of the slice is the lane's load q); the activations
+// follow the same k order, which is any order as long as both operands share
+// it.  The weights of a tile (128 bytes a lane) go
 // straight to registers, the next tile's while the current one is computed
 // (two register sets, used alternately).  Past K the activations are zero.  The
 // partial tiles of the waves are added in LDS in wave order (one barrier a
@@ -812,18 +816,26 @@ __global__ __launch_bounds__(640) void gemv_fp8w_kernel(const uint8_t* __restric
   __shared__ floatx4 part[2][kF8MaxWaves][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, l16 = lane & 15, g = lane >> 4;
   const int waves = blockDim.x >> 6;
-  const int k0 = wave * 512 + 128 * g;  // this lane's first k
   const bool mvalid = l16 < M;
+  // k of the lane's W load q (16 weights): piece 4q + g of the wave's slice.
+  // kA8: MFMA step s takes loads 2s and 2s+1 (32 k), so those are pieces
+  // 8s + 2g and 8s + 2g + 1, i.e. 32-k pieces 4s + g.
+  auto wk = [&](int q) {
+    return wave * 512 + (kA8 ? 32 * (4 * (q >> 1) + g) + 16 * (q & 1) : 16 * (4 * q + g));
+  };
 
-  // activations of the slice: 128 k of row l16 (zeros past K and for m >= M)
+  // activations of the slice in the same k order (zeros past K and for
+  // m >= M): kA8: 16 FP8 values per load, as W; bf16: MFMA step s (8 k) is
+  // half s & 1 of W load s >> 1
   constexpr int kXq = kA8 ? 8 : 16;  // uint4 per lane
   uint4 xv[kXq];
   {
-    const uint8_t* xr = x + (size_t)(mvalid ? l16 : 0) * ld_x_bytes + (size_t)k0 * (kA8 ? 1u : 2u);
+    const uint8_t* xr = x + (size_t)(mvalid ? l16 : 0) * ld_x_bytes;
 #pragma unroll
     for (int q = 0; q < kXq; ++q) {
-      const int kq = k0 + q * (kA8 ? 16 : 8);
-      xv[q] = (mvalid && kq < K) ? reinterpret_cast<const uint4*>(xr)[q] : make_uint4(0, 0, 0, 0);
+      const int kq = kA8 ? wk(q) : wk(q >> 1) + 8 * (q & 1);
+      xv[q] = (mvalid && kq < K) ? *reinterpret_cast<const uint4*>(xr + (size_t)kq * (kA8 ? 1u : 2u))
+                                 : make_uint4(0, 0, 0, 0);
     }
   }
 
@@ -836,7 +848,7 @@ __global__ __launch_bounds__(640) void gemv_fp8w_kernel(const uint8_t* __restric
     const uint8_t* wr = wq + (size_t)n * (size_t)K;
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
-      const int kq = k0 + 16 * q < K ? k0 + 16 * q : K - 16;
+      const int kq = wk(q) < K ? wk(q) : K - 16;
       w[q] = *reinterpret_cast<const uint4*>(wr + kq);
     }
   };

@@ -247,30 +247,38 @@ __global__ __launch_bounds__(64) void gemv_stream_kernel(const uint8_t* __restri
 // elements) into its own LDS while its first weight transfers are already in
 // flight.
 //
+// With both operands quantized, the contraction runs on the FP4 MFMA
+// (16x16x128, E2M1 operands with unit scales) over the raw codes, so no
+// weight element is converted: each output column of an MFMA collects one
+// 16-element block, and its exact sum is multiplied by the block's two E4M3
+// scales afterwards (the product of two NVFP4 blocks, paper "Why Gated
+// DeltaNet Survives 4-Bit Quantization", section 2 "NVFP4").  Only the fp32
+// accumulation over blocks rounds, as in every other contraction kernel, in
+// another order.
+//
 // A workgroup is kFuWaves waves, one 16-row weight tile each, sharing the
-// fp16 expansion of the quantized row in LDS.  The row's 16-element blocks
-// are dealt to the waves in sets of 64 (set j to wave j % kFuWaves; lane l
-// takes block 64 j + l).  Order of work in a wave:
+// quantized row in LDS.  The row's 16-element blocks are dealt to the waves
+// in sets of 64 (set j to wave j % kFuWaves; lane l takes block 64 j + l).
+// Order of work in a wave:
 //   1. direct transfers into LDS, in this order: the bf16 bytes of its own
-//      sets of blocks, into the LDS region of the fp16 copy at the offsets
-//      their expansion will take (a bf16 block and its fp16 expansion are
-//      both 32 B); its tile's scale bytes (16 rows x K/16, contiguous); the
-//      first D chunks of codes (16 rows x 128 B per chunk, two transfers
-//      filling 8 lines each).  Transfers complete in the order issued, so
-//      the wave then waits for its row bytes alone;
+//      sets of blocks (into the row's LDS region at their row offsets); its
+//      tile's scale bytes (16 rows x K/16, contiguous); the first D chunks of
+//      codes (16 rows x 128 B per chunk, two transfers filling 8 lines each).
+//      Transfers complete in the order issued, so the wave then waits for
+//      its row bytes alone;
 //   2. the absmax of its blocks (exact: integer max of the magnitudes),
 //      combined over the wave and, through LDS and a barrier, over the
 //      workgroup; the tensor scale RN(amax / 2688) (or the given one);
-//   3. the encode of its blocks, each written over its own bf16 bytes as
-//      fp16 values E2M1 * E4M3 (only this lane reads or writes them);
-//   4. one barrier, then the streaming loop of the M <= 4 kernel above with
-//      the activation operand read from the shared LDS copy;
-//   5. workgroup 0 copies the quantized row and the tensor scale to the
-//      workspace, where nvfp4_gemm_prepare would leave them.  Stored last: a
-//      store can be acknowledged before older loads return, so stores issued
-//      while loads are in flight would let a compiler-counted wait for those
-//      loads pass early.
-// The accumulation order is the same as the two-launch path's.
+//   3. the encode of its blocks into codes, scale bytes and their E4M3
+//      values, written over the row's bf16 bytes (after a barrier: they
+//      overlap other waves' blocks);
+//   4. one barrier, then the streaming loop below;
+//   5. workgroup 0 writes the quantized row to the workspace as fp16 values
+//      E2M1 * E4M3 and the tensor scale, where nvfp4_gemm_prepare would
+//      leave them.  Stored last: a store can be acknowledged before older
+//      loads return, so stores issued while loads are in flight would let a
+//      compiler-counted wait for those loads pass early.
+typedef int i32x8 __attribute__((ext_vector_type(8)));  // operands of the scaled MFMAs
 constexpr int kFuWaves = 3;
 constexpr int kFuDepth = 4;
 
@@ -288,7 +296,8 @@ __global__ __launch_bounds__(64 * kFuWaves) void gemv_fused_m1_kernel(const uint
   static_assert(NB % 64 == 0, "whole sets of 64 blocks");
   constexpr uint32_t kh = K / 2, ks = K / 16;
   constexpr uint32_t kScBytes = (16u * ks + 1023u) / 1024u * 1024u;
-  // X16 [K / 8] | ring [wave][D][2048 B] | scales [wave][kScBytes] | wave maxima [4]
+  // row [2K B: bf16, then codes | scale values | scale bytes] | ring [wave][D][2048 B] |
+  // scales [wave][kScBytes] | wave maxima [4]
   extern __shared__ uint4 smem[];
   const int lane = threadIdx.x & 63, l16 = lane & 15, g = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));  // uniform: scalar bases
@@ -375,7 +384,16 @@ __global__ __launch_bounds__(64 * kFuWaves) void gemv_fused_m1_kernel(const uint
     gs = tensor_scale(__uint_as_float(m));
   }
 
-  // 3. encode this wave's blocks over their bf16 bytes
+  // 3. encode this wave's blocks: codes (8 B a block) at the front of the
+  //    row's LDS region, E4M3 values of the scales (fp32) after them, the
+  //    scale bytes after those.  These overwrite bf16 bytes of other blocks,
+  //    so every wave has read its blocks first (the barrier above, or this
+  //    one with a given scale).
+  if constexpr (kGiven) asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  uint8_t* xrow = reinterpret_cast<uint8_t*>(xs);
+  uint2* xcodes = reinterpret_cast<uint2*>(xrow);                 // [NB]
+  float* xsc = reinterpret_cast<float*>(xrow + K / 2);             // [NB]
+  uint8_t* xsb = xrow + K / 2 + 4 * NB;                            // [NB]
   const FastScale fsc = fast_scale(gs);
 #pragma unroll
   for (int j = 0; j < BPL; ++j) {
@@ -386,62 +404,82 @@ __global__ __launch_bounds__(64 * kFuWaves) void gemv_fused_m1_kernel(const uint
     uint32_t sb, lo, hi;
     if (!encode_block_fast(xv, words_absmax_bits<true>(xw[j]), fsc, sb, lo, hi))
       sb = encode_block_exact(xv, gs, lo, hi);
-    const half2_t q2 = scale_f16x2(sb);
-    uint32_t e0[4], e1[4];
-    expand8(lo, q2, e0);
-    expand8(hi, q2, e1);
-    xs[2 * b] = make_uint4(e0[0], e0[1], e0[2], e0[3]);
-    xs[2 * b + 1] = make_uint4(e1[0], e1[1], e1[2], e1[3]);
+    xcodes[b] = make_uint2(lo, hi);
+    xsc[b] = __builtin_amdgcn_cvt_f32_fp8((int)sb, 0);
+    xsb[b] = (uint8_t)sb;
   }
-  // X16 complete and visible to every wave (the transfers in flight are not
-  // waited for: a bare barrier, no fence)
+  // the quantized row complete and visible to every wave (the transfers in
+  // flight are not waited for: a bare barrier, no fence)
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 
-  // 4. the streaming loop
+  // 4. the streaming loop.  Per chunk (256 k), two FP4 MFMAs 16x16x128 on
+  //    the raw codes (E2M1 x E2M1, unit scales) give, in output column c,
+  //    the dot product of each weight row with block c of the chunk alone:
+  //    MFMA H takes k 128H .. 128H+127 of the chunk, lane group g k 32g ..
+  //    32g+31 of that (weight piece 4H + g of the row); the activation
+  //    operand of lane (c, g) holds the codes of block c in its half c % 2
+  //    when g = (c % 8) / 2 and c / 8 = H, zeros elsewhere.  The products and
+  //    their 16-term sums are small multiples of 1/4, exact in fp32, and so
+  //    is each sum times the two block scales (at most 18 significant bits):
+  //    lane (c, g) adds them to the partial sums of rows 4g .. 4g+3 in fp32
+  //    in chunk order, and the 16 lanes of a row group are added at the end
+  //    in a fixed tree.
   const uint32_t sw = (uint32_t)(l16 & 7);
-  const uint32_t cpos0 = (uint32_t)l16 * 128u + 16u * ((2u * g) ^ sw);
-  const uint32_t cpos1 = (uint32_t)l16 * 128u + 16u * ((2u * g + 1u) ^ sw);
-  const bool col0 = l16 == 0;
-  // two accumulators: alternate MFMAs do not wait for each other's result
-  floatx4 acc[2] = {floatx4{0.0f, 0.0f, 0.0f, 0.0f}, floatx4{0.0f, 0.0f, 0.0f, 0.0f}};
+  const uint32_t apos0 = (uint32_t)l16 * 128u + 16u * ((uint32_t)g ^ sw);
+  const uint32_t apos1 = (uint32_t)l16 * 128u + 16u * ((4u + (uint32_t)g) ^ sw);
+  const bool act = g == ((l16 & 7) >> 1);
+  const uint32_t mk[2][2] = {
+      {(act && (l16 >> 3) == 0 && (l16 & 1) == 0) ? ~0u : 0u, (act && (l16 >> 3) == 0 && (l16 & 1) == 1) ? ~0u : 0u},
+      {(act && (l16 >> 3) == 1 && (l16 & 1) == 0) ? ~0u : 0u, (act && (l16 >> 3) == 1 && (l16 & 1) == 1) ? ~0u : 0u}};
+  const uint32_t srow = (uint32_t)(4 * g) * ks + (uint32_t)l16;  // scale byte of row 4g, block l16 of chunk 0
+  float part[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
   for (int c = 0; c < NCK; ++c) {
     const int d = c % D;
     wait_vmcnt<(D - 1) * 2>();
     const uint8_t* slot = ring + d * kGvChunkCodes;
-    const uint4 w0 = *reinterpret_cast<const uint4*>(slot + cpos0);
-    const uint4 w1 = *reinterpret_cast<const uint4*>(slot + cpos1);
-    uint4 xv[8];
+    const uint4 a0 = *reinterpret_cast<const uint4*>(slot + apos0);
+    const uint4 a1 = *reinterpret_cast<const uint4*>(slot + apos1);
+    const uint2 xv = xcodes[16 * c + l16];
+    const float sx = xsc[16 * c + l16];
+    uint32_t swb[4];
 #pragma unroll
-    for (int t = 0; t < 8; ++t) xv[t] = make_uint4(0, 0, 0, 0);
-    if (col0) {
-#pragma unroll
-      for (int t = 0; t < 8; ++t) xv[t] = xs[32 * c + 8 * g + t];
-    }
-    const uint32_t sd = *reinterpret_cast<const uint32_t*>(sc_lds + (uint32_t)l16 * ks + 4u * g + 16u * c);
+    for (int j = 0; j < 4; ++j) swb[j] = sc_lds[srow + (uint32_t)j * ks + 16u * (uint32_t)c];
     // the slot's reads are complete: refill it before computing, so the
     // transfer is not held back by this chunk's arithmetic
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     issue(c + D, d);
-    const uint32_t s0 = O::scale_bits(sd), s1 = O::scale_bits(sd >> 8), s2 = O::scale_bits(sd >> 16),
-                   s3 = O::scale_bits(sd >> 24);
+    const i32x8 A0 = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, 0, 0, 0, 0};
+    const i32x8 A1 = {(int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w, 0, 0, 0, 0};
+    const i32x8 B0 = {(int)(xv.x & mk[0][0]), (int)(xv.y & mk[0][0]), (int)(xv.x & mk[0][1]), (int)(xv.y & mk[0][1]),
+                      0, 0, 0, 0};
+    const i32x8 B1 = {(int)(xv.x & mk[1][0]), (int)(xv.y & mk[1][0]), (int)(xv.x & mk[1][1]), (int)(xv.y & mk[1][1]),
+                      0, 0, 0, 0};
+    floatx4 acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A0, B0, floatx4{0.0f, 0.0f, 0.0f, 0.0f}, 4, 4, 0,
+                                                                    127, 0, 127);
+    acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A1, B1, acc, 4, 4, 0, 127, 0, 127);
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      const uint32_t sp = t < 2 ? s0 : (t < 4 ? s1 : (t < 6 ? s2 : s3));
-      uint32_t e[4];
-      O::expand(dword_of(t < 4 ? w0 : w1, t & 3), sp, e);
-      acc[t & 1] = O::mfma16(O::vec(make_uint4(e[0], e[1], e[2], e[3])), O::vec(xv[t]), acc[t & 1]);
-    }
+    for (int j = 0; j < 4; ++j)
+      part[j] = __builtin_fmaf(acc[j] * sx, __builtin_amdgcn_cvt_f32_fp8((int)(swb[j] & 0x7Fu), 0), part[j]);
   }
   wait_vmcnt<0>();
-  if (col0 && tile_raw < tiles) {
+  // rows 4g .. 4g+3: the 16 lanes of the row group, added in a fixed tree
+#pragma unroll
+  for (int o = 8; o > 0; o >>= 1)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) part[j] += __shfl_xor(part[j], o, 64);
+  if (l16 == 0 && tile_raw < tiles) {
     const float scale = gs * (*gsw_p);
-    const floatx4 a = acc[0] + acc[1];
-    store4<kYBf16>(y, n0 + 4 * g, N, a[0] * scale, a[1] * scale, a[2] * scale, a[3] * scale);
+    store4<kYBf16>(y, n0 + 4 * g, N, part[0] * scale, part[1] * scale, part[2] * scale, part[3] * scale);
   }
-  // 5. the quantized row for the workspace
+  // 5. the quantized row for the workspace, as fp16 values E2M1 * E4M3
   if (blockIdx.x == 0) {
-    for (int i = (int)threadIdx.x; i < K / 8; i += 64 * kFuWaves) x16_out[i] = xs[i];
+    for (int i = (int)threadIdx.x; i < K / 8; i += 64 * kFuWaves) {
+      const uint2 cw = xcodes[i >> 1];
+      uint32_t e[4];
+      expand8((i & 1) ? cw.y : cw.x, scale_f16x2(xsb[i >> 1]), e);
+      x16_out[i] = make_uint4(e[0], e[1], e[2], e[3]);
+    }
     if (threadIdx.x == 0) *gsx_out = gs;
   }
 }
@@ -804,7 +842,6 @@ __global__ __launch_bounds__(640) void gemv_ksplit_kernel(const uint8_t* __restr
 //     16 MFMA 16x16x32 bf16 steps of 8 k.
 //   kA8 = true: FP8 activations; 4 MFMA 16x16x128 FP8 steps of 32 k, both
 //     operands unconverted (unit block scales).
-typedef int i32x8 __attribute__((ext_vector_type(8)));
 constexpr int kF8MaxWaves = 10;    // K <= 5120 (wider K takes the tile kernel)
 
 template <bool kA8, bool kYBf16>

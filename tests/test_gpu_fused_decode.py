@@ -1,18 +1,19 @@
 """One-launch decode: for one bf16 activation row with K = 4096 or 5120,
-nvfp4_gemm quantizes the row and runs the GEMV in a single kernel.
+nvfp4_gemm quantizes the row and runs the GEMV in a single kernel, whose
+contraction runs on the FP4 MFMA over the raw codes with the block scales
+applied to each block's exact sum.
 
-Three checks per case (paper "Why Gated DeltaNet Survives 4-Bit
-Quantization", section 2 "NVFP4": activations quantized on the fly, one FP32
-tensor scale, E4M3 scale per 16 elements, the product of the two NVFP4
-operands):
-  * the output against the oracle's W4A4 product, under the GEMM gate;
-  * the output bit-identical to the two-launch path, reached by handing the
-    same values over as fp32 (the fp32 row quantizes to the same bytes and
-    the GEMV accumulates in the same order);
+Checks per case (paper "Why Gated DeltaNet Survives 4-Bit Quantization",
+section 2 "NVFP4": activations quantized on the fly, one FP32 tensor scale,
+E4M3 scale per 16 elements, the product of the two NVFP4 operands):
+  * the output against the oracle's W4A4 product, under the GEMM gate, and
+    the same for the two-launch path (quantize, then the fp16 GEMV) reached
+    by handing the same values over as fp32; the two paths add the same
+    exact block products in different orders, so only the gate binds them;
   * the workspace left as nvfp4_gemm_prepare leaves it: gs_x (byte 8192)
     with the oracle's bits and the fp16 operand E2M1 * E4M3 (from byte
     8448) equal to the one built from the oracle's codes and scale bytes.
-Shapes cover a single tile (one wave of the pair idle), ragged N, an odd
+Shapes cover a single tile (one wave of the three idle), ragged N, an odd
 tile count, and the full fused gate/up weight; inputs include rows on or
 next to every E2M1 and scale-byte rounding tie, and calibrated scales."""
 import numpy as np
@@ -70,7 +71,6 @@ def _check_case(nv, orc, xb, w_host, w_dev, out, what, gs=None):
     ref = orc.gemm_exact(oc, os_, og, wc, ws, gsw)
     check_gemm(y, ref, out == "bf16", what + " (one launch)")
     check_gemm(y2, ref, out == "bf16", what + " (two launches)")
-    assert np.array_equal(y.view(np.uint8), y2.view(np.uint8)), "%s: differs from the two-launch path" % what
 
 
 @pytest.mark.parametrize("out", ["f32", "bf16"])
@@ -134,7 +134,6 @@ def test_fused_decode_full_weight(nv, orc):
     y = to_np(nv.nvfp4_gemm(to_gpu(p.x), wc, ws, shared, out_dtype=torch.bfloat16))
     y2 = to_np(nv.nvfp4_gemm(to_gpu(_bf16_as_f32(p.x)), wc, ws, shared, out_dtype=torch.bfloat16))
     torch.cuda.synchronize()
-    assert np.array_equal(y, y2), "full weight: differs from the two-launch path"
     gss = [orc.tensor_scale(w) for w in p.w_parts]
     codes, scales = [], []
     for w, g in zip(p.w_parts, gss):
@@ -143,4 +142,5 @@ def test_fused_decode_full_weight(nv, orc):
         scales.append(s)
     scales, S = orc.fuse_rescale(scales, gss)
     ref, _ = orc.linear(p.x, np.concatenate(codes), np.concatenate(scales), np.float32(S))
-    check_gemm(y, ref, True, "fused decode full weight")
+    check_gemm(y, ref, True, "fused decode full weight (one launch)")
+    check_gemm(y2, ref, True, "fused decode full weight (two launches)")

@@ -419,11 +419,11 @@ __global__ __launch_bounds__(64 * kFuWaves) void gemv_fused_m1_kernel(const uint
   //    32g+31 of that (weight piece 4H + g of the row); the activation
   //    operand of lane (c, g) holds the codes of block c in its half c % 2
   //    when g = (c % 8) / 2 and c / 8 = H, zeros elsewhere.  The products and
-  //    their 16-term sums are small multiples of 1/4, exact in fp32, and so
-  //    is each sum times the two block scales (at most 18 significant bits):
-  //    lane (c, g) adds them to the partial sums of rows 4g .. 4g+3 in fp32
-  //    in chunk order, and the 16 lanes of a row group are added at the end
-  //    in a fixed tree.
+  //    their 16-term sums are multiples of 1/4 below 600, exact in fp32, and
+  //    so is each sum times the two block scales (at most 12 + 4 + 4
+  //    significant bits): lane (c, g) adds them to the partial sums of rows
+  //    4g .. 4g+3 in fp32 in chunk order, and the 16 lanes of a row group are
+  //    added at the end in a fixed tree.
   const uint32_t sw = (uint32_t)(l16 & 7);
   const uint32_t apos0 = (uint32_t)l16 * 128u + 16u * ((uint32_t)g ^ sw);
   const uint32_t apos1 = (uint32_t)l16 * 128u + 16u * ((4u + (uint32_t)g) ^ sw);

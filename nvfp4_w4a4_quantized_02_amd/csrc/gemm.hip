@@ -86,7 +86,7 @@ __device__ __forceinline__ void tile_coords(int tile, int full_tiles, int tiles_
 struct GemmSmem {
   uint4 x[3][kGemmBM * 8];      // 3 x 32 KB
   uint4 wc[3][kGemmBN * 4];     // 3 x 16 KB
-  uint32_t ws[3][kGemmBN * 4];  // 3 x 4 KB
+  uint32_t ws[3][kGemmBN * 2];  // 3 x 2 KB
 };
 
 constexpr int kGemmWaves = 8;
@@ -143,11 +143,11 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const uint4* __restrict__ 
   // W codes: the transfer of half hh fills rows 128 hh + 16 wave + lane/4,
   // slot lane%4 of the row, with piece (lane%4) ^ swz(row).  Pieces past the
   // end of a row (a group reaching past K) re-read the row's last 16 bytes.
-  // W scales: the transfer of quarter qq fills (lanes 0..31) rows
-  // 64 qq + 8 wave + lane/4, dword slot lane%4 of the row, with dword
-  // (lane%4) ^ ((row >> 3) & 3) = (lane%4) ^ (wave & 3).  Rows past N repeat
-  // the last one (never stored).  These offsets are recomputed per transfer
-  // (a few integer operations) rather than held in registers.
+  // W scales: the transfer of half hh fills (lanes 0..31) rows
+  // 128 hh + 16 wave + lane/2, dword lane%2 of the row (one dword per step
+  // of the group).  Rows past N repeat the last one (never stored).  These
+  // offsets are recomputed per transfer (a few integer operations) rather
+  // than held in registers.
   // LDS byte address of a place in sm: one address-space conversion for the
   // whole kernel, then integer offsets (a conversion per use would also test
   // the pointer for null every time)
@@ -157,7 +157,7 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const uint4* __restrict__ 
   };
   const int nrows = N - n0;
   const int last = n - 1;
-  const int glast = last >> 1, Glast = last >> 2;
+  const int glast = last >> 1;
 
   // Transfers into buffer b of each ring.  Sources past the range repeat
   // the last step or group (into buffers that are no longer read).
@@ -174,12 +174,14 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const uint4* __restrict__ 
     const uint32_t off = (uint32_t)(row < nrows ? row : nrows - 1) * kh + min(goff + piece, kh - 16u);
     lds_dma16(wcbase, off, soff(&sm.wc[b][(128 * hh + 16 * wave) * 4]));
   };
-  auto issue_ws = [&](int G, int qq, int b) {
-    const uint32_t goff = (uint32_t)(kb + 4 * (G < Glast ? G : Glast)) * 4u;
-    const int row = 64 * qq + 8 * wave + (l32 >> 2);
-    const uint32_t dw = (((uint32_t)lane & 3u) ^ ((uint32_t)wave & 3u)) * 4u;
+  auto issue_ws = [&](int g, int hh, int b) {
+    const uint32_t goff = (uint32_t)(kb + 2 * (g < glast ? g : glast)) * 4u;
+    const int row = 128 * hh + 16 * wave + (l32 >> 1);
+    const uint32_t dw = ((uint32_t)lane & 1u) * 4u;
     const uint32_t off = (uint32_t)(row < nrows ? row : nrows - 1) * ks + min(goff + dw, ks - 4u);
-    if (lane < 32) lds_dma4(wsbase, off, soff(&sm.ws[b][(64 * qq + 8 * wave) * 4]));
+    // the LDS address is wave-uniform: taken out of the divergent branch
+    const uint32_t lds = __builtin_amdgcn_readfirstlane(soff(&sm.ws[b][(128 * hh + 16 * wave) * 2]));
+    if (lane < 32) lds_dma4(wsbase, off, lds);
   };
 
   floatx16 acc[2][4];
@@ -206,14 +208,14 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const uint4* __restrict__ 
   // W codes of one step (one 16-byte piece per row and lane) and the two
   // block scales of this lane: step s of code group buffer bc (s%2 = its
   // position in the group) and scale group buffer bs (s%4).
-  auto read_w = [&](int bc, int sp2, int bs, int sp4, uint4 (&wv)[2], uint32_t (&sw)[2]) {
+  auto read_w = [&](int bc, int sp2, uint4 (&wv)[2], uint32_t (&sw)[2]) {
     const uint4* cb = sm.wc[bc];
-    const uint32_t* sb = sm.ws[bs];
+    const uint32_t* sb = sm.ws[bc];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       const uint32_t row = wave_n * 64 + t * 32 + l32;
       wv[t] = cb[row * 4 + ((uint32_t)(2 * sp2 + h) ^ wc_swz(row))];
-      sw[t] = sb[row * 4 + ((uint32_t)sp4 ^ ((row >> 3) & 3u))] >> (16 * h);
+      sw[t] = sb[row * 2 + (uint32_t)sp2] >> (16 * h);
     }
   };
   auto split_w = [&](const uint32_t (&sw)[2], uint32_t (&sp)[2][2]) {
@@ -245,10 +247,9 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const uint4* __restrict__ 
   uint32_t sp[2][2];
   V bx[4], aw[2];
 
-  // Ring buffer of code group g and scale group G (wave-uniform).
-  auto mod3 = [](int v) { return (int)((uint32_t)v % 3u); };
-
-  // One main-loop step, i = I (mod 3).  Sub-steps 0..2 run from X buffer I,
+  // One main-loop step, i = I (mod 6), so that every ring index is known
+  // when compiling: X buffer i % 3, code and scale group buffer (i / 2) % 3,
+  // position i % 2 in the group.  Sub-steps 0..2 run from X buffer i % 3,
   // each overlapping the LDS reads and expansion of the following sub-step.
   // Then the wave waits for its transfers issued one step earlier and meets
   // the barrier with the operands of sub-step 3 in registers; its 16 MFMAs
@@ -257,14 +258,14 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const uint4* __restrict__ 
   // last step (the buffers then hold repeated, finite data), which keeps
   // this branch-free.
   auto step = [&](auto ic, int i) {
-    constexpr int I = decltype(ic)::value;
-    issue_x(i + 2, (I + 2) % 3);
-    issue_wc((i >> 1) + 2, i & 1, mod3((i >> 1) + 2));
-    issue_ws((i >> 2) + 2, i & 3, mod3((i >> 2) + 2));
+    constexpr int I = decltype(ic)::value, X = I % 3, I1 = I + 1;
+    issue_x(i + 2, (X + 2) % 3);
+    issue_wc((i >> 1) + 2, I & 1, ((I >> 1) + 2) % 3);
+    issue_ws((i >> 1) + 2, I & 1, ((I >> 1) + 2) % 3);
 #pragma unroll
     for (int j = 0; j < 3; ++j) {
       V bxn[4], awn[2];
-      read_x(I, j + 1, bxn);
+      read_x(X, j + 1, bxn);
       mfma8(aw, bx);
       expand_w(wv, sp, j + 1, awn);
 #pragma unroll
@@ -282,10 +283,9 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const uint4* __restrict__ 
     for (int q = 0; q < 4; ++q) bx3[q] = bx[q];
 #pragma unroll
     for (int q = 0; q < 2; ++q) aw3[q] = aw[q];
-    const int i1 = i + 1;
     uint32_t sw[2];
-    read_w(mod3(i1 >> 1), i1 & 1, mod3(i1 >> 2), i1 & 3, wv, sw);
-    read_x((I + 1) % 3, 0, bx);
+    read_w((I1 >> 1) % 3, I1 & 1, wv, sw);
+    read_x(I1 % 3, 0, bx);
     mfma8(aw3, bx3);
     split_w(sw, sp);
     expand_w(wv, sp, 0, aw);
@@ -293,31 +293,39 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const uint4* __restrict__ 
   static_assert(kDmaPerStep == 6, "the wait count above must match the transfers per step");
 
   if (n > 0) {
-    // Steps 0 and 1 of X, code groups 0 and 1 (steps 0..3), scale groups 0
-    // and 1 (steps 0..7): ten transfers for step 0, then ten more.
+    // Steps 0 and 1 of X, code and scale groups 0 and 1 (steps 0..3): eight
+    // transfers for step 0, then eight more.
     issue_x(0, 0);
     issue_wc(0, 0, 0);
     issue_wc(0, 1, 0);
-#pragma unroll
-    for (int qq = 0; qq < 4; ++qq) issue_ws(0, qq, 0);
+    issue_ws(0, 0, 0);
+    issue_ws(0, 1, 0);
     issue_x(1, 1);
     issue_wc(1, 0, 1);
     issue_wc(1, 1, 1);
-#pragma unroll
-    for (int qq = 0; qq < 4; ++qq) issue_ws(1, qq, 1);
+    issue_ws(1, 0, 1);
+    issue_ws(1, 1, 1);
     // the scale table above is written with ordinary LDS stores
-    asm volatile("s_waitcnt vmcnt(10) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");
     {
       uint32_t sw[2];
-      read_w(0, 0, 0, 0, wv, sw);
+      read_w(0, 0, wv, sw);
       read_x(0, 0, bx);
       split_w(sw, sp);
       expand_w(wv, sp, 0, aw);
     }
-    for (int i = 0; i < n; i += 3) {
+    for (int i = 0; i < n; i += 6) {
       step(std::integral_constant<int, 0>{}, i);
-      if (i + 1 < n) step(std::integral_constant<int, 1>{}, i + 1);
-      if (i + 2 < n) step(std::integral_constant<int, 2>{}, i + 2);
+      if (i + 1 >= n) break;
+      step(std::integral_constant<int, 1>{}, i + 1);
+      if (i + 2 >= n) break;
+      step(std::integral_constant<int, 2>{}, i + 2);
+      if (i + 3 >= n) break;
+      step(std::integral_constant<int, 3>{}, i + 3);
+      if (i + 4 >= n) break;
+      step(std::integral_constant<int, 4>{}, i + 4);
+      if (i + 5 >= n) break;
+      step(std::integral_constant<int, 5>{}, i + 5);
     }
     // drain the repeated transfers before the workgroup can exit
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");

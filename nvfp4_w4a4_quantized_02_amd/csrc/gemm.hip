@@ -144,10 +144,12 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const uint4* __restrict__ 
   // slot lane%4 of the row, with piece (lane%4) ^ swz(row).  Pieces past the
   // end of a row (a group reaching past K) re-read the row's last 16 bytes.
   // W scales: the transfer of half hh fills (lanes 0..31) rows
-  // 128 hh + 16 wave + lane/2, dword lane%2 of the row (one dword per step
-  // of the group).  Rows past N repeat the last one (never stored).  These
-  // offsets are recomputed per transfer (a few integer operations) rather
-  // than held in registers.
+  // 128 hh + 16 wave + lane/2, dword slot lane%2 of the row holding the
+  // group's step (lane%2) ^ ((row >> 4) & 1) = (lane%2) ^ (wave & 1), so that
+  // rows 16 apart, read by one pass of the LDS, use different banks.  Rows
+  // past N repeat the last one (never stored).  These offsets are
+  // recomputed per transfer (a few integer operations) rather than held in
+  // registers.
   // LDS byte address of a place in sm: one address-space conversion for the
   // whole kernel, then integer offsets (a conversion per use would also test
   // the pointer for null every time)
@@ -177,7 +179,7 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const uint4* __restrict__ 
   auto issue_ws = [&](int g, int hh, int b) {
     const uint32_t goff = (uint32_t)(kb + 2 * (g < glast ? g : glast)) * 4u;
     const int row = 128 * hh + 16 * wave + (l32 >> 1);
-    const uint32_t dw = ((uint32_t)lane & 1u) * 4u;
+    const uint32_t dw = (((uint32_t)lane & 1u) ^ ((uint32_t)wave & 1u)) * 4u;
     const uint32_t off = (uint32_t)(row < nrows ? row : nrows - 1) * ks + min(goff + dw, ks - 4u);
     // the LDS address is wave-uniform: taken out of the divergent branch
     const uint32_t lds = __builtin_amdgcn_readfirstlane(soff(&sm.ws[b][(128 * hh + 16 * wave) * 2]));
@@ -215,7 +217,7 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const uint4* __restrict__ 
     for (int t = 0; t < 2; ++t) {
       const uint32_t row = wave_n * 64 + t * 32 + l32;
       wv[t] = cb[row * 4 + ((uint32_t)(2 * sp2 + h) ^ wc_swz(row))];
-      sw[t] = sb[row * 2 + (uint32_t)sp2] >> (16 * h);
+      sw[t] = sb[row * 2 + ((uint32_t)sp2 ^ ((row >> 4) & 1u))] >> (16 * h);
     }
   };
   auto split_w = [&](const uint32_t (&sw)[2], uint32_t (&sp)[2][2]) {

@@ -194,10 +194,12 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const uint4* __restrict__ 
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[t][u][r] = 0.0f;
 
-  // Scale-byte table: entry b holds what scale byte b becomes for the W
-  // expansion, so a scale costs one LDS read (the sign bit of a scale byte
-  // is ignored).
-  if (tid < 128) scale_lut[tid] = O::scale_bits((uint32_t)tid);
+  // What a scale byte becomes for the W expansion (the sign bit ignored).
+  // fp16 operands: the magnitude bits shifted into an fp16 pair, a few
+  // instructions, computed in place.  bf16 operands: the fp32 E4M3 value,
+  // longer to compute, so a table in LDS (entry b for byte b) is read
+  // instead.
+  if (kA16 && tid < 128) scale_lut[tid] = O::scale_bits((uint32_t)tid);
 
   // Operand fragments of sub-step j from X buffer b.
   auto read_x = [&](int b, int j, V (&bx)[4]) {
@@ -223,8 +225,13 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const uint4* __restrict__ 
   auto split_w = [&](const uint32_t (&sw)[2], uint32_t (&sp)[2][2]) {
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      sp[t][0] = scale_lut[sw[t] & 0x7Fu];
-      sp[t][1] = scale_lut[(sw[t] >> 8) & 0x7Fu];
+      if constexpr (kA16) {
+        sp[t][0] = scale_lut[sw[t] & 0x7Fu];
+        sp[t][1] = scale_lut[(sw[t] >> 8) & 0x7Fu];
+      } else {
+        sp[t][0] = O::scale_bits(sw[t] & 0x7Fu);
+        sp[t][1] = O::scale_bits((sw[t] >> 8) & 0x7Fu);
+      }
     }
   };
   auto expand_w = [&](const uint4 (&wv)[2], const uint32_t (&sp)[2][2], int j, V (&aw)[2]) {
@@ -307,7 +314,7 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const uint4* __restrict__ 
     issue_wc(1, 1, 1);
     issue_ws(1, 0, 1);
     issue_ws(1, 1, 1);
-    // the scale table above is written with ordinary LDS stores
+    // (bf16 operands) the scale table above is written with ordinary LDS stores
     asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");
     {
       uint32_t sw[2];

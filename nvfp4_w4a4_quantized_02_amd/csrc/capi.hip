@@ -185,6 +185,11 @@ size_t nvfp4_gemm_w4a16_workspace_size(int64_t M, int64_t N, int64_t K) {
   return partial_bytes(M, N, round_up(K, kGemmBK));
 }
 
+// One prepared row also keeps its packed codes (K/2 bytes) and scale bytes
+// (K/16) at the start of the workspace, where the absmax partials of larger
+// tensors go (one row needs none), for the FP4 GEMV of nvfp4_gemm_run.
+static bool keeps_row_codes(int64_t M, int64_t K) { return M == 1 && (uint64_t)K * 9u / 16u <= kWsGs; }
+
 nvfp4_status_t nvfp4_gemm_prepare(const void* x, nvfp4_dtype_t x_dtype, int64_t M, int64_t K, int64_t ld_x,
                                   void* workspace, size_t workspace_bytes, void* stream) {
   nvfp4_status_t st = check_input(x, x_dtype, M, K, ld_x);
@@ -199,7 +204,9 @@ nvfp4_status_t nvfp4_gemm_prepare(const void* x, nvfp4_dtype_t x_dtype, int64_t 
   float* gsx = (float*)((char*)workspace + kWsGs);
   void* x16 = (char*)workspace + kWsX16;
   int np = launch_amax(x, xb, M, K, ld_x, partials, s);
-  launch_quantize_f16(x, xb, M, K, ld_x, round_up(K, kGemmBK), partials, np, nullptr, x16, gsx, s);
+  uint8_t* q = keeps_row_codes(M, K) ? (uint8_t*)workspace : nullptr;
+  launch_quantize_f16(x, xb, M, K, ld_x, round_up(K, kGemmBK), partials, np, nullptr, x16, gsx, q,
+                      q ? q + K / 2 : nullptr, s);
   return launched();
 }
 
@@ -216,7 +223,9 @@ nvfp4_status_t nvfp4_gemm_prepare_static(const void* x, nvfp4_dtype_t x_dtype, i
   hipStream_t s = (hipStream_t)stream;
   float* gsx = (float*)((char*)workspace + kWsGs);
   void* x16 = (char*)workspace + kWsX16;
-  launch_quantize_f16(x, x_dtype == NVFP4_BF16, M, K, ld_x, round_up(K, kGemmBK), nullptr, 0, gs_x, x16, gsx, s);
+  uint8_t* q = keeps_row_codes(M, K) ? (uint8_t*)workspace : nullptr;
+  launch_quantize_f16(x, x_dtype == NVFP4_BF16, M, K, ld_x, round_up(K, kGemmBK), nullptr, 0, gs_x, x16, gsx, q,
+                      q ? q + K / 2 : nullptr, s);
   return launched();
 }
 
@@ -242,6 +251,9 @@ nvfp4_status_t nvfp4_gemm_run(int64_t M, int64_t K, const uint8_t* w_codes, cons
   const void* x16 = (const char*)workspace + kWsX16;
   void* wsv = workspace;
   const int64_t Kp = round_up(K, kGemmBK);
+  if (keeps_row_codes(M, K) &&
+      launch_gemv_m1_prepared((const uint8_t*)workspace, K, gsx, w_codes, w_scales, N, w_gs, y, yb, s))
+    return launched();
   if (M <= kGemvMaxM)
     launch_gemv(false, x16, (size_t)Kp * 2, M, K, w_codes, w_scales, N, gsx, w_gs, y, yb, ld_y, s);
   else
@@ -288,7 +300,8 @@ static bool fused_m1(const void* x, nvfp4_dtype_t x_dtype, int64_t M, int64_t K,
                      nvfp4_dtype_t y_dtype, void* workspace, void* stream) {
   if (M != 1 || x_dtype != NVFP4_BF16 || K == 0) return false;
   return launch_gemv_fused_m1(x, true, K, gs_x, w_codes, w_scales, N, w_gs, y, y_dtype == NVFP4_BF16,
-                              (char*)workspace + kWsX16, (float*)((char*)workspace + kWsGs), (hipStream_t)stream);
+                              (char*)workspace + kWsX16, (float*)((char*)workspace + kWsGs), (uint8_t*)workspace,
+                              (hipStream_t)stream);
 }
 
 nvfp4_status_t nvfp4_gemm(const void* x, nvfp4_dtype_t x_dtype, int64_t M, int64_t K, int64_t ld_x,

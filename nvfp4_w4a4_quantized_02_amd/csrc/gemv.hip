@@ -239,50 +239,54 @@ __global__ __launch_bounds__(64) void gemv_stream_kernel(const uint8_t* __restri
                    a[3] * scale);
 }
 
-// --------------------------------------------------- M == 1, one launch
-// The whole decode step for one bf16 activation row: its quantization
-// (tensor scale, block scales, codes, exactly as the quantize kernels do it)
-// and the GEMV, in one kernel.  A separate quantize launch costs the step
-// more than its work; here every workgroup quantizes the row (at most 8192
-// elements) into its own LDS while its first weight transfers are already in
-// flight.
+// --------------------------------------------------- M == 1, FP4 contraction
+// One activation row against W with both operands NVFP4: the contraction
+// runs on the FP4 MFMA (16x16x128, E2M1 operands with unit scales) over the
+// raw codes, so no weight element is converted: each output column of an
+// MFMA collects one 16-element block, and its exact sum is multiplied by the
+// block's two E4M3 scales afterwards (the product of two NVFP4 blocks, paper
+// "Why Gated DeltaNet Survives 4-Bit Quantization", section 2 "NVFP4").  Only
+// the fp32 accumulation over blocks rounds, as in every other contraction
+// kernel, in another order.
 //
-// With both operands quantized, the contraction runs on the FP4 MFMA
-// (16x16x128, E2M1 operands with unit scales) over the raw codes, so no
-// weight element is converted: each output column of an MFMA collects one
-// 16-element block, and its exact sum is multiplied by the block's two E4M3
-// scales afterwards (the product of two NVFP4 blocks, paper "Why Gated
-// DeltaNet Survives 4-Bit Quantization", section 2 "NVFP4").  Only the fp32
-// accumulation over blocks rounds, as in every other contraction kernel, in
-// another order.
+// The row comes either as bf16, quantized by the kernel itself (the whole
+// decode step in one launch; the tensor scale from its absmax, or given), or
+// already quantized: the packed codes and scale bytes nvfp4_gemm_prepare
+// leaves at the start of its workspace for one row, with gs_x.  A separate
+// quantize launch costs the step more than its work; here every workgroup
+// quantizes the row (at most 8192 elements) into its own LDS while its first
+// weight transfers are already in flight.
 //
 // A workgroup is kFuWaves waves, one 16-row weight tile each, sharing the
-// quantized row in LDS.  The row's 16-element blocks are dealt to the waves
-// in sets of 64 (set j to wave j % kFuWaves; lane l takes block 64 j + l).
-// Order of work in a wave:
-//   1. direct transfers into LDS, in this order: the bf16 bytes of its own
-//      sets of blocks (into the row's LDS region at their row offsets); its
+// quantized row in LDS (codes, 8 B a block, then the scale bytes).  The
+// row's 16-element blocks are dealt to the waves in sets of 64 (set j to
+// wave j % kFuWaves; lane l takes block 64 j + l).  Order of work in a wave:
+//   1. direct transfers into LDS, in this order: its part of the row (bf16:
+//      the bytes of its own sets, at their row offsets; prepared: 1 KB
+//      pieces q with q % kFuWaves = wave of the codes and scale bytes); its
 //      tile's scale bytes (16 rows x K/16, contiguous); the first D chunks of
-//      codes (16 rows x 128 B per chunk, two transfers filling 8 lines each).
-//      Transfers complete in the order issued, so the wave then waits for
-//      its row bytes alone;
-//   2. the absmax of its blocks (exact: integer max of the magnitudes),
-//      combined over the wave and, through LDS and a barrier, over the
-//      workgroup; the tensor scale RN(amax / 2688) (or the given one);
-//   3. the encode of its blocks into codes, scale bytes and their E4M3
-//      values, written over the row's bf16 bytes (after a barrier: they
-//      overlap other waves' blocks);
-//   4. one barrier, then the streaming loop below;
-//   5. workgroup 0 writes the quantized row to the workspace as fp16 values
-//      E2M1 * E4M3 and the tensor scale, where nvfp4_gemm_prepare would
-//      leave them.  Stored last: a store can be acknowledged before older
-//      loads return, so stores issued while loads are in flight would let a
-//      compiler-counted wait for those loads pass early.
+//      codes (16 rows x 128 B per chunk, two transfers filling 8 lines
+//      each).  Transfers complete in the order issued, so the wave then
+//      waits for its row bytes alone;
+//   2. bf16 row: the absmax of its blocks (exact: integer max of the
+//      magnitudes), combined over the wave and, through LDS and a barrier,
+//      over the workgroup; the tensor scale RN(amax / 2688) (or the given
+//      one); the encode of its blocks into codes and scale bytes, written
+//      over the row's bf16 bytes (after a barrier: they overlap other waves'
+//      blocks).  Prepared row: a barrier (the pieces of the other waves);
+//   3. one barrier, then the streaming loop below;
+//   4. bf16 row: workgroup 0 writes the quantized row to the workspace as
+//      nvfp4_gemm_prepare would (the fp16 values E2M1 * E4M3, the codes and
+//      scale bytes, the tensor scale).  Stored last: a store can be
+//      acknowledged before older loads return, so stores issued while loads
+//      are in flight would let a compiler-counted wait for those loads pass
+//      early.
 typedef int i32x8 __attribute__((ext_vector_type(8)));  // operands of the scaled MFMAs
 constexpr int kFuWaves = 3;
 constexpr int kFuDepth = 4;
+enum FuMode { kFuDynamic = 0, kFuGiven = 1, kFuPrepared = 2 };
 
-template <int NCK, bool kGiven, bool kYBf16>
+template <int NCK, int kMode, bool kYBf16>
 __global__ __launch_bounds__(64 * kFuWaves) void gemv_fused_m1_kernel(const uint8_t* __restrict__ x,
                                                                       const float* __restrict__ gs_in,
                                                                       const uint8_t* __restrict__ wc,
@@ -290,37 +294,47 @@ __global__ __launch_bounds__(64 * kFuWaves) void gemv_fused_m1_kernel(const uint
                                                                       int tiles, const float* __restrict__ gsw_p,
                                                                       uint8_t* __restrict__ y,
                                                                       uint4* __restrict__ x16_out,
-                                                                      float* __restrict__ gsx_out) {
-  using O = Op<false>;
+                                                                      float* __restrict__ gsx_out,
+                                                                      uint8_t* __restrict__ q_out) {
   constexpr int K = NCK * 256, NB = K / 16, BPL = (NB + 63) / 64, D = kFuDepth;
   static_assert(NB % 64 == 0, "whole sets of 64 blocks");
   constexpr uint32_t kh = K / 2, ks = K / 16;
   constexpr uint32_t kScBytes = (16u * ks + 1023u) / 1024u * 1024u;
-  // row [2K B: bf16, then codes | scale values | scale bytes] | ring [wave][D][2048 B] |
+  constexpr uint32_t kQPieces = (kh + ks + 1023u) / 1024u;  // prepared codes and scale bytes, 1 KB pieces
+  constexpr uint32_t kRowBytes = kMode == kFuPrepared ? kQPieces * 1024u : 2u * K;
+  // row [kRowBytes: bf16, then codes | scale bytes] | ring [wave][D][2048 B] |
   // scales [wave][kScBytes] | wave maxima [4]
   extern __shared__ uint4 smem[];
   const int lane = threadIdx.x & 63, l16 = lane & 15, g = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));  // uniform: scalar bases
   const int tile_raw = blockIdx.x * kFuWaves + wave;
   const int tile = tile_raw < tiles ? tile_raw : tiles - 1;  // a surplus wave redoes the last tile, unstored
-  uint4* xs = smem;
-  uint8_t* ring = reinterpret_cast<uint8_t*>(smem + K / 8) + (size_t)wave * D * kGvChunkCodes;
-  uint8_t* sc_lds = reinterpret_cast<uint8_t*>(smem + K / 8) + (size_t)kFuWaves * D * kGvChunkCodes +
-                    (size_t)wave * kScBytes;
-  uint32_t* wmax = reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(smem + K / 8) +
-                                               (size_t)kFuWaves * (D * kGvChunkCodes + kScBytes));
+  uint8_t* xrow = reinterpret_cast<uint8_t*>(smem);
+  uint8_t* ring = xrow + kRowBytes + (size_t)wave * D * kGvChunkCodes;
+  uint8_t* sc_lds = xrow + kRowBytes + (size_t)kFuWaves * D * kGvChunkCodes + (size_t)wave * kScBytes;
+  uint32_t* wmax = reinterpret_cast<uint32_t*>(xrow + kRowBytes + (size_t)kFuWaves * (D * kGvChunkCodes + kScBytes));
+  uint2* xcodes = reinterpret_cast<uint2*>(xrow);  // [NB]
+  uint8_t* xsb = xrow + kh;                         // [NB]
 
-  // 1. transfers: this wave's sets of the row (set j = bytes 2048 j ..
-  //    2048 j + 2047, two 1 KB transfers), the scale bytes (pieces past the
-  //    end re-read the last piece; their LDS bytes are never read), the first
-  //    D chunks of codes
+  // 1. transfers: this wave's part of the row, the scale bytes (pieces past
+  //    the end re-read the last piece; their LDS bytes are never read), the
+  //    first D chunks of codes
   {
-    const uint32_t xs0 = lds_addr(xs);
+    const uint32_t x0 = lds_addr(xrow);
+    if constexpr (kMode == kFuPrepared) {
 #pragma unroll
-    for (int j = 0; j < BPL; ++j) {
-      if (j % kFuWaves != wave) continue;
-      lds_dma16(x, 2048u * j + 16u * (uint32_t)lane, xs0 + 2048u * j);
-      lds_dma16(x, 2048u * j + 1024u + 16u * (uint32_t)lane, xs0 + 2048u * j + 1024u);
+      for (uint32_t q = 0; q < kQPieces; ++q) {
+        if (q % kFuWaves != (uint32_t)wave) continue;
+        lds_dma16(x, 1024u * q + 16u * (uint32_t)lane, x0 + 1024u * q);
+      }
+    } else {
+      // set j = bytes 2048 j .. 2048 j + 2047 of the bf16 row, two 1 KB transfers
+#pragma unroll
+      for (int j = 0; j < BPL; ++j) {
+        if (j % kFuWaves != wave) continue;
+        lds_dma16(x, 2048u * j + 16u * (uint32_t)lane, x0 + 2048u * j);
+        lds_dma16(x, 2048u * j + 1024u + 16u * (uint32_t)lane, x0 + 2048u * j + 1024u);
+      }
     }
   }
   const int n0 = tile * 16;
@@ -356,74 +370,70 @@ __global__ __launch_bounds__(64 * kFuWaves) void gemv_fused_m1_kernel(const uint
   // them may still be in flight)
   wait_vmcnt<(int)(kScBytes / 1024u) + 2 * D>();
 
-  // 2. this wave's blocks, their absmax, the tensor scale
-  uint32_t xw[BPL][BlockWords<true>::n];
-#pragma unroll
-  for (int j = 0; j < BPL; ++j) {
-    if (j % kFuWaves != wave) continue;
-    const uint4 a = xs[2 * (lane + 64 * j)], b = xs[2 * (lane + 64 * j) + 1];
-    xw[j][0] = a.x; xw[j][1] = a.y; xw[j][2] = a.z; xw[j][3] = a.w;
-    xw[j][4] = b.x; xw[j][5] = b.y; xw[j][6] = b.z; xw[j][7] = b.w;
-  }
+  // 2. the quantized row
   float gs;
-  if constexpr (kGiven) {
+  if constexpr (kMode == kFuPrepared) {
     gs = *gs_in;
   } else {
-    uint32_t m = 0;
+    uint32_t xw[BPL][BlockWords<true>::n];
+    const uint4* xs = reinterpret_cast<const uint4*>(xrow);
 #pragma unroll
     for (int j = 0; j < BPL; ++j) {
       if (j % kFuWaves != wave) continue;
-      const uint32_t a = words_absmax_bits<true>(xw[j]);
-      m = m > a ? m : a;
+      const uint4 a = xs[2 * (lane + 64 * j)], b = xs[2 * (lane + 64 * j) + 1];
+      xw[j][0] = a.x; xw[j][1] = a.y; xw[j][2] = a.z; xw[j][3] = a.w;
+      xw[j][4] = b.x; xw[j][5] = b.y; xw[j][6] = b.z; xw[j][7] = b.w;
     }
-    m = wave_max_u32(m);
-    if (lane == 0) wmax[wave] = m;
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if constexpr (kMode == kFuGiven) {
+      gs = *gs_in;
+    } else {
+      uint32_t m = 0;
 #pragma unroll
-    for (int w = 0; w < kFuWaves; ++w) m = m > wmax[w] ? m : wmax[w];
-    gs = tensor_scale(__uint_as_float(m));
-  }
-
-  // 3. encode this wave's blocks: codes (8 B a block) at the front of the
-  //    row's LDS region, E4M3 values of the scales (fp32) after them, the
-  //    scale bytes after those.  These overwrite bf16 bytes of other blocks,
-  //    so every wave has read its blocks first (the barrier above, or this
-  //    one with a given scale).
-  if constexpr (kGiven) asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  uint8_t* xrow = reinterpret_cast<uint8_t*>(xs);
-  uint2* xcodes = reinterpret_cast<uint2*>(xrow);                 // [NB]
-  float* xsc = reinterpret_cast<float*>(xrow + K / 2);             // [NB]
-  uint8_t* xsb = xrow + K / 2 + 4 * NB;                            // [NB]
-  const FastScale fsc = fast_scale(gs);
+      for (int j = 0; j < BPL; ++j) {
+        if (j % kFuWaves != wave) continue;
+        const uint32_t a = words_absmax_bits<true>(xw[j]);
+        m = m > a ? m : a;
+      }
+      m = wave_max_u32(m);
+      if (lane == 0) wmax[wave] = m;
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 #pragma unroll
-  for (int j = 0; j < BPL; ++j) {
-    if (j % kFuWaves != wave) continue;
-    const int b = lane + 64 * j;
-    float xv[16];
-    words_to_floats<true>(xw[j], xv);
-    uint32_t sb, lo, hi;
-    if (!encode_block_fast(xv, words_absmax_bits<true>(xw[j]), fsc, sb, lo, hi))
-      sb = encode_block_exact(xv, gs, lo, hi);
-    xcodes[b] = make_uint2(lo, hi);
-    xsc[b] = __builtin_amdgcn_cvt_f32_fp8((int)sb, 0);
-    xsb[b] = (uint8_t)sb;
+      for (int w = 0; w < kFuWaves; ++w) m = m > wmax[w] ? m : wmax[w];
+      gs = tensor_scale(__uint_as_float(m));
+    }
+    // The codes and scale bytes overwrite bf16 bytes of other blocks, so
+    // every wave has read its blocks first (the barrier above, or this one
+    // with a given scale).
+    if constexpr (kMode == kFuGiven) asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    const FastScale fsc = fast_scale(gs);
+#pragma unroll
+    for (int j = 0; j < BPL; ++j) {
+      if (j % kFuWaves != wave) continue;
+      const int b = lane + 64 * j;
+      float xv[16];
+      words_to_floats<true>(xw[j], xv);
+      uint32_t sb, lo, hi;
+      if (!encode_block_fast(xv, words_absmax_bits<true>(xw[j]), fsc, sb, lo, hi))
+        sb = encode_block_exact(xv, gs, lo, hi);
+      xcodes[b] = make_uint2(lo, hi);
+      xsb[b] = (uint8_t)sb;
+    }
   }
-  // the quantized row complete and visible to every wave (the transfers in
-  // flight are not waited for: a bare barrier, no fence)
+  // 3. the quantized row complete and visible to every wave (the transfers
+  //    in flight are not waited for: a bare barrier, no fence)
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 
-  // 4. the streaming loop.  Per chunk (256 k), two FP4 MFMAs 16x16x128 on
-  //    the raw codes (E2M1 x E2M1, unit scales) give, in output column c,
-  //    the dot product of each weight row with block c of the chunk alone:
-  //    MFMA H takes k 128H .. 128H+127 of the chunk, lane group g k 32g ..
-  //    32g+31 of that (weight piece 4H + g of the row); the activation
-  //    operand of lane (c, g) holds the codes of block c in its half c % 2
-  //    when g = (c % 8) / 2 and c / 8 = H, zeros elsewhere.  The products and
-  //    their 16-term sums are multiples of 1/4 below 600, exact in fp32, and
-  //    so is each sum times the two block scales (at most 12 + 4 + 4
-  //    significant bits): lane (c, g) adds them to the partial sums of rows
-  //    4g .. 4g+3 in fp32 in chunk order, and the 16 lanes of a row group are
-  //    added at the end in a fixed tree.
+  // The streaming loop.  Per chunk (256 k), two FP4 MFMAs 16x16x128 on the
+  // raw codes (E2M1 x E2M1, unit scales) give, in output column c, the dot
+  // product of each weight row with block c of the chunk alone: MFMA H takes
+  // k 128H .. 128H+127 of the chunk, lane group g k 32g .. 32g+31 of that
+  // (weight piece 4H + g of the row); the activation operand of lane (c, g)
+  // holds the codes of block c in its half c % 2 when g = (c % 8) / 2 and
+  // c / 8 = H, zeros elsewhere.  The products and their 16-term sums are
+  // multiples of 1/4 below 600, exact in fp32, and so is each sum times the
+  // two block scales (at most 12 + 4 + 4 significant bits): lane (c, g) adds
+  // them to the partial sums of rows 4g .. 4g+3 in fp32 in chunk order, and
+  // the 16 lanes of a row group are added at the end in a fixed tree.
   const uint32_t sw = (uint32_t)(l16 & 7);
   const uint32_t apos0 = (uint32_t)l16 * 128u + 16u * ((uint32_t)g ^ sw);
   const uint32_t apos1 = (uint32_t)l16 * 128u + 16u * ((4u + (uint32_t)g) ^ sw);
@@ -441,7 +451,7 @@ __global__ __launch_bounds__(64 * kFuWaves) void gemv_fused_m1_kernel(const uint
     const uint4 a0 = *reinterpret_cast<const uint4*>(slot + apos0);
     const uint4 a1 = *reinterpret_cast<const uint4*>(slot + apos1);
     const uint2 xv = xcodes[16 * c + l16];
-    const float sx = xsc[16 * c + l16];
+    const uint32_t xsc_b = xsb[16 * c + l16];
     uint32_t swb[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) swb[j] = sc_lds[srow + (uint32_t)j * ks + 16u * (uint32_t)c];
@@ -458,6 +468,7 @@ __global__ __launch_bounds__(64 * kFuWaves) void gemv_fused_m1_kernel(const uint
     floatx4 acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A0, B0, floatx4{0.0f, 0.0f, 0.0f, 0.0f}, 4, 4, 0,
                                                                     127, 0, 127);
     acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A1, B1, acc, 4, 4, 0, 127, 0, 127);
+    const float sx = __builtin_amdgcn_cvt_f32_fp8((int)xsc_b, 0);
 #pragma unroll
     for (int j = 0; j < 4; ++j)
       part[j] = __builtin_fmaf(acc[j] * sx, __builtin_amdgcn_cvt_f32_fp8((int)(swb[j] & 0x7Fu), 0), part[j]);
@@ -472,16 +483,48 @@ __global__ __launch_bounds__(64 * kFuWaves) void gemv_fused_m1_kernel(const uint
     const float scale = gs * (*gsw_p);
     store4<kYBf16>(y, n0 + 4 * g, N, part[0] * scale, part[1] * scale, part[2] * scale, part[3] * scale);
   }
-  // 5. the quantized row for the workspace, as fp16 values E2M1 * E4M3
-  if (blockIdx.x == 0) {
-    for (int i = (int)threadIdx.x; i < K / 8; i += 64 * kFuWaves) {
-      const uint2 cw = xcodes[i >> 1];
-      uint32_t e[4];
-      expand8((i & 1) ? cw.y : cw.x, scale_f16x2(xsb[i >> 1]), e);
-      x16_out[i] = make_uint4(e[0], e[1], e[2], e[3]);
+  // 4. the quantized row for the workspace: fp16 values E2M1 * E4M3, codes
+  //    and scale bytes, tensor scale
+  if constexpr (kMode != kFuPrepared) {
+    if (blockIdx.x == 0) {
+      for (int i = (int)threadIdx.x; i < K / 8; i += 64 * kFuWaves) {
+        const uint2 cw = xcodes[i >> 1];
+        uint32_t e[4];
+        expand8((i & 1) ? cw.y : cw.x, scale_f16x2(xsb[i >> 1]), e);
+        x16_out[i] = make_uint4(e[0], e[1], e[2], e[3]);
+      }
+      for (int i = (int)threadIdx.x; i < (int)(kh + ks) / 16; i += 64 * kFuWaves)
+        reinterpret_cast<uint4*>(q_out)[i] = reinterpret_cast<const uint4*>(xrow)[i];
+      if (threadIdx.x == 0) *gsx_out = gs;
     }
-    if (threadIdx.x == 0) *gsx_out = gs;
   }
+}
+
+static size_t fused_m1_lds(int64_t K, bool prepared) {
+  const size_t kh = (size_t)K / 2, ks = (size_t)K / 16;
+  const size_t row = prepared ? (kh + ks + 1023u) / 1024u * 1024u : (size_t)K * 2u;
+  return row + (size_t)kFuWaves * kFuDepth * kGvChunkCodes +
+         (size_t)kFuWaves * ((16u * ks + 1023u) / 1024u * 1024u) +  // 16 rows of K/16 scale bytes
+         16u;                                                        // the waves' maxima
+}
+
+template <int kMode>
+static void fused_m1_go(int64_t K, const void* x, const float* gs_in, const uint8_t* wc, const uint8_t* ws,
+                        int64_t N, const float* gsw, void* y, bool y_bf16, void* x16_out, float* gsx_out,
+                        uint8_t* q_out, hipStream_t s) {
+  const int tiles = (int)((N + 15) / 16);
+  const int grid = (tiles + kFuWaves - 1) / kFuWaves;
+  const size_t lds = fused_m1_lds(K, kMode == kFuPrepared);
+  auto go = [&](auto nc, auto yb) {
+    gemv_fused_m1_kernel<decltype(nc)::value, kMode, decltype(yb)::value><<<grid, 64 * kFuWaves, lds, s>>>(
+        (const uint8_t*)x, gs_in, wc, ws, (int)N, tiles, gsw, (uint8_t*)y, (uint4*)x16_out, gsx_out, q_out);
+  };
+  auto by_y = [&](auto nc) {
+    if (y_bf16) go(nc, std::true_type());
+    else go(nc, std::false_type());
+  };
+  if (K == 5120) by_y(std::integral_constant<int, 20>());
+  else by_y(std::integral_constant<int, 16>());
 }
 
 // One-launch decode step for M == 1 when the row is bf16 and its length has
@@ -489,28 +532,21 @@ __global__ __launch_bounds__(64 * kFuWaves) void gemv_fused_m1_kernel(const uint
 // and runs the GEMV in two launches).
 bool launch_gemv_fused_m1(const void* x, bool x_bf16, int64_t K, const float* gs_in, const uint8_t* wc,
                           const uint8_t* ws, int64_t N, const float* gsw, void* y, bool y_bf16, void* x16_out,
-                          float* gsx_out, hipStream_t s) {
+                          float* gsx_out, uint8_t* q_out, hipStream_t s) {
   if (!x_bf16 || (K != 4096 && K != 5120)) return false;
-  const int tiles = (int)((N + 15) / 16);
-  const int grid = (tiles + kFuWaves - 1) / kFuWaves;
-  const size_t lds = (size_t)K * 2u + (size_t)kFuWaves * kFuDepth * kGvChunkCodes +
-                     (size_t)kFuWaves * (((size_t)K + 1023u) / 1024u * 1024u) +  // 16 rows of K/16 scale bytes
-                     16u;                                                          // the waves' maxima
-  auto go = [&](auto nc, auto gv, auto yb) {
-    gemv_fused_m1_kernel<decltype(nc)::value, decltype(gv)::value, decltype(yb)::value>
-        <<<grid, 64 * kFuWaves, lds, s>>>((const uint8_t*)x, gs_in, wc, ws, (int)N, tiles, gsw, (uint8_t*)y,
-                                          (uint4*)x16_out, gsx_out);
-  };
-  auto by_y = [&](auto nc, auto gv) {
-    if (y_bf16) go(nc, gv, std::true_type());
-    else go(nc, gv, std::false_type());
-  };
-  auto by_gs = [&](auto nc) {
-    if (gs_in) by_y(nc, std::true_type());
-    else by_y(nc, std::false_type());
-  };
-  if (K == 5120) by_gs(std::integral_constant<int, 20>());
-  else by_gs(std::integral_constant<int, 16>());
+  if (gs_in)
+    fused_m1_go<kFuGiven>(K, x, gs_in, wc, ws, N, gsw, y, y_bf16, x16_out, gsx_out, q_out, s);
+  else
+    fused_m1_go<kFuDynamic>(K, x, gs_in, wc, ws, N, gsw, y, y_bf16, x16_out, gsx_out, q_out, s);
+  return true;
+}
+
+// The GEMV for one prepared row (codes at q, scale bytes at q + K/2, tensor
+// scale *gsx) when its length has an instantiation; false otherwise.
+bool launch_gemv_m1_prepared(const uint8_t* q, int64_t K, const float* gsx, const uint8_t* wc, const uint8_t* ws,
+                             int64_t N, const float* gsw, void* y, bool y_bf16, hipStream_t s) {
+  if (K != 4096 && K != 5120) return false;
+  fused_m1_go<kFuPrepared>(K, q, gsx, wc, ws, N, gsw, y, y_bf16, nullptr, nullptr, nullptr, s);
   return true;
 }
 

@@ -117,9 +117,11 @@ int launch_amax(const void* x, bool bf16, int64_t rows, int64_t K, int64_t ld, u
 void launch_quantize_packed(const void* x, bool bf16, int64_t rows, int64_t K, int64_t ld,
                             const uint32_t* partials, int npartials, const float* gs_in, uint8_t* codes,
                             uint8_t* scales, float* gs, hipStream_t s);
+// codes/scales (may be null): the small-tensor kernel (at most 8192 blocks)
+// also writes the packed codes and scale bytes there.
 void launch_quantize_f16(const void* x, bool bf16, int64_t rows, int64_t K, int64_t ld, int64_t Kp,
                          const uint32_t* partials, int npartials, const float* gs_in, void* x16, float* gs,
-                         hipStream_t s);
+                         uint8_t* codes, uint8_t* scales, hipStream_t s);
 void launch_fill_f32(float* p, float v, hipStream_t s);
 void launch_copy_f32(float* p, const float* v, hipStream_t s);
 void launch_dequant(const uint8_t* codes, const uint8_t* scales, const float* gs, int64_t rows, int64_t K,
@@ -154,13 +156,19 @@ void launch_gemv_fp8w(bool a8, const void* x, size_t ld_x_bytes, int64_t M, int6
 constexpr int64_t kFp8GemvMaxK = 5120;
 
 // The W4A4 decode step for one activation row in one launch: quantize x
-// ([1, K], bf16 or fp32; with gs_in given, that tensor scale) and contract
-// with W.  Also writes the fp16 operand and the tensor scale to x16_out /
-// gsx_out, as nvfp4_gemm_prepare would.  Returns false (nothing launched) for
-// a K it has no form for.
+// ([1, K], bf16; with gs_in given, that tensor scale) and contract with W.
+// Also writes what nvfp4_gemm_prepare would: the fp16 operand to x16_out,
+// the tensor scale to gsx_out, the packed codes and scale bytes to q_out
+// (K/2 + K/16 bytes).  Returns false (nothing launched) for a K it has no
+// form for.
 bool launch_gemv_fused_m1(const void* x, bool x_bf16, int64_t K, const float* gs_in, const uint8_t* wc,
                           const uint8_t* ws, int64_t N, const float* gsw, void* y, bool y_bf16, void* x16_out,
-                          float* gsx_out, hipStream_t s);
+                          float* gsx_out, uint8_t* q_out, hipStream_t s);
+// The GEMV for one prepared row: its packed codes at q, its scale bytes at
+// q + K/2, its tensor scale at gsx.  Returns false (nothing launched) for a
+// K it has no form for.
+bool launch_gemv_m1_prepared(const uint8_t* q, int64_t K, const float* gsx, const uint8_t* wc, const uint8_t* ws,
+                             int64_t N, const float* gsw, void* y, bool y_bf16, hipStream_t s);
 
 void launch_gemv(bool a16, const void* x, size_t ld_x_bytes, int64_t M, int64_t K, const uint8_t* wc,
                  const uint8_t* ws, int64_t N, const float* gsx, const float* gsw, void* y, bool y_bf16,

@@ -385,7 +385,8 @@ __global__ __launch_bounds__(kThreads) void quantize_small_kernel(const uint8_t*
     expand8(hi, q2, e1);
     x16[(size_t)b * 2u] = make_uint4(e0[0], e0[1], e0[2], e0[3]);
     x16[(size_t)b * 2u + 1u] = make_uint4(e1[0], e1[1], e1[2], e1[3]);
-  } else {
+  }
+  if (!kF16 || codes) {  // the fp16 form may also keep the packed codes and scale bytes
     *reinterpret_cast<uint2*>(codes + (size_t)b * 8u) = make_uint2(lo, hi);
     scales[b] = (uint8_t)sb;
   }
@@ -570,8 +571,8 @@ void launch_quantize_packed(const void* x, bool bf16, int64_t rows, int64_t K, i
 
 void launch_quantize_f16(const void* x, bool bf16, int64_t rows, int64_t K, int64_t ld, int64_t Kp,
                          const uint32_t* partials, int npartials, const float* gs_in, void* x16, float* gs,
-                         hipStream_t s) {
-  launch_quantize<true>(x, bf16, rows, K, ld, Kp, partials, npartials, gs_in, nullptr, nullptr, x16, gs, s);
+                         uint8_t* codes, uint8_t* scales, hipStream_t s) {
+  launch_quantize<true>(x, bf16, rows, K, ld, Kp, partials, npartials, gs_in, codes, scales, x16, gs, s);
 }
 
 void launch_fill_f32(float* p, float v, hipStream_t s) { fill_f32_kernel<<<1, 1, 0, s>>>(p, v); }

@@ -20,7 +20,7 @@ void launch_quantize_packed(const void*, bool, int64_t, int64_t, int64_t, const 
   launched("quantize_packed");
 }
 void launch_quantize_f16(const void*, bool, int64_t, int64_t, int64_t, int64_t, const uint32_t*, int, const float*,
-                         void*, float*, hipStream_t) {
+                         void*, float*, uint8_t*, uint8_t*, hipStream_t) {
   launched("quantize_f16");
 }
 void launch_fill_f32(float*, float, hipStream_t) { launched("fill_f32"); }
@@ -54,8 +54,12 @@ void launch_gemv(bool, const void*, size_t, int64_t, int64_t, const uint8_t*, co
   launched("gemv");
 }
 bool launch_gemv_fused_m1(const void*, bool, int64_t, const float*, const uint8_t*, const uint8_t*, int64_t,
-                          const float*, void*, bool, void*, float*, hipStream_t) {
+                          const float*, void*, bool, void*, float*, uint8_t*, hipStream_t) {
   launched("gemv_fused_m1");
+}
+bool launch_gemv_m1_prepared(const uint8_t*, int64_t, const float*, const uint8_t*, const uint8_t*, int64_t,
+                             const float*, void*, bool, hipStream_t) {
+  launched("gemv_m1_prepared");
 }
 
 }  // namespace nvfp4

@@ -11,8 +11,9 @@ E4M3 scale per 16 elements, the product of the two NVFP4 operands):
     by handing the same values over as fp32; the two paths add the same
     exact block products in different orders, so only the gate binds them;
   * the workspace left as nvfp4_gemm_prepare leaves it: gs_x (byte 8192)
-    with the oracle's bits and the fp16 operand E2M1 * E4M3 (from byte
-    8448) equal to the one built from the oracle's codes and scale bytes.
+    with the oracle's bits, the fp16 operand E2M1 * E4M3 (from byte 8448)
+    equal to the one built from the oracle's codes and scale bytes, and the
+    oracle's packed codes and scale bytes from byte 0.
 Shapes cover a single tile (one wave of the three idle), ragged N, an odd
 tile count, and the full fused gate/up weight; inputs include rows on or
 next to every E2M1 and scale-byte rounding tie, and calibrated scales."""
@@ -22,7 +23,7 @@ import torch
 
 import workloads
 from parity import check_gemm, to_gpu, to_np
-from test_gpu_prepare import WS_GS, WS_X16, _expected_f16_bits
+from test_gpu_prepare import WS_GS, WS_X16, _expected_f16_bits, check_row_codes
 from test_gpu_quantize import _scale_tie_tensor, _tie_tensor
 
 pytestmark = pytest.mark.gpu
@@ -68,6 +69,7 @@ def _check_case(nv, orc, xb, w_host, w_dev, out, what, gs=None):
     x16 = wsb[WS_X16:WS_X16 + 2 * K].view(np.uint16).reshape(1, K)
     exp = _expected_f16_bits(orc, oc, os_)
     assert np.array_equal(x16, exp), "%s: %d fp16 operand values differ" % (what, int((x16 != exp).sum()))
+    check_row_codes(wsb, oc, os_, what)
     ref = orc.gemm_exact(oc, os_, og, wc, ws, gsw)
     check_gemm(y, ref, out == "bf16", what + " (one launch)")
     check_gemm(y2, ref, out == "bf16", what + " (two launches)")

@@ -11,6 +11,10 @@ have the oracle's bits (paper "Why Gated DeltaNet Survives 4-Bit
 Quantization", section 2 "NVFP4": activations quantized on the fly to E2M1
 with an E4M3 scale per 16 and one FP32 tensor scale).
 
+A prepared single row (M = 1, K <= 14563) also keeps its packed codes (K/2
+bytes from byte 0) and scale bytes (K/16 bytes after them), which the one-row
+FP4 GEMV contracts directly; those must equal the oracle's bytes.
+
 Cases cover every instantiation of the quantize kernels that writes this
 form: the one-launch kernel with one workgroup (absmax from its own blocks,
 M <= 3 at K = 5120) and with several, the two-pass absmax + encode kernels,
@@ -46,8 +50,13 @@ def _expected_f16_bits(orc, codes, scales):
     return val.astype(np.float16).view(np.uint16)
 
 
+def keeps_row_codes(M, K):
+    return M == 1 and K * 9 // 16 <= WS_GS
+
+
 def _prepared(nv, x: np.ndarray, gs=None):
-    """Run prepare on the GPU; return (gs_x bits, fp16 operand bits [M, K])."""
+    """Run prepare on the GPU; return (gs_x bits, fp16 operand bits [M, K],
+    workspace bytes)."""
     M, K = x.shape
     xg = to_gpu(x)
     x_gs = None if gs is None else torch.tensor([float(gs)], dtype=torch.float32, device=xg.device)
@@ -56,13 +65,24 @@ def _prepared(nv, x: np.ndarray, gs=None):
     ws = prep.ws.cpu().numpy()
     gbits = ws[WS_GS:WS_GS + 4].view(np.uint32)[0]
     x16 = ws[WS_X16:WS_X16 + M * K * 2].view(np.uint16).reshape(M, K)
-    return gbits, x16
+    return gbits, x16, ws
+
+
+def check_row_codes(ws, oc, os_, what):
+    """One prepared row: packed codes from byte 0, scale bytes after them."""
+    K = oc.shape[1] * 2
+    codes = ws[:K // 2].reshape(1, K // 2)
+    scales = ws[K // 2:K // 2 + K // 16].reshape(1, K // 16)
+    assert np.array_equal(codes, oc), "%s: %d code bytes differ" % (what, int((codes != oc).sum()))
+    assert np.array_equal(scales, os_), "%s: %d scale bytes differ" % (what, int((scales != os_).sum()))
 
 
 def _check(nv, orc, x, what, gs=None):
     print("case: prepare", what, x.shape, x.dtype, "given gs" if gs is not None else "", flush=True)
-    gbits, x16 = _prepared(nv, x, gs)
+    gbits, x16, ws = _prepared(nv, x, gs)
     oc, os_, og = orc.quantize(x, gs=gs)
+    if keeps_row_codes(*x.shape):
+        check_row_codes(ws, oc, os_, what)
     assert gbits == np.float32(og).view(np.uint32), "%s: gs_x %r vs %r" % (
         what, np.uint32(gbits).view(np.float32), og)
     exp = _expected_f16_bits(orc, oc, os_)

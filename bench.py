@@ -389,8 +389,8 @@ def secondary(torch, np, nv, workloads, to_gpu, dev, args):
             nbytes = wbytes + M * K * 2 + M * N * 2
             gbs = nbytes / (t["w4a4"] * 1e-3) / 1e9
             kgbs = nbytes / (t["gemv"] * 1e-3) / 1e9
-            if M == 1:   # one launch does the whole step: that kernel is the one on the roofline
-                kname, kkey, kgbs = "nvfp4_gemm: gemv_fused_m1_kernel (quantize + GEMV)", "gemv_fused_m1", gbs
+            if M <= 4:   # one launch does the whole step: that kernel is the one on the roofline
+                kname, kkey, kgbs = "nvfp4_gemm: gemv_fp4_kernel (quantize + FP4 GEMV)", "gemv_fp4_m%d" % M, gbs
             else:
                 kname, kkey = "nvfp4_gemm_run: gemv kernel", "gemv_m%d" % M
             res.append({"metric": "decode GEMV GB/s at M=%d" % M, "value": round(gbs, 1), "unit": "GB/s",

@@ -213,9 +213,11 @@ nvfp4_status_t nvfp4_gemm(const void *x, nvfp4_dtype_t x_dtype, int64_t M, int64
  * A prepared workspace holds, at byte 8192, gs_x (one float) and, from byte
  * 8448, the quantized activations as fp16 values E2M1(code) * E4M3(scale)
  * (exact; gs_x not applied), row-major [M, K] with a row stride of 2K bytes.
- * One row (M == 1, 9K/16 <= 8192) also keeps its packed codes (K/2 bytes)
- * from byte 0 and its scale bytes (K/16) after them, which nvfp4_gemm_run
- * contracts directly on the FP4 MFMA where it has a form for K (4096, 5120).
+ * Up to four rows with K = 4096 or 5120 also keep their packed codes
+ * ([M, K/2]) and then their scale bytes ([M, K/16]) right after the fp16
+ * operand (whose size is rounded up to 256 bytes), which nvfp4_gemm_run
+ * contracts directly on the FP4 MFMA.  For such shapes nvfp4_gemm with bf16
+ * rows does the whole step in one launch and leaves the same workspace.
  * The layout is stable, so callers and tests may inspect the operand.
  * ---------------------------------------------------------------------- */
 nvfp4_status_t nvfp4_gemm_prepare(const void *x, nvfp4_dtype_t x_dtype, int64_t M, int64_t K,

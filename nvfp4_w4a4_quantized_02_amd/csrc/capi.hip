@@ -174,9 +174,19 @@ static size_t partial_bytes(int64_t M, int64_t N, int64_t K) {
   return plan_gemm(M, N, K).partial_bytes;
 }
 
+// Up to four prepared rows also keep their packed codes ([M][K/2]) and scale
+// bytes ([M][K/16]) after the fp16 operand, for the FP4 GEMV of
+// nvfp4_gemm_run, where it has a form for the shape.
+static bool keeps_codes(int64_t M, int64_t K) { return gemv_fp4_has_form(M, K); }
+static size_t q_offset(int64_t M, int64_t K) { return kWsX16 + x16_bytes(M, K); }
+static size_t q_bytes(int64_t M, int64_t K) {
+  return keeps_codes(M, K) ? (size_t)round_up(M * K / 16 * 9, 1024) : 0;
+}
+static size_t prepared_bytes(int64_t M, int64_t K) { return q_offset(M, K) + q_bytes(M, K); }
+
 size_t nvfp4_gemm_workspace_size(int64_t M, int64_t N, int64_t K) {
   if (!dims_ok(M, N, K) || !tile_rows_ok(K)) return 0;
-  return kWsX16 + x16_bytes(M, K) + partial_bytes(M, N, K);
+  return prepared_bytes(M, K) + partial_bytes(M, N, K);
 }
 
 // W4A16 needs only the fp32 K-part sums of the split tiles.
@@ -185,18 +195,13 @@ size_t nvfp4_gemm_w4a16_workspace_size(int64_t M, int64_t N, int64_t K) {
   return partial_bytes(M, N, round_up(K, kGemmBK));
 }
 
-// One prepared row also keeps its packed codes (K/2 bytes) and scale bytes
-// (K/16) at the start of the workspace, where the absmax partials of larger
-// tensors go (one row needs none), for the FP4 GEMV of nvfp4_gemm_run.
-static bool keeps_row_codes(int64_t M, int64_t K) { return M == 1 && (uint64_t)K * 9u / 16u <= kWsGs; }
-
 nvfp4_status_t nvfp4_gemm_prepare(const void* x, nvfp4_dtype_t x_dtype, int64_t M, int64_t K, int64_t ld_x,
                                   void* workspace, size_t workspace_bytes, void* stream) {
   nvfp4_status_t st = check_input(x, x_dtype, M, K, ld_x);
   if (st != NVFP4_OK) return st;
   if (K % 64 != 0) return NVFP4_ERR_SHAPE;
   if (M == 0) return NVFP4_OK;
-  if (!workspace || !aligned(workspace, 256) || workspace_bytes < kWsX16 + x16_bytes(M, K))
+  if (!workspace || !aligned(workspace, 256) || workspace_bytes < prepared_bytes(M, K))
     return NVFP4_ERR_WORKSPACE;
   hipStream_t s = (hipStream_t)stream;
   const bool xb = x_dtype == NVFP4_BF16;
@@ -204,9 +209,9 @@ nvfp4_status_t nvfp4_gemm_prepare(const void* x, nvfp4_dtype_t x_dtype, int64_t 
   float* gsx = (float*)((char*)workspace + kWsGs);
   void* x16 = (char*)workspace + kWsX16;
   int np = launch_amax(x, xb, M, K, ld_x, partials, s);
-  uint8_t* q = keeps_row_codes(M, K) ? (uint8_t*)workspace : nullptr;
+  uint8_t* q = keeps_codes(M, K) ? (uint8_t*)workspace + q_offset(M, K) : nullptr;
   launch_quantize_f16(x, xb, M, K, ld_x, round_up(K, kGemmBK), partials, np, nullptr, x16, gsx, q,
-                      q ? q + K / 2 : nullptr, s);
+                      q ? q + M * K / 2 : nullptr, s);
   return launched();
 }
 
@@ -218,14 +223,14 @@ nvfp4_status_t nvfp4_gemm_prepare_static(const void* x, nvfp4_dtype_t x_dtype, i
   if (K % 64 != 0) return NVFP4_ERR_SHAPE;
   if (!gs_x) return NVFP4_ERR_NULL;
   if (M == 0) return NVFP4_OK;
-  if (!workspace || !aligned(workspace, 256) || workspace_bytes < kWsX16 + x16_bytes(M, K))
+  if (!workspace || !aligned(workspace, 256) || workspace_bytes < prepared_bytes(M, K))
     return NVFP4_ERR_WORKSPACE;
   hipStream_t s = (hipStream_t)stream;
   float* gsx = (float*)((char*)workspace + kWsGs);
   void* x16 = (char*)workspace + kWsX16;
-  uint8_t* q = keeps_row_codes(M, K) ? (uint8_t*)workspace : nullptr;
+  uint8_t* q = keeps_codes(M, K) ? (uint8_t*)workspace + q_offset(M, K) : nullptr;
   launch_quantize_f16(x, x_dtype == NVFP4_BF16, M, K, ld_x, round_up(K, kGemmBK), nullptr, 0, gs_x, x16, gsx, q,
-                      q ? q + K / 2 : nullptr, s);
+                      q ? q + M * K / 2 : nullptr, s);
   return launched();
 }
 
@@ -251,8 +256,9 @@ nvfp4_status_t nvfp4_gemm_run(int64_t M, int64_t K, const uint8_t* w_codes, cons
   const void* x16 = (const char*)workspace + kWsX16;
   void* wsv = workspace;
   const int64_t Kp = round_up(K, kGemmBK);
-  if (keeps_row_codes(M, K) &&
-      launch_gemv_m1_prepared((const uint8_t*)workspace, K, gsx, w_codes, w_scales, N, w_gs, y, yb, s))
+  if (keeps_codes(M, K) &&
+      launch_gemv_fp4_prepared((const uint8_t*)workspace + q_offset(M, K), M, K, gsx, w_codes, w_scales, N, w_gs,
+                               y, yb, (size_t)ld_y * esize(y_dtype), s))
     return launched();
   if (M <= kGemvMaxM)
     launch_gemv(false, x16, (size_t)Kp * 2, M, K, w_codes, w_scales, N, gsx, w_gs, y, yb, ld_y, s);
@@ -291,17 +297,18 @@ static nvfp4_status_t run_args_ok(int64_t M, int64_t K, const uint8_t* w_codes, 
   return NVFP4_OK;
 }
 
-// One bf16 activation row (decode): the quantize and the GEMV in one launch,
-// which also leaves the quantized row and gs_x in the workspace as
+// Up to four bf16 activation rows (decode): the quantize and the GEMV in one
+// launch, which also leaves the quantized rows and gs_x in the workspace as
 // nvfp4_gemm_prepare would.  False when the shape has no such form
 // (nothing launched); arguments already validated.
-static bool fused_m1(const void* x, nvfp4_dtype_t x_dtype, int64_t M, int64_t K, const float* gs_x,
-                     const uint8_t* w_codes, const uint8_t* w_scales, const float* w_gs, int64_t N, void* y,
-                     nvfp4_dtype_t y_dtype, void* workspace, void* stream) {
-  if (M != 1 || x_dtype != NVFP4_BF16 || K == 0) return false;
-  return launch_gemv_fused_m1(x, true, K, gs_x, w_codes, w_scales, N, w_gs, y, y_dtype == NVFP4_BF16,
-                              (char*)workspace + kWsX16, (float*)((char*)workspace + kWsGs), (uint8_t*)workspace,
-                              (hipStream_t)stream);
+static bool fused_decode(const void* x, nvfp4_dtype_t x_dtype, int64_t M, int64_t K, int64_t ld_x,
+                         const float* gs_x, const uint8_t* w_codes, const uint8_t* w_scales, const float* w_gs,
+                         int64_t N, void* y, nvfp4_dtype_t y_dtype, int64_t ld_y, void* workspace, void* stream) {
+  if (x_dtype != NVFP4_BF16 || !keeps_codes(M, K)) return false;
+  return launch_gemv_fp4(x, true, M, K, (size_t)ld_x * 2u, gs_x, w_codes, w_scales, N, w_gs, y,
+                         y_dtype == NVFP4_BF16, (size_t)ld_y * esize(y_dtype), (char*)workspace + kWsX16,
+                         (float*)((char*)workspace + kWsGs), (uint8_t*)workspace + q_offset(M, K),
+                         (hipStream_t)stream);
 }
 
 nvfp4_status_t nvfp4_gemm(const void* x, nvfp4_dtype_t x_dtype, int64_t M, int64_t K, int64_t ld_x,
@@ -313,7 +320,7 @@ nvfp4_status_t nvfp4_gemm(const void* x, nvfp4_dtype_t x_dtype, int64_t M, int64
   if (st != NVFP4_OK) return st;
   st = run_args_ok(M, K, w_codes, w_scales, w_gs, N, y, y_dtype, ld_y, workspace, workspace_bytes);
   if (st != NVFP4_OK || M == 0 || N == 0) return st;
-  if (fused_m1(x, x_dtype, M, K, nullptr, w_codes, w_scales, w_gs, N, y, y_dtype, workspace, stream))
+  if (fused_decode(x, x_dtype, M, K, ld_x, nullptr, w_codes, w_scales, w_gs, N, y, y_dtype, ld_y, workspace, stream))
     return launched();
   st = nvfp4_gemm_prepare(x, x_dtype, M, K, ld_x, workspace, workspace_bytes, stream);
   if (st != NVFP4_OK) return st;
@@ -330,7 +337,7 @@ nvfp4_status_t nvfp4_gemm_static(const void* x, nvfp4_dtype_t x_dtype, int64_t M
   if (!gs_x) return NVFP4_ERR_NULL;
   st = run_args_ok(M, K, w_codes, w_scales, w_gs, N, y, y_dtype, ld_y, workspace, workspace_bytes);
   if (st != NVFP4_OK || M == 0 || N == 0) return st;
-  if (fused_m1(x, x_dtype, M, K, gs_x, w_codes, w_scales, w_gs, N, y, y_dtype, workspace, stream))
+  if (fused_decode(x, x_dtype, M, K, ld_x, gs_x, w_codes, w_scales, w_gs, N, y, y_dtype, ld_y, workspace, stream))
     return launched();
   st = nvfp4_gemm_prepare_static(x, x_dtype, M, K, ld_x, gs_x, workspace, workspace_bytes, stream);
   if (st != NVFP4_OK) return st;

@@ -239,116 +239,102 @@ __global__ __launch_bounds__(64) void gemv_stream_kernel(const uint8_t* __restri
                    a[3] * scale);
 }
 
-// --------------------------------------------------- M == 1, FP4 contraction
-// One activation row against W with both operands NVFP4: the contraction
-// runs on the FP4 MFMA (16x16x128, E2M1 operands with unit scales) over the
-// raw codes, so no weight element is converted: each output column of an
-// MFMA collects one 16-element block, and its exact sum is multiplied by the
-// block's two E4M3 scales afterwards (the product of two NVFP4 blocks, paper
-// "Why Gated DeltaNet Survives 4-Bit Quantization", section 2 "NVFP4").  Only
-// the fp32 accumulation over blocks rounds, as in every other contraction
-// kernel, in another order.
+// --------------------------------------------------- M <= 4, FP4 contraction
+// Up to four activation rows against W with both operands NVFP4: the
+// contraction runs on the FP4 MFMA (16x16x128, E2M1 operands with unit
+// scales) over the raw codes, so no weight element is converted: each output
+// column of an MFMA collects one (activation row, 16-element block) pair, and
+// its exact sum is multiplied by the block's two E4M3 scales afterwards (the
+// product of two NVFP4 blocks, paper "Why Gated DeltaNet Survives 4-Bit
+// Quantization", section 2 "NVFP4").  Only the fp32 accumulation over blocks
+// rounds, as in every other contraction kernel, in another order.
 //
-// The row comes either as bf16, quantized by the kernel itself (the whole
-// decode step in one launch; the tensor scale from its absmax, or given), or
-// already quantized: the packed codes and scale bytes nvfp4_gemm_prepare
-// leaves at the start of its workspace for one row, with gs_x.  A separate
-// quantize launch costs the step more than its work; here every workgroup
-// quantizes the row (at most 8192 elements) into its own LDS while its first
-// weight transfers are already in flight.
+// The rows come either as bf16, quantized by the kernel itself (the whole
+// decode step in one launch; the tensor scale from their absmax, or given),
+// or already quantized: the packed codes [M][K/2] and scale bytes [M][K/16]
+// nvfp4_gemm_prepare leaves in its workspace, with gs_x.  A separate quantize
+// launch costs the step more than its work; here every workgroup quantizes
+// the rows (at most 4 x 5120 elements) into its own LDS while its weight
+// transfers are in flight.
 //
-// A workgroup is kFuWaves waves, one 16-row weight tile each, sharing the
-// quantized row in LDS (codes, 8 B a block, then the scale bytes).  The
-// row's 16-element blocks are dealt to the waves in sets of 64 (set j to
-// wave j % kFuWaves; lane l takes block 64 j + l).  Order of work in a wave:
-//   1. direct transfers into LDS, in this order: its part of the row (bf16:
-//      the bytes of its own sets, at their row offsets; prepared: 1 KB
-//      pieces q with q % kFuWaves = wave of the codes and scale bytes); its
-//      tile's scale bytes (16 rows x K/16, contiguous); the first D chunks of
+// A workgroup is kW waves, one 16-row weight tile each, sharing the
+// quantized rows in LDS (codes, 8 B a block, then the scale bytes, both in
+// row order).  The M * K/16 blocks, counted row after row, are dealt to the
+// waves in sets of 64 (set j to wave j % kW; lane l takes block
+// 64 j + l).  Order of work in a wave:
+//   1. prepared rows: direct transfers into LDS of 1 KB pieces q with
+//      q % kW = wave of the codes and scale bytes, then of its tile's
+//      scale bytes (16 rows x K/16, contiguous) and the first D chunks of
 //      codes (16 rows x 128 B per chunk, two transfers filling 8 lines
-//      each).  Transfers complete in the order issued, so the wave then
-//      waits for its row bytes alone;
-//   2. bf16 row: the absmax of its blocks (exact: integer max of the
+//      each); transfers complete in the order issued, so the wave waits for
+//      its pieces alone.
+//      One bf16 row: the same, with the bytes of its own sets in place of
+//      the pieces (staged at their row offsets).
+//      Two to four bf16 rows (twice to four times the LDS): its sets are
+//      loaded into registers, and the weight transfers are issued once the
+//      loads have landed (the compiler's wait for a register load would
+//      also wait for every transfer issued before it is used);
+//   2. bf16 rows: the absmax of its blocks (exact: integer max of the
 //      magnitudes), combined over the wave and, through LDS and a barrier,
 //      over the workgroup; the tensor scale RN(amax / 2688) (or the given
-//      one); the encode of its blocks into codes and scale bytes, written
-//      over the row's bf16 bytes (after a barrier: they overlap other waves'
-//      blocks).  Prepared row: a barrier (the pieces of the other waves);
+//      one); the encode of its blocks into codes and scale bytes in LDS
+//      (one staged row: written over its bf16 bytes, after a barrier, as
+//      they overlap other waves' blocks);
 //   3. one barrier, then the streaming loop below;
-//   4. bf16 row: workgroup 0 writes the quantized row to the workspace as
+//   4. bf16 rows: workgroup 0 writes the quantized rows to the workspace as
 //      nvfp4_gemm_prepare would (the fp16 values E2M1 * E4M3, the codes and
 //      scale bytes, the tensor scale).  Stored last: a store can be
 //      acknowledged before older loads return, so stores issued while loads
 //      are in flight would let a compiler-counted wait for those loads pass
 //      early.
 typedef int i32x8 __attribute__((ext_vector_type(8)));  // operands of the scaled MFMAs
-constexpr int kFuWaves = 3;
 constexpr int kFuDepth = 4;
+constexpr int kFuMaxWaves = 16;
+// Waves per workgroup: the quantizing forms repeat the encode of all rows in
+// every workgroup, so more rows take wider (and fewer) workgroups.
+constexpr int fp4_waves(int M) { return M == 1 ? 3 : 9; }
 enum FuMode { kFuDynamic = 0, kFuGiven = 1, kFuPrepared = 2 };
 
-template <int NCK, int kMode, bool kYBf16>
-__global__ __launch_bounds__(64 * kFuWaves) void gemv_fused_m1_kernel(const uint8_t* __restrict__ x,
-                                                                      const float* __restrict__ gs_in,
-                                                                      const uint8_t* __restrict__ wc,
-                                                                      const uint8_t* __restrict__ ws, int N,
-                                                                      int tiles, const float* __restrict__ gsw_p,
-                                                                      uint8_t* __restrict__ y,
-                                                                      uint4* __restrict__ x16_out,
-                                                                      float* __restrict__ gsx_out,
-                                                                      uint8_t* __restrict__ q_out) {
-  constexpr int K = NCK * 256, NB = K / 16, BPL = (NB + 63) / 64, D = kFuDepth;
+template <int NCK, int kM, int kW, int kMode, bool kYBf16>
+__global__ __launch_bounds__(64 * kW) void gemv_fp4_kernel(const uint8_t* __restrict__ x, size_t ldx,
+                                                                 const float* __restrict__ gs_in,
+                                                                 const uint8_t* __restrict__ wc,
+                                                                 const uint8_t* __restrict__ ws, int N, int tiles,
+                                                                 const float* __restrict__ gsw_p,
+                                                                 uint8_t* __restrict__ y, size_t ldy,
+                                                                 uint4* __restrict__ x16_out,
+                                                                 float* __restrict__ gsx_out,
+                                                                 uint8_t* __restrict__ q_out) {
+  constexpr int K = NCK * 256, NB = K / 16, D = kFuDepth;
   static_assert(NB % 64 == 0, "whole sets of 64 blocks");
+  static_assert(kM >= 1 && kM <= 4, "one to four rows");
+  static_assert(kW >= 1 && kW <= kFuMaxWaves, "waves");
+  constexpr int SPR = NB / 64;                          // sets per row
+  constexpr int NS = kM * SPR;                          // sets over all rows
+  constexpr int SPW = (NS + kW - 1) / kW;   // sets of the busiest wave
+  constexpr bool kStage = kMode != kFuPrepared && kM == 1;  // the bf16 row staged in LDS
   constexpr uint32_t kh = K / 2, ks = K / 16;
   constexpr uint32_t kScBytes = (16u * ks + 1023u) / 1024u * 1024u;
-  constexpr uint32_t kQPieces = (kh + ks + 1023u) / 1024u;  // prepared codes and scale bytes, 1 KB pieces
-  constexpr uint32_t kRowBytes = kMode == kFuPrepared ? kQPieces * 1024u : 2u * K;
-  // row [kRowBytes: bf16, then codes | scale bytes] | ring [wave][D][2048 B] |
-  // scales [wave][kScBytes] | wave maxima [4]
+  constexpr uint32_t kQBytes = (uint32_t)kM * (kh + ks);        // codes, then scale bytes
+  constexpr uint32_t kQPieces = (kQBytes + 1023u) / 1024u;      // in 1 KB pieces
+  constexpr uint32_t kRowBytes = kStage ? 2u * K : kQPieces * 1024u;
+  constexpr int kScT = (int)(kScBytes / 1024u);                 // scale transfers per wave
+  // rows [kRowBytes: bf16 (one staged row), then codes | scale bytes] |
+  // ring [wave][D][2048 B] | scales [wave][kScBytes] | wave maxima [kW]
   extern __shared__ uint4 smem[];
   const int lane = threadIdx.x & 63, l16 = lane & 15, g = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));  // uniform: scalar bases
-  const int tile_raw = blockIdx.x * kFuWaves + wave;
+  const int tile_raw = blockIdx.x * kW + wave;
   const int tile = tile_raw < tiles ? tile_raw : tiles - 1;  // a surplus wave redoes the last tile, unstored
   uint8_t* xrow = reinterpret_cast<uint8_t*>(smem);
   uint8_t* ring = xrow + kRowBytes + (size_t)wave * D * kGvChunkCodes;
-  uint8_t* sc_lds = xrow + kRowBytes + (size_t)kFuWaves * D * kGvChunkCodes + (size_t)wave * kScBytes;
-  uint32_t* wmax = reinterpret_cast<uint32_t*>(xrow + kRowBytes + (size_t)kFuWaves * (D * kGvChunkCodes + kScBytes));
-  uint2* xcodes = reinterpret_cast<uint2*>(xrow);  // [NB]
-  uint8_t* xsb = xrow + kh;                         // [NB]
+  uint8_t* sc_lds = xrow + kRowBytes + (size_t)kW * D * kGvChunkCodes + (size_t)wave * kScBytes;
+  uint32_t* wmax = reinterpret_cast<uint32_t*>(xrow + kRowBytes + (size_t)kW * (D * kGvChunkCodes + kScBytes));
+  uint2* xcodes = reinterpret_cast<uint2*>(xrow);  // [kM][NB]
+  uint8_t* xsb = xrow + kM * kh;                    // [kM][NB]
+  const uint32_t x0 = lds_addr(xrow);
 
-  // 1. transfers: this wave's part of the row, the scale bytes (pieces past
-  //    the end re-read the last piece; their LDS bytes are never read), the
-  //    first D chunks of codes
-  {
-    const uint32_t x0 = lds_addr(xrow);
-    if constexpr (kMode == kFuPrepared) {
-#pragma unroll
-      for (uint32_t q = 0; q < kQPieces; ++q) {
-        if (q % kFuWaves != (uint32_t)wave) continue;
-        lds_dma16(x, 1024u * q + 16u * (uint32_t)lane, x0 + 1024u * q);
-      }
-    } else {
-      // set j = bytes 2048 j .. 2048 j + 2047 of the bf16 row, two 1 KB transfers
-#pragma unroll
-      for (int j = 0; j < BPL; ++j) {
-        if (j % kFuWaves != wave) continue;
-        lds_dma16(x, 2048u * j + 16u * (uint32_t)lane, x0 + 2048u * j);
-        lds_dma16(x, 2048u * j + 1024u + 16u * (uint32_t)lane, x0 + 2048u * j + 1024u);
-      }
-    }
-  }
   const int n0 = tile * 16;
-  {
-    const uint32_t rows_here = (uint32_t)((N - n0) < 16 ? (N - n0) : 16);
-    const uint32_t bytes = rows_here * ks;  // a multiple of 16 (K % 256 == 0)
-    const uint32_t sc0 = lds_addr(sc_lds);
-#pragma unroll
-    for (uint32_t q = 0; q < kScBytes / 1024u; ++q) {
-      uint32_t off = q * 1024u + 16u * (uint32_t)lane;
-      off = off + 16u <= bytes ? off : bytes - 16u;
-      lds_dma16(ws + (size_t)n0 * ks, off, sc0 + q * 1024u);
-    }
-  }
   const uint8_t* wtile = wc + (size_t)n0 * kh;
   uint32_t coff[2];
 #pragma unroll
@@ -364,84 +350,161 @@ __global__ __launch_bounds__(64 * kFuWaves) void gemv_fused_m1_kernel(const uint
     lds_dma16(wtile, coff[0] + (uint32_t)c * 128u, slot);
     lds_dma16(wtile, coff[1] + (uint32_t)c * 128u, slot + 1024u);
   };
+  // the tile's scale bytes (pieces past the end re-read the last piece;
+  // their LDS bytes are never read), then the first D chunks of codes
+  auto issue_weights = [&]() {
+    const uint32_t rows_here = (uint32_t)((N - n0) < 16 ? (N - n0) : 16);
+    const uint32_t bytes = rows_here * ks;  // a multiple of 16 (K % 256 == 0)
+    const uint32_t sc0 = lds_addr(sc_lds);
 #pragma unroll
-  for (int d = 0; d < D; ++d) issue(d, d);
-  // this wave's row bytes have landed (the scale and code transfers after
-  // them may still be in flight)
-  wait_vmcnt<(int)(kScBytes / 1024u) + 2 * D>();
+    for (uint32_t q = 0; q < kScBytes / 1024u; ++q) {
+      uint32_t off = q * 1024u + 16u * (uint32_t)lane;
+      off = off + 16u <= bytes ? off : bytes - 16u;
+      lds_dma16(ws + (size_t)n0 * ks, off, sc0 + q * 1024u);
+    }
+#pragma unroll
+    for (int d = 0; d < D; ++d) issue(d, d);
+  };
 
-  // 2. the quantized row
+  // 1. the activation bytes, then the weight transfers
+  uint32_t xw[kMode == kFuPrepared ? 1 : SPW][BlockWords<true>::n];
+  if constexpr (kMode == kFuPrepared) {
+#pragma unroll
+    for (uint32_t q = 0; q < kQPieces; ++q) {
+      if (q % kW != (uint32_t)wave) continue;
+      uint32_t off = 1024u * q + 16u * (uint32_t)lane;
+      off = off + 16u <= kQBytes ? off : kQBytes - 16u;  // bytes past the rows are never read
+      lds_dma16(x, off, x0 + 1024u * q);
+    }
+    issue_weights();
+    wait_vmcnt<kScT + 2 * D>();  // this wave's pieces have landed
+  } else if constexpr (kStage) {
+    // set j = bytes 2048 j .. 2048 j + 2047 of the bf16 row, two 1 KB transfers
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+      if (j % kW != wave) continue;
+      lds_dma16(x, 2048u * j + 16u * (uint32_t)lane, x0 + 2048u * j);
+      lds_dma16(x, 2048u * j + 1024u + 16u * (uint32_t)lane, x0 + 2048u * j + 1024u);
+    }
+    issue_weights();
+    wait_vmcnt<kScT + 2 * D>();  // this wave's row bytes have landed
+    const uint4* xs = reinterpret_cast<const uint4*>(xrow);
+#pragma unroll
+    for (int i = 0; i < SPW; ++i) {
+      const int j = wave + kW * i;
+      if (j >= NS) continue;
+      const uint4 a = xs[2 * (lane + 64 * j)], b = xs[2 * (lane + 64 * j) + 1];
+      xw[i][0] = a.x; xw[i][1] = a.y; xw[i][2] = a.z; xw[i][3] = a.w;
+      xw[i][4] = b.x; xw[i][5] = b.y; xw[i][6] = b.z; xw[i][7] = b.w;
+    }
+  } else {
+    // a surplus set (the last wave may own one fewer) reloads the last set:
+    // its absmax repeats a max, and it is not encoded
+#pragma unroll
+    for (int i = 0; i < SPW; ++i) {
+      const int j = wave + kW * i < NS ? wave + kW * i : NS - 1;
+      const uint4* p = reinterpret_cast<const uint4*>(x + (size_t)(j / SPR) * ldx) + 2 * (64 * (j % SPR) + lane);
+      const uint4 a = p[0], b = p[1];
+      xw[i][0] = a.x; xw[i][1] = a.y; xw[i][2] = a.z; xw[i][3] = a.w;
+      xw[i][4] = b.x; xw[i][5] = b.y; xw[i][6] = b.z; xw[i][7] = b.w;
+    }
+    // every loaded word is in its register before the first transfer is
+    // issued (ordered volatile asm statements that read them)
+#pragma unroll
+    for (int i = 0; i < SPW; ++i)
+#pragma unroll
+      for (int k = 0; k < BlockWords<true>::n; ++k) asm volatile("" ::"v"(xw[i][k]));
+    issue_weights();
+  }
+
+  // 2. the quantized rows
   float gs;
   if constexpr (kMode == kFuPrepared) {
     gs = *gs_in;
   } else {
-    uint32_t xw[BPL][BlockWords<true>::n];
-    const uint4* xs = reinterpret_cast<const uint4*>(xrow);
-#pragma unroll
-    for (int j = 0; j < BPL; ++j) {
-      if (j % kFuWaves != wave) continue;
-      const uint4 a = xs[2 * (lane + 64 * j)], b = xs[2 * (lane + 64 * j) + 1];
-      xw[j][0] = a.x; xw[j][1] = a.y; xw[j][2] = a.z; xw[j][3] = a.w;
-      xw[j][4] = b.x; xw[j][5] = b.y; xw[j][6] = b.z; xw[j][7] = b.w;
-    }
     if constexpr (kMode == kFuGiven) {
       gs = *gs_in;
     } else {
       uint32_t m = 0;
 #pragma unroll
-      for (int j = 0; j < BPL; ++j) {
-        if (j % kFuWaves != wave) continue;
-        const uint32_t a = words_absmax_bits<true>(xw[j]);
+      for (int i = 0; i < SPW; ++i) {
+        if (kStage && wave + kW * i >= NS) continue;
+        const uint32_t a = words_absmax_bits<true>(xw[i]);
         m = m > a ? m : a;
       }
       m = wave_max_u32(m);
       if (lane == 0) wmax[wave] = m;
       asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 #pragma unroll
-      for (int w = 0; w < kFuWaves; ++w) m = m > wmax[w] ? m : wmax[w];
+      for (int w = 0; w < kW; ++w) m = m > wmax[w] ? m : wmax[w];
       gs = tensor_scale(__uint_as_float(m));
     }
-    // The codes and scale bytes overwrite bf16 bytes of other blocks, so
-    // every wave has read its blocks first (the barrier above, or this one
-    // with a given scale).
-    if constexpr (kMode == kFuGiven) asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    // A staged row's codes and scale bytes overwrite bf16 bytes of other
+    // blocks, so every wave has read its blocks first (the barrier above, or
+    // this one with a given scale).
+    if constexpr (kStage && kMode == kFuGiven) asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     const FastScale fsc = fast_scale(gs);
 #pragma unroll
-    for (int j = 0; j < BPL; ++j) {
-      if (j % kFuWaves != wave) continue;
+    for (int i = 0; i < SPW; ++i) {
+      const int j = wave + kW * i;
+      if (j >= NS) continue;
       const int b = lane + 64 * j;
       float xv[16];
-      words_to_floats<true>(xw[j], xv);
+      words_to_floats<true>(xw[i], xv);
       uint32_t sb, lo, hi;
-      if (!encode_block_fast(xv, words_absmax_bits<true>(xw[j]), fsc, sb, lo, hi))
+      if (!encode_block_fast(xv, words_absmax_bits<true>(xw[i]), fsc, sb, lo, hi))
         sb = encode_block_exact(xv, gs, lo, hi);
       xcodes[b] = make_uint2(lo, hi);
       xsb[b] = (uint8_t)sb;
     }
   }
-  // 3. the quantized row complete and visible to every wave (the transfers
+  // 3. the quantized rows complete and visible to every wave (the transfers
   //    in flight are not waited for: a bare barrier, no fence)
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 
-  // The streaming loop.  Per chunk (256 k), two FP4 MFMAs 16x16x128 on the
-  // raw codes (E2M1 x E2M1, unit scales) give, in output column c, the dot
-  // product of each weight row with block c of the chunk alone: MFMA H takes
-  // k 128H .. 128H+127 of the chunk, lane group g k 32g .. 32g+31 of that
-  // (weight piece 4H + g of the row); the activation operand of lane (c, g)
-  // holds the codes of block c in its half c % 2 when g = (c % 8) / 2 and
-  // c / 8 = H, zeros elsewhere.  The products and their 16-term sums are
+  // The streaming loop.  Per chunk (256 k), MFMA H of each pair takes k
+  // 128H .. 128H+127 of the chunk, lane group g k 32g .. 32g+31 of that
+  // (weight piece 4H + g of the row), and output column c holds one
+  // (activation row, block) pair:
+  //   M = 1: block c of the chunk; both MFMAs accumulate into one tile, MFMA
+  //          H filling columns 8H .. 8H+7;
+  //   M = 2: row c / 8, block 8H + c % 8 (one MFMA per half);
+  //   M = 3, 4: row c / 4, block 8H + 4Q + c % 4 (MFMAs Q = 0, 1 per half;
+  //          a fourth row of zeros for M = 3).
+  // The activation operand of lane (c, g) holds the codes of its column's
+  // block in half (block % 2) of its 32 k when g = (block % 8) / 2, zeros
+  // elsewhere (per-lane masks).  The products and their 16-term sums are
   // multiples of 1/4 below 600, exact in fp32, and so is each sum times the
   // two block scales (at most 12 + 4 + 4 significant bits): lane (c, g) adds
-  // them to the partial sums of rows 4g .. 4g+3 in fp32 in chunk order, and
-  // the 16 lanes of a row group are added at the end in a fixed tree.
+  // them to its partial sums of weight rows 4g .. 4g+3 in fp32 in a fixed
+  // order, and the lanes of one activation row are added at the end in a
+  // fixed tree.
+  constexpr int kRM = kM == 1 ? 1 : (kM == 2 ? 2 : 4);  // activation rows per MFMA, padded
+  constexpr int kBPM = kRM == 4 ? 4 : 8;                // blocks per activation row and MFMA
+  constexpr int kQ = kRM == 4 ? 2 : 1;                  // MFMAs per 128-k half
   const uint32_t sw = (uint32_t)(l16 & 7);
   const uint32_t apos0 = (uint32_t)l16 * 128u + 16u * ((uint32_t)g ^ sw);
   const uint32_t apos1 = (uint32_t)l16 * 128u + 16u * ((4u + (uint32_t)g) ^ sw);
-  const bool act = g == ((l16 & 7) >> 1);
-  const uint32_t mk[2][2] = {
-      {(act && (l16 >> 3) == 0 && (l16 & 1) == 0) ? ~0u : 0u, (act && (l16 >> 3) == 0 && (l16 & 1) == 1) ? ~0u : 0u},
-      {(act && (l16 >> 3) == 1 && (l16 & 1) == 0) ? ~0u : 0u, (act && (l16 >> 3) == 1 && (l16 & 1) == 1) ? ~0u : 0u}};
-  const uint32_t srow = (uint32_t)(4 * g) * ks + (uint32_t)l16;  // scale byte of row 4g, block l16 of chunk 0
+  const int mrow = kRM == 1 ? 0 : l16 / kBPM;           // this column's activation row
+  const int bl = l16 % kBPM;                            // its block within the MFMA's set
+  const int mc = mrow < kM ? mrow : kM - 1;             // clamped for addressing
+  const int ql = kQ == 2 ? (g >> 1) : 0;                // the only MFMA of a half this lane feeds
+  const bool act = mrow < kM && (kQ == 2 ? ((bl >> 1) == (g & 1)) : (g == (bl >> 1)));
+  uint32_t mk[kRM == 1 ? 2 : kQ][2];
+  if constexpr (kRM == 1) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int e = 0; e < 2; ++e) mk[h][e] = (act && (l16 >> 3) == h && (l16 & 1) == e) ? ~0u : 0u;
+  } else {
+#pragma unroll
+    for (int q = 0; q < kQ; ++q)
+#pragma unroll
+      for (int e = 0; e < 2; ++e) mk[q][e] = (act && q == ql && (bl & 1) == e) ? ~0u : 0u;
+  }
+  const uint32_t xbase = (uint32_t)mc * NB + (uint32_t)(kRM == 1 ? l16 : kBPM * ql + bl);  // + 16c (+ 8H)
+  const uint32_t sxbase = (uint32_t)mc * NB + (uint32_t)(kRM == 1 ? l16 : bl);           // + 16c (+ 8H + kBPM Q)
+  const uint32_t srow = (uint32_t)(4 * g) * ks + (uint32_t)(kRM == 1 ? l16 : bl);       // + j ks + 16c (+ ...)
   float part[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
   for (int c = 0; c < NCK; ++c) {
@@ -450,103 +513,150 @@ __global__ __launch_bounds__(64 * kFuWaves) void gemv_fused_m1_kernel(const uint
     const uint8_t* slot = ring + d * kGvChunkCodes;
     const uint4 a0 = *reinterpret_cast<const uint4*>(slot + apos0);
     const uint4 a1 = *reinterpret_cast<const uint4*>(slot + apos1);
-    const uint2 xv = xcodes[16 * c + l16];
-    const uint32_t xsc_b = xsb[16 * c + l16];
-    uint32_t swb[4];
+    const i32x8 A[2] = {{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, 0, 0, 0, 0},
+                        {(int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w, 0, 0, 0, 0}};
+    if constexpr (kRM == 1) {
+      const uint2 xv = xcodes[16 * c + xbase];
+      const uint32_t xsc_b = xsb[16 * c + sxbase];
+      uint32_t swb[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) swb[j] = sc_lds[srow + (uint32_t)j * ks + 16u * (uint32_t)c];
-    // the slot's reads are complete: refill it before computing, so the
-    // transfer is not held back by this chunk's arithmetic
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    issue(c + D, d);
-    const i32x8 A0 = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, 0, 0, 0, 0};
-    const i32x8 A1 = {(int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w, 0, 0, 0, 0};
-    const i32x8 B0 = {(int)(xv.x & mk[0][0]), (int)(xv.y & mk[0][0]), (int)(xv.x & mk[0][1]), (int)(xv.y & mk[0][1]),
-                      0, 0, 0, 0};
-    const i32x8 B1 = {(int)(xv.x & mk[1][0]), (int)(xv.y & mk[1][0]), (int)(xv.x & mk[1][1]), (int)(xv.y & mk[1][1]),
-                      0, 0, 0, 0};
-    floatx4 acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A0, B0, floatx4{0.0f, 0.0f, 0.0f, 0.0f}, 4, 4, 0,
-                                                                    127, 0, 127);
-    acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A1, B1, acc, 4, 4, 0, 127, 0, 127);
-    const float sx = __builtin_amdgcn_cvt_f32_fp8((int)xsc_b, 0);
+      for (int j = 0; j < 4; ++j) swb[j] = sc_lds[srow + (uint32_t)j * ks + 16u * (uint32_t)c];
+      // the slot's reads are complete: refill it before computing, so the
+      // transfer is not held back by this chunk's arithmetic
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      issue(c + D, d);
+      floatx4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      part[j] = __builtin_fmaf(acc[j] * sx, __builtin_amdgcn_cvt_f32_fp8((int)(swb[j] & 0x7Fu), 0), part[j]);
+      for (int h = 0; h < 2; ++h) {
+        const i32x8 B = {(int)(xv.x & mk[h][0]), (int)(xv.y & mk[h][0]), (int)(xv.x & mk[h][1]),
+                         (int)(xv.y & mk[h][1]), 0, 0, 0, 0};
+        acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[h], B, acc, 4, 4, 0, 127, 0, 127);
+      }
+      const float sx = __builtin_amdgcn_cvt_f32_fp8((int)xsc_b, 0);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        part[j] = __builtin_fmaf(acc[j] * sx, __builtin_amdgcn_cvt_f32_fp8((int)(swb[j] & 0x7Fu), 0), part[j]);
+    } else {
+      uint2 xv[2];
+      uint32_t xsc_b[2][kQ], swb[2][kQ][4];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        xv[h] = xcodes[16 * c + 8 * h + xbase];
+#pragma unroll
+        for (int q = 0; q < kQ; ++q) {
+          const uint32_t o = 16u * (uint32_t)c + 8u * (uint32_t)h + (uint32_t)(kBPM * q);
+          xsc_b[h][q] = xsb[sxbase + o];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) swb[h][q][j] = sc_lds[srow + (uint32_t)j * ks + o];
+        }
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      issue(c + D, d);
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int q = 0; q < kQ; ++q) {
+          const i32x8 B = {(int)(xv[h].x & mk[q][0]), (int)(xv[h].y & mk[q][0]), (int)(xv[h].x & mk[q][1]),
+                           (int)(xv[h].y & mk[q][1]), 0, 0, 0, 0};
+          const floatx4 acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+              A[h], B, floatx4{0.0f, 0.0f, 0.0f, 0.0f}, 4, 4, 0, 127, 0, 127);
+          const float sx = __builtin_amdgcn_cvt_f32_fp8((int)xsc_b[h][q], 0);
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            part[j] = __builtin_fmaf(acc[j] * sx, __builtin_amdgcn_cvt_f32_fp8((int)(swb[h][q][j] & 0x7Fu), 0),
+                                     part[j]);
+        }
+    }
   }
   wait_vmcnt<0>();
-  // rows 4g .. 4g+3: the 16 lanes of the row group, added in a fixed tree
+  // weight rows 4g .. 4g+3: the lanes of one activation row (M = 1: all 16
+  // of the row group), added in a fixed tree
 #pragma unroll
-  for (int o = 8; o > 0; o >>= 1)
+  for (int o = (kRM == 1 ? 16 : kBPM) / 2; o > 0; o >>= 1)
 #pragma unroll
     for (int j = 0; j < 4; ++j) part[j] += __shfl_xor(part[j], o, 64);
-  if (l16 == 0 && tile_raw < tiles) {
+  if (bl == 0 && (kRM == 1 ? l16 == 0 : mrow < kM) && tile_raw < tiles) {
     const float scale = gs * (*gsw_p);
-    store4<kYBf16>(y, n0 + 4 * g, N, part[0] * scale, part[1] * scale, part[2] * scale, part[3] * scale);
+    store4<kYBf16>(y + (size_t)mrow * ldy, n0 + 4 * g, N, part[0] * scale, part[1] * scale, part[2] * scale,
+                   part[3] * scale);
   }
-  // 4. the quantized row for the workspace: fp16 values E2M1 * E4M3, codes
+  // 4. the quantized rows for the workspace: fp16 values E2M1 * E4M3, codes
   //    and scale bytes, tensor scale
   if constexpr (kMode != kFuPrepared) {
     if (blockIdx.x == 0) {
-      for (int i = (int)threadIdx.x; i < K / 8; i += 64 * kFuWaves) {
+      for (int i = (int)threadIdx.x; i < kM * K / 8; i += 64 * kW) {
         const uint2 cw = xcodes[i >> 1];
         uint32_t e[4];
         expand8((i & 1) ? cw.y : cw.x, scale_f16x2(xsb[i >> 1]), e);
         x16_out[i] = make_uint4(e[0], e[1], e[2], e[3]);
       }
-      for (int i = (int)threadIdx.x; i < (int)(kh + ks) / 16; i += 64 * kFuWaves)
+      for (int i = (int)threadIdx.x; i < (int)kQBytes / 16; i += 64 * kW)
         reinterpret_cast<uint4*>(q_out)[i] = reinterpret_cast<const uint4*>(xrow)[i];
       if (threadIdx.x == 0) *gsx_out = gs;
     }
   }
 }
 
-static size_t fused_m1_lds(int64_t K, bool prepared) {
+static size_t fp4_lds(int64_t M, int64_t K, bool prepared, int W) {
   const size_t kh = (size_t)K / 2, ks = (size_t)K / 16;
-  const size_t row = prepared ? (kh + ks + 1023u) / 1024u * 1024u : (size_t)K * 2u;
-  return row + (size_t)kFuWaves * kFuDepth * kGvChunkCodes +
-         (size_t)kFuWaves * ((16u * ks + 1023u) / 1024u * 1024u) +  // 16 rows of K/16 scale bytes
-         16u;                                                        // the waves' maxima
+  const size_t row = (!prepared && M == 1) ? (size_t)K * 2u : ((size_t)M * (kh + ks) + 1023u) / 1024u * 1024u;
+  return row + (size_t)W * kFuDepth * kGvChunkCodes +
+         (size_t)W * ((16u * ks + 1023u) / 1024u * 1024u) +  // 16 rows of K/16 scale bytes
+         4u * kFuMaxWaves;                                           // the waves' maxima
 }
 
 template <int kMode>
-static void fused_m1_go(int64_t K, const void* x, const float* gs_in, const uint8_t* wc, const uint8_t* ws,
-                        int64_t N, const float* gsw, void* y, bool y_bf16, void* x16_out, float* gsx_out,
-                        uint8_t* q_out, hipStream_t s) {
+static void fp4_go(int64_t M, int64_t K, const void* x, size_t ldx, const float* gs_in, const uint8_t* wc,
+                   const uint8_t* ws, int64_t N, const float* gsw, void* y, bool y_bf16, size_t ldy,
+                   void* x16_out, float* gsx_out, uint8_t* q_out, hipStream_t s) {
   const int tiles = (int)((N + 15) / 16);
-  const int grid = (tiles + kFuWaves - 1) / kFuWaves;
-  const size_t lds = fused_m1_lds(K, kMode == kFuPrepared);
-  auto go = [&](auto nc, auto yb) {
-    gemv_fused_m1_kernel<decltype(nc)::value, kMode, decltype(yb)::value><<<grid, 64 * kFuWaves, lds, s>>>(
-        (const uint8_t*)x, gs_in, wc, ws, (int)N, tiles, gsw, (uint8_t*)y, (uint4*)x16_out, gsx_out, q_out);
+  auto go = [&](auto nc, auto m, auto yb) {
+    constexpr int W = fp4_waves(decltype(m)::value);
+    const int grid = (tiles + W - 1) / W;
+    const size_t lds = fp4_lds(M, K, kMode == kFuPrepared, W);
+    gemv_fp4_kernel<decltype(nc)::value, decltype(m)::value, W, kMode, decltype(yb)::value>
+        <<<grid, 64 * W, lds, s>>>((const uint8_t*)x, ldx, gs_in, wc, ws, (int)N, tiles, gsw, (uint8_t*)y, ldy,
+                                   (uint4*)x16_out, gsx_out, q_out);
   };
-  auto by_y = [&](auto nc) {
-    if (y_bf16) go(nc, std::true_type());
-    else go(nc, std::false_type());
+  auto by_y = [&](auto nc, auto m) {
+    if (y_bf16) go(nc, m, std::true_type());
+    else go(nc, m, std::false_type());
   };
-  if (K == 5120) by_y(std::integral_constant<int, 20>());
-  else by_y(std::integral_constant<int, 16>());
+  auto by_m = [&](auto nc) {
+    switch (M) {
+      case 1: by_y(nc, std::integral_constant<int, 1>()); break;
+      case 2: by_y(nc, std::integral_constant<int, 2>()); break;
+      case 3: by_y(nc, std::integral_constant<int, 3>()); break;
+      default: by_y(nc, std::integral_constant<int, 4>()); break;
+    }
+  };
+  if (K == 5120) by_m(std::integral_constant<int, 20>());
+  else by_m(std::integral_constant<int, 16>());
 }
 
-// One-launch decode step for M == 1 when the row is bf16 and its length has
-// an instantiation; false otherwise (nothing launched: the caller quantizes
-// and runs the GEMV in two launches).
-bool launch_gemv_fused_m1(const void* x, bool x_bf16, int64_t K, const float* gs_in, const uint8_t* wc,
-                          const uint8_t* ws, int64_t N, const float* gsw, void* y, bool y_bf16, void* x16_out,
-                          float* gsx_out, uint8_t* q_out, hipStream_t s) {
-  if (!x_bf16 || (K != 4096 && K != 5120)) return false;
+// One-launch decode step for up to four bf16 rows when the shape has an
+// instantiation; false otherwise (nothing launched: the caller quantizes and
+// runs the GEMV in two launches).
+bool launch_gemv_fp4(const void* x, bool x_bf16, int64_t M, int64_t K, size_t ldx_bytes, const float* gs_in,
+                     const uint8_t* wc, const uint8_t* ws, int64_t N, const float* gsw, void* y, bool y_bf16,
+                     size_t ldy_bytes, void* x16_out, float* gsx_out, uint8_t* q_out, hipStream_t s) {
+  if (!x_bf16 || !gemv_fp4_has_form(M, K)) return false;
   if (gs_in)
-    fused_m1_go<kFuGiven>(K, x, gs_in, wc, ws, N, gsw, y, y_bf16, x16_out, gsx_out, q_out, s);
+    fp4_go<kFuGiven>(M, K, x, ldx_bytes, gs_in, wc, ws, N, gsw, y, y_bf16, ldy_bytes, x16_out, gsx_out, q_out, s);
   else
-    fused_m1_go<kFuDynamic>(K, x, gs_in, wc, ws, N, gsw, y, y_bf16, x16_out, gsx_out, q_out, s);
+    fp4_go<kFuDynamic>(M, K, x, ldx_bytes, gs_in, wc, ws, N, gsw, y, y_bf16, ldy_bytes, x16_out, gsx_out, q_out,
+                       s);
   return true;
 }
 
-// The GEMV for one prepared row (codes at q, scale bytes at q + K/2, tensor
-// scale *gsx) when its length has an instantiation; false otherwise.
-bool launch_gemv_m1_prepared(const uint8_t* q, int64_t K, const float* gsx, const uint8_t* wc, const uint8_t* ws,
-                             int64_t N, const float* gsw, void* y, bool y_bf16, hipStream_t s) {
-  if (K != 4096 && K != 5120) return false;
-  fused_m1_go<kFuPrepared>(K, q, gsx, wc, ws, N, gsw, y, y_bf16, nullptr, nullptr, nullptr, s);
+// The GEMV for up to four prepared rows (codes [M][K/2] at q, scale bytes
+// [M][K/16] after them, tensor scale *gsx) when the shape has an
+// instantiation; false otherwise.
+bool launch_gemv_fp4_prepared(const uint8_t* q, int64_t M, int64_t K, const float* gsx, const uint8_t* wc,
+                              const uint8_t* ws, int64_t N, const float* gsw, void* y, bool y_bf16,
+                              size_t ldy_bytes, hipStream_t s) {
+  if (!gemv_fp4_has_form(M, K)) return false;
+  fp4_go<kFuPrepared>(M, K, q, 0, gsx, wc, ws, N, gsw, y, y_bf16, ldy_bytes, nullptr, nullptr, nullptr, s);
   return true;
 }
 

@@ -155,20 +155,24 @@ void launch_gemv_fp8w(bool a8, const void* x, size_t ld_x_bytes, int64_t M, int6
                       const float* sx, const float* sw, void* y, bool y_bf16, int64_t ld_y, hipStream_t s);
 constexpr int64_t kFp8GemvMaxK = 5120;
 
-// The W4A4 decode step for one activation row in one launch: quantize x
-// ([1, K], bf16; with gs_in given, that tensor scale) and contract with W.
-// Also writes what nvfp4_gemm_prepare would: the fp16 operand to x16_out,
-// the tensor scale to gsx_out, the packed codes and scale bytes to q_out
-// (K/2 + K/16 bytes).  Returns false (nothing launched) for a K it has no
-// form for.
-bool launch_gemv_fused_m1(const void* x, bool x_bf16, int64_t K, const float* gs_in, const uint8_t* wc,
-                          const uint8_t* ws, int64_t N, const float* gsw, void* y, bool y_bf16, void* x16_out,
-                          float* gsx_out, uint8_t* q_out, hipStream_t s);
-// The GEMV for one prepared row: its packed codes at q, its scale bytes at
-// q + K/2, its tensor scale at gsx.  Returns false (nothing launched) for a
-// K it has no form for.
-bool launch_gemv_m1_prepared(const uint8_t* q, int64_t K, const float* gsx, const uint8_t* wc, const uint8_t* ws,
-                             int64_t N, const float* gsw, void* y, bool y_bf16, hipStream_t s);
+// Whether the FP4-MFMA GEMV has a form for M activation rows of length K.
+inline bool gemv_fp4_has_form(int64_t M, int64_t K) { return M >= 1 && M <= 4 && (K == 4096 || K == 5120); }
+// The W4A4 decode step for up to four activation rows in one launch:
+// quantize x ([M, K] bf16, row stride ldx_bytes; with gs_in given, that
+// tensor scale) and contract with W into y (row stride ldy_bytes).  Also
+// writes what nvfp4_gemm_prepare would: the fp16 operand to x16_out
+// ([M, K]), the tensor scale to gsx_out, the packed codes [M][K/2] and then
+// the scale bytes [M][K/16] to q_out.  Returns false (nothing launched)
+// for a shape it has no form for.
+bool launch_gemv_fp4(const void* x, bool x_bf16, int64_t M, int64_t K, size_t ldx_bytes, const float* gs_in,
+                     const uint8_t* wc, const uint8_t* ws, int64_t N, const float* gsw, void* y, bool y_bf16,
+                     size_t ldy_bytes, void* x16_out, float* gsx_out, uint8_t* q_out, hipStream_t s);
+// The GEMV for up to four prepared rows: their packed codes [M][K/2] at q,
+// then their scale bytes [M][K/16], the tensor scale at gsx.  Returns false
+// (nothing launched) for a shape it has no form for.
+bool launch_gemv_fp4_prepared(const uint8_t* q, int64_t M, int64_t K, const float* gsx, const uint8_t* wc,
+                              const uint8_t* ws, int64_t N, const float* gsw, void* y, bool y_bf16,
+                              size_t ldy_bytes, hipStream_t s);
 
 void launch_gemv(bool a16, const void* x, size_t ld_x_bytes, int64_t M, int64_t K, const uint8_t* wc,
                  const uint8_t* ws, int64_t N, const float* gsx, const float* gsw, void* y, bool y_bf16,

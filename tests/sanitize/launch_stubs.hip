@@ -53,13 +53,13 @@ void launch_gemv(bool, const void*, size_t, int64_t, int64_t, const uint8_t*, co
                  const float*, const float*, void*, bool, int64_t, hipStream_t) {
   launched("gemv");
 }
-bool launch_gemv_fused_m1(const void*, bool, int64_t, const float*, const uint8_t*, const uint8_t*, int64_t,
-                          const float*, void*, bool, void*, float*, uint8_t*, hipStream_t) {
-  launched("gemv_fused_m1");
+bool launch_gemv_fp4(const void*, bool, int64_t, int64_t, size_t, const float*, const uint8_t*, const uint8_t*,
+                     int64_t, const float*, void*, bool, size_t, void*, float*, uint8_t*, hipStream_t) {
+  launched("gemv_fp4");
 }
-bool launch_gemv_m1_prepared(const uint8_t*, int64_t, const float*, const uint8_t*, const uint8_t*, int64_t,
-                             const float*, void*, bool, hipStream_t) {
-  launched("gemv_m1_prepared");
+bool launch_gemv_fp4_prepared(const uint8_t*, int64_t, int64_t, const float*, const uint8_t*, const uint8_t*,
+                              int64_t, const float*, void*, bool, size_t, hipStream_t) {
+  launched("gemv_fp4_prepared");
 }
 
 }  // namespace nvfp4

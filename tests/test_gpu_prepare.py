@@ -11,9 +11,10 @@ have the oracle's bits (paper "Why Gated DeltaNet Survives 4-Bit
 Quantization", section 2 "NVFP4": activations quantized on the fly to E2M1
 with an E4M3 scale per 16 and one FP32 tensor scale).
 
-A prepared single row (M = 1, K <= 14563) also keeps its packed codes (K/2
-bytes from byte 0) and scale bytes (K/16 bytes after them), which the one-row
-FP4 GEMV contracts directly; those must equal the oracle's bytes.
+Up to four prepared rows at K = 4096 or 5120 also keep their packed codes
+([M, K/2]) and then their scale bytes ([M, K/16]) right after the fp16
+operand, which the FP4 GEMV contracts directly; those must equal the
+oracle's bytes.
 
 Cases cover every instantiation of the quantize kernels that writes this
 form: the one-launch kernel with one workgroup (absmax from its own blocks,
@@ -50,8 +51,15 @@ def _expected_f16_bits(orc, codes, scales):
     return val.astype(np.float16).view(np.uint16)
 
 
-def keeps_row_codes(M, K):
-    return M == 1 and K * 9 // 16 <= WS_GS
+def keeps_codes(M, K):
+    return 1 <= M <= 4 and K in (4096, 5120)
+
+
+def codes_offset(M, K):
+    """Byte offset of the packed codes: after the fp16 operand [M, K rounded
+    up to 64], itself rounded up to 256 bytes."""
+    kp = (K + 63) // 64 * 64
+    return WS_X16 + (M * kp * 2 + 255) // 256 * 256
 
 
 def _prepared(nv, x: np.ndarray, gs=None):
@@ -69,10 +77,11 @@ def _prepared(nv, x: np.ndarray, gs=None):
 
 
 def check_row_codes(ws, oc, os_, what):
-    """One prepared row: packed codes from byte 0, scale bytes after them."""
-    K = oc.shape[1] * 2
-    codes = ws[:K // 2].reshape(1, K // 2)
-    scales = ws[K // 2:K // 2 + K // 16].reshape(1, K // 16)
+    """Prepared rows: packed codes [M, K/2], then scale bytes [M, K/16]."""
+    M, K = oc.shape[0], oc.shape[1] * 2
+    o = codes_offset(M, K)
+    codes = ws[o:o + M * K // 2].reshape(M, K // 2)
+    scales = ws[o + M * K // 2:o + M * K // 2 + M * K // 16].reshape(M, K // 16)
     assert np.array_equal(codes, oc), "%s: %d code bytes differ" % (what, int((codes != oc).sum()))
     assert np.array_equal(scales, os_), "%s: %d scale bytes differ" % (what, int((scales != os_).sum()))
 
@@ -81,7 +90,7 @@ def _check(nv, orc, x, what, gs=None):
     print("case: prepare", what, x.shape, x.dtype, "given gs" if gs is not None else "", flush=True)
     gbits, x16, ws = _prepared(nv, x, gs)
     oc, os_, og = orc.quantize(x, gs=gs)
-    if keeps_row_codes(*x.shape):
+    if keeps_codes(*x.shape):
         check_row_codes(ws, oc, os_, what)
     assert gbits == np.float32(og).view(np.uint32), "%s: gs_x %r vs %r" % (
         what, np.uint32(gbits).view(np.float32), og)

@@ -295,6 +295,23 @@ constexpr int kFuMaxWaves = 16;
 constexpr int fp4_waves(int M) { return M == 1 ? 3 : 9; }
 enum FuMode { kFuDynamic = 0, kFuGiven = 1, kFuPrepared = 2 };
 
+// Set i of wave w among NS sets of 64 blocks (NS or more: none).  Fewer than
+// four waves take every W-th set.  With four or more, the sets go to the
+// four SIMDs in turn (wave w runs on SIMD w % 4) and then to the waves of
+// each SIMD in turn, so the SIMDs get equal shares of the encode.
+constexpr int fp4_set(int W, int w, int i) {
+  return W < 4 ? w + W * i : (w & 3) + 4 * ((w >> 2) + (W - (w & 3) + 3) / 4 * i);
+}
+constexpr int fp4_sets_per_wave(int W, int NS) {
+  int most = 0;
+  for (int w = 0; w < W; ++w) {
+    int n = 0;
+    while (fp4_set(W, w, n) < NS) ++n;
+    most = most > n ? most : n;
+  }
+  return most;
+}
+
 template <int NCK, int kM, int kW, int kMode, bool kYBf16>
 __global__ __launch_bounds__(64 * kW) void gemv_fp4_kernel(const uint8_t* __restrict__ x, size_t ldx,
                                                                  const float* __restrict__ gs_in,
@@ -311,7 +328,7 @@ __global__ __launch_bounds__(64 * kW) void gemv_fp4_kernel(const uint8_t* __rest
   static_assert(kW >= 1 && kW <= kFuMaxWaves, "waves");
   constexpr int SPR = NB / 64;                          // sets per row
   constexpr int NS = kM * SPR;                          // sets over all rows
-  constexpr int SPW = (NS + kW - 1) / kW;   // sets of the busiest wave
+  constexpr int SPW = fp4_sets_per_wave(kW, NS);        // sets of the busiest wave
   constexpr bool kStage = kMode != kFuPrepared && kM == 1;  // the bf16 row staged in LDS
   constexpr uint32_t kh = K / 2, ks = K / 16;
   constexpr uint32_t kScBytes = (16u * ks + 1023u) / 1024u * 1024u;
@@ -391,7 +408,7 @@ __global__ __launch_bounds__(64 * kW) void gemv_fp4_kernel(const uint8_t* __rest
     const uint4* xs = reinterpret_cast<const uint4*>(xrow);
 #pragma unroll
     for (int i = 0; i < SPW; ++i) {
-      const int j = wave + kW * i;
+      const int j = fp4_set(kW, wave, i);
       if (j >= NS) continue;
       const uint4 a = xs[2 * (lane + 64 * j)], b = xs[2 * (lane + 64 * j) + 1];
       xw[i][0] = a.x; xw[i][1] = a.y; xw[i][2] = a.z; xw[i][3] = a.w;
@@ -402,7 +419,7 @@ __global__ __launch_bounds__(64 * kW) void gemv_fp4_kernel(const uint8_t* __rest
     // its absmax repeats a max, and it is not encoded
 #pragma unroll
     for (int i = 0; i < SPW; ++i) {
-      const int j = wave + kW * i < NS ? wave + kW * i : NS - 1;
+      const int j = fp4_set(kW, wave, i) < NS ? fp4_set(kW, wave, i) : NS - 1;
       const uint4* p = reinterpret_cast<const uint4*>(x + (size_t)(j / SPR) * ldx) + 2 * (64 * (j % SPR) + lane);
       const uint4 a = p[0], b = p[1];
       xw[i][0] = a.x; xw[i][1] = a.y; xw[i][2] = a.z; xw[i][3] = a.w;
@@ -428,7 +445,7 @@ __global__ __launch_bounds__(64 * kW) void gemv_fp4_kernel(const uint8_t* __rest
       uint32_t m = 0;
 #pragma unroll
       for (int i = 0; i < SPW; ++i) {
-        if (kStage && wave + kW * i >= NS) continue;
+        if (kStage && fp4_set(kW, wave, i) >= NS) continue;
         const uint32_t a = words_absmax_bits<true>(xw[i]);
         m = m > a ? m : a;
       }
@@ -446,7 +463,7 @@ __global__ __launch_bounds__(64 * kW) void gemv_fp4_kernel(const uint8_t* __rest
     const FastScale fsc = fast_scale(gs);
 #pragma unroll
     for (int i = 0; i < SPW; ++i) {
-      const int j = wave + kW * i;
+      const int j = fp4_set(kW, wave, i);
       if (j >= NS) continue;
       const int b = lane + 64 * j;
       float xv[16];

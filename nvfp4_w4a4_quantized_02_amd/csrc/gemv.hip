@@ -557,17 +557,38 @@ __global__ __launch_bounds__(64 * kW) void gemv_fp4_kernel(const uint8_t* __rest
       uint2 xv[2];
       uint32_t xsc_b[2][kQ], swb[2][kQ][4];
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        xv[h] = xcodes[16 * c + 8 * h + xbase];
+      for (int h = 0; h < 2; ++h) xv[h] = xcodes[16 * c + 8 * h + xbase];
+      if constexpr (kRM == 4) {
+        // the chunk's 16 scale bytes of activation row mc and of weight rows
+        // 4g .. 4g+3, one read each: the block of MFMA (H, Q) in this lane's
+        // column is byte bl of dword 2H + Q
+        const uint4 xr = *reinterpret_cast<const uint4*>(xsb + sxbase - bl + 16u * (uint32_t)c);
+        uint4 wr[4];
 #pragma unroll
-        for (int q = 0; q < kQ; ++q) {
-          const uint32_t o = 16u * (uint32_t)c + 8u * (uint32_t)h + (uint32_t)(kBPM * q);
-          xsc_b[h][q] = xsb[sxbase + o];
+        for (int j = 0; j < 4; ++j)
+          wr[j] = *reinterpret_cast<const uint4*>(sc_lds + srow - bl + (uint32_t)j * ks + 16u * (uint32_t)c);
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        const uint32_t sh = 8u * (uint32_t)bl;
 #pragma unroll
-          for (int j = 0; j < 4; ++j) swb[h][q][j] = sc_lds[srow + (uint32_t)j * ks + o];
-        }
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int q = 0; q < kQ; ++q) {
+            xsc_b[h][q] = dword_of(xr, 2 * h + q) >> sh;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) swb[h][q][j] = dword_of(wr[j], 2 * h + q) >> sh;
+          }
+      } else {
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int q = 0; q < kQ; ++q) {
+            const uint32_t o = 16u * (uint32_t)c + 8u * (uint32_t)h + (uint32_t)(kBPM * q);
+            xsc_b[h][q] = xsb[sxbase + o];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) swb[h][q][j] = sc_lds[srow + (uint32_t)j * ks + o];
+          }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       }
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       issue(c + D, d);
 #pragma unroll
       for (int h = 0; h < 2; ++h)
@@ -577,7 +598,7 @@ __global__ __launch_bounds__(64 * kW) void gemv_fp4_kernel(const uint8_t* __rest
                            (int)(xv[h].y & mk[q][1]), 0, 0, 0, 0};
           const floatx4 acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
               A[h], B, floatx4{0.0f, 0.0f, 0.0f, 0.0f}, 4, 4, 0, 127, 0, 127);
-          const float sx = __builtin_amdgcn_cvt_f32_fp8((int)xsc_b[h][q], 0);
+          const float sx = __builtin_amdgcn_cvt_f32_fp8((int)xsc_b[h][q], 0);  // byte 0
 #pragma unroll
           for (int j = 0; j < 4; ++j)
             part[j] = __builtin_fmaf(acc[j] * sx, __builtin_amdgcn_cvt_f32_fp8((int)(swb[h][q][j] & 0x7Fu), 0),

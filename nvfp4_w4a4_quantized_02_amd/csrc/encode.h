@@ -236,14 +236,15 @@ __device__ __forceinline__ uint32_t exact_codes8(const float (&x)[16], int base,
   return r;
 }
 
-// x: the 16 values as fp32 (bf16 widened exactly); bm: fp32 bits of the
-// largest |x|.  On success writes the scale byte and the codes; a half-block
-// with an element on or next to a decision point is settled by division.
-// Returns false only
-// for a tensor scale out of the fast range, a subnormal es or a reciprocal
-// that overflows (see above); the block then takes the exact path.
-__device__ __forceinline__ bool encode_block_fast(const float (&x)[16], uint32_t bm, const FastScale& f,
-                                                  uint32_t& sb, uint32_t& code_lo, uint32_t& code_hi) {
+// The fast encoder without its code fix-ups: writes the scale byte (settled
+// by division when its bracket straddles a midpoint), es, and the codes of
+// each half-block (8 elements) whose brackets agree; bit h of `straddle` is
+// set for a half whose brackets differ somewhere, whose codes are then
+// exact_codes8(x, 8h, es).  Returns false (outputs undefined) when the block
+// takes the exact path (see encode_block_fast).
+__device__ __forceinline__ bool encode_block_fast_parts(const float (&x)[16], uint32_t bm, const FastScale& f,
+                                                        uint32_t& sb, uint32_t& code_lo, uint32_t& code_hi,
+                                                        float& es_out, uint32_t& straddle) {
   // Both scale bracket ends in one hardware E4M3 conversion (OCP E4M3FN,
   // round to nearest even, subnormals kept; clamped first so it saturates
   // at 448 = 0x7E).  When they differ, the quotient sits on or next to an
@@ -267,11 +268,26 @@ __device__ __forceinline__ bool encode_block_fast(const float (&x)[16], uint32_t
   uint32_t hi_a = cvt_fp4x8(x, 8, ylo);
   const uint32_t hi_b = cvt_fp4x8(x, 8, yhi);
   const bool es_ok = (es == 0.0f) || (es >= 0x1p-126f && y < 0x1p+126f);
-  if (!(f.ok && es_ok)) return false;
-  if (__builtin_expect(lo_a != lo_b, 0)) lo_a = exact_codes8(x, 0, es);
-  if (__builtin_expect(hi_a != hi_b, 0)) hi_a = exact_codes8(x, 8, es);
   code_lo = lo_a;
   code_hi = hi_a;
+  es_out = es;
+  straddle = (lo_a != lo_b ? 1u : 0u) | (hi_a != hi_b ? 2u : 0u);
+  return f.ok && es_ok;
+}
+
+// x: the 16 values as fp32 (bf16 widened exactly); bm: fp32 bits of the
+// largest |x|.  On success writes the scale byte and the codes; a half-block
+// with an element on or next to a decision point is settled by division.
+// Returns false only
+// for a tensor scale out of the fast range, a subnormal es or a reciprocal
+// that overflows (see above); the block then takes the exact path.
+__device__ __forceinline__ bool encode_block_fast(const float (&x)[16], uint32_t bm, const FastScale& f,
+                                                  uint32_t& sb, uint32_t& code_lo, uint32_t& code_hi) {
+  float es;
+  uint32_t straddle;
+  if (!encode_block_fast_parts(x, bm, f, sb, code_lo, code_hi, es, straddle)) return false;
+  if (__builtin_expect(straddle & 1u, 0)) code_lo = exact_codes8(x, 0, es);
+  if (__builtin_expect(straddle & 2u, 0)) code_hi = exact_codes8(x, 8, es);
   return true;
 }
 

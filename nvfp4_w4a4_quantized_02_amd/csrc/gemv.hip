@@ -460,7 +460,18 @@ __global__ __launch_bounds__(64 * kW) void gemv_fp4_kernel(const uint8_t* __rest
     // blocks, so every wave has read its blocks first (the barrier above, or
     // this one with a given scale).
     if constexpr (kStage && kMode == kFuGiven) asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    // Half-blocks whose code brackets straddle a decision point (nearly
+    // every set has one in some lane on decode rows with outlier channels)
+    // are settled after the fast pass: each lane keeps up to two of them
+    // (their bf16 words, es and position; picked with compile-time set
+    // indices, so the sets stay in registers), settled in two passes over
+    // the wave, so the divisions run once or twice per wave rather than once
+    // per set.  A lane's third one is settled at once.
     const FastScale fsc = fast_scale(gs);
+    uint32_t dw[2][4] = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}};
+    float des[2] = {0.0f, 0.0f};
+    uint32_t dpos[2] = {0u, 0u};  // 2 * block + half
+    uint32_t nd = 0;
 #pragma unroll
     for (int i = 0; i < SPW; ++i) {
       const int j = fp4_set(kW, wave, i);
@@ -468,11 +479,48 @@ __global__ __launch_bounds__(64 * kW) void gemv_fp4_kernel(const uint8_t* __rest
       const int b = lane + 64 * j;
       float xv[16];
       words_to_floats<true>(xw[i], xv);
-      uint32_t sb, lo, hi;
-      if (!encode_block_fast(xv, words_absmax_bits<true>(xw[i]), fsc, sb, lo, hi))
+      uint32_t sb, lo, hi, straddle;
+      float es;
+      if (!encode_block_fast_parts(xv, words_absmax_bits<true>(xw[i]), fsc, sb, lo, hi, es, straddle)) {
         sb = encode_block_exact(xv, gs, lo, hi);
+        straddle = 0;
+      }
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        if (straddle & (1u << h)) {
+          if (nd < 2) {
+#pragma unroll
+            for (int d = 0; d < 2; ++d)
+              if (nd == (uint32_t)d) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) dw[d][q] = xw[i][4 * h + q];
+                des[d] = es;
+                dpos[d] = 2u * (uint32_t)b + (uint32_t)h;
+              }
+          } else {
+            const uint32_t c = exact_codes8(xv, 8 * h, es);
+            if (h) hi = c; else lo = c;
+          }
+          ++nd;
+        }
+      }
       xcodes[b] = make_uint2(lo, hi);
       xsb[b] = (uint8_t)sb;
+    }
+    uint32_t* xcw = reinterpret_cast<uint32_t*>(xcodes);
+#pragma unroll
+    for (int d = 0; d < 2; ++d) {
+      if (__ballot(nd > (uint32_t)d) && nd > (uint32_t)d) {
+        float x8[16];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          x8[2 * q] = __uint_as_float(dw[d][q] << 16);
+          x8[2 * q + 1] = __uint_as_float(dw[d][q] & 0xFFFF0000u);
+          x8[8 + 2 * q] = 0.0f;
+          x8[9 + 2 * q] = 0.0f;
+        }
+        xcw[dpos[d]] = exact_codes8(x8, 0, des[d]);
+      }
     }
   }
   // 3. the quantized rows complete and visible to every wave (the transfers

@@ -106,6 +106,19 @@ def test_gemv_shapes(nv, orc, M, N, K, out):
     check_gemm(_run(nv, p, od), _full_ref(orc, p), out == "bf16", "gemv %dx%dx%d" % (M, N, K))
 
 
+# More small-M shapes over the kernels that serve them: K-split (K = 1536,
+# 2560, 4096, 5120: three to ten waves of 512 k), shared (K = 3840) and
+# general (K = 640, 1920); ragged N and padded activation rows.
+@pytest.mark.parametrize("M,N,K", [(16, 520, 640), (7, 300, 1920), (11, 33, 2560), (12, 260, 3840),
+                                   (16, 1000, 5120), (6, 300, 1536), (16, 200, 4096)])
+@pytest.mark.parametrize("out", ["bf16", "f32"])
+def test_gemv_small_m_shapes(nv, orc, M, N, K, out):
+    p = workloads.prefill(M=M, K=K, N=N)
+    print("case: gemv small-M M=%d N=%d K=%d %s" % (M, N, K, out), flush=True)
+    od = torch.bfloat16 if out == "bf16" else torch.float32
+    check_gemm(_run(nv, p, od), _full_ref(orc, p), out == "bf16", "gemv small-M %dx%dx%d" % (M, N, K))
+
+
 def test_gemm_fp32_activations(nv, orc):
     p = workloads.tiny(M=100, K=256, N=200)
     check_gemm(_run(nv, p, torch.float32), _full_ref(orc, p), False, "fp32 X, M=100")

@@ -30,10 +30,12 @@ def _weight(orc, w):
 
 
 # (M, N, K): streaming (M <= 4, K % 256 == 0), K-split (4 < M <= 16,
-# K % 512 == 0), shared (4 < M <= 16, K % 256 == 0), general (other K),
+# K % 512 == 0, K <= 5120), shared (4 < M <= 16, K % 256 == 0), general
+# (other K),
 # tile GEMM (M > 16) with and without a split-K tail
 SHAPES = [(1, 300, 512), (2, 520, 5120), (4, 40, 256), (3, 200, 320), (1, 7, 64),
           (5, 520, 5120), (16, 520, 512), (13, 129, 768), (9, 100, 1088), (16, 129, 768),
+          (16, 520, 640), (7, 300, 1920), (16, 200, 4096),
           (17, 64, 64), (100, 200, 320), (300, 257, 1088), (513, 300, 256)]
 
 

@@ -603,7 +603,7 @@ __global__ __launch_bounds__(64 * kW) void gemv_fp4_kernel(const uint8_t* __rest
         part[j] = __builtin_fmaf(acc[j] * sx, __builtin_amdgcn_cvt_f32_fp8((int)(swb[j] & 0x7Fu), 0), part[j]);
     } else {
       uint2 xv[2];
-      uint32_t xsc_b[2][kQ], swb[2][kQ][4];
+      float sxf[2][kQ], swf[2][kQ][4];  // the E4M3 values of each MFMA's two block scales
 #pragma unroll
       for (int h = 0; h < 2; ++h) xv[h] = xcodes[16 * c + 8 * h + xbase];
       if constexpr (kRM == 4) {
@@ -616,16 +616,26 @@ __global__ __launch_bounds__(64 * kW) void gemv_fp4_kernel(const uint8_t* __rest
         for (int j = 0; j < 4; ++j)
           wr[j] = *reinterpret_cast<const uint4*>(sc_lds + srow - bl + (uint32_t)j * ks + 16u * (uint32_t)c);
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        const uint32_t sh = 8u * (uint32_t)bl;
+        // byte bl of dwords 2H and 2H + 1 side by side (one byte permute
+        // with a per-lane selector), both decoded by one conversion
+        const uint32_t sel = (uint32_t)bl | ((4u + (uint32_t)bl) << 8) | 0x0C0C0000u;
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
+        for (int h = 0; h < 2; ++h) {
+          const auto x2 = __builtin_amdgcn_cvt_pk_f32_fp8(
+              (int)__builtin_amdgcn_perm(dword_of(xr, 2 * h + 1), dword_of(xr, 2 * h), sel), false);
+          sxf[h][0] = x2[0];
+          sxf[h][1] = x2[1];
 #pragma unroll
-          for (int q = 0; q < kQ; ++q) {
-            xsc_b[h][q] = dword_of(xr, 2 * h + q) >> sh;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) swb[h][q][j] = dword_of(wr[j], 2 * h + q) >> sh;
+          for (int j = 0; j < 4; ++j) {
+            const auto w2 = __builtin_amdgcn_cvt_pk_f32_fp8(
+                (int)(__builtin_amdgcn_perm(dword_of(wr[j], 2 * h + 1), dword_of(wr[j], 2 * h), sel) & 0x7F7Fu),
+                false);
+            swf[h][0][j] = w2[0];
+            swf[h][1][j] = w2[1];
           }
+        }
       } else {
+        uint32_t xsc_b[2][kQ], swb[2][kQ][4];
 #pragma unroll
         for (int h = 0; h < 2; ++h)
 #pragma unroll
@@ -636,6 +646,14 @@ __global__ __launch_bounds__(64 * kW) void gemv_fp4_kernel(const uint8_t* __rest
             for (int j = 0; j < 4; ++j) swb[h][q][j] = sc_lds[srow + (uint32_t)j * ks + o];
           }
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int q = 0; q < kQ; ++q) {
+            sxf[h][q] = __builtin_amdgcn_cvt_f32_fp8((int)xsc_b[h][q], 0);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) swf[h][q][j] = __builtin_amdgcn_cvt_f32_fp8((int)(swb[h][q][j] & 0x7Fu), 0);
+          }
       }
       issue(c + D, d);
 #pragma unroll
@@ -646,11 +664,8 @@ __global__ __launch_bounds__(64 * kW) void gemv_fp4_kernel(const uint8_t* __rest
                            (int)(xv[h].y & mk[q][1]), 0, 0, 0, 0};
           const floatx4 acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
               A[h], B, floatx4{0.0f, 0.0f, 0.0f, 0.0f}, 4, 4, 0, 127, 0, 127);
-          const float sx = __builtin_amdgcn_cvt_f32_fp8((int)xsc_b[h][q], 0);  // byte 0
 #pragma unroll
-          for (int j = 0; j < 4; ++j)
-            part[j] = __builtin_fmaf(acc[j] * sx, __builtin_amdgcn_cvt_f32_fp8((int)(swb[h][q][j] & 0x7Fu), 0),
-                                     part[j]);
+          for (int j = 0; j < 4; ++j) part[j] = __builtin_fmaf(acc[j] * sxf[h][q], swf[h][q][j], part[j]);
         }
     }
   }
